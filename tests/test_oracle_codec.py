@@ -1,0 +1,133 @@
+"""Pins for the oracle codec (quantize / restore / scale storage).
+
+Every check here is fixed by something other than the oracle itself: the
+worked grid examples printed in "KV Cache quantization and compression"
+section 03, the scale-shape and zero-range contracts of "KV Cache
+Quantization Strategies" Step 4 tests, the definition of round-half-to-even,
+or closed-form bounds of a uniform quantizer.
+"""
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st
+from hypothesis.extra import numpy as hnp
+
+from oracle import codec
+
+
+def test_key_grid_example(golden):
+    g = golden("worked_example_sec03.json")
+    scale = np.float32(1.0 / g["k_grid_step"])        # inverse step
+    codes = codec.quantize_with_scale(np.array(g["k"], np.float32), scale, qmax=127)
+    assert codes.tolist() == [1, 1]
+    k_hat = codec.restore(codes, np.float32(scale), dtype=np.float64)
+    assert np.allclose(k_hat, g["k_hat"], rtol=0, atol=1e-7)
+
+
+def test_value_grid_example(golden):
+    g = golden("worked_example_sec03.json")
+    scale = np.float32(1.0 / g["v_grid_step"])
+    codes = codec.quantize_with_scale(np.array(g["v_only_values"], np.float32), scale, qmax=127)
+    assert codes.tolist() == [2, 6]
+    v_hat = codec.restore(codes, np.float32(scale), dtype=np.float64)
+    assert v_hat.tolist() == g["v_hat"]
+    w = np.array(g["v_only_weights"])
+    assert abs(w @ np.array(g["v_only_values"]) - g["v_only_output_before"]) < 1e-12
+    assert abs(w @ v_hat - g["v_only_output_after"]) < 1e-12
+
+
+def test_round_half_to_even_ties():
+    # scale = 7 / 7 = 1 exactly, so every product below is an exact tie or integer.
+    x = np.array([7, 2.5, -2.5, 0.5, 1.5, -0.5, 3.5], np.float32).reshape(1, 1, 1, 7)
+    codes, scale = codec.quantize_value_per_token(x, qmax=7)
+    assert scale.ravel().tolist() == [1.0]
+    assert codes.ravel().tolist() == [7, 2, -2, 0, 2, 0, 4]
+
+
+def test_scale_shapes_follow_the_axes():
+    rng = np.random.default_rng(0)
+    key = rng.standard_normal((1, 2, 5, 8)).astype(np.float32)
+    k_q, k_s = codec.quantize_key_per_channel(key)
+    v_q, v_s = codec.quantize_value_per_token(key)
+    assert k_q.shape == key.shape and k_s.shape == (1, 2, 1, 8)
+    assert v_q.shape == key.shape and v_s.shape == (1, 2, 5, 1)
+
+
+def test_axes_reduce_over_the_right_dimension():
+    # One huge Key token must set every channel's scale; one huge Value
+    # channel must set every token's scale -- and nothing else.
+    x = np.ones((1, 1, 4, 3), np.float32)
+    x[0, 0, 2, :] = 70.0
+    _, k_s = codec.quantize_key_per_channel(x, qmax=7)
+    assert np.all(k_s == np.float32(7) / np.float32(70))
+    _, v_s = codec.quantize_value_per_token(x, qmax=7)
+    assert v_s.ravel().tolist() == [7.0, 7.0, np.float32(7) / np.float32(70), 7.0]
+
+
+def test_rank_is_checked():
+    with pytest.raises(ValueError):
+        codec.quantize_key_per_channel(np.zeros((2, 3, 4), np.float32))
+    with pytest.raises(ValueError):
+        codec.quantize_value_per_token(np.zeros((2, 3, 4), np.float32))
+
+
+@pytest.mark.parametrize("storage", ["fp32", "fp16"])
+def test_zero_range_scale_is_finite(storage):
+    zeros = np.zeros((1, 1, 3, 4), np.float32)
+    k_q, k_s = codec.quantize_key_per_channel(zeros, storage=storage)
+    v_q, v_s = codec.quantize_value_per_token(zeros, storage=storage)
+    assert np.isfinite(k_s.astype(np.float64)).all() and np.isfinite(v_s.astype(np.float64)).all()
+    assert not k_q.any() and not v_q.any()
+    assert not codec.restore(k_q, k_s, dtype=np.float64).any()
+    if storage == "fp16":
+        # 7 / 1e-8 overflows fp16; the stored scale saturates at the largest finite fp16.
+        assert k_s.dtype == np.float16 and np.all(k_s == np.float16(65504))
+
+
+def test_fp16_storage_rounding_and_saturation():
+    # Normal range: the stored scale is within half an fp16 ulp (2^-11 relative).
+    absmax = np.array([0.5, 1.0, 2.8, 3.3, 29.0, 1000.0], np.float32)
+    s16 = codec.scale_from_absmax(absmax, 7, 1e-8, "fp16").astype(np.float64)
+    s32 = (np.float32(7) / absmax).astype(np.float64)
+    assert np.all(np.abs(s16 - s32) <= s32 * 2.0 ** -11)
+    # A tiny range saturates instead of overflowing.
+    tiny = codec.scale_from_absmax(np.float32(1e-6), 7, 1e-8, "fp16")
+    assert tiny == np.float16(65504)
+    # Exactly representable scales are kept exactly.
+    assert codec.scale_from_absmax(np.float32(7.0), 7, 1e-8, "fp16") == np.float16(1.0)
+    assert codec.scale_from_absmax(np.float32(0.5), 1, 1e-8, "fp16") == np.float16(2.0)
+
+
+def test_overwritten_scale_scales_old_values():
+    # "KV Cache quantization and compression", section 02: codes made with step
+    # 0.1 and read back with step 0.2 come back exactly doubled.
+    x = np.array([0.3, -0.7, 1.2], np.float32)
+    codes = codec.quantize_with_scale(x, np.float32(10.0), qmax=127)
+    good = codec.restore(codes, np.float32(10.0), dtype=np.float64)
+    bad = codec.restore(codes, np.float32(5.0), dtype=np.float64)
+    assert np.array_equal(bad, 2 * good)
+
+
+@settings(max_examples=60, deadline=None)
+@given(
+    x=hnp.arrays(np.float32, (2, 3, 5, 8),
+                 elements=st.floats(-50, 50, width=32, allow_nan=False)),
+    qmax=st.sampled_from([1, 7, 127]),
+    storage=st.sampled_from(["fp32", "fp16"]),
+    axis=st.sampled_from(["key", "value"]),
+)
+def test_uniform_quantizer_bounds(x, qmax, storage, axis):
+    quant = codec.quantize_key_per_channel if axis == "key" else codec.quantize_value_per_token
+    codes, scale = quant(x, qmax=qmax, storage=storage)
+    s = np.broadcast_to(scale.astype(np.float64), x.shape)
+    assert np.all(np.abs(codes.astype(np.int32)) <= qmax)
+    # Half a step of error, plus the float32 rounding of the product x * s.
+    err = np.abs(x.astype(np.float64) - codes / s)
+    assert np.all(err <= 0.5 / s * (1 + 1e-6) + 1e-30)
+    # The element that sets a channel's / token's range lands on +-qmax
+    # unless the scale saturated (fp16 storage of a tiny range).
+    red = -2 if axis == "key" else -1
+    amax = np.abs(x).max(axis=red, keepdims=True)
+    is_max = (np.abs(x) == amax) & (amax > 0)
+    unsaturated = np.broadcast_to(scale.astype(np.float64) < 65504, x.shape)
+    hit = np.abs(codes.astype(np.int32)) == qmax
+    assert np.all(hit[is_max & unsaturated])
