@@ -1,0 +1,201 @@
+/*
+ * libkvq -- KIVI-style asymmetric-axis quantized KV cache for AMD MI355X (gfx950).
+ *
+ * C ABI.  Plain pointers and sizes only; no C++ types and no exceptions cross
+ * this boundary.  Device pointers are caller-owned (allocated however the
+ * caller likes, e.g. through torch); the library never allocates, frees or
+ * synchronizes.  Every call validates all arguments before it enqueues any
+ * work; on error it returns a status, enqueues nothing and leaves the
+ * caller's kvq_state unchanged.  All device work is enqueued on the caller's
+ * HIP stream (passed as an opaque hipStream_t, NULL = the null stream) and
+ * is asynchronous.
+ *
+ * The method ("KV Cache Quantization Strategies", Steps 2-4):
+ *   - Keys are quantized per channel: absmax over the token axis, one scale
+ *     per channel per segment ([..., 1, head_dim]).
+ *   - Values are quantized per token: absmax over head_dim, one scale per
+ *     token ([..., tokens, 1]).
+ *   - scale = qmax / max(absmax, eps) (an inverse step, computed in fp32,
+ *     stored as fp16 clamped to 65504); code = clamp(round_half_even(
+ *     fp32(x) * scale), -qmax, qmax); restore = code / max(scale, eps).
+ *   - The newest tokens stay in a high-precision residual window of
+ *     ``residual`` tokens; only tokens that overflow it are quantized, as new
+ *     segments appended after the existing ones, which are never rewritten.
+ *
+ * Data layout in device memory (per (batch b, KV head h) "stream"; all
+ * arrays are dense, row-major, in the order given):
+ *   W = head_dim * code_bits / 8 bytes per token row; C = capacity.
+ *   k_codes : uint8 [batch, kv_heads, C * W].  Token t, channel c: byte
+ *             (t/64)*64*W + (r/16)*1024 + (t%64)*16 + r%16, r = c*bits/8,
+ *             field at bit (c*bits)%8.
+ *   v_codes : uint8 [batch, kv_heads, C * W].  Token t, channel c: byte
+ *             (t/64)*64*W + c*8*bits + ((t%64)*bits)/8, field at bit
+ *             ((t%64)*bits)%8.
+ *             Fields are ``bits``-bit two's complement (int8 for bits = 8).
+ *   k_scale : fp16 [batch, kv_heads, max_segments, head_dim], one row per
+ *             segment.  With group G > 0 segment s holds tokens [sG, (s+1)G).
+ *   v_scale : fp16 [batch, kv_heads, C], one per quantized token.
+ *   k_tail, v_tail : kv_dtype [batch, kv_heads, ring, head_dim]; the tail
+ *             token at absolute position p sits in slot p % ring, with
+ *             ring = residual + group (group > 0) or residual (group == 0).
+ *   seg_index : int32 [C]; with group == 0 the segment id of each quantized
+ *             token (shared by all batch rows / heads); unused when group > 0.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kvq_status {
+  KVQ_OK = 0,
+  KVQ_EINVAL = 1,     /* bad argument, shape or configuration            */
+  KVQ_ECAPACITY = 2,  /* append would exceed capacity or max_segments     */
+  KVQ_EWORKSPACE = 3, /* workspace missing or smaller than required       */
+  KVQ_EDEVICE = 4     /* a HIP launch or device query failed              */
+} kvq_status;
+
+typedef enum kvq_dtype {
+  KVQ_BF16 = 0,  /* bfloat16 K/V/Q                                         */
+  KVQ_F32 = 1    /* float32 K/V/Q (the exercise's teaching case)          */
+} kvq_dtype;
+
+/* Static description of one cache (one layer).  Source: the exercise's
+ * class constructor (qmax, eps) and ``append_and_partition``'s
+ * residual_length; ``group`` and ``code_bits`` are the library's storage
+ * choices (whole-group flushes; packed fields). */
+typedef struct kvq_config {
+  int32_t batch;        /* >= 1                                                   */
+  int32_t kv_heads;     /* >= 1                                                   */
+  int32_t head_dim;     /* 16, 32, 64 or 128; head_dim * code_bits % 128 == 0     */
+  int32_t capacity;     /* max quantized tokens per sequence; multiple of 64      */
+  int32_t code_bits;    /* 8, 4 or 2                                              */
+  int32_t qmax;         /* 1 .. 2^(code_bits-1) - 1 (e.g. 127, 7, 1)              */
+  int32_t residual;     /* residual window R > 0                                  */
+  int32_t group;        /* G: 0 = one segment per flush (the exercise's rule),    */
+                        /*    else a multiple of 64: flush whole groups of G      */
+  int32_t max_segments; /* rows of k_scale; >= capacity / group when group > 0    */
+  int32_t kv_dtype;     /* kvq_dtype of appended K/V, of the tail and of queries  */
+  float eps;            /* range floor, 1e-8 in the exercise                      */
+} kvq_config;
+
+/* Host-side token accounting, owned by the caller and updated by kvq_append
+ * only when it returns KVQ_OK.  Mirrors the counters returned by the
+ * exercise's ``append_and_partition``.  Zero-initialise for an empty cache. */
+typedef struct kvq_state {
+  int64_t quantized;    /* tokens in the quantized prefix                        */
+  int64_t tail;         /* tokens in the high-precision tail                      */
+  int64_t total;        /* quantized + tail                                       */
+  int64_t flushed_last; /* tokens flushed by the most recent append               */
+  int64_t segments;     /* quantized segments (rows of k_scale in use)            */
+} kvq_state;
+
+/* Caller-owned device buffers of one cache; sizes from kvq_buffer_sizes. */
+typedef struct kvq_cache {
+  void* k_codes;
+  void* v_codes;
+  void* k_scale;
+  void* v_scale;
+  void* k_tail;
+  void* v_tail;
+  void* seg_index;      /* may be NULL when group > 0                             */
+} kvq_cache;
+
+typedef struct kvq_sizes {
+  size_t k_codes, v_codes, k_scale, v_scale, k_tail, v_tail, seg_index; /* bytes */
+  int32_t ring;         /* tail ring slots                                        */
+  int32_t row_bytes;    /* W                                                      */
+} kvq_sizes;
+
+/* Validate a configuration and report the byte size of every buffer.
+ * Errors: KVQ_EINVAL for an unsupported configuration. */
+kvq_status kvq_buffer_sizes(const kvq_config* cfg, kvq_sizes* out);
+
+/* Pure host planning of one append (no device work): the state the cache
+ * would have after appending n_new tokens.  Token accounting of the
+ * exercise's Step 4 (TODO 3): overflow = max(tail + n_new - residual, 0);
+ * flushed = overflow (group == 0) or (overflow / group) * group; quantized
+ * += flushed; tail = tail + n_new - flushed; segments += 1 (group == 0,
+ * flushed > 0) or flushed / group.
+ * Errors: KVQ_EINVAL (n_new < 0, bad state), KVQ_ECAPACITY. */
+kvq_status kvq_plan_append(const kvq_config* cfg, const kvq_state* st, int64_t n_new,
+                           kvq_state* next);
+
+/* Append n_new tokens (the exercise's ``append_and_partition``, and the
+ * "encode, then cache.append" write of "KV Cache quantization and
+ * compression", section 02).
+ *   k_new, v_new : device, kv_dtype [batch, kv_heads, n_new, head_dim].
+ * Tokens that overflow the residual window are quantized in place into the
+ * next segment(s) (Keys per channel, Values per token) straight from the old
+ * tail and from k_new / v_new, with no concatenation; the tokens that remain
+ * in the window are copied into the tail ring.  Earlier segments, their
+ * scales and the surviving tail slots are never written.  n_new == 0 is a
+ * valid no-op.  On KVQ_OK *st is advanced exactly as kvq_plan_append says.
+ * Errors: KVQ_EINVAL, KVQ_ECAPACITY, KVQ_EDEVICE. */
+kvq_status kvq_append(const kvq_config* cfg, kvq_state* st, const kvq_cache* cache,
+                      const void* k_new, const void* v_new, int64_t n_new, void* stream);
+
+/* Bytes of device workspace needed by kvq_decode_attn (tq = 1) or
+ * kvq_block_attn (tq = query block length) for q_heads query heads.
+ * Errors: KVQ_EINVAL. */
+kvq_status kvq_workspace_size(const kvq_config* cfg, int32_t q_heads, int32_t tq,
+                              size_t* bytes);
+
+/* Prepare a freshly allocated workspace (clears its arrival counters with a
+ * fill kernel; no memset node).  Call once per workspace before first use;
+ * the attention kernels leave the counters cleared when they finish.
+ * Errors: KVQ_EINVAL, KVQ_EDEVICE. */
+kvq_status kvq_workspace_init(void* workspace, size_t bytes, void* stream);
+
+/* Single-query grouped-query decode attention over the whole cache
+ * ("KV Cache and autoregressive video generation", section 3.1, incremental
+ * decode o_t = sum_j softmax_j(q_t k_j^T sigma) v_j; query head h reads KV
+ * head h / (q_heads / kv_heads), section 04).  Keys and Values of the
+ * quantized prefix are restored inside the kernel (read path "decode inside
+ * the kernel", "KV Cache quantization and compression", section 06); the
+ * tail is read as stored.  The sequence axis is split across workgroups and
+ * the partial softmax states are merged (flash-decoding split, the former
+ * page, section 05) by the last workgroup of each (batch, KV head).
+ *   q   : device, kv_dtype [batch, q_heads, head_dim]
+ *   out : device, float32 [batch, q_heads, head_dim]
+ *   softmax_scale : sigma (1/sqrt(head_dim) for standard attention)
+ *   num_splits : sequence splits per (batch, KV head); 0 = library's choice
+ *   workspace : from kvq_workspace_size(cfg, q_heads, 1), initialised once
+ * The cache must hold at least one token.  Calls that share a workspace
+ * must be ordered (same stream).
+ * Errors: KVQ_EINVAL, KVQ_EWORKSPACE, KVQ_EDEVICE. */
+kvq_status kvq_decode_attn(const kvq_config* cfg, const kvq_state* st, const kvq_cache* cache,
+                           const void* q, int32_t q_heads, float softmax_scale,
+                           int32_t num_splits, float* out, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/* Causal attention of a block of tq new queries against the cache plus the
+ * block's own keys/values (Attn = softmax(Q K^T sigma + M) V with
+ * M_ij = -inf for j > i, "KV Cache and autoregressive video generation",
+ * section 3.1).  Query i sits at absolute position N + i after the N cached
+ * tokens: it sees all N cached tokens and block tokens 0..i.  The block's
+ * own K/V are read as given and are not appended.  Matrix products run on
+ * the MFMA units over dequantized fp16 tiles.
+ *   q            : device, kv_dtype [batch, tq, q_heads, head_dim]
+ *   k_blk, v_blk : device, kv_dtype [batch, tq, kv_heads, head_dim]
+ *   out          : device, float32 [batch, tq, q_heads, head_dim]
+ *   num_splits   : splits of the cached sequence; 0 = library's choice
+ *   workspace    : from kvq_workspace_size(cfg, q_heads, tq), initialised once
+ * Errors: KVQ_EINVAL, KVQ_EWORKSPACE, KVQ_EDEVICE. */
+kvq_status kvq_block_attn(const kvq_config* cfg, const kvq_state* st, const kvq_cache* cache,
+                          const void* q, const void* k_blk, const void* v_blk, int32_t tq,
+                          int32_t q_heads, float softmax_scale, int32_t num_splits,
+                          float* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static string naming a status code. */
+const char* kvq_status_str(kvq_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

@@ -1,0 +1,215 @@
+"""Python binding of libkvq (KIVI-style quantized KV cache on MI355X).
+
+Argument marshalling only: every step of append, decode attention and block
+attention runs in the HIP kernels of ``libkvq.so`` behind the C ABI declared
+in ``include/kvq.h``.  The functions below carry the C names and take torch
+tensors for device buffers (PyTorch supplies device memory and streams).
+There is no CPU fallback: if the library is not built, or no GPU is present,
+the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvq.so")
+
+KVQ_OK, KVQ_EINVAL, KVQ_ECAPACITY, KVQ_EWORKSPACE, KVQ_EDEVICE = range(5)
+KVQ_BF16, KVQ_F32 = 0, 1
+
+EXPORTED = ("kvq_buffer_sizes", "kvq_plan_append", "kvq_append", "kvq_workspace_size",
+            "kvq_workspace_init", "kvq_decode_attn", "kvq_block_attn", "kvq_status_str")
+
+
+class kvq_config(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "batch", "kv_heads", "head_dim", "capacity", "code_bits", "qmax", "residual", "group",
+        "max_segments", "kv_dtype")] + [("eps", ctypes.c_float)]
+
+
+class kvq_state(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in ("quantized", "tail", "total", "flushed_last", "segments")]
+
+    def as_tuple(self):
+        return (self.quantized, self.tail, self.total, self.flushed_last, self.segments)
+
+
+class kvq_cache(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "k_codes", "v_codes", "k_scale", "v_scale", "k_tail", "v_tail", "seg_index")]
+
+
+class kvq_sizes(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in (
+        "k_codes", "v_codes", "k_scale", "v_scale", "k_tail", "v_tail", "seg_index")] + \
+        [("ring", ctypes.c_int32), ("row_bytes", ctypes.c_int32)]
+
+
+class KVQError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_str(status)}")
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libkvq.so (built in-tree); raise if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                           "or python -m quantized_kv_cache_kvq_amd.build")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER
+    vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    sig = {
+        "kvq_buffer_sizes": [P(kvq_config), P(kvq_sizes)],
+        "kvq_plan_append": [P(kvq_config), P(kvq_state), i64, P(kvq_state)],
+        "kvq_append": [P(kvq_config), P(kvq_state), P(kvq_cache), vp, vp, i64, vp],
+        "kvq_workspace_size": [P(kvq_config), i32, i32, P(sz)],
+        "kvq_workspace_init": [vp, sz, vp],
+        "kvq_decode_attn": [P(kvq_config), P(kvq_state), P(kvq_cache), vp, i32, f32, i32, vp, vp, sz, vp],
+        "kvq_block_attn": [P(kvq_config), P(kvq_state), P(kvq_cache), vp, vp, vp, i32, i32, f32, i32,
+                           vp, vp, sz, vp],
+    }
+    for name, args in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int
+    lib.kvq_status_str.argtypes = [ctypes.c_int]
+    lib.kvq_status_str.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def status_str(status: int) -> str:
+    return load().kvq_status_str(status).decode()
+
+
+def _check(status: int, what: str):
+    if status != KVQ_OK:
+        raise KVQError(status, what)
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("libkvq takes device tensors")
+    if not t.is_contiguous():
+        raise ValueError("libkvq takes contiguous tensors")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def make_config(batch, kv_heads, head_dim, capacity, code_bits, qmax, residual, group,
+                max_segments=None, kv_dtype=KVQ_BF16, eps=1e-8) -> kvq_config:
+    capacity = int(math.ceil(capacity / 64) * 64)
+    if max_segments is None:
+        max_segments = capacity // group if group else max(capacity, 1)
+    return kvq_config(batch, kv_heads, head_dim, capacity, code_bits, qmax, residual, group,
+                      max(max_segments, 1), kv_dtype, eps)
+
+
+# ---- the C entry points, one to one ----------------------------------------------
+
+def kvq_buffer_sizes(cfg: kvq_config) -> kvq_sizes:
+    out = kvq_sizes()
+    _check(load().kvq_buffer_sizes(ctypes.byref(cfg), ctypes.byref(out)), "kvq_buffer_sizes")
+    return out
+
+
+def kvq_plan_append(cfg: kvq_config, st: kvq_state, n_new: int) -> kvq_state:
+    nxt = kvq_state()
+    _check(load().kvq_plan_append(ctypes.byref(cfg), ctypes.byref(st), n_new, ctypes.byref(nxt)),
+           "kvq_plan_append")
+    return nxt
+
+
+def kvq_append(cfg, st, cache: kvq_cache, k_new, v_new, n_new: int, stream=None):
+    _check(load().kvq_append(ctypes.byref(cfg), ctypes.byref(st), ctypes.byref(cache),
+                             _ptr(k_new), _ptr(v_new), n_new, _stream(stream)), "kvq_append")
+
+
+def kvq_workspace_size(cfg, q_heads: int, tq: int) -> int:
+    n = ctypes.c_size_t()
+    _check(load().kvq_workspace_size(ctypes.byref(cfg), q_heads, tq, ctypes.byref(n)),
+           "kvq_workspace_size")
+    return n.value
+
+
+def kvq_workspace_init(ws, stream=None):
+    _check(load().kvq_workspace_init(_ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "kvq_workspace_init")
+
+
+def kvq_decode_attn(cfg, st, cache, q, q_heads, softmax_scale, num_splits, out, ws, stream=None):
+    _check(load().kvq_decode_attn(ctypes.byref(cfg), ctypes.byref(st), ctypes.byref(cache), _ptr(q),
+                                  q_heads, softmax_scale, num_splits, _ptr(out), _ptr(ws),
+                                  ws.numel() * ws.element_size(), _stream(stream)), "kvq_decode_attn")
+
+
+def kvq_block_attn(cfg, st, cache, q, k_blk, v_blk, tq, q_heads, softmax_scale, num_splits,
+                   out, ws, stream=None):
+    _check(load().kvq_block_attn(ctypes.byref(cfg), ctypes.byref(st), ctypes.byref(cache), _ptr(q),
+                                 _ptr(k_blk), _ptr(v_blk), tq, q_heads, softmax_scale, num_splits,
+                                 _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
+                                 _stream(stream)), "kvq_block_attn")
+
+
+# ---- device buffers (plumbing) -----------------------------------------------------
+
+class KVCache:
+    """Caller-side owner of one cache's device buffers and host state."""
+
+    def __init__(self, cfg: kvq_config, device="cuda", zero=True):
+        import torch
+        self.cfg = cfg
+        self.sizes = kvq_buffer_sizes(cfg)
+        alloc = torch.zeros if zero else torch.empty
+        B, H, D = cfg.batch, cfg.kv_heads, cfg.head_dim
+        u8 = torch.uint8
+        self.k_codes = alloc(B, H, self.sizes.k_codes // (B * H), dtype=u8, device=device)
+        self.v_codes = alloc(B, H, self.sizes.v_codes // (B * H), dtype=u8, device=device)
+        self.k_scale = alloc(B, H, cfg.max_segments, D, dtype=torch.float16, device=device)
+        self.v_scale = alloc(B, H, cfg.capacity, dtype=torch.float16, device=device)
+        tdt = torch.bfloat16 if cfg.kv_dtype == KVQ_BF16 else torch.float32
+        self.k_tail = alloc(B, H, self.sizes.ring, D, dtype=tdt, device=device)
+        self.v_tail = alloc(B, H, self.sizes.ring, D, dtype=tdt, device=device)
+        self.seg_index = (alloc(max(cfg.capacity, 1), dtype=torch.int32, device=device)
+                          if cfg.group == 0 else None)
+        self.state = kvq_state()
+        self.c = kvq_cache(*[_ptr(t) for t in (self.k_codes, self.v_codes, self.k_scale,
+                                               self.v_scale, self.k_tail, self.v_tail,
+                                               self.seg_index)])
+
+    def append(self, k_new, v_new, stream=None):
+        kvq_append(self.cfg, self.state, self.c, k_new, v_new, k_new.shape[2], stream)
+
+    def workspace(self, q_heads: int, tq: int = 1, stream=None):
+        import torch
+        n = kvq_workspace_size(self.cfg, q_heads, tq)
+        ws = torch.empty(n // 4, dtype=torch.int32, device=self.k_codes.device)
+        kvq_workspace_init(ws, stream)
+        return ws
+
+    def decode_attn(self, q, out, ws, softmax_scale=None, num_splits=0, stream=None):
+        D = self.cfg.head_dim
+        s = 1.0 / math.sqrt(D) if softmax_scale is None else softmax_scale
+        kvq_decode_attn(self.cfg, self.state, self.c, q, q.shape[1], s, num_splits, out, ws, stream)
+
+    def block_attn(self, q, k_blk, v_blk, out, ws, softmax_scale=None, num_splits=0, stream=None):
+        D = self.cfg.head_dim
+        s = 1.0 / math.sqrt(D) if softmax_scale is None else softmax_scale
+        kvq_block_attn(self.cfg, self.state, self.c, q, k_blk, v_blk, q.shape[1], q.shape[2], s,
+                       num_splits, out, ws, stream)

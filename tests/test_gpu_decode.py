@@ -1,0 +1,121 @@
+"""GPU parity of kvq_decode_attn against the fp64 oracle (max-abs 2e-3).
+
+The oracle attends over the restored codes the oracle itself produced (which
+the append tests show are byte-identical to the device's), so the comparison
+isolates the attention kernel.
+"""
+import numpy as np
+import pytest
+import torch
+
+import kvq_synth as ks
+from harness import Pair, max_abs, note
+
+pytestmark = pytest.mark.gpu
+needs_gpu = pytest.mark.skipif(not torch.cuda.is_available(), reason="no GPU")
+
+TOL = 2e-3
+
+
+def build(w, n, capacity=None, seed=None):
+    p = Pair(w, capacity or (n + 128))
+    s = ks.Stream(w, seed)
+    k, v = ks.kv_pair(s, n)
+    note(f"decode build {w.name} n={n}")
+    p.append(k, v)
+    return p, s
+
+
+@needs_gpu
+def test_tiny_decode_steps():
+    w = ks.TINY
+    p, s = build(w, w.prefill, capacity=128)
+    ws = p.cache.workspace(w.q_heads)
+    for step in range(w.steps):
+        k, v = ks.kv_pair(s, 1)
+        p.append(k, v)
+        q = ks.decode_query(s)
+        note(f"tiny decode step {step}")
+        got, _ = p.decode(q, ws=ws)
+        err = max_abs(got, p.decode_ref(q))
+        assert err <= TOL, (step, err)
+
+
+@needs_gpu
+@pytest.mark.parametrize("D,bits,qmax,g", [(128, 4, 7, 4), (128, 8, 127, 4), (128, 2, 1, 4),
+                                           (64, 4, 7, 2), (64, 2, 1, 8), (32, 4, 7, 1),
+                                           (32, 8, 127, 8), (16, 8, 7, 4), (128, 4, 7, 8)])
+def test_decode_shapes(D, bits, qmax, g):
+    w = ks.small(ks.LLAMA3_DECODE, batch=2, kv_heads=2, q_heads=2 * g, head_dim=D, code_bits=bits,
+                 qmax=qmax, residual=128, group=128 if D != 16 else 64)
+    p, s = build(w, 1000)         # 768 quantized (6 groups) + 232 tail: ragged tail tiles
+    q = ks.decode_query(s)
+    got, _ = p.decode(q)
+    assert max_abs(got, p.decode_ref(q)) <= TOL
+
+
+@needs_gpu
+@pytest.mark.parametrize("splits", [1, 2, 3, 7, 16, 40])
+def test_decode_split_invariance(splits):
+    w = ks.small(ks.LLAMA3_DECODE, batch=2, kv_heads=2, q_heads=8)
+    p, s = build(w, 1500)
+    q = ks.decode_query(s)
+    ref = p.decode_ref(q)
+    ws = p.cache.workspace(8)
+    note(f"decode splits={splits}")
+    got, _ = p.decode(q, num_splits=splits, ws=ws)
+    assert max_abs(got, ref) <= TOL
+    # the workspace counters are left cleared: a second call on it is still right
+    got2, _ = p.decode(q, num_splits=splits, ws=ws)
+    assert max_abs(got2, ref) <= TOL
+
+
+@needs_gpu
+@pytest.mark.parametrize("n", [1, 2, 63, 64, 127, 128, 129, 255, 256, 257])
+def test_decode_edge_lengths(n):
+    w = ks.small(ks.LLAMA3_DECODE, batch=1, kv_heads=2, q_heads=8)
+    p, s = build(w, n)
+    q = ks.decode_query(s)
+    got, _ = p.decode(q)
+    assert max_abs(got, p.decode_ref(q)) <= TOL
+
+
+@needs_gpu
+def test_decode_overflow_only_segments():
+    w = ks.small(ks.TINY, batch=2, kv_heads=2, q_heads=4, head_dim=64, code_bits=4, qmax=7,
+                 residual=10, group=0, kv_dtype="bf16")
+    p = Pair(w, 512)
+    s = ks.Stream(w)
+    for n in (100, 1, 7, 64, 3):
+        k, v = ks.kv_pair(s, n)
+        p.append(k, v)
+    q = ks.decode_query(s)
+    got, _ = p.decode(q)
+    assert max_abs(got, p.decode_ref(q)) <= TOL
+
+
+@needs_gpu
+def test_decode_llama3_full_size():
+    w = ks.LLAMA3_DECODE
+    p, s = build(w, w.prefill)
+    k, v = ks.kv_pair(s, 1)          # decode step: append the new token, then attend
+    p.append(k, v)
+    q = ks.decode_query(s)
+    note("decode llama3 full")
+    got, ws = p.decode(q)
+    ref = p.decode_ref(q)
+    err = max_abs(got, ref)
+    assert err <= TOL, err
+    torch.cuda.synchronize()
+    assert not ws[:64].any()         # arrival counters cleared
+
+
+@needs_gpu
+def test_decode_long_context_one_layer():
+    w = ks.LONG_CONTEXT
+    p, s = build(w, w.prefill)
+    q = ks.decode_query(s)
+    note("decode long context layer 0")
+    got, _ = p.decode(q)
+    ref = p.decode_ref(q, units=[(0, 0), (0, 5)])   # two KV heads (8 query heads) in full
+    assert max_abs(got, ref) <= TOL
