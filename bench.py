@@ -1,0 +1,229 @@
+"""Benchmark of the quantized-KV decode hot path on one MI355X.
+
+One step = append one new token to a cache (token accounting, tail-ring
+write, and a flush-quantize when the window overflows by a whole group)
+followed by single-query GQA decode attention over that cache, on the
+Llama-3-8B attention shape: batch 8, 32 query / 8 KV heads, head_dim 128,
+4096 cached tokens, int4 codes with per-channel Key and per-token Value fp16
+scales, bf16 residual window of 128.
+
+Steps rotate over independent caches whose combined footprint (> 512 MB) is
+more than twice the 256 MB Infinity Cache, so the decode reads come from HBM.
+Inputs are resident in HBM before timing starts.
+
+Printed: one JSON line.  ``value`` = effective KV bytes read by the decode
+attention per step (packed codes + Key scales + Value scales + bf16 tail +
+queries) / measured wall time per step (append + decode, launch gaps
+included).  ``roofline`` prices the decode kernel alone: the same bytes over
+its average launch duration, measured with HIP events recorded on the
+launch stream around every decode launch of the timed region.
+``cpu_baseline`` times the CPU oracle's decode attention on a bounded sample
+of (batch, KV head) units of the same workload.
+
+Other workloads (``--workload``) print their own line; the default run is
+the decode workload above.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def decode_bytes(cfg, nq: int, nt: int, q_heads: int) -> int:
+    """Algorithmic bytes one decode call must read (codes, scales, tail, q)."""
+    B, H, D = cfg.batch, cfg.kv_heads, cfg.head_dim
+    W = D * cfg.code_bits // 8
+    es = 2 if cfg.kv_dtype == 0 else 4
+    nseg = nq // cfg.group if cfg.group else None
+    per_unit = 2 * nq * W + nq * 2 + 2 * nt * D * es
+    per_unit += (nseg if nseg is not None else 0) * D * 2
+    return B * H * per_unit + B * q_heads * D * es
+
+
+def build_caches(w, n_caches, capacity, log):
+    import torch
+
+    import kvq_synth as ks
+    from quantized_kv_cache_kvq_amd import KVCache, make_config
+
+    cfg = make_config(batch=w.batch, kv_heads=w.kv_heads, head_dim=w.head_dim, capacity=capacity,
+                      code_bits=w.code_bits, qmax=w.qmax, residual=w.residual, group=w.group)
+    caches = []
+    for i in range(n_caches):
+        s = ks.Stream(w, seed=i)
+        k, v = ks.kv_pair(s, w.prefill)
+        c = KVCache(cfg, zero=False)
+        c.append(k.cuda(), v.cuda())
+        caches.append(c)
+        del k, v
+    torch.cuda.synchronize()
+    log(f"built {n_caches} caches of {w.prefill} tokens")
+    return cfg, caches
+
+
+def run_decode(args, log):
+    import torch
+
+    import kvq_synth as ks
+
+    w = ks.LLAMA3_DECODE
+    steps, warmup = args.steps, args.warmup
+    capacity = w.prefill + (steps + warmup) // args.caches + 256
+    cfg, caches = build_caches(w, args.caches, capacity, log)
+    pool = 32
+    s = ks.Stream(w, seed=10_000)
+    new_k, new_v, qs = [], [], []
+    for _ in range(pool):
+        k, v = ks.kv_pair(s, 1)
+        new_k.append(k.cuda())
+        new_v.append(v.cuda())
+        qs.append(ks.decode_query(s).cuda())
+    out = torch.empty(w.batch, w.q_heads, w.head_dim, device="cuda")
+    ws = caches[0].workspace(w.q_heads, 1)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        c = caches[i % len(caches)]
+        c.append(new_k[i % pool], new_v[i % pool])
+        return c
+
+    for i in range(warmup):
+        c = step(i)
+        c.decode_attn(qs[i % pool], out, ws)
+    torch.cuda.synchronize()
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    total_bytes = 0
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(steps):
+        c = step(warmup + i)
+        total_bytes += decode_bytes(cfg, c.state.quantized, c.state.tail, w.q_heads)
+        ev[i][0].record(stream)
+        c.decode_attn(qs[(warmup + i) % pool], out, ws)
+        ev[i][1].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = start.elapsed_time(end) / steps
+    dec_ms = sum(a.elapsed_time(b) for a, b in ev) / steps
+    bytes_step = total_bytes / steps
+    value = bytes_step / (ms_step * 1e-3) / 1e9
+    achieved = bytes_step / (dec_ms * 1e-3) / 1e9
+    log(f"wall {wall:.3f}s for {steps} steps; decode kernel {dec_ms*1e3:.2f} us")
+    res = {
+        "metric": "decode-attn effective KV GB/s (% of HBM peak) + us/step, Llama-3-8B shape int4",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": round(ms_step, 5),
+        "us_per_step": round(ms_step * 1e3, 3),
+        "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "q_heads": w.q_heads,
+                   "kv_heads": w.kv_heads, "head_dim": w.head_dim, "context": w.prefill,
+                   "codes": f"int{w.code_bits}", "residual": w.residual, "group": w.group,
+                   "caches_rotated": args.caches, "parallelism": "single-gpu"},
+        "decode_kernel_us": round(dec_ms * 1e3, 3),
+        "decode_bytes_per_step": int(bytes_step),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None, "kernel": "decode_kernel<128,4,4>"},
+    }
+    return res, (cfg, w)
+
+
+def cpu_baseline_decode(budget_s: float, log):
+    """Time the CPU oracle's decode attention on a bounded sample of units."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import kvq_synth as ks
+    from oracle import attention as oatt
+    from oracle.cache import KVQuantizationStrategies
+    from quantized_kv_cache_kvq_amd import make_config
+
+    w = ks.LLAMA3_DECODE
+    s = ks.Stream(w, seed=0)
+    k, v = ks.kv_pair(s, w.prefill)
+    o = KVQuantizationStrategies(qmax=w.qmax, scale_storage="fp16", group=w.group)
+    st = o.append_and_partition(None, k.float().numpy(), v.float().numpy(), w.residual)
+    q = ks.decode_query(s).float().numpy()
+    sigma = 1.0 / math.sqrt(w.head_dim)
+    cfg = make_config(batch=1, kv_heads=1, head_dim=w.head_dim, capacity=w.prefill,
+                      code_bits=w.code_bits, qmax=w.qmax, residual=w.residual, group=w.group)
+    nq, nt = st["quantized_tokens"], st["key_residual"].shape[-2]
+    unit_bytes = decode_bytes(cfg, nq, nt, w.q_heads // w.kv_heads)
+    units = [(b, h) for b in range(w.batch) for h in range(w.kv_heads)]
+    # Whole decode calls (all 64 units) repeated until the budget is spent.
+    with threadpool_limits(limits=1):
+        calls = 0
+        t = time.perf_counter()
+        while True:
+            oatt.decode_attention(st, q, sigma)
+            calls += 1
+            dt = time.perf_counter() - t
+            if dt >= budget_s:
+                break
+    n = calls * len(units)
+    log(f"cpu oracle: {calls} decode calls in {dt:.2f}s")
+    return {"value": round(n * unit_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{calls} full fp64 decode-attention calls (restore + softmax over all "
+                      f"{len(units)} (batch, KV head) units) of the Llama-3-8B int4 workload "
+                      f"at {w.prefill} tokens, one thread, {dt:.1f} s; "
+                      f"{dt / calls * 1e3:.1f} ms per call",
+            "cpu": platform.processor() or platform.machine()}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--caches", type=int, default=16)
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--quiet", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build runs on a single MI355X and has no "
+              "multi-GPU path; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    def log(msg):
+        if not args.quiet:
+            print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    import quantized_kv_cache_kvq_amd as kvq
+    if not os.path.exists(kvq.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    kvq.load()
+    res, _ = run_decode(args, log)
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_decode(args.cpu_budget, log)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

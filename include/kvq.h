@@ -158,8 +158,8 @@ kvq_status kvq_workspace_init(void* workspace, size_t bytes, void* stream);
  * quantized prefix are restored inside the kernel (read path "decode inside
  * the kernel", "KV Cache quantization and compression", section 06); the
  * tail is read as stored.  The sequence axis is split across workgroups and
- * the partial softmax states are merged (flash-decoding split, the former
- * page, section 05) by the last workgroup of each (batch, KV head).
+ * the partial softmax states are merged by a second, small kernel
+ * (flash-decoding split, the former page, section 05).
  *   q   : device, kv_dtype [batch, q_heads, head_dim]
  *   out : device, float32 [batch, q_heads, head_dim]
  *   softmax_scale : sigma (1/sqrt(head_dim) for standard attention)

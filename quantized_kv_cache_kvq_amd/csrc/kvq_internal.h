@@ -50,19 +50,55 @@ __device__ __forceinline__ int sext_field(uint32_t word, int shift) {
   return static_cast<int>(word << (32 - BITS - shift)) >> (32 - BITS);
 }
 
-// ---- wave reductions -------------------------------------------------------------
+// ---- cross-lane reductions ---------------------------------------------------------
+// Within a row of 16 lanes: DPP quad permutations, then half-row and row
+// mirrors (every lane of the row ends with the result).  Across the wave: the
+// four row results are read into scalar registers.
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                               0xF, 0xF, false));
+}
+
+constexpr int kDppQuadXor1 = 0xB1;     // quad_perm [1, 0, 3, 2]
+constexpr int kDppQuadXor2 = 0x4E;     // quad_perm [2, 3, 0, 1]
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_f<kDppQuadXor1>(v));
+  v = fmaxf(v, dpp_f<kDppQuadXor2>(v));
+  v = fmaxf(v, dpp_f<kDppRowHalfMirror>(v));
+  v = fmaxf(v, dpp_f<kDppRowMirror>(v));
+  return v;
+}
+
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f<kDppQuadXor1>(v);
+  v += dpp_f<kDppQuadXor2>(v);
+  v += dpp_f<kDppRowHalfMirror>(v);
+  v += dpp_f<kDppRowMirror>(v);
+  return v;
+}
+
+// Value of lane `lane` (wave-uniform index) as a wave-uniform scalar.
+__device__ __forceinline__ float lane_value(float v, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
 
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+  v = row16_max(v);
+  return fmaxf(fmaxf(lane_value(v, 0), lane_value(v, 16)), fmaxf(lane_value(v, 32), lane_value(v, 48)));
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  v = row16_sum(v);
+  return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
 }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
 // ---- host helpers ----------------------------------------------------------------
 
