@@ -143,7 +143,8 @@ def run_decode(args, log):
         "decode_bytes_per_step": int(bytes_step),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None, "kernel": "decode_kernel<128,4,4>"},
+                     "traffic": None,
+                     "kernel": "kvq_decode_attn = decode_mfma_kernel<128,4> + merge_kernel<128,4>"},
     }
     return res, (cfg, w)
 

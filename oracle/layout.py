@@ -27,7 +27,7 @@ Per (batch, KV head) stream, with W = head_dim * b / 8 bytes per token row
   token at absolute position p lives in slot p % ring, with
   ring = R + G (G > 0) or R (G = 0).
 
-Parity: pinned by tests/test_oracle_layout.py (hand-written bytes for small
+Parity: pinned by tests/test_oracle_layout_ledger.py (hand-written bytes for small
 cases, read straight off the formulas above).
 """
 from __future__ import annotations

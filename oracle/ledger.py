@@ -12,7 +12,7 @@
   ceil(n * bits / 8) plus scale bytes (the page hard-codes bits = 4 via
   (n + 1) // 2; ``bits`` generalises it).
 
-Parity: pinned by tests/test_oracle_ledger.py against the printed budgets
+Parity: pinned by tests/test_oracle_layout_ledger.py against the printed budgets
 (512 / 256 / 128 / 260 / 132 / 140 MiB, 131072 bytes per token, 52.73 GiB for
 432000 tokens).
 """
