@@ -6,7 +6,10 @@
  * caller likes, e.g. through torch); the library never allocates, frees or
  * synchronizes.  Every call validates all arguments before it enqueues any
  * work; on error it returns a status, enqueues nothing and leaves the
- * caller's kvq_state unchanged.  All device work is enqueued on the caller's
+ * caller's kvq_state unchanged.  KVQ_EDEVICE reports a failed launch of the
+ * call's own kernels: an entry point clears the calling thread's HIP
+ * last-error slot (left over from earlier, unrelated HIP calls) before it
+ * launches.  All device work is enqueued on the caller's
  * HIP stream (passed as an opaque hipStream_t, NULL = the null stream) and
  * is asynchronous.
  *

@@ -38,9 +38,19 @@ COMMON = [
 ]
 
 
+# Attention kernels: NaN inputs are outside the contract, so fmax needs no
+# NaN canonicalization and max reductions fuse with their DPP moves.  Device
+# code only: the host-side argument checks keep IEEE NaN semantics.
+PER_FILE = {
+    "kvq_decode.hip": ["-Xarch_device", "-fno-honor-nans"],
+    "kvq_block.hip": ["-Xarch_device", "-fno-honor-nans"],
+}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *COMMON, "-I", INCLUDE, "-c", src, "-o", obj]
+    extra = PER_FILE.get(os.path.basename(src), [])
+    cmd = [hipcc(), *COMMON, *extra, "-I", INCLUDE, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr[-6000:]}")

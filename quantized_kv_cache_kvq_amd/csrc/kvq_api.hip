@@ -102,6 +102,7 @@ extern "C" kvq_status kvq_workspace_init(void* workspace, size_t bytes, void* st
   const int64_t n = static_cast<int64_t>(bytes / 4);
   int64_t blocks = (n + 255) / 256;
   if (blocks > 2048) blocks = 2048;
+  clear_stale_hip_error();
   hipLaunchKernelGGL(fill_zero_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
                      static_cast<hipStream_t>(stream), static_cast<uint32_t*>(workspace), n);
   return hipGetLastError() == hipSuccess ? KVQ_OK : KVQ_EDEVICE;

@@ -270,6 +270,7 @@ extern "C" kvq_status kvq_append(const kvq_config* cfg, kvq_state* st, const kvq
       !cache->v_scale || !cache->k_tail || !cache->v_tail || (g.G == 0 && !cache->seg_index))
     return KVQ_EINVAL;
   hipStream_t hs = static_cast<hipStream_t>(stream);
+  clear_stale_hip_error();
   const int64_t flush = next.flushed_last;
   if (flush > 0) {
     FlushArgs a;

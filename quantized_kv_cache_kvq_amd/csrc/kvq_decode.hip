@@ -52,9 +52,6 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kTailChunk = 16;
 
-typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
-typedef float f4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
 
 struct DecodeArgs {
   Geom g;
@@ -74,8 +71,6 @@ struct DecodeArgs {
   float* part;           // [unit][split][gqa][D + 2]
   int splits;
   int tiles_q, items;    // quantized tiles; work items = tiles_q + tail chunks
-  uint32_t nib_mask;     // 0x03C003C0, see nibbles_to_h8
-  uint32_t nib_one;      // 0x3C003C00
 };
 
 // Order LDS traffic between the lanes of one wave.  A wave's LDS operations
@@ -116,58 +111,75 @@ __device__ __forceinline__ int tail_slot(const DecodeArgs& a, int tt) {
 // Tail chunk of 16 tokens (values stored as bf16/fp32 in the ring), on the
 // vector ALUs.  Keys: lane = (token lane % 16, channel quarter lane / 16),
 // partial dot products summed across the quarters.  Values: lane = channel
-// owner (TailMap), sixteen tokens.  Key and Value loads are issued together
-// and kept raw until use.  Updates m/l (uniform per head), returns alpha[]
-// for the caller's other accumulators, accumulates into acc_tail.
-// kBf16Only drops the fp32 branch (and its registers).
-template <int D, int GQA, bool kBf16Only = false>
-__device__ __forceinline__ void tail_chunk(const DecodeArgs& a, int unit, int chunk,
-                                           const float (*qsT)[GQA], float (*pw)[GQA], float* m,
-                                           float* l, float* alpha,
-                                           float (&acc_tail)[TailMap<D>::TCPL][GQA]) {
-  constexpr int CPQ = D / 4;               // channels per quarter
+// owner (TailMap), sixteen tokens.  tail_load issues every load of a chunk
+// (kept raw in registers); tail_compute updates m/l (uniform per head),
+// returns alpha[] for the caller's other accumulators and accumulates into
+// acc_tail.  kBf16Only drops the fp32 branch (and its registers).
+template <int D, bool kBf16Only>
+struct TailRegs {
+  static constexpr int CPQ = D / 4;        // channels per quarter
+  uint32_t kraw[kBf16Only ? CPQ / 2 : CPQ];  // bf16: CPQ/2 words; fp32: CPQ words
+  uint32_t vraw[kTailChunk][TailMap<D>::TCPL];
+  int nvalid;
+};
+
+template <int D, bool kBf16Only>
+__device__ __forceinline__ void tail_load(const DecodeArgs& a, int unit, int chunk, TailRegs<D, kBf16Only>& r) {
+  constexpr int CPQ = D / 4;
   constexpr int TCPL = TailMap<D>::TCPL;
   const Geom& g = a.g;
   const int lane = threadIdx.x % kWave;
   const int col = lane % 16, quarter = lane / 16;
   const int tt0 = chunk * kTailChunk;
-  const int nvalid = a.nt - tt0 < kTailChunk ? a.nt - tt0 : kTailChunk;
+  r.nvalid = a.nt - tt0 < kTailChunk ? a.nt - tt0 : kTailChunk;
   const bool bf16 = kBf16Only || g.dtype == KVQ_BF16;
   const int64_t ring_row0 = (int64_t)unit * g.ring;
-  // ---- loads: Keys (CPQ channels of one token), Values (TCPL channels x 16 tokens)
-  const int kslot = tail_slot(a, tt0 + (col < nvalid ? col : 0));
+  const int kslot = tail_slot(a, tt0 + (col < r.nvalid ? col : 0));
   const int64_t krow = (ring_row0 + kslot) * D + quarter * CPQ;
-  uint32_t kraw[kBf16Only ? CPQ / 2 : CPQ];  // bf16: CPQ/2 words; fp32: CPQ words
   if (bf16) {
     const uint32_t* p = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(a.k_tail) + krow);
 #pragma unroll
-    for (int j = 0; j < CPQ / 2; ++j) kraw[j] = p[j];
+    for (int j = 0; j < CPQ / 2; ++j) r.kraw[j] = p[j];
+    if constexpr (!kBf16Only) {     // every element defined on both paths: the array stays in registers
+#pragma unroll
+      for (int j = CPQ / 2; j < CPQ; ++j) r.kraw[j] = 0u;
+    }
   } else if constexpr (!kBf16Only) {
     const uint32_t* p = reinterpret_cast<const uint32_t*>(static_cast<const float*>(a.k_tail) + krow);
 #pragma unroll
-    for (int j = 0; j < CPQ; ++j) kraw[j] = p[j];
+    for (int j = 0; j < CPQ; ++j) r.kraw[j] = p[j];
   }
-  const bool owner = TailMap<D>::owns(lane);
-  const int c0 = owner ? lane * TCPL : 0;
-  uint32_t vraw[kTailChunk][TCPL];          // bf16: packed pair (TCPL = 2) or one value
+  const int c0 = TailMap<D>::owns(lane) ? lane * TCPL : 0;
 #pragma unroll
   for (int t = 0; t < kTailChunk; ++t) {
-    const int64_t base = (ring_row0 + tail_slot(a, tt0 + (t < nvalid ? t : 0))) * D + c0;
+    const int64_t base = (ring_row0 + tail_slot(a, tt0 + (t < r.nvalid ? t : 0))) * D + c0;
     if (bf16) {
-      if constexpr (TCPL == 2) {
-        vraw[t][0] = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(a.v_tail) + base);
+      if constexpr (TCPL == 2) {   // one word holds the lane's two bf16 channels
+        r.vraw[t][0] = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(a.v_tail) + base);
+        r.vraw[t][1] = 0u;
       } else {
 #pragma unroll
-        for (int k = 0; k < TCPL; ++k) vraw[t][k] = static_cast<const uint16_t*>(a.v_tail)[base + k];
+        for (int k = 0; k < TCPL; ++k) r.vraw[t][k] = static_cast<const uint16_t*>(a.v_tail)[base + k];
       }
     } else if constexpr (!kBf16Only) {
 #pragma unroll
       for (int k = 0; k < TCPL; ++k)
-        vraw[t][k] = reinterpret_cast<const uint32_t*>(static_cast<const float*>(a.v_tail))[base + k];
+        r.vraw[t][k] = reinterpret_cast<const uint32_t*>(static_cast<const float*>(a.v_tail))[base + k];
     }
   }
-  // ---- logits and softmax ----
-  const bool valid = col < nvalid;
+}
+
+template <int D, int GQA, bool kBf16Only>
+__device__ __forceinline__ void tail_compute(const DecodeArgs& a, const TailRegs<D, kBf16Only>& r,
+                                             const float (*qsT)[GQA], float (*pw)[GQA], float* m,
+                                             float* l, float* alpha,
+                                             float (&acc_tail)[TailMap<D>::TCPL][GQA]) {
+  constexpr int CPQ = D / 4;
+  constexpr int TCPL = TailMap<D>::TCPL;
+  const int lane = threadIdx.x % kWave;
+  const int col = lane % 16, quarter = lane / 16;
+  const bool bf16 = kBf16Only || a.g.dtype == KVQ_BF16;
+  const bool valid = col < r.nvalid;
   wave_lds_sync();
 #pragma unroll
   for (int h = 0; h < GQA; ++h) {
@@ -175,12 +187,12 @@ __device__ __forceinline__ void tail_chunk(const DecodeArgs& a, int unit, int ch
     if (bf16) {
 #pragma unroll
       for (int j = 0; j < CPQ / 2; ++j) {
-        s = fmaf(qsT[quarter * CPQ + 2 * j][h], bf16_lo(kraw[j]), s);
-        s = fmaf(qsT[quarter * CPQ + 2 * j + 1][h], bf16_hi(kraw[j]), s);
+        s = fmaf(qsT[quarter * CPQ + 2 * j][h], bf16_lo(r.kraw[j]), s);
+        s = fmaf(qsT[quarter * CPQ + 2 * j + 1][h], bf16_hi(r.kraw[j]), s);
       }
     } else if constexpr (!kBf16Only) {
 #pragma unroll
-      for (int j = 0; j < CPQ; ++j) s = fmaf(qsT[quarter * CPQ + j][h], __uint_as_float(kraw[j]), s);
+      for (int j = 0; j < CPQ; ++j) s = fmaf(qsT[quarter * CPQ + j][h], __uint_as_float(r.kraw[j]), s);
     }
     s += __shfl_xor(s, 16, kWave);
     s += __shfl_xor(s, 32, kWave);
@@ -193,21 +205,21 @@ __device__ __forceinline__ void tail_chunk(const DecodeArgs& a, int unit, int ch
     for (int k = 0; k < TCPL; ++k) acc_tail[k][h] *= alpha[h];
   }
   wave_lds_sync();
-  if (!owner) return;
+  if (!TailMap<D>::owns(lane)) return;
 #pragma unroll
   for (int t = 0; t < kTailChunk; ++t) {
     float v[TCPL];
     if (bf16) {
       if constexpr (TCPL == 2) {
-        v[0] = bf16_lo(vraw[t][0]);
-        v[1] = bf16_hi(vraw[t][0]);
+        v[0] = bf16_lo(r.vraw[t][0]);
+        v[1] = bf16_hi(r.vraw[t][0]);
       } else {
 #pragma unroll
-        for (int k = 0; k < TCPL; ++k) v[k] = bf16_lo(vraw[t][k]);
+        for (int k = 0; k < TCPL; ++k) v[k] = bf16_lo(r.vraw[t][k]);
       }
     } else if constexpr (!kBf16Only) {
 #pragma unroll
-      for (int k = 0; k < TCPL; ++k) v[k] = __uint_as_float(vraw[t][k]);
+      for (int k = 0; k < TCPL; ++k) v[k] = __uint_as_float(r.vraw[t][k]);
     }
 #pragma unroll
     for (int h = 0; h < GQA; ++h) {
@@ -218,8 +230,51 @@ __device__ __forceinline__ void tail_chunk(const DecodeArgs& a, int unit, int ch
   }
 }
 
-// Fold the four waves of a workgroup and write a partial (or the output).
-// red[w][c][h] holds wave w's accumulator relative to its own maximum.
+// One workgroup per (batch, KV head): combine the splits' partials
+// (m, l, acc) and write the output.  Eight splits are read per round trip
+// and folded with an online maximum.
+template <int D, int GQA>
+__global__ __launch_bounds__(kThreads) void merge_kernel(DecodeArgs a) {
+  const int unit = blockIdx.x;
+  const Geom& g = a.g;
+  const int b = unit / g.H, kvh = unit % g.H;
+  const float* pu = a.part + (int64_t)unit * a.splits * GQA * (D + 2);
+  for (int i = threadIdx.x; i < GQA * D; i += kThreads) {
+    const int h = i / D, c = i % D;
+    float M = -INFINITY, num = 0.0f, den = 0.0f;
+    for (int s0 = 0; s0 < a.splits; s0 += 8) {
+      float ms[8], ls[8], vs[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int s = s0 + k < a.splits ? s0 + k : s0;
+        const float* ps = pu + (s * GQA + h) * (D + 2);
+        ms[k] = ps[D];
+        ls[k] = ps[D + 1];
+        vs[k] = ps[c];
+      }
+      float mx = M;
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (s0 + k < a.splits) mx = fmaxf(mx, ms[k]);
+      if (mx == -INFINITY) continue;               // every split so far is empty
+      const float r = M == -INFINITY ? 0.0f : fast_exp2(M - mx);
+      num *= r;
+      den *= r;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float e = (s0 + k < a.splits && ms[k] != -INFINITY) ? fast_exp2(ms[k] - mx) : 0.0f;
+        num = fmaf(vs[k], e, num);
+        den = fmaf(ls[k], e, den);
+      }
+      M = mx;
+    }
+    a.out[((int64_t)b * g.H * GQA + kvh * GQA + h) * D + c] = num / den;
+  }
+}
+
+// Fold the four waves of a workgroup and write a partial (or, with a single
+// split, the output).  red[w][c][h] holds wave w's accumulator relative to
+// its own maximum.
 template <int D, int GQA>
 __device__ __forceinline__ void fold_and_store(const DecodeArgs& a, int unit, int split,
                                                float (*red)[D][GQA], float (*wml)[2][GQA],
@@ -268,12 +323,29 @@ __device__ __forceinline__ void load_q(const DecodeArgs& a, int unit, float (*qs
   }
 }
 
-// The contiguous run of work items [begin, end) of this wave.
-__device__ __forceinline__ void wave_items(const DecodeArgs& a, int split, int wave, int& begin, int& end) {
-  const int s0 = (int)(((int64_t)a.items * split) / a.splits);
-  const int s1 = (int)(((int64_t)a.items * (split + 1)) / a.splits);
-  begin = s0 + ((s1 - s0) * wave) / kWaves;
-  end = s0 + ((s1 - s0) * (wave + 1)) / kWaves;
+// Work of one wave: quantized tiles [t0, t1) and tail chunks [c0, c1).
+// Split s owns an equal share of the tiles and of the chunks (so the tail is
+// spread over the splits); its four waves share the concatenated list
+// (tiles, then chunks) in contiguous runs, so a wave meets each Key segment
+// once.
+struct WaveWork {
+  int t0, t1, c0, c1;
+};
+__device__ __forceinline__ WaveWork wave_work(const DecodeArgs& a, int split, int wave) {
+  const int chunks = a.items - a.tiles_q;
+  const int ts0 = (int)(((int64_t)a.tiles_q * split) / a.splits);
+  const int ts1 = (int)(((int64_t)a.tiles_q * (split + 1)) / a.splits);
+  const int cs0 = (int)(((int64_t)chunks * split) / a.splits);
+  const int cs1 = (int)(((int64_t)chunks * (split + 1)) / a.splits);
+  const int n = (ts1 - ts0) + (cs1 - cs0);
+  const int lo = (n * wave) / kWaves, hi = (n * (wave + 1)) / kWaves;
+  const int nt = ts1 - ts0;
+  WaveWork w;
+  w.t0 = ts0 + (lo < nt ? lo : nt);
+  w.t1 = ts0 + (hi < nt ? hi : nt);
+  w.c0 = cs0 + (lo > nt ? lo - nt : 0);
+  w.c1 = cs0 + (hi > nt ? hi - nt : 0);
+  return w;
 }
 
 // ---- vector-ALU kernel (every shape) ------------------------------------------------
@@ -286,7 +358,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   constexpr int FPW = 32 / BITS;         // fields per 32-bit word
   constexpr int TCPL = TailMap<D>::TCPL;
   const Geom& g = a.g;
-  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int unit = blockIdx.y;
   const int split = blockIdx.x;
 
@@ -310,23 +383,23 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     for (int k = 0; k < TCPL; ++k) acc_tail[k][h] = 0.0f;
   }
 
-  int w_begin, w_end;
-  wave_items(a, split, wave, w_begin, w_end);
+  const WaveWork ww = wave_work(a, split, wave);
   const uint8_t* kbase = a.k_codes + (int64_t)unit * g.code_stream;
   const uint8_t* vbase = a.v_codes + (int64_t)unit * g.code_stream;
   const uint16_t* ksbase = a.k_scale + (int64_t)unit * g.max_seg * D;
   const uint16_t* vsbase = a.v_scale + (int64_t)unit * g.C;
   int cur_seg = -1;
 
-  for (int tile = w_begin; tile < w_end; ++tile) {
-    if (tile >= a.tiles_q) {
-      tail_chunk<D, GQA>(a, unit, tile - a.tiles_q, qsT, pw[wave], m, l, alpha, acc_tail);
+  for (int chunk = ww.c0; chunk < ww.c1; ++chunk) {
+    TailRegs<D, false> tr;
+    tail_load<D, false>(a, unit, chunk, tr);
+    tail_compute<D, GQA, false>(a, tr, qsT, pw[wave], m, l, alpha, acc_tail);
 #pragma unroll
-      for (int h = 0; h < GQA; ++h)
+    for (int h = 0; h < GQA; ++h)
 #pragma unroll
-        for (int k = 0; k < NSLOT; ++k) acc[k][h] *= alpha[h];
-      continue;
-    }
+      for (int k = 0; k < NSLOT; ++k) acc[k][h] *= alpha[h];
+  }
+  for (int tile = ww.t0; tile < ww.t1; ++tile) {
     const int t = tile * kTile + lane;
     const bool valid = t < a.nq;
     const uint8_t* kt = kbase + (int64_t)tile * (kTile * W);
@@ -458,280 +531,434 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   fold_and_store<D, GQA>(a, unit, split, red, wml, m, l);
 }
 
-// ---- MFMA kernel (int4 codes, head_dim 64 / 128, whole-group segments) ---------------
+// ---- int8-MFMA kernel (int4 / int2 codes, head_dim 64 / 128, whole-group segments) ----
+//
+// Both contractions of a 64-token tile run on v_mfma_i32_16x16x64_i8.  Lane l
+// supplies row l % 16 of A and column l % 16 of B for k-group l / 16 (16 bytes
+// each); element i of the result in lane l is row 4 (l / 16) + i, column l % 16.
+//
+// Codes: a b-bit two's-complement field moved to the top of a byte is the
+// signed int8 value 2^(8-b) * code, so a packed word unpacks with a shift and
+// an and per four fields and needs no bias correction.
+//
+// Key side: logit[head][token] = sum_c a[head][c] code[token][c] with
+// a = sigma log2(e) q / kscale (per segment).  a is rounded to the 21-bit
+// fixed-point integer v = round(a F) (F per head and segment, from a bound on
+// |a|) and split into three balanced base-128 digits; MFMA row 4 h + d holds
+// digit d of head h, so a head's three partial sums land in one lane and
+// recombine exactly in fp32 (each is below 2^24).
+//
+// Value side: acc[head][c] += sum_t P[head][t] code[t][c] with
+// P = Fv p / vscale[t], p = exp2(logit - running max) <= 1 and Fv fixed for the
+// wave's run of tiles (from the largest 1 / vscale in it), so P is an unsigned
+// 21-bit integer; its three base-128 digits go in rows 4 h + d and the
+// products accumulate in int32 across tiles.  When a running maximum moves,
+// the int32 sums are folded into an fp32 accumulator and rescaled.
+//
+// Token order: slot j of the Value operand of k-group kg holds token
+// 16 kg + f(j) (f = field order of the unpacked word); column col of Key MFMA
+// g is token 16 (col / 4) + f(4 (col % 4) + g), so a lane owns the four tokens
+// of one Value-operand dword and stores each digit with one 32-bit LDS write.
 
-// One 32-bit word of eight int4 fields -> eight fp16 values 1 + (code + 8) / 16
-// in MFMA slot order: slot 2v holds field v, slot 2v+1 holds field v + 4.
-// mask = 0x03C003C0 (mantissa bits 6..9 of both halves) and one = 0x3C003C00
-// (two fp16 ones) arrive as kernel arguments: kept in registers, each pair of
-// fields costs a shift and one v_and_or_b32 (literal operands would force a
-// separate and + or).
-__device__ __forceinline__ h8_t nibbles_to_h8(uint32_t w, uint32_t mask, uint32_t one) {
-  const uint32_t x = w ^ 0x88888888u;          // u = code + 8 in every field
-  u4_t r;
-  r[0] = ((x << 6) & mask) | one;              // 1 + u / 16, fields 0 and 4
-  r[1] = ((x << 2) & mask) | one;
-  r[2] = ((x >> 2) & mask) | one;
-  r[3] = ((x >> 6) & mask) | one;
-  return __builtin_bit_cast(h8_t, r);
+typedef int i4_t __attribute__((ext_vector_type(4)));
+
+// Sixteen packed b-bit fields (one operand k-group) -> four dwords of int8
+// values 2^(8-b) * field; field(j) = the field held in operand slot j.
+template <int BITS>
+struct Fields16;
+
+template <>
+struct Fields16<4> {
+  typedef uint2 raw_t;
+  static constexpr float kMul = 16.0f;
+  __device__ static i4_t unpack(raw_t r) {
+    const uint32_t m = 0xF0F0F0F0u;
+    return i4_t{(int)((r.x << 4) & m), (int)(r.x & m), (int)((r.y << 4) & m), (int)(r.y & m)};
+  }
+  // dword j/4 = even or odd nibbles of word j/8; byte j%4
+  __host__ __device__ static constexpr int field(int j) { return 8 * (j / 8) + 2 * (j % 4) + (j / 4) % 2; }
+};
+
+template <>
+struct Fields16<2> {
+  typedef uint32_t raw_t;
+  static constexpr float kMul = 64.0f;
+  __device__ static i4_t unpack(raw_t w) {
+    const uint32_t m = 0xC0C0C0C0u;
+    return i4_t{(int)((w << 6) & m), (int)((w << 4) & m), (int)((w << 2) & m), (int)(w & m)};
+  }
+  // dword j/4 = field j/4 of every byte; byte j%4
+  __host__ __device__ static constexpr int field(int j) { return 4 * (j % 4) + j / 4; }
+};
+
+// Low bytes of four registers -> one dword (byte k from bk).
+__device__ __forceinline__ uint32_t pack_bytes(uint32_t b0, uint32_t b1, uint32_t b2, uint32_t b3) {
+  const uint32_t lo = __builtin_amdgcn_perm(b1, b0, 0x0c0c0400u);
+  const uint32_t hi = __builtin_amdgcn_perm(b3, b2, 0x0c0c0400u);
+  return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
 }
 
-// Element (0..7) of a word held in MFMA slot r, and its inverse.
-__device__ __forceinline__ constexpr int slot_elem(int r) { return (r % 2) * 4 + r / 2; }
-__device__ __forceinline__ constexpr int elem_slot(int e) { return 2 * (e % 4) + e / 4; }
-
-// Head held in MFMA result row 4q + i.  Rows >= GQA are padding; they are
-// mapped onto a real head so every value they carry stays finite.
-template <int GQA>
-__device__ __forceinline__ int row_head(int q, int i) {
-  return GQA > 4 ? (4 * (q & 1) + i) % GQA : i % GQA;
+// round(x) + 0x102040 for |x| <= 2^20, from one fma: the magic constant
+// 1.5 * 2^23 places the rounded integer in the low mantissa bits.
+__device__ __forceinline__ uint32_t fixed_biased(float a, float f) {
+  return __float_as_uint(fmaf(a, f, 12582912.0f)) - (0x4B400000u - 0x102040u);
 }
 
-template <int D, int GQA>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
-void decode_mfma_kernel(DecodeArgs a) {
-  constexpr int BITS = 4;
+// Recombine three base-128 digit sums (rows 4 h + 0..2 of an i32 MFMA result).
+__device__ __forceinline__ float digits_value(const i4_t s) {
+  return fmaf((float)s[0], 16384.0f, fmaf((float)s[1], 128.0f, (float)s[2]));
+}
+
+// Two waves per SIMD (<= 256 registers); eight heads per KV head need the
+// register file of one wave per SIMD.
+template <int D, int BITS, int GQA>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(GQA > 4 ? 1 : 2)))
+void decode_i8_kernel(DecodeArgs a) {
+  using F16 = Fields16<BITS>;
+  using raw_t = typename F16::raw_t;
   constexpr int W = D * BITS / 8;         // bytes per token row
-  constexpr int MK = D / 32;              // Key MFMAs per 16 tokens (32 channels each)
-  constexpr int NV = D / 16;              // Value MFMA column blocks (16 channels each)
+  constexpr int MK = D / 64;              // Key MFMAs per token group (64 channels each)
+  constexpr int NV = D / 16;              // Value MFMAs per head group (16 channels each)
+  constexpr int HG = (GQA + 3) / 4;       // head groups of four MFMA row quads
   constexpr int TCPL = TailMap<D>::TCPL;
-  static_assert(GQA <= 16, "query rows must fit the MFMA M dimension");
+  constexpr int RPL = D / 64;             // Key-scale slots per lane in the operand build
+  constexpr float kFixQ = 1047552.0f;     // 2^20 (1 - 2^-10): |round(a F)| <= 2^20
+  constexpr float kFixP = 2097150.0f;     // P < 2^21: top digit <= 127
   const Geom& g = a.g;
-  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int q4 = lane / 16, col = lane % 16;
   const int unit = blockIdx.y;
   const int split = blockIdx.x;
 
-  __shared__ float qsT[D][GQA];
-  __shared__ __attribute__((aligned(16))) _Float16 pV[kWaves][16][8][8];  // [row][token block][slot]
-  __shared__ h8_t aKs[kWaves][2 * MK][kWave];     // folded-query operands, [hi/lo x mk][lane]
-  __shared__ float pw[kWaves][kTile][GQA];
+  __shared__ float qsT[D][GQA];                       // sigma log2e q (tail path)
+  __shared__ __attribute__((aligned(16))) float qsP[GQA][D];     // same, channels in slot order
+  __shared__ __attribute__((aligned(16))) float rkP[kWaves][D];  // 1 / kscale, slot order
+  __shared__ __attribute__((aligned(16))) uint32_t qD[kWaves][HG][MK][16][4][4];  // Key operand digits
+  __shared__ __attribute__((aligned(16))) uint32_t pD[kWaves][HG][16][4][4];      // Value operand digits
+  __shared__ float pw[kWaves][kTailChunk][GQA];
   __shared__ float red[kWaves][D][GQA];
   __shared__ float wml[kWaves][2][GQA];
 
-  load_q<D, GQA>(a, unit, qsT);
-  for (int i = tid; i < kWaves * 16 * 8 * 8; i += kThreads) (&pV[0][0][0][0])[i] = (_Float16)0.0f;
-  __syncthreads();
+  // Channel (or token) held in slot position p of a 64-wide group.
+  auto chan = [](int p) { return (p & ~15) + F16::field(p & 15); };
 
-  float m[GQA], l[GQA], alpha[GQA], acc_tail[TCPL][GQA];
-#pragma unroll
-  for (int h = 0; h < GQA; ++h) {
-    m[h] = -INFINITY;
-    l[h] = 0.0f;
-#pragma unroll
-    for (int k = 0; k < TCPL; ++k) acc_tail[k][h] = 0.0f;
-  }
-  f4_t acc[NV];
-#pragma unroll
-  for (int n = 0; n < NV; ++n) acc[n] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-  int w_begin, w_end;
-  wave_items(a, split, wave, w_begin, w_end);
+  const WaveWork ww = wave_work(a, split, wave);
+  const int w_begin = ww.t0, q_end = ww.t1;
   const uint8_t* kbase = a.k_codes + (int64_t)unit * g.code_stream;
   const uint8_t* vbase = a.v_codes + (int64_t)unit * g.code_stream;
   const uint16_t* ksbase = a.k_scale + (int64_t)unit * g.max_seg * D;
   const uint16_t* vsbase = a.v_scale + (int64_t)unit * g.C;
-  // Per-lane byte offsets inside a tile (the tile base is wave-uniform).
-  const int lk = col * 16 + 4 * q4;               // Key word: token 16 grp + col, channels 8 q4..
-  const int lv = col * (8 * BITS) + 8 * q4;       // Value words: channel 16 n + col, blocks 2 q4, 2 q4 + 1
-  const int pv_slot = (col / 8) * 8 + elem_slot(col % 8);   // this lane's token in pV[row][.][.]
-  const int hq = col < GQA ? col : 0;
-  const float row_mask = col < GQA ? 16.0f : 0.0f;   // 16x pre-scale; padding rows are zero
-  uint32_t nib_mask = a.nib_mask;
-  const uint32_t nib_one = a.nib_one;
-  // Keep the mask in a vector register (an empty statement, no instruction):
-  // v_and_or_b32 may read only one scalar operand.
-  asm("" : "+v"(nib_mask));
-  float corrK[4];         // 1.5 * sum of the Key operand over channels, result rows 4 q4 + i
-  float corrV[GQA];       // 1.5 * sum of the Value weights (running, rescaled like acc)
-#pragma unroll
-  for (int h = 0; h < GQA; ++h) corrV[h] = 0.0f;
-  h8_t* aK = &aKs[wave][0][lane];              // [hi/lo][mk] operands of this lane, stride 64
 
-  // Code words of one tile, as this lane needs them.
-  struct TileRegs {
-    uint32_t kw[4][MK];   // [token group][channel block]: 8 channels of token 16 grp + col
-    uint2 vw[NV];         // channel 16 n + col, token blocks 2 q4 and 2 q4 + 1
-    float vs[4];          // Value scales of tokens 16 grp + col
-    bool new_seg;         // the tile opens a Key segment: ksn holds its scales
+  // Per-lane constants: tokens T(gg, col) of the Key MFMAs, code byte offsets.
+  int tok[4];
+#pragma unroll
+  for (int gg = 0; gg < 4; ++gg) tok[gg] = 16 * (col / 4) + F16::field(4 * (col % 4) + gg);
+  int koff[4][MK];
+#pragma unroll
+  for (int gg = 0; gg < 4; ++gg)
+#pragma unroll
+    for (int mk = 0; mk < MK; ++mk) {
+      const int r0 = 8 * BITS * mk + 2 * BITS * q4;
+      koff[gg][mk] = (r0 / 16) * 1024 + tok[gg] * 16 + r0 % 16;
+    }
+  const int voff = col * (8 * BITS) + 2 * BITS * q4;
+
+  // Online-softmax state: head 4 hg + q4 of this lane's row quad.
+  float m[HG], lsum[HG], inv[HG], mq[HG];
+  float acc_f[HG][NV];
+  i4_t acc_i[HG][NV];
+  auto init_state = [&]() {
+#pragma unroll
+    for (int hg = 0; hg < HG; ++hg) {
+      m[hg] = -INFINITY;
+      lsum[hg] = 0.0f;
+      inv[hg] = 0.0f;
+#pragma unroll
+      for (int n = 0; n < NV; ++n) {
+        acc_f[hg][n] = 0.0f;
+        acc_i[hg][n] = i4_t{0, 0, 0, 0};
+      }
+      // max |q| of head 4 hg + q4 (bounds the fixed-point query with max 1/kscale)
+      const int h = 4 * hg + q4;
+      float mx = 0.0f;
+      if (h < GQA) {
+#pragma unroll
+        for (int k = 0; k < D / 16; ++k) mx = fmaxf(mx, fabsf(qsP[h][col * (D / 16) + k]));
+      }
+      mq[hg] = row16_max(mx);
+    }
   };
-  uint4 ksn[MK];          // Key scales of channels 32 mk + 8 q4 .. +7 of the next segment
+
+  struct TileRegs {
+    raw_t kw[4][MK];
+    raw_t vw[NV];
+    float vs[4];
+    uint16_t ks[RPL];     // Key scales (slot order lane * RPL + i) when the tile opens a segment
+    bool new_seg;
+  };
   auto load_tile = [&](int tile, TileRegs& r) {
     r.new_seg = tile == w_begin || tile % a.tiles_per_seg == 0;
-    if (r.new_seg) {      // first, so that waiting for it leaves the code words in flight
+    if (r.new_seg) {
       const uint16_t* ks = ksbase + (tile / a.tiles_per_seg) * D;
 #pragma unroll
-      for (int mk = 0; mk < MK; ++mk) ksn[mk] = *reinterpret_cast<const uint4*>(ks + 32 * mk + 8 * q4);
+      for (int i = 0; i < RPL; ++i) r.ks[i] = ks[chan(lane * RPL + i)];
     }
     const uint8_t* kt = kbase + (int64_t)tile * (kTile * W);
     const uint8_t* vt = vbase + (int64_t)tile * (kTile * W);
     const uint16_t* vst = vsbase + tile * kTile;
 #pragma unroll
-    for (int grp = 0; grp < 4; ++grp)
+    for (int gg = 0; gg < 4; ++gg)
 #pragma unroll
-      for (int mk = 0; mk < MK; ++mk)
-        r.kw[grp][mk] = *reinterpret_cast<const uint32_t*>(kt + lk + grp * 256 + mk * 1024);
+      for (int mk = 0; mk < MK; ++mk) r.kw[gg][mk] = *reinterpret_cast<const raw_t*>(kt + koff[gg][mk]);
 #pragma unroll
-    for (int n = 0; n < NV; ++n) r.vw[n] = *reinterpret_cast<const uint2*>(vt + lv + n * 16 * (8 * BITS));
+    for (int n = 0; n < NV; ++n) r.vw[n] = *reinterpret_cast<const raw_t*>(vt + n * 16 * (8 * BITS) + voff);
 #pragma unroll
-    for (int grp = 0; grp < 4; ++grp) r.vs[grp] = half_bits_to_f32(vst[16 * grp + col]);
+    for (int gg = 0; gg < 4; ++gg) r.vs[gg] = half_bits_to_f32(vst[tok[gg]]);
   };
 
-  // Key operands of a segment: 16 * sigma*log2e * q / kscale as hi + lo fp16,
-  // written to this wave's LDS slab (MFMA slot order).
-  auto build_key_operands = [&]() {
-    float rowsum = 0.0f;
+  // Key operands of a segment: digit d of round(F a[head][c]) in row 4 h + d.
+  // Lane items: head 4 hg + q4, k-group (lane / 4) % 4, dword lane % 4, both halves mk.
+  i4_t qop[HG][MK];
+  auto build_key_operands = [&](const TileRegs& r) {
+    float rkmax = 0.0f;
 #pragma unroll
-    for (int mk = 0; mk < MK; ++mk) {
-      const uint32_t kh[4] = {ksn[mk].x, ksn[mk].y, ksn[mk].z, ksn[mk].w};
-      h8_t hi8, lo8;
-#pragma unroll
-      for (int rr = 0; rr < 8; ++rr) {
-        const int e = slot_elem(rr);
-        const uint16_t bits = static_cast<uint16_t>(kh[e / 2] >> (16 * (e % 2)));
-        const float rk = fast_rcp(fmaxf(half_bits_to_f32(bits), g.eps));
-        const float v = row_mask * qsT[32 * mk + 8 * q4 + e][hq] * rk;
-        const _Float16 hi = (_Float16)v;
-        const _Float16 lo = (_Float16)(v - (float)hi);
-        hi8[rr] = hi;
-        lo8[rr] = lo;
-        rowsum += (float)hi + (float)lo;
-      }
-      aK[(0 * MK + mk) * kWave] = hi8;
-      aK[(1 * MK + mk) * kWave] = lo8;
+    for (int i = 0; i < RPL; ++i) {
+      const float rk = fast_rcp(fmaxf(half_bits_to_f32(r.ks[i]), g.eps));
+      rkP[wave][lane * RPL + i] = rk;
+      rkmax = fmaxf(rkmax, rk);
     }
-    // Row col's sum over all channels: its four channel quarters sit in lanes col + 16 q.
-    rowsum += __shfl_xor(rowsum, 16, kWave);
-    rowsum += __shfl_xor(rowsum, 32, kWave);
+    rkmax = wave_max(rkmax);
+    wave_lds_sync();
+    const int kgi = (lane / 4) % 4, qi = lane % 4;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) corrK[i] = 1.5f * __shfl(rowsum, 4 * q4 + i, kWave);
-  };
-
-  auto compute_tile = [&](const TileRegs& r) {
-    float vsr[4];         // 16 / max(vscale, eps)
+    for (int hg = 0; hg < HG; ++hg) {
+      const int h = 4 * hg + q4;
+      const float F = kFixQ / fmaxf(mq[hg] * rkmax, 1e-30f);   // all-zero query: any finite F
+      inv[hg] = h < GQA ? 1.0f / (F * F16::kMul) : 0.0f;
+      if (h < GQA) {
 #pragma unroll
-    for (int grp = 0; grp < 4; ++grp) vsr[grp] = 16.0f * fast_rcp(fmaxf(r.vs[grp], g.eps));
-
-    // ---- logits: S[head][token] = aK . (code / 16) ----
-    f4_t S[4];
-#pragma unroll
-    for (int grp = 0; grp < 4; ++grp) S[grp] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int mk = 0; mk < MK; ++mk) {
-      const h8_t ah = aK[(0 * MK + mk) * kWave];
-      const h8_t al = aK[(1 * MK + mk) * kWave];
-#pragma unroll
-      for (int grp = 0; grp < 4; ++grp) {
-        const h8_t kb = nibbles_to_h8(r.kw[grp][mk], nib_mask, nib_one);
-        S[grp] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, kb, S[grp], 0, 0, 0);
-        S[grp] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, kb, S[grp], 0, 0, 0);
+        for (int mk = 0; mk < MK; ++mk) {
+          const int p0 = 64 * mk + 16 * kgi + 4 * qi;
+          const float4 qv = *reinterpret_cast<const float4*>(&qsP[h][p0]);
+          const float4 rv = *reinterpret_cast<const float4*>(&rkP[wave][p0]);
+          const uint32_t u[4] = {fixed_biased(qv.x * rv.x, F), fixed_biased(qv.y * rv.y, F),
+                                 fixed_biased(qv.z * rv.z, F), fixed_biased(qv.w * rv.w, F)};
+          uint32_t* dst = &qD[wave][hg][mk][4 * q4][kgi][qi];
+          // balanced digits: (u & 127) - 64, ((u >> 7) & 127) - 64, (u >> 14) - 64
+          dst[0 * 16] = pack_bytes((u[0] >> 14) - 64u, (u[1] >> 14) - 64u, (u[2] >> 14) - 64u,
+                                   (u[3] >> 14) - 64u);
+          dst[1 * 16] = pack_bytes(((u[0] >> 7) & 127u) - 64u, ((u[1] >> 7) & 127u) - 64u,
+                                   ((u[2] >> 7) & 127u) - 64u, ((u[3] >> 7) & 127u) - 64u);
+          dst[2 * 16] = pack_bytes((u[0] & 127u) - 64u, (u[1] & 127u) - 64u, (u[2] & 127u) - 64u,
+                                   (u[3] & 127u) - 64u);
+        }
       }
-    }
-#pragma unroll
-    for (int grp = 0; grp < 4; ++grp)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) S[grp][i] -= corrK[i];
-
-    // ---- online softmax (rows 4 q4 + i of this lane; tokens 16 grp + col) ----
-    float rmax[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      rmax[i] = row16_max(fmaxf(fmaxf(S[0][i], S[1][i]), fmaxf(S[2][i], S[3][i])));
-#pragma unroll
-    for (int h = 0; h < GQA; ++h) alpha[h] = fold_max(m[h], lane_value(rmax[h % 4], 16 * (h / 4)));
-    bool moved = false;   // did any head's running maximum change?
-#pragma unroll
-    for (int h = 0; h < GQA; ++h) moved |= alpha[h] != 1.0f;
-    float rsum[4], rcs[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int hh = row_head<GQA>(q4, i);
-      const float mrow = m[hh];
-      float ps = 0.0f, cs = 0.0f;
-#pragma unroll
-      for (int grp = 0; grp < 4; ++grp) {
-        const float p = fast_exp2(S[grp][i] - mrow);
-        ps += p;
-        const _Float16 ap = (_Float16)(p * vsr[grp]);
-        cs += (float)ap;
-        if (4 * q4 + i < GQA) (&pV[wave][4 * q4 + i][0][0])[grp * 16 + pv_slot] = ap;
-      }
-      rsum[i] = row16_sum(ps);
-      rcs[i] = row16_sum(cs);
-    }
-    if (moved) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float al = alpha[row_head<GQA>(q4, i)];
-#pragma unroll
-        for (int n = 0; n < NV; ++n) acc[n][i] *= al;
-      }
-#pragma unroll
-      for (int h = 0; h < GQA; ++h)
-#pragma unroll
-        for (int k = 0; k < TCPL; ++k) acc_tail[k][h] *= alpha[h];
-    }
-#pragma unroll
-    for (int h = 0; h < GQA; ++h) {
-      l[h] = l[h] * alpha[h] + lane_value(rsum[h % 4], 16 * (h / 4));
-      corrV[h] = corrV[h] * alpha[h] + 1.5f * lane_value(rcs[h % 4], 16 * (h / 4));
     }
     wave_lds_sync();
-
-    // ---- values: acc[head][channel] += (16 p / vscale) . (1 + (code + 8) / 16) ----
-    const h8_t A0 = *reinterpret_cast<const h8_t*>(&pV[wave][col][2 * q4][0]);
-    const h8_t A1 = *reinterpret_cast<const h8_t*>(&pV[wave][col][2 * q4 + 1][0]);
 #pragma unroll
-    for (int n = 0; n < NV; ++n) {
-      acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, nibbles_to_h8(r.vw[n].x, nib_mask, nib_one), acc[n], 0, 0, 0);
-      acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, nibbles_to_h8(r.vw[n].y, nib_mask, nib_one), acc[n], 0, 0, 0);
-    }
-    wave_lds_sync();      // pV is rewritten by the next tile
+    for (int hg = 0; hg < HG; ++hg)
+#pragma unroll
+      for (int mk = 0; mk < MK; ++mk) qop[hg][mk] = *reinterpret_cast<const i4_t*>(&qD[wave][hg][mk][col][q4][0]);
   };
 
-  // Quantized tiles, double-buffered: the next tile's loads are in flight
-  // while the current one is computed.
-  const int q_end = w_end < a.tiles_q ? w_end : a.tiles_q;
+  // int32 digit sums -> fp32 accumulator (before a rescale and at the end)
+  auto fold_int = [&](int hg, float scale) {
+#pragma unroll
+    for (int n = 0; n < NV; ++n) {
+      acc_f[hg][n] = (acc_f[hg][n] + digits_value(acc_i[hg][n])) * scale;
+      acc_i[hg][n] = i4_t{0, 0, 0, 0};
+    }
+  };
+
+  float fv = 0.0f;        // Fv: P = fv * p / vscale
+  auto compute_tile = [&](const TileRegs& r) {
+    float x[HG][4];
+#pragma unroll
+    for (int gg = 0; gg < 4; ++gg) {
+      i4_t s[HG];
+#pragma unroll
+      for (int hg = 0; hg < HG; ++hg) s[hg] = i4_t{0, 0, 0, 0};
+#pragma unroll
+      for (int mk = 0; mk < MK; ++mk) {
+        const i4_t kb = F16::unpack(r.kw[gg][mk]);
+#pragma unroll
+        for (int hg = 0; hg < HG; ++hg) s[hg] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qop[hg][mk], kb, s[hg], 0, 0, 0);
+      }
+#pragma unroll
+      for (int hg = 0; hg < HG; ++hg) x[hg][gg] = digits_value(s[hg]) * inv[hg];
+    }
+    float alpha[HG];
+    bool moved = false;   // a running maximum moved (the first tile only sets it)
+#pragma unroll
+    for (int hg = 0; hg < HG; ++hg) {
+      const float tm = row16_max(fmaxf(fmaxf(x[hg][0], x[hg][1]), fmaxf(x[hg][2], x[hg][3])));
+      const float mn = fmaxf(m[hg], tm);
+      alpha[hg] = fast_exp2(m[hg] - mn);
+      moved |= alpha[hg] != 1.0f && m[hg] != -INFINITY;
+      m[hg] = mn;
+    }
+    if (__any(moved)) {
+#pragma unroll
+      for (int hg = 0; hg < HG; ++hg) {
+        lsum[hg] *= alpha[hg];
+        fold_int(hg, alpha[hg]);
+      }
+    }
+    float vsrf[4];
+#pragma unroll
+    for (int gg = 0; gg < 4; ++gg) vsrf[gg] = fv * fast_rcp(fmaxf(r.vs[gg], g.eps));
+#pragma unroll
+    for (int hg = 0; hg < HG; ++hg) {
+      uint32_t P[4];
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg) {
+        const float p = fast_exp2(x[hg][gg] - m[hg]);
+        lsum[hg] += p;
+        P[gg] = (uint32_t)(p * vsrf[gg]);
+      }
+      uint32_t* dst = &pD[wave][hg][4 * q4][col / 4][col % 4];
+      dst[0 * 16] = pack_bytes(P[0] >> 14, P[1] >> 14, P[2] >> 14, P[3] >> 14);
+      dst[1 * 16] = pack_bytes((P[0] >> 7) & 127u, (P[1] >> 7) & 127u, (P[2] >> 7) & 127u, (P[3] >> 7) & 127u);
+      dst[2 * 16] = pack_bytes(P[0] & 127u, P[1] & 127u, P[2] & 127u, P[3] & 127u);
+    }
+    wave_lds_sync();
+    i4_t pop[HG];
+#pragma unroll
+    for (int hg = 0; hg < HG; ++hg) pop[hg] = *reinterpret_cast<const i4_t*>(&pD[wave][hg][col][q4][0]);
+#pragma unroll
+    for (int n = 0; n < NV; ++n) {
+      const i4_t vb = F16::unpack(r.vw[n]);
+#pragma unroll
+      for (int hg = 0; hg < HG; ++hg) acc_i[hg][n] = __builtin_amdgcn_mfma_i32_16x16x64_i8(pop[hg], vb, acc_i[hg][n], 0, 0, 0);
+    }
+    wave_lds_sync();      // pD is rewritten by the next tile
+  };
+
+  // Every global load of the first two tiles (and the run's Value scales,
+  // which fix Fv) is issued before the query is read: one memory round trip.
   int tile = w_begin;
   TileRegs bufA, bufB;
-  if (tile < q_end) load_tile(tile, bufA);
-  while (tile < q_end) {
-    if (bufA.new_seg) {
-      build_key_operands();
-      wave_lds_sync();
-    }
-    if (tile + 1 < q_end) load_tile(tile + 1, bufB);
-    compute_tile(bufA);
-    if (++tile >= q_end) break;
-    if (bufB.new_seg) {
-      build_key_operands();
-      wave_lds_sync();
-    }
-    if (tile + 1 < q_end) load_tile(tile + 1, bufA);
-    compute_tile(bufB);
-    ++tile;
+  float vs_run[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int t = (w_begin + k) * kTile + lane;
+    vs_run[k] = t < q_end * kTile ? half_bits_to_f32(vsbase[t]) : INFINITY;
   }
-  // Tail chunks (bf16), after the quantized tiles of this wave.
-  for (tile = tile > w_begin ? tile : w_begin; tile < w_end; ++tile) {
-    if (tile < a.tiles_q) continue;
-    tail_chunk<D, GQA, true>(a, unit, tile - a.tiles_q, qsT, pw[wave], m, l, alpha, acc_tail);
+  if (tile < q_end) load_tile(tile, bufA);
+  if (tile + 1 < q_end) load_tile(tile + 1, bufB);
+  TailRegs<D, true> trA, trB;
+  if (ww.c0 < ww.c1) tail_load<D, true>(a, unit, ww.c0, trA);
+
+  {
+    const int b = unit / g.H, kvh = unit % g.H;
+    for (int i = tid; i < GQA * D; i += kThreads) {
+      const int h = i / D, c = i % D;
+      const int64_t row = ((int64_t)b * g.H * GQA + kvh * GQA + h) * D;
+      qsT[c][h] = load_elem(a.q, row + c, g.dtype) * a.qscale;
+      qsP[h][c] = load_elem(a.q, row + chan(c), g.dtype) * a.qscale;
+    }
+    uint4* z0 = reinterpret_cast<uint4*>(&qD[0][0][0][0][0][0]);
+    for (int i = tid; i < (int)(sizeof(qD) / 16); i += kThreads) z0[i] = uint4{0u, 0u, 0u, 0u};
+    uint4* z1 = reinterpret_cast<uint4*>(&pD[0][0][0][0][0]);
+    for (int i = tid; i < (int)(sizeof(pD) / 16); i += kThreads) z1[i] = uint4{0u, 0u, 0u, 0u};
+  }
+  __syncthreads();
+  init_state();
+
+  if (tile < q_end) {
+    // Fv from the largest 1 / vscale of the run.
+    float vsr_max = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) vsr_max = fmaxf(vsr_max, fast_rcp(fmaxf(vs_run[k], g.eps)));
+    for (int t0 = (w_begin + 4) * kTile; t0 < q_end * kTile; t0 += 4 * kTile) {
+      float vs4[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int t = t0 + k * kTile + lane;
+        vs4[k] = t < q_end * kTile ? half_bits_to_f32(vsbase[t]) : INFINITY;
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) vsr_max = fmaxf(vsr_max, fast_rcp(fmaxf(vs4[k], g.eps)));
+    }
+    fv = kFixP / wave_max(vsr_max);
+  }
+  // Quantized tiles, two in flight: while one is computed the other's loads
+  // are outstanding.  The int32 Value sums are folded into fp32 at least
+  // every 1024 tiles (no overflow).
+  int since_fold = 0;
+  while (tile < q_end) {
+    if (bufA.new_seg) build_key_operands(bufA);
+    compute_tile(bufA);
+    if (tile + 2 < q_end) load_tile(tile + 2, bufA);
+    if (++tile >= q_end) break;
+    if (bufB.new_seg) build_key_operands(bufB);
+    compute_tile(bufB);
+    if (tile + 2 < q_end) load_tile(tile + 2, bufB);
+    ++tile;
+    if ((since_fold += 2) >= 1024) {
+      since_fold = 0;
+#pragma unroll
+      for (int hg = 0; hg < HG; ++hg) fold_int(hg, 1.0f);
+    }
+  }
+#pragma unroll
+  for (int hg = 0; hg < HG; ++hg) fold_int(hg, 1.0f);
+
+  // Per-head state as wave-uniform values (head 4 hg + i lives in lanes 16 i..).
+  float mu[GQA], lu[GQA], alpha_u[GQA], acc_tail[TCPL][GQA];
+#pragma unroll
+  for (int hg = 0; hg < HG; ++hg) {
+    const float ls = row16_sum(lsum[hg]);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float al = alpha[row_head<GQA>(q4, i)];
-#pragma unroll
-      for (int n = 0; n < NV; ++n) acc[n][i] *= al;
+      const int h = 4 * hg + i;
+      if (h < GQA) {
+        mu[h] = lane_value(m[hg], 16 * i);
+        lu[h] = lane_value(ls, 16 * i);
+      }
     }
+  }
 #pragma unroll
-    for (int h = 0; h < GQA; ++h) corrV[h] *= alpha[h];
+  for (int h = 0; h < GQA; ++h)
+#pragma unroll
+    for (int k = 0; k < TCPL; ++k) acc_tail[k][h] = 0.0f;
+  // Rescale the quantized-tile accumulator of this lane's head by a tail
+  // chunk's alpha (wave-uniform per head).
+  auto rescale_tail = [&](const float* al_u) {
+#pragma unroll
+    for (int hg = 0; hg < HG; ++hg) {
+      float al = 1.0f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (4 * hg + i < GQA && q4 == i) al = al_u[4 * hg + i];
+#pragma unroll
+      for (int n = 0; n < NV; ++n) acc_f[hg][n] *= al;
+    }
+  };
+
+  // Tail chunks (bf16) after the quantized tiles of this wave; the first
+  // chunk's loads were issued with the tiles', each later one is loaded
+  // while the one before is computed.
+  for (int chunk = ww.c0; chunk < ww.c1; chunk += 2) {
+    if (chunk + 1 < ww.c1) tail_load<D, true>(a, unit, chunk + 1, trB);
+    tail_compute<D, GQA, true>(a, trA, qsT, pw[wave], mu, lu, alpha_u, acc_tail);
+    rescale_tail(alpha_u);
+    if (chunk + 1 >= ww.c1) break;
+    if (chunk + 2 < ww.c1) tail_load<D, true>(a, unit, chunk + 2, trA);
+    tail_compute<D, GQA, true>(a, trB, qsT, pw[wave], mu, lu, alpha_u, acc_tail);
+    rescale_tail(alpha_u);
   }
 
   // ---- wave result into red[wave][channel][head] ----
+  const float vscale_out = fv > 0.0f ? 1.0f / (fv * F16::kMul) : 0.0f;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int h = 4 * q4 + i;
+  for (int hg = 0; hg < HG; ++hg) {
+    const int h = 4 * hg + q4;
     if (h < GQA) {
 #pragma unroll
-      for (int n = 0; n < NV; ++n) red[wave][16 * n + col][h] = acc[n][i] - corrV[h];
+      for (int n = 0; n < NV; ++n) red[wave][16 * n + col][h] = acc_f[hg][n] * vscale_out;
     }
   }
   wave_lds_sync();
@@ -741,38 +968,15 @@ void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
       for (int h = 0; h < GQA; ++h) red[wave][lane * TCPL + k][h] += acc_tail[k][h];
   }
-  fold_and_store<D, GQA>(a, unit, split, red, wml, m, l);
-}
-
-// One workgroup per (batch, KV head): combine the splits' (m, l, acc).
-template <int D, int GQA>
-__global__ __launch_bounds__(kThreads) void merge_kernel(DecodeArgs a) {
-  const int unit = blockIdx.x;
-  const int b = unit / a.g.H, kvh = unit % a.g.H;
-  const float* pu = a.part + (int64_t)unit * a.splits * GQA * (D + 2);
-  for (int i = threadIdx.x; i < GQA * D; i += kThreads) {
-    const int h = i / D, c = i % D;
-    float mx = -INFINITY;
-    for (int s = 0; s < a.splits; ++s) mx = fmaxf(mx, pu[(s * GQA + h) * (D + 2) + D]);
-    float num = 0.0f, den = 0.0f;
-#pragma unroll 8
-    for (int s = 0; s < a.splits; ++s) {
-      const float* ps = pu + (s * GQA + h) * (D + 2);
-      const float ms = ps[D];
-      const float e = (ms == -INFINITY) ? 0.0f : fast_exp2(ms - mx);
-      num = fmaf(ps[c], e, num);
-      den = fmaf(ps[D + 1], e, den);
-    }
-    a.out[((int64_t)b * a.g.H * GQA + kvh * GQA + h) * D + c] = num / den;
-  }
+  fold_and_store<D, GQA>(a, unit, split, red, wml, mu, lu);
 }
 
 template <int D, int BITS, int GQA>
 void launch(const DecodeArgs& a, hipStream_t s) {
   dim3 grid(a.splits, a.g.B * a.g.H);
-  if constexpr (BITS == 4 && D >= 64) {
+  if constexpr ((BITS == 4 || BITS == 2) && D >= 64) {
     if (a.g.G > 0 && a.g.dtype == KVQ_BF16)
-      hipLaunchKernelGGL((decode_mfma_kernel<D, GQA>), grid, dim3(kThreads), 0, s, a);
+      hipLaunchKernelGGL((decode_i8_kernel<D, BITS, GQA>), grid, dim3(kThreads), 0, s, a);
     else
       hipLaunchKernelGGL((decode_kernel<D, BITS, GQA>), grid, dim3(kThreads), 0, s, a);
   } else {
@@ -862,12 +1066,11 @@ extern "C" kvq_status kvq_decode_attn(const kvq_config* cfg, const kvq_state* st
   a.qscale = softmax_scale * 1.4426950408889634f;
   a.out = out;
   a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + workspace_counter_bytes(g, 1));
-  a.nib_mask = 0x03C003C0u;
-  a.nib_one = 0x3C003C00u;
   a.tiles_q = (a.nq + kTile - 1) / kTile;
   a.items = a.tiles_q + (a.nt + kTailChunk - 1) / kTailChunk;
   const int units = g.B * g.H;
   a.splits = num_splits > 0 ? num_splits : auto_splits(units, a.items);
+  clear_stale_hip_error();
   if (!dispatch(a, gqa, static_cast<hipStream_t>(stream))) return KVQ_EINVAL;
   return hipGetLastError() == hipSuccess ? KVQ_OK : KVQ_EDEVICE;
 }

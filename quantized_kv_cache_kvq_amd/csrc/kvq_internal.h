@@ -55,10 +55,11 @@ __device__ __forceinline__ int sext_field(uint32_t word, int shift) {
 // mirrors (every lane of the row ends with the result).  Across the wave: the
 // four row results are read into scalar registers.
 
+// Full-row permutations only (every lane has a source), so the DPP move has
+// no "old" operand and folds into the consuming add / max (v_add_f32_dpp).
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
-                                                               0xF, 0xF, false));
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
 }
 
 constexpr int kDppQuadXor1 = 0xB1;     // quad_perm [1, 0, 3, 2]
@@ -101,6 +102,11 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
 // ---- host helpers ----------------------------------------------------------------
+
+// HIP reports a failed launch through the calling thread's last-error slot.
+// Entry points clear whatever an earlier, unrelated HIP call left there
+// before they launch, so KVQ_EDEVICE reports their own launches only.
+inline void clear_stale_hip_error() { (void)hipGetLastError(); }
 
 kvq_status validate_config(const kvq_config* cfg, Geom* g);
 

@@ -126,3 +126,42 @@ def test_decode_long_context_one_layer():
     err = max_abs(got, ref)
     note(f"decode long context layer 0: max-abs {err:.3e}")
     assert err <= TOL
+
+
+@needs_gpu
+@pytest.mark.parametrize("D,bits,qmax", [(128, 4, 7), (128, 2, 1), (64, 8, 127)])
+def test_decode_zero_query_is_mean_of_values(D, bits, qmax):
+    """q = 0 gives uniform weights: the output is the mean of the restored values."""
+    w = ks.small(ks.LLAMA3_DECODE, batch=1, kv_heads=2, q_heads=8, head_dim=D, code_bits=bits,
+                 qmax=qmax)
+    p, s = build(w, 700)
+    q = torch.zeros(w.batch, w.q_heads, w.head_dim, dtype=torch.bfloat16)
+    got, _ = p.decode(q)
+    err = max_abs(got, p.decode_ref(q))
+    note(f"decode zero query D={D} bits={bits}: max-abs {err:.3e}")
+    assert err <= TOL
+
+
+@needs_gpu
+@pytest.mark.parametrize("splits", [0, 5, 24])
+def test_decode_back_to_back_on_one_workspace(splits):
+    """Calls queued back to back on one workspace each see their own partials.
+
+    The split partials are merged by the last workgroup of each (batch, KV
+    head); a stale or early read would mix in the previous call's values.
+    """
+    w = ks.small(ks.LLAMA3_DECODE, batch=2, kv_heads=4, q_heads=16)
+    p, s = build(w, 2000)
+    qs = [ks.decode_query(s) for _ in range(4)]
+    refs = [p.decode_ref(q) for q in qs]
+    ws = p.cache.workspace(w.q_heads)
+    outs = []
+    note(f"decode back to back splits={splits}")
+    for q in qs + qs:
+        out = torch.empty(w.batch, w.q_heads, w.head_dim, device="cuda")
+        p.cache.decode_attn(q.cuda(), out, ws, num_splits=splits)
+        outs.append(out)
+    torch.cuda.synchronize()
+    for i, out in enumerate(outs):
+        assert max_abs(out.cpu().numpy(), refs[i % 4]) <= TOL, i
+    assert not ws[:64].any()
