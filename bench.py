@@ -149,6 +149,63 @@ def run_decode(args, log):
     return res, (cfg, w)
 
 
+def block_flops(nq_total: int, tq: int, q_heads: int, head_dim: int, batch: int = 1) -> float:
+    """Algorithmic FLOPs of one causal block: QK^T and PV over N cached tokens
+    plus the block's own visible tokens (query i sees i + 1 of them)."""
+    pairs = tq * nq_total + tq * (tq + 1) // 2
+    return 4.0 * batch * q_heads * head_dim * pairs
+
+
+def run_video_block(args, log):
+    """One causal block of 1024 queries against the 432000-token int2 cache."""
+    import torch
+
+    import kvq_synth as ks
+    from quantized_kv_cache_kvq_amd import KVCache, make_config
+
+    w = ks.VIDEO_BLOCK
+    cfg = make_config(batch=w.batch, kv_heads=w.kv_heads, head_dim=w.head_dim,
+                      capacity=w.prefill + 128, code_bits=w.code_bits, qmax=w.qmax,
+                      residual=w.residual, group=w.group)
+    s = ks.Stream(w, seed=0)
+    k, v = ks.kv_pair(s, w.prefill)
+    c = KVCache(cfg, zero=False)
+    c.append(k.cuda(), v.cuda())
+    del k, v
+    q, kb, vb = (t.cuda() for t in ks.block_inputs(s, w.block_q))
+    out = torch.empty(w.batch, w.block_q, w.q_heads, w.head_dim, device="cuda")
+    ws = c.workspace(w.q_heads, w.block_q)
+    stream = torch.cuda.current_stream()
+    steps, warmup = max(1, args.steps // 20), max(1, args.warmup // 10)
+    for _ in range(warmup):
+        c.block_attn(q, kb, vb, out, ws)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record(stream)
+        c.block_attn(q, kb, vb, out, ws)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in ev) / steps
+    flops = block_flops(c.state.total, w.block_q, w.q_heads, w.head_dim, w.batch)
+    tflops = flops / (ms * 1e-3) / 1e12
+    log(f"video block: {ms:.3f} ms per block, {tflops:.1f} TFLOP/s")
+    return {
+        "metric": "causal block attention over the quantized cache, ms per block",
+        "value": round(ms, 4), "unit": "ms", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16/f16 MFMA, f32 accumulate", "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "q_heads": w.q_heads,
+                   "kv_heads": w.kv_heads, "head_dim": w.head_dim, "cached": c.state.total,
+                   "block_q": w.block_q, "codes": f"int{w.code_bits}", "parallelism": "single-gpu"},
+        "flops_per_block": flops,
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": 2500.0,
+                     "unit": "TFLOP/s", "frac": round(tflops / 2500.0, 4), "traffic": None,
+                     "kernel": "kvq_block_attn = block_kernel<128,2> + block_merge_kernel<128>"},
+    }
+
+
 def cpu_baseline_decode(budget_s: float, log):
     """Time the CPU oracle's decode attention on a bounded sample of units."""
     import numpy as np
@@ -201,6 +258,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quiet", action="store_true")
+    ap.add_argument("--workload", choices=["llama3_decode", "video_block"], default="llama3_decode",
+                    help="llama3_decode (default): the append + decode step; video_block: one "
+                         "1024-query causal block against the 432000-token int2 cache")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build runs on a single MI355X and has no "
@@ -220,9 +280,12 @@ def main():
         import __graft_entry__
         __graft_entry__.build()
     kvq.load()
-    res, _ = run_decode(args, log)
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline_decode(args.cpu_budget, log)
+    if args.workload == "video_block":
+        res = run_video_block(args, log)
+    else:
+        res, _ = run_decode(args, log)
+        if not args.no_cpu_baseline:
+            res["cpu_baseline"] = cpu_baseline_decode(args.cpu_budget, log)
     print(json.dumps(res), flush=True)
 
 

@@ -1,13 +1,486 @@
-// Block attention entry point (MFMA kernels land in this file).
+// Causal block attention over the quantized cache, on the MFMA units.
+//
+// Definition ("KV Cache and autoregressive video generation", section 3.1,
+// causal mask M_ij = -inf for j > i): a block of tq new queries at absolute
+// positions N .. N + tq - 1 (N cached tokens) attends to every cached token
+// and to the block's own keys and values up to its own position; query head h
+// reads KV head h / g (section 04).  The quantized prefix is restored inside
+// the kernel (k = code / kscale, v = code / vscale: "KV Cache Quantization
+// Strategies", Step 4 ``restore``); tail and block tokens are used as stored.
+//
+// Work: grid = (query row tiles, KV splits, batch * KV heads).  A workgroup
+// owns 128 query rows of one KV head -- a row is a (position, head) pair --
+// and a contiguous range of 64-token KV tiles: quantized tiles, then tail
+// tiles (bf16 ring), then own-block tiles (bf16, causal).  Its 256 threads
+// restore each tile once into LDS, shared by the four waves (32 rows each):
+//   Khi, Klo [token][channel]  bf16 hi + lo of code / kscale (tail and block
+//                              tokens: the stored value, lo = 0)
+//   V [channel][token]         fp16: the codes (exact), or the stored values
+//   vsr [token]                1 / vscale, 1 for tail and block tokens
+// Logits are computed transposed, S^T = Khat . Q^T, on
+// v_mfma_f32_16x16x32_bf16: queries are bf16 (exact) and Khat = hi + lo keeps
+// ~16 significant bits (one 16-bit rounding of an outlier channel's 1/kscale
+// alone moves logits by ~1e-3).  A lane then holds four consecutive tokens of
+// one query in each 16-token block -- exactly its operand of the P.V product
+// on v_mfma_f32_16x16x32_f16 once that MFMA's k slots of lane group kg are the
+// tokens 32 ks + 4 kg + j (j < 4) and 32 ks + 16 + 4 kg + (j - 4): no transpose
+// of P.  The weights p / vscale are rounded to fp16.
+// Online softmax per query row in the log2 domain.  When a running maximum
+// moves, the output accumulator (whose rows live in other lanes) is rescaled
+// through LDS.  With several splits, partials (m, l, acc) are merged by
+// block_merge_kernel.
 #include "kvq_internal.h"
+
+namespace kvq {
+
+size_t workspace_bytes(const Geom& g, int q_heads, int tq);
+size_t workspace_counter_bytes(const Geom& g, int tq);
+
+namespace {
+
+constexpr int kBT = 256;                 // threads per workgroup
+constexpr int kBWaves = kBT / kWave;
+constexpr int kRowsWave = 32;            // two 16-row query blocks per wave
+constexpr int kRowsWG = kRowsWave * kBWaves;
+constexpr int kBlockMaxSplits = 8;       // partial slots the workspace holds for tq > 1
+
+typedef __bf16 bf8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
+typedef float f4_t __attribute__((ext_vector_type(4)));
+
+struct BlockArgs {
+  Geom g;
+  const uint8_t* k_codes;
+  const uint8_t* v_codes;
+  const uint16_t* k_scale;
+  const uint16_t* v_scale;
+  const uint16_t* k_tail;   // bf16
+  const uint16_t* v_tail;
+  const int32_t* seg_index;
+  const uint16_t* q;        // bf16 [B, tq, Hq, D]
+  const uint16_t* k_blk;    // bf16 [B, tq, Hkv, D]
+  const uint16_t* v_blk;
+  float* out;               // fp32 [B, tq, Hq, D]
+  float* part;              // [unit][split][row][D + 2]
+  int nq, nt, nq_slot;
+  int tq, gqa, rows;        // rows = tq * gqa query rows per KV head
+  float qscale;             // sigma * log2(e)
+  int tiles_q, tiles_t, tiles_b, splits;
+};
+
+// Token a tile slot covers, and whether it exists (per tile kind).
+enum TileKind { kQuant = 0, kTail = 1, kOwn = 2 };
+
+template <int D, int BITS>
+__global__ __launch_bounds__(kBT) __attribute__((amdgpu_waves_per_eu(2)))
+void block_kernel(BlockArgs a) {
+  constexpr int CG = D / 4;                // channels per thread in the K fill
+  constexpr int KROW = D + 8;              // LDS row pitch (bf16) of Khi / Klo: no bank conflicts
+  constexpr int VROW = kTile + 8;          // LDS row pitch (fp16) of V
+  constexpr int KS = D / 32;               // k steps of the logit MFMAs
+  constexpr int CB = D / 16;               // channel blocks of the output
+  constexpr int TPC = kBT / D;             // threads per channel in the V fill
+  constexpr int NTV = kTile / TPC;         // tokens per thread in the V fill
+  constexpr int KW = (CG * BITS + 31) / 32;   // code words per thread (K fill)
+  constexpr int VW = (NTV * BITS + 31) / 32;  // code words per thread (V fill)
+  const Geom& g = a.g;
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int q4 = lane / 16, col = lane % 16;
+  const int unit = blockIdx.z;
+  const int split = blockIdx.y;
+  const int b = unit / g.H, kvh = unit % g.H;
+  const int r0 = blockIdx.x * kRowsWG;
+  const int Hq = g.H * a.gqa;
+
+  __shared__ __attribute__((aligned(16))) __bf16 Khi[kTile][KROW];
+  __shared__ __attribute__((aligned(16))) __bf16 Klo[kTile][KROW];
+  __shared__ __attribute__((aligned(16))) _Float16 Vs[D][VROW];
+  __shared__ float vsr[kTile];
+  __shared__ float xch[kBWaves][kRowsWave];   // per-row values exchanged inside a wave
+
+  // ---- this wave's query rows: operand B of S^T = Khat . Q^T ----
+  bf8_t qop[2][KS];
+  int qpos[2];        // position of query row col of block qb (or -1 past the end)
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int r = r0 + wave * kRowsWave + qb * 16 + col;
+    const bool ok = r < a.rows;
+    const int pos = ok ? r / a.gqa : 0, h = ok ? r % a.gqa : 0;
+    qpos[qb] = ok ? pos : -1;
+    const uint16_t* qrow = a.q + (((int64_t)b * a.tq + pos) * Hq + kvh * a.gqa + h) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      uint4 w = ok ? *reinterpret_cast<const uint4*>(qrow + 32 * ks + 8 * q4) : uint4{0u, 0u, 0u, 0u};
+      qop[qb][ks] = __builtin_bit_cast(bf8_t, w);
+    }
+  }
+  const int pos_hi = (min(r0 + kRowsWG, a.rows) - 1) / a.gqa;   // last position in the workgroup
+
+  float m[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.0f, 0.0f};
+  f4_t acc[2][CB];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) acc[qb][cb] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  const int items = a.tiles_q + a.tiles_t + a.tiles_b;
+  const int i0 = (int)(((int64_t)items * split) / a.splits);
+  const int i1 = (int)(((int64_t)items * (split + 1)) / a.splits);
+  const int64_t stream = (int64_t)unit * g.code_stream;
+
+  for (int item = i0; item < i1; ++item) {
+    const int kind = item < a.tiles_q ? kQuant : (item < a.tiles_q + a.tiles_t ? kTail : kOwn);
+    const int tile = kind == kQuant ? item : (kind == kTail ? item - a.tiles_q : item - a.tiles_q - a.tiles_t);
+    const int t0 = tile * kTile;
+    if (kind == kOwn && t0 > pos_hi) break;   // later block tiles are masked for every row here
+    const int count = kind == kQuant ? min(kTile, a.nq - t0)
+                                     : (kind == kTail ? min(kTile, a.nt - t0) : min(kTile, a.tq - t0));
+
+    // ---- fill: restore the tile into LDS ----
+    {
+      const int i = tid % kTile, grp = tid / kTile;     // K: token i, channels grp * CG ..
+      const bool tv = i < count;
+      if (kind == kQuant) {
+        const uint8_t* kt = a.k_codes + stream + (int64_t)tile * (kTile * g.W);
+        uint32_t w[KW];
+        const int rb = grp * CG * BITS / 8;              // first byte of the run in the token row
+#pragma unroll
+        for (int k = 0; k < KW; ++k) {
+          const int rr = rb + 4 * k;
+          w[k] = tv ? *reinterpret_cast<const uint32_t*>(kt + (rr / 16) * 1024 + i * 16 + rr % 16) : 0u;
+        }
+        const int seg = !tv ? 0 : (g.G > 0 ? (t0 + i) / g.G : a.seg_index[t0 + i]);
+        const uint16_t* ks = a.k_scale + ((int64_t)unit * g.max_seg + seg) * D + grp * CG;
+#pragma unroll
+        for (int e = 0; e < CG; e += 8) {
+          const uint4 sw = *reinterpret_cast<const uint4*>(ks + e);
+          const uint32_t sv[4] = {sw.x, sw.y, sw.z, sw.w};
+          __bf16 hi[8], lo[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int f = e + j;
+            const int code = sext_field<BITS>(w[f * BITS / 32], (f * BITS) % 32);
+            const float rk = fast_rcp(fmaxf(half_bits_to_f32((uint16_t)(sv[j / 2] >> (16 * (j % 2)))), g.eps));
+            const float x = (float)code * rk;
+            hi[j] = (__bf16)x;
+            lo[j] = (__bf16)(x - (float)hi[j]);
+          }
+          *reinterpret_cast<uint4*>(&Khi[i][grp * CG + e]) = __builtin_bit_cast(uint4, hi);
+          *reinterpret_cast<uint4*>(&Klo[i][grp * CG + e]) = __builtin_bit_cast(uint4, lo);
+        }
+        // V: channel c, tokens vt0 .. vt0 + NTV - 1 (a run of the channel's row)
+        const int c = tid % D, vt0 = (tid / D) * NTV;
+        const uint8_t* vt = a.v_codes + stream + (int64_t)tile * (kTile * g.W) + c * (8 * BITS) + vt0 * BITS / 8;
+        uint32_t vw[VW];
+#pragma unroll
+        for (int k = 0; k < VW; ++k) vw[k] = *reinterpret_cast<const uint32_t*>(vt + 4 * k);
+#pragma unroll
+        for (int j0 = 0; j0 < NTV; j0 += 8) {
+          _Float16 v8[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int f = j0 + j;
+            v8[j] = (_Float16)(float)sext_field<BITS>(vw[f * BITS / 32], (f * BITS) % 32);
+          }
+          *reinterpret_cast<uint4*>(&Vs[c][vt0 + j0]) = __builtin_bit_cast(uint4, v8);
+        }
+        if (tid < kTile) {
+          const int t = t0 + tid;
+          vsr[tid] = tid < count ? fast_rcp(fmaxf(half_bits_to_f32(a.v_scale[(int64_t)unit * g.C + t]), g.eps)) : 0.0f;
+        }
+      } else {
+        // bf16 rows: K copied as the hi part (lo = 0), V transposed into fp16
+        const uint16_t* krow;
+        const uint16_t* vrow;
+        if (kind == kTail) {
+          int slot = a.nq_slot + t0 + (tv ? i : 0);
+          slot = slot >= g.ring ? slot - g.ring : slot;
+          krow = a.k_tail + ((int64_t)unit * g.ring + slot) * D;
+          vrow = a.v_tail + ((int64_t)unit * g.ring + slot) * D;
+        } else {
+          const int j = t0 + (tv ? i : 0);
+          krow = a.k_blk + (((int64_t)b * a.tq + j) * g.H + kvh) * D;
+          vrow = a.v_blk + (((int64_t)b * a.tq + j) * g.H + kvh) * D;
+        }
+#pragma unroll
+        for (int e = 0; e < CG; e += 8) {
+          const uint4 kw = tv ? *reinterpret_cast<const uint4*>(krow + grp * CG + e) : uint4{0u, 0u, 0u, 0u};
+          const uint4 vv = tv ? *reinterpret_cast<const uint4*>(vrow + grp * CG + e) : uint4{0u, 0u, 0u, 0u};
+          *reinterpret_cast<uint4*>(&Khi[i][grp * CG + e]) = kw;
+          *reinterpret_cast<uint4*>(&Klo[i][grp * CG + e]) = uint4{0u, 0u, 0u, 0u};
+          const uint32_t vs4[4] = {vv.x, vv.y, vv.z, vv.w};
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const float v = __uint_as_float((vs4[j / 2] >> (16 * (j % 2))) << 16);
+            Vs[grp * CG + e + j][i] = (_Float16)v;
+          }
+        }
+        if (tid < kTile) vsr[tid] = tid < count ? 1.0f : 0.0f;
+      }
+    }
+    __syncthreads();
+
+    // ---- logits S^T[token][query] (token block tb, query block qb) ----
+    f4_t S[4][2];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) S[tb][qb] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf8_t ah = *reinterpret_cast<const bf8_t*>(&Khi[tb * 16 + col][32 * ks + 8 * q4]);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) S[tb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, qop[qb][ks], S[tb][qb], 0, 0, 0);
+        if (kind == kQuant) {
+          const bf8_t al = *reinterpret_cast<const bf8_t*>(&Klo[tb * 16 + col][32 * ks + 8 * q4]);
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb) S[tb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, qop[qb][ks], S[tb][qb], 0, 0, 0);
+        }
+      }
+    }
+
+    // ---- online softmax per query (lane's column col of block qb) ----
+    // S[tb][qb][i]: token t0 + 16 tb + 4 q4 + i.
+    h8_t pa[2][2];        // P operands: [qb][k step] (tokens 32 ks + 4 q4 + j, 32 ks + 16 + 4 q4 + j)
+    float alpha[2];
+    bool moved = false;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      float x[4][4];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int tt = 16 * tb + 4 * q4 + i;
+          const bool vis = tt < count && qpos[qb] >= 0 && (kind != kOwn || t0 + tt <= qpos[qb]);
+          x[tb][i] = vis ? S[tb][qb][i] * a.qscale : -INFINITY;
+          mx = fmaxf(mx, x[tb][i]);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+      const float mn = fmaxf(m[qb], mx);
+      alpha[qb] = (mn == -INFINITY) ? 1.0f : fast_exp2(m[qb] - mn);
+      moved |= alpha[qb] != 1.0f && m[qb] != -INFINITY;
+      m[qb] = mn;
+      const float mu = mn == -INFINITY ? 0.0f : mn;
+      float ps = 0.0f;
+      _Float16 ph[4][4];
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p = fast_exp2(x[tb][i] - mu);
+          ps += p;
+          ph[tb][i] = (_Float16)(p * vsr[16 * tb + 4 * q4 + i]);
+        }
+      lsum[qb] = lsum[qb] * alpha[qb] + ps;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        pa[qb][ks] = h8_t{ph[2 * ks][0], ph[2 * ks][1], ph[2 * ks][2], ph[2 * ks][3],
+                          ph[2 * ks + 1][0], ph[2 * ks + 1][1], ph[2 * ks + 1][2], ph[2 * ks + 1][3]};
+    }
+    if (__any(moved)) {
+      // acc row 4 q4 + i of block qb needs alpha of query 4 q4 + i (held by lanes col == 4 q4 + i)
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        if (q4 == 0) xch[wave][qb * 16 + col] = alpha[qb];
+      }
+      wave_lds_sync();
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float al = xch[wave][qb * 16 + 4 * q4 + i];
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb) acc[qb][cb][i] *= al;
+        }
+      wave_lds_sync();
+    }
+
+    // ---- acc[query][channel] += P' . V ----
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const h4_t v0 = *reinterpret_cast<const h4_t*>(&Vs[16 * cb + col][32 * ks + 4 * q4]);
+        const h4_t v1 = *reinterpret_cast<const h4_t*>(&Vs[16 * cb + col][32 * ks + 16 + 4 * q4]);
+        const h8_t vb = h8_t{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) acc[qb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[qb][ks], vb, acc[qb][cb], 0, 0, 0);
+      }
+    }
+    __syncthreads();      // the next tile overwrites the LDS tile
+  }
+
+  // ---- write: rows 4 q4 + i of block qb, channel 16 cb + col ----
+  // Row sums: lanes col, col + 16, col + 32, col + 48 hold parts of query col.
+  float ltot[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    float l = lsum[qb];
+    l += __shfl_xor(l, 16, kWave);
+    l += __shfl_xor(l, 32, kWave);
+    ltot[qb] = l;
+  }
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    if (q4 == 0) xch[wave][qb * 16 + col] = ltot[qb];
+  }
+  wave_lds_sync();
+  float lrow[2][4];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lrow[qb][i] = xch[wave][qb * 16 + 4 * q4 + i];
+  wave_lds_sync();
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    if (q4 == 0) xch[wave][qb * 16 + col] = m[qb];
+  }
+  wave_lds_sync();
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = r0 + wave * kRowsWave + qb * 16 + 4 * q4 + i;
+      if (r >= a.rows) continue;
+      const float mrow = xch[wave][qb * 16 + 4 * q4 + i];
+      if (a.splits == 1) {
+        const int pos = r / a.gqa, h = r % a.gqa;
+        float* o = a.out + (((int64_t)b * a.tq + pos) * Hq + kvh * a.gqa + h) * D;
+        const float inv = 1.0f / lrow[qb][i];
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) o[16 * cb + col] = acc[qb][cb][i] * inv;
+      } else {
+        float* p = a.part + (((int64_t)unit * a.splits + split) * a.rows + r) * (D + 2);
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) p[16 * cb + col] = acc[qb][cb][i];
+        if (col == 0) {
+          p[D] = mrow;
+          p[D + 1] = lrow[qb][i];
+        }
+      }
+    }
+}
+
+// Combine the splits' partials of each query row: one thread per (row, channel).
+template <int D>
+__global__ __launch_bounds__(kBT) void block_merge_kernel(BlockArgs a) {
+  const int unit = blockIdx.y;
+  const int b = unit / a.g.H, kvh = unit % a.g.H;
+  const int Hq = a.g.H * a.gqa;
+  const int64_t idx = (int64_t)blockIdx.x * kBT + threadIdx.x;
+  if (idx >= (int64_t)a.rows * D) return;
+  const int r = (int)(idx / D), c = (int)(idx % D);
+  float M = -INFINITY;
+  for (int s = 0; s < a.splits; ++s)
+    M = fmaxf(M, a.part[(((int64_t)unit * a.splits + s) * a.rows + r) * (D + 2) + D]);
+  float num = 0.0f, den = 0.0f;
+  for (int s = 0; s < a.splits; ++s) {
+    const float* p = a.part + (((int64_t)unit * a.splits + s) * a.rows + r) * (D + 2);
+    const float e = p[D] == -INFINITY ? 0.0f : fast_exp2(p[D] - M);
+    num = fmaf(p[c], e, num);
+    den = fmaf(p[D + 1], e, den);
+  }
+  const int pos = r / a.gqa, h = r % a.gqa;
+  a.out[(((int64_t)b * a.tq + pos) * Hq + kvh * a.gqa + h) * D + c] = num / den;
+}
+
+template <int D, int BITS>
+void launch_block(const BlockArgs& a, hipStream_t s) {
+  dim3 grid((a.rows + kRowsWG - 1) / kRowsWG, a.splits, a.g.B * a.g.H);
+  hipLaunchKernelGGL((block_kernel<D, BITS>), grid, dim3(kBT), 0, s, a);
+  if (a.splits > 1) {
+    dim3 mg((unsigned)(((int64_t)a.rows * D + kBT - 1) / kBT), a.g.B * a.g.H);
+    hipLaunchKernelGGL((block_merge_kernel<D>), mg, dim3(kBT), 0, s, a);
+  }
+}
+
+bool dispatch_block(const BlockArgs& a, hipStream_t s) {
+  const int D = a.g.D, bits = a.g.bits;
+  if (D == 128 && bits == 2) { launch_block<128, 2>(a, s); return true; }
+  if (D == 128 && bits == 4) { launch_block<128, 4>(a, s); return true; }
+  if (D == 128 && bits == 8) { launch_block<128, 8>(a, s); return true; }
+  if (D == 64 && bits == 2) { launch_block<64, 2>(a, s); return true; }
+  if (D == 64 && bits == 4) { launch_block<64, 4>(a, s); return true; }
+  if (D == 64 && bits == 8) { launch_block<64, 8>(a, s); return true; }
+  return false;
+}
+
+int block_auto_splits(int row_tiles, int units, int items) {
+  // Aim for about two workgroups per compute unit (256 CUs) and at least
+  // eight tiles per split.
+  const int64_t wgs = (int64_t)row_tiles * units;
+  int s = (int)((512 + wgs - 1) / wgs);
+  if (s > kBlockMaxSplits) s = kBlockMaxSplits;
+  if (s > items / 8) s = items / 8;
+  return s < 1 ? 1 : s;
+}
+
+}  // namespace
+}  // namespace kvq
 
 using namespace kvq;
 
 extern "C" kvq_status kvq_block_attn(const kvq_config* cfg, const kvq_state* st, const kvq_cache* cache,
                                      const void* q, const void* k_blk, const void* v_blk, int32_t tq,
                                      int32_t q_heads, float softmax_scale, int32_t num_splits,
-                                     float* out, void* workspace, size_t workspace_bytes, void* stream) {
-  (void)cfg; (void)st; (void)cache; (void)q; (void)k_blk; (void)v_blk; (void)tq; (void)q_heads;
-  (void)softmax_scale; (void)num_splits; (void)out; (void)workspace; (void)workspace_bytes; (void)stream;
-  return KVQ_EINVAL;
+                                     float* out, void* workspace, size_t workspace_size, void* stream) {
+  Geom g;
+  kvq_status s = validate_config(cfg, &g);
+  if (s != KVQ_OK) return s;
+  if (!st || !cache || !q || !k_blk || !v_blk || !out) return KVQ_EINVAL;
+  if (g.dtype != KVQ_BF16 || (g.D != 64 && g.D != 128)) return KVQ_EINVAL;
+  if (tq < 1 || q_heads < 1 || q_heads % g.H != 0) return KVQ_EINVAL;
+  const int gqa = q_heads / g.H;
+  if (gqa != 1 && gqa != 2 && gqa != 4 && gqa != 8) return KVQ_EINVAL;
+  if (st->quantized < 0 || st->tail < 0 || st->total != st->quantized + st->tail || st->quantized > g.C ||
+      st->tail > g.ring)
+    return KVQ_EINVAL;
+  if (g.G > 0 && st->quantized % g.G != 0) return KVQ_EINVAL;
+  if (!(softmax_scale == softmax_scale) || num_splits < 0 || num_splits > kBlockMaxSplits) return KVQ_EINVAL;
+  if ((int64_t)tq * gqa > (1 << 30)) return KVQ_EINVAL;
+  if (st->quantized > 0 && (!cache->k_codes || !cache->v_codes || !cache->k_scale || !cache->v_scale ||
+                            (g.G == 0 && !cache->seg_index)))
+    return KVQ_EINVAL;
+  if (st->tail > 0 && (!cache->k_tail || !cache->v_tail)) return KVQ_EINVAL;
+  if (!workspace || workspace_size < workspace_bytes(g, q_heads, tq)) return KVQ_EWORKSPACE;
+
+  BlockArgs a;
+  a.g = g;
+  a.k_codes = static_cast<const uint8_t*>(cache->k_codes);
+  a.v_codes = static_cast<const uint8_t*>(cache->v_codes);
+  a.k_scale = static_cast<const uint16_t*>(cache->k_scale);
+  a.v_scale = static_cast<const uint16_t*>(cache->v_scale);
+  a.k_tail = static_cast<const uint16_t*>(cache->k_tail);
+  a.v_tail = static_cast<const uint16_t*>(cache->v_tail);
+  a.seg_index = static_cast<const int32_t*>(cache->seg_index);
+  a.q = static_cast<const uint16_t*>(q);
+  a.k_blk = static_cast<const uint16_t*>(k_blk);
+  a.v_blk = static_cast<const uint16_t*>(v_blk);
+  a.out = out;
+  a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + workspace_counter_bytes(g, tq));
+  a.nq = static_cast<int>(st->quantized);
+  a.nt = static_cast<int>(st->tail);
+  a.nq_slot = static_cast<int>(st->quantized % g.ring);
+  a.tq = tq;
+  a.gqa = gqa;
+  a.rows = tq * gqa;
+  a.qscale = softmax_scale * 1.4426950408889634f;
+  a.tiles_q = (a.nq + kTile - 1) / kTile;
+  a.tiles_t = (a.nt + kTile - 1) / kTile;
+  a.tiles_b = (tq + kTile - 1) / kTile;
+  const int row_tiles = (a.rows + kRowsWG - 1) / kRowsWG;
+  const int items = a.tiles_q + a.tiles_t + a.tiles_b;
+  a.splits = num_splits > 0 ? num_splits : block_auto_splits(row_tiles, g.B * g.H, items);
+  if (a.splits > items) a.splits = items;
+  if (row_tiles > 65535) return KVQ_EINVAL;
+  clear_stale_hip_error();
+  if (!dispatch_block(a, static_cast<hipStream_t>(stream))) return KVQ_EINVAL;
+  return hipGetLastError() == hipSuccess ? KVQ_OK : KVQ_EDEVICE;
 }

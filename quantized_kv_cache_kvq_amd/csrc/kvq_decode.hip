@@ -73,13 +73,6 @@ struct DecodeArgs {
   int tiles_q, items;    // quantized tiles; work items = tiles_q + tail chunks
 };
 
-// Order LDS traffic between the lanes of one wave.  A wave's LDS operations
-// complete in issue order, so only the compiler needs fencing; a wider fence
-// would also wait for every outstanding global load of the wave.
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-}
 
 // ---- shared pieces ---------------------------------------------------------------
 

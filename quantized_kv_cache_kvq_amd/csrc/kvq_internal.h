@@ -98,6 +98,14 @@ __device__ __forceinline__ float wave_sum(float v) {
   return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
 }
 
+// Order LDS traffic between the lanes of one wave.  A wave's LDS operations
+// complete in issue order, so only the compiler needs fencing; a wider fence
+// would also wait for every outstanding global load of the wave.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 

@@ -1,0 +1,121 @@
+"""GPU parity of kvq_block_attn against the fp64 oracle (max-abs 2e-3).
+
+Causal block attention: query i of the block sees every cached token and
+block tokens 0..i ("KV Cache and autoregressive video generation", section
+3.1).  The oracle restores the codes it produced itself, which the append
+tests show are byte-identical to the device's.
+"""
+import numpy as np
+import pytest
+import torch
+
+import kvq_synth as ks
+from harness import Pair, max_abs, note
+
+pytestmark = pytest.mark.gpu
+needs_gpu = pytest.mark.skipif(not torch.cuda.is_available(), reason="no GPU")
+
+TOL = 2e-3
+
+
+def build(w, n, capacity=None, seed=None):
+    p = Pair(w, capacity or (n + 128))
+    s = ks.Stream(w, seed)
+    k, v = ks.kv_pair(s, n)          # n = 0: an empty append (a no-op) gives the empty state
+    note(f"block build {w.name} n={n}")
+    p.append(k, v)
+    return p, s
+
+
+@needs_gpu
+@pytest.mark.parametrize("D,bits,qmax,g,n,tq", [
+    (128, 2, 1, 4, 1000, 100),    # int2 like the video cache; ragged tiles everywhere
+    (128, 4, 7, 4, 700, 64),
+    (128, 8, 127, 2, 600, 33),
+    (64, 2, 1, 8, 500, 70),
+    (64, 4, 7, 1, 900, 130),
+    (128, 4, 7, 8, 257, 17),
+])
+def test_block_shapes(D, bits, qmax, g, n, tq):
+    w = ks.small(ks.VIDEO_BLOCK, batch=2, kv_heads=2, q_heads=2 * g, head_dim=D, code_bits=bits,
+                 qmax=qmax, residual=128, group=128)
+    p, s = build(w, n)
+    q, kb, vb = ks.block_inputs(s, tq)
+    note(f"block D={D} bits={bits} g={g} n={n} tq={tq}")
+    got = p.block(q, kb, vb)
+    ref = p.block_ref(q, kb, vb)
+    err = max_abs(got, ref)
+    note(f"block D={D} bits={bits} g={g} n={n} tq={tq}: max-abs {err:.3e}")
+    assert err <= TOL
+
+
+@needs_gpu
+@pytest.mark.parametrize("splits", [1, 2, 3, 8])
+def test_block_split_invariance(splits):
+    w = ks.small(ks.VIDEO_BLOCK, batch=1, kv_heads=2, q_heads=8)
+    p, s = build(w, 1500)
+    q, kb, vb = ks.block_inputs(s, 40)
+    ref = p.block_ref(q, kb, vb)
+    note(f"block splits={splits}")
+    got = p.block(q, kb, vb, num_splits=splits)
+    assert max_abs(got, ref) <= TOL
+
+
+@needs_gpu
+@pytest.mark.parametrize("n", [0, 1, 100, 128, 129, 300])
+def test_block_short_caches(n):
+    """Empty cache, tail only, exactly one group, one token past a flush."""
+    w = ks.small(ks.VIDEO_BLOCK, batch=1, kv_heads=2, q_heads=8, code_bits=4, qmax=7)
+    p, s = build(w, n, capacity=512)
+    q, kb, vb = ks.block_inputs(s, 50)
+    note(f"block short cache n={n}")
+    got = p.block(q, kb, vb)
+    ref = p.block_ref(q, kb, vb)
+    assert max_abs(got, ref) <= TOL
+
+
+@needs_gpu
+def test_block_of_one_equals_decode_after_append():
+    """tq = 1: the block path equals appending the token, then decoding."""
+    w = ks.small(ks.VIDEO_BLOCK, batch=2, kv_heads=2, q_heads=8, code_bits=4, qmax=7)
+    p, s = build(w, 900)
+    q, kb, vb = ks.block_inputs(s, 1)
+    note("block tq=1 vs decode")
+    got_block = p.block(q, kb, vb)[:, 0]
+    p.append(kb.transpose(1, 2).contiguous(), vb.transpose(1, 2).contiguous())
+    got_dec, _ = p.decode(q[:, 0].contiguous())
+    ref = p.decode_ref(q[:, 0].contiguous())
+    assert max_abs(got_block, ref) <= TOL
+    assert max_abs(got_dec, ref) <= TOL
+    assert max_abs(got_block, got_dec) <= TOL
+
+
+@needs_gpu
+def test_block_rejects_unsupported():
+    w = ks.small(ks.TINY, batch=1, kv_heads=2, q_heads=2)       # fp32 K/V, head_dim 16
+    p, s = build(w, 20, capacity=64)
+    q = torch.zeros(1, 4, 2, 16)
+    with pytest.raises(Exception):
+        p.block(q, torch.zeros(1, 4, 2, 16), torch.zeros(1, 4, 2, 16))
+
+
+@needs_gpu
+def test_block_video_full_size_sampled_rows():
+    """The video block at full size: 432000 int2 tokens, 1024 causal queries.
+
+    The fp64 oracle computes a sample of rows (first, last, and a seeded
+    spread) for the query heads of two KV heads; the kernel computes all.
+    """
+    w = ks.VIDEO_BLOCK
+    p, s = build(w, w.prefill)
+    q, kb, vb = ks.block_inputs(s, w.block_q)
+    note("block video full size")
+    got = p.block(q, kb, vb)
+    assert np.isfinite(got).all()
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate(([0, 1, 511, w.block_q - 1], rng.choice(w.block_q, 8, replace=False))))
+    heads = [0, 3, 20, 23]                     # KV heads 0 and 5
+    ref = p.block_ref(q, kb, vb, rows=rows, heads=heads)
+    err = max_abs(got[:, rows][:, :, heads], ref[:, rows][:, :, heads])
+    note(f"block video full size: max-abs {err:.3e}")
+    assert err <= TOL
