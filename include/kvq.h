@@ -182,11 +182,13 @@ kvq_status kvq_decode_attn(const kvq_config* cfg, const kvq_state* st, const kvq
  * section 3.1).  Query i sits at absolute position N + i after the N cached
  * tokens: it sees all N cached tokens and block tokens 0..i.  The block's
  * own K/V are read as given and are not appended.  Matrix products run on
- * the MFMA units over dequantized fp16 tiles.
+ * the MFMA units over tiles restored into LDS.  Supported: kv_dtype bf16 and
+ * head_dim 64 or 128 (other configurations return KVQ_EINVAL).
  *   q            : device, kv_dtype [batch, tq, q_heads, head_dim]
  *   k_blk, v_blk : device, kv_dtype [batch, tq, kv_heads, head_dim]
  *   out          : device, float32 [batch, tq, q_heads, head_dim]
- *   num_splits   : splits of the cached sequence; 0 = library's choice
+ *   softmax_scale: sigma > 0 (1/sqrt(head_dim) for standard attention)
+ *   num_splits   : splits of the cached sequence, at most 8; 0 = library's choice
  *   workspace    : from kvq_workspace_size(cfg, q_heads, tq), initialised once
  * Errors: KVQ_EINVAL, KVQ_EWORKSPACE, KVQ_EDEVICE. */
 kvq_status kvq_block_attn(const kvq_config* cfg, const kvq_state* st, const kvq_cache* cache,

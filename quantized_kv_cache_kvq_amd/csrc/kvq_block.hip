@@ -77,7 +77,8 @@ __global__ __launch_bounds__(kBT) __attribute__((amdgpu_waves_per_eu(2)))
 void block_kernel(BlockArgs a) {
   constexpr int CG = D / 4;                // channels per thread in the K fill
   constexpr int KROW = D + 8;              // LDS row pitch (bf16) of Khi / Klo: no bank conflicts
-  constexpr int VROW = kTile + 8;          // LDS row pitch (fp16) of V
+  constexpr int VROW = kTile + 4;          // LDS row pitch (fp16) of V: 34 banks, 16 rows of a
+                                           // 64-bit operand read hit 32 distinct banks
   constexpr int KS = D / 32;               // k steps of the logit MFMAs
   constexpr int CB = D / 16;               // channel blocks of the output
   constexpr int TPC = kBT / D;             // threads per channel in the V fill
@@ -97,7 +98,9 @@ void block_kernel(BlockArgs a) {
   __shared__ __attribute__((aligned(16))) __bf16 Khi[kTile][KROW];
   __shared__ __attribute__((aligned(16))) __bf16 Klo[kTile][KROW];
   __shared__ __attribute__((aligned(16))) _Float16 Vs[D][VROW];
-  __shared__ float vsr[kTile];
+  __shared__ __attribute__((aligned(16))) float vsr[kTile];
+  __shared__ __attribute__((aligned(16))) float2 rkL[2][D];  // 1 / kscale split into bf16 hi, lo (as fp32),
+                                                             // by item parity (G > 0)
   __shared__ float xch[kBWaves][kRowsWave];   // per-row values exchanged inside a wave
 
   // ---- this wave's query rows: operand B of S^T = Khat . Q^T ----
@@ -129,6 +132,42 @@ void block_kernel(BlockArgs a) {
   const int i0 = (int)(((int64_t)items * split) / a.splits);
   const int i1 = (int)(((int64_t)items * (split + 1)) / a.splits);
   const int64_t stream = (int64_t)unit * g.code_stream;
+  const uint16_t* kscale_unit = a.k_scale + (int64_t)unit * g.max_seg * D;
+  // With whole-group segments every token of a tile shares one Key-scale row:
+  // its reciprocals are computed once per tile (one per thread) into rkL.
+  auto seg_rk = [&](int item) {
+    const float r = fast_rcp(fmaxf(half_bits_to_f32(kscale_unit[(item * kTile / g.G) * D + tid]), g.eps));
+    const float hi = (float)(__bf16)r;
+    return float2{hi, (float)(__bf16)(r - hi)};
+  };
+  if (g.G > 0 && i0 < i1 && i0 < a.tiles_q && tid < D) rkL[i0 & 1][tid] = seg_rk(i0);
+  // Raw codes and the Value scale a thread restores from a quantized tile;
+  // the next tile's are loaded while the current one is computed.
+  struct QRaw {
+    uint32_t w[KW];       // Key: token tid % 64, channels (tid / 64) * CG ..
+    uint32_t vw[VW];      // Value: channel tid % D, tokens (tid / D) * NTV ..
+    uint16_t vs;          // Value scale of token tid (tid < 64)
+  };
+  auto load_qraw = [&](int item, QRaw& r) {
+    const int t0 = item * kTile;
+    const int count = min(kTile, a.nq - t0);
+    const int i = tid % kTile, grp = tid / kTile;
+    const uint8_t* kt = a.k_codes + stream + (int64_t)item * (kTile * g.W);
+    const int rb = grp * CG * BITS / 8;
+#pragma unroll
+    for (int k = 0; k < KW; ++k) {
+      const int rr = rb + 4 * k;
+      r.w[k] = i < count ? *reinterpret_cast<const uint32_t*>(kt + (rr / 16) * 1024 + i * 16 + rr % 16) : 0u;
+    }
+    const int c = tid % D, vt0 = (tid / D) * NTV;
+    const uint8_t* vt = a.v_codes + stream + (int64_t)item * (kTile * g.W) + c * (8 * BITS) + vt0 * BITS / 8;
+#pragma unroll
+    for (int k = 0; k < VW; ++k) r.vw[k] = *reinterpret_cast<const uint32_t*>(vt + 4 * k);
+    r.vs = tid < count ? a.v_scale[(int64_t)unit * g.C + t0 + tid] : (uint16_t)0;
+  };
+  QRaw cur;
+  if (i0 < i1 && i0 < a.tiles_q) load_qraw(i0, cur);
+  __syncthreads();
 
   for (int item = i0; item < i1; ++item) {
     const int kind = item < a.tiles_q ? kQuant : (item < a.tiles_q + a.tiles_t ? kTail : kOwn);
@@ -143,39 +182,47 @@ void block_kernel(BlockArgs a) {
       const int i = tid % kTile, grp = tid / kTile;     // K: token i, channels grp * CG ..
       const bool tv = i < count;
       if (kind == kQuant) {
-        const uint8_t* kt = a.k_codes + stream + (int64_t)tile * (kTile * g.W);
-        uint32_t w[KW];
-        const int rb = grp * CG * BITS / 8;              // first byte of the run in the token row
-#pragma unroll
-        for (int k = 0; k < KW; ++k) {
-          const int rr = rb + 4 * k;
-          w[k] = tv ? *reinterpret_cast<const uint32_t*>(kt + (rr / 16) * 1024 + i * 16 + rr % 16) : 0u;
-        }
-        const int seg = !tv ? 0 : (g.G > 0 ? (t0 + i) / g.G : a.seg_index[t0 + i]);
-        const uint16_t* ks = a.k_scale + ((int64_t)unit * g.max_seg + seg) * D + grp * CG;
+        const uint32_t* w = cur.w;
+        // one segment per flush (G == 0): each token reads its own Key-scale row
+        const uint16_t* ks = kscale_unit + (g.G > 0 ? 0 : (tv ? a.seg_index[t0 + i] : 0)) * D + grp * CG;
+        const float2* rks = &rkL[item & 1][grp * CG];
 #pragma unroll
         for (int e = 0; e < CG; e += 8) {
-          const uint4 sw = *reinterpret_cast<const uint4*>(ks + e);
-          const uint32_t sv[4] = {sw.x, sw.y, sw.z, sw.w};
           __bf16 hi[8], lo[8];
+          if (g.G > 0) {
 #pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const int f = e + j;
-            const int code = sext_field<BITS>(w[f * BITS / 32], (f * BITS) % 32);
-            const float rk = fast_rcp(fmaxf(half_bits_to_f32((uint16_t)(sv[j / 2] >> (16 * (j % 2)))), g.eps));
-            const float x = (float)code * rk;
-            hi[j] = (__bf16)x;
-            lo[j] = (__bf16)(x - (float)hi[j]);
+            for (int j = 0; j < 8; ++j) {
+              const int f = e + j;
+              const float code = (float)sext_field<BITS>(w[f * BITS / 32], (f * BITS) % 32);
+              const float2 rk = rks[e + j];     // 1 / kscale = rk.x + rk.y, both bf16 values
+              if constexpr (BITS == 2) {
+                // code in {-1, 0, 1}: code * rk.x and code * rk.y are exact bf16 values
+                hi[j] = (__bf16)(code * rk.x);
+                lo[j] = (__bf16)(code * rk.y);
+              } else {
+                const float x = fmaf(code, rk.x, code * rk.y);
+                hi[j] = (__bf16)x;
+                lo[j] = (__bf16)(x - (float)hi[j]);
+              }
+            }
+          } else {
+            const uint4 sw = *reinterpret_cast<const uint4*>(ks + e);
+            const uint32_t sv[4] = {sw.x, sw.y, sw.z, sw.w};
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              const int f = e + j;
+              const float rk = fast_rcp(fmaxf(half_bits_to_f32((uint16_t)(sv[j / 2] >> (16 * (j % 2)))), g.eps));
+              const float x = (float)sext_field<BITS>(w[f * BITS / 32], (f * BITS) % 32) * rk;
+              hi[j] = (__bf16)x;
+              lo[j] = (__bf16)(x - (float)hi[j]);
+            }
           }
           *reinterpret_cast<uint4*>(&Khi[i][grp * CG + e]) = __builtin_bit_cast(uint4, hi);
           *reinterpret_cast<uint4*>(&Klo[i][grp * CG + e]) = __builtin_bit_cast(uint4, lo);
         }
         // V: channel c, tokens vt0 .. vt0 + NTV - 1 (a run of the channel's row)
         const int c = tid % D, vt0 = (tid / D) * NTV;
-        const uint8_t* vt = a.v_codes + stream + (int64_t)tile * (kTile * g.W) + c * (8 * BITS) + vt0 * BITS / 8;
-        uint32_t vw[VW];
-#pragma unroll
-        for (int k = 0; k < VW; ++k) vw[k] = *reinterpret_cast<const uint32_t*>(vt + 4 * k);
+        const uint32_t* vw = cur.vw;
 #pragma unroll
         for (int j0 = 0; j0 < NTV; j0 += 8) {
           _Float16 v8[8];
@@ -184,12 +231,11 @@ void block_kernel(BlockArgs a) {
             const int f = j0 + j;
             v8[j] = (_Float16)(float)sext_field<BITS>(vw[f * BITS / 32], (f * BITS) % 32);
           }
-          *reinterpret_cast<uint4*>(&Vs[c][vt0 + j0]) = __builtin_bit_cast(uint4, v8);
+          const uint4 v8w = __builtin_bit_cast(uint4, v8);
+          *reinterpret_cast<uint2*>(&Vs[c][vt0 + j0]) = uint2{v8w.x, v8w.y};
+          *reinterpret_cast<uint2*>(&Vs[c][vt0 + j0 + 4]) = uint2{v8w.z, v8w.w};
         }
-        if (tid < kTile) {
-          const int t = t0 + tid;
-          vsr[tid] = tid < count ? fast_rcp(fmaxf(half_bits_to_f32(a.v_scale[(int64_t)unit * g.C + t]), g.eps)) : 0.0f;
-        }
+        if (tid < kTile) vsr[tid] = tid < count ? fast_rcp(fmaxf(half_bits_to_f32(cur.vs), g.eps)) : 0.0f;
       } else {
         // bf16 rows: K copied as the hi part (lo = 0), V transposed into fp16
         const uint16_t* krow;
@@ -221,6 +267,13 @@ void block_kernel(BlockArgs a) {
       }
     }
     __syncthreads();
+    // The next quantized tile's Key-scale reciprocals (read by its fill after
+    // the closing barrier); the load's latency hides behind this tile.
+    const bool next_q = item + 1 < i1 && item + 1 < a.tiles_q;
+    const bool next_rk = g.G > 0 && next_q && tid < D;
+    float2 rk_next = float2{0.0f, 0.0f};
+    if (next_rk) rk_next = seg_rk(item + 1);
+    if (next_q) load_qraw(item + 1, cur);    // cur's fill is done: its registers are free
 
     // ---- logits S^T[token][query] (token block tb, query block qb) ----
     f4_t S[4][2];
@@ -228,14 +281,18 @@ void block_kernel(BlockArgs a) {
     for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) S[tb][qb] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    // k step outermost: eight independent accumulators between dependent MFMAs
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
+    for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
+      for (int tb = 0; tb < 4; ++tb) {
         const bf8_t ah = *reinterpret_cast<const bf8_t*>(&Khi[tb * 16 + col][32 * ks + 8 * q4]);
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) S[tb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, qop[qb][ks], S[tb][qb], 0, 0, 0);
-        if (kind == kQuant) {
+      }
+      if (kind == kQuant) {
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
           const bf8_t al = *reinterpret_cast<const bf8_t*>(&Klo[tb * 16 + col][32 * ks + 8 * q4]);
 #pragma unroll
           for (int qb = 0; qb < 2; ++qb) S[tb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, qop[qb][ks], S[tb][qb], 0, 0, 0);
@@ -244,45 +301,57 @@ void block_kernel(BlockArgs a) {
     }
 
     // ---- online softmax per query (lane's column col of block qb) ----
-    // S[tb][qb][i]: token t0 + 16 tb + 4 q4 + i.
+    // S[tb][qb][i]: token t0 + 16 tb + 4 q4 + i; the logit (log2 domain) is
+    // S * qscale, folded into the exponent.
+    float vr[4][4];       // 1 / vscale of the lane's tokens (shared by both query blocks)
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      const float4 v4 = *reinterpret_cast<const float4*>(&vsr[16 * tb + 4 * q4]);
+      vr[tb][0] = v4.x; vr[tb][1] = v4.y; vr[tb][2] = v4.z; vr[tb][3] = v4.w;
+    }
+    const bool full = kind == kQuant && count == kTile;   // no masking needed
     h8_t pa[2][2];        // P operands: [qb][k step] (tokens 32 ks + 4 q4 + j, 32 ks + 16 + 4 q4 + j)
     float alpha[2];
     bool moved = false;
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      float x[4][4];
       float mx = -INFINITY;
+      if (!full) {
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int tt = 16 * tb + 4 * q4 + i;
+            const bool vis = tt < count && qpos[qb] >= 0 && (kind != kOwn || t0 + tt <= qpos[qb]);
+            S[tb][qb][i] = vis ? S[tb][qb][i] : -INFINITY;
+          }
+      }
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int tt = 16 * tb + 4 * q4 + i;
-          const bool vis = tt < count && qpos[qb] >= 0 && (kind != kOwn || t0 + tt <= qpos[qb]);
-          x[tb][i] = vis ? S[tb][qb][i] * a.qscale : -INFINITY;
-          mx = fmaxf(mx, x[tb][i]);
-        }
+        mx = fmaxf(mx, fmaxf(fmaxf(S[tb][qb][0], S[tb][qb][1]), fmaxf(S[tb][qb][2], S[tb][qb][3])));
       mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
       mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-      const float mn = fmaxf(m[qb], mx);
+      const float mn = fmaxf(m[qb], mx * a.qscale);
       alpha[qb] = (mn == -INFINITY) ? 1.0f : fast_exp2(m[qb] - mn);
       moved |= alpha[qb] != 1.0f && m[qb] != -INFINITY;
       m[qb] = mn;
       const float mu = mn == -INFINITY ? 0.0f : mn;
       float ps = 0.0f;
-      _Float16 ph[4][4];
+      float pv[4][4];
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float p = fast_exp2(x[tb][i] - mu);
+          const float p = fast_exp2(fmaf(S[tb][qb][i], a.qscale, -mu));
           ps += p;
-          ph[tb][i] = (_Float16)(p * vsr[16 * tb + 4 * q4 + i]);
+          pv[tb][i] = p * vr[tb][i];
         }
       lsum[qb] = lsum[qb] * alpha[qb] + ps;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
-        pa[qb][ks] = h8_t{ph[2 * ks][0], ph[2 * ks][1], ph[2 * ks][2], ph[2 * ks][3],
-                          ph[2 * ks + 1][0], ph[2 * ks + 1][1], ph[2 * ks + 1][2], ph[2 * ks + 1][3]};
+        pa[qb][ks] = h8_t{(_Float16)pv[2 * ks][0], (_Float16)pv[2 * ks][1], (_Float16)pv[2 * ks][2],
+                          (_Float16)pv[2 * ks][3], (_Float16)pv[2 * ks + 1][0], (_Float16)pv[2 * ks + 1][1],
+                          (_Float16)pv[2 * ks + 1][2], (_Float16)pv[2 * ks + 1][3]};
     }
     if (__any(moved)) {
       // acc row 4 q4 + i of block qb needs alpha of query 4 q4 + i (held by lanes col == 4 q4 + i)
@@ -302,11 +371,11 @@ void block_kernel(BlockArgs a) {
       wave_lds_sync();
     }
 
-    // ---- acc[query][channel] += P' . V ----
+    // ---- acc[query][channel] += P' . V (k step outermost) ----
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
+    for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
+      for (int cb = 0; cb < CB; ++cb) {
         const h4_t v0 = *reinterpret_cast<const h4_t*>(&Vs[16 * cb + col][32 * ks + 4 * q4]);
         const h4_t v1 = *reinterpret_cast<const h4_t*>(&Vs[16 * cb + col][32 * ks + 16 + 4 * q4]);
         const h8_t vb = h8_t{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
@@ -314,6 +383,7 @@ void block_kernel(BlockArgs a) {
         for (int qb = 0; qb < 2; ++qb) acc[qb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[qb][ks], vb, acc[qb][cb], 0, 0, 0);
       }
     }
+    if (next_rk) rkL[(item + 1) & 1][tid] = rk_next;
     __syncthreads();      // the next tile overwrites the LDS tile
   }
 
@@ -443,7 +513,7 @@ extern "C" kvq_status kvq_block_attn(const kvq_config* cfg, const kvq_state* st,
       st->tail > g.ring)
     return KVQ_EINVAL;
   if (g.G > 0 && st->quantized % g.G != 0) return KVQ_EINVAL;
-  if (!(softmax_scale == softmax_scale) || num_splits < 0 || num_splits > kBlockMaxSplits) return KVQ_EINVAL;
+  if (!(softmax_scale > 0.0f) || num_splits < 0 || num_splits > kBlockMaxSplits) return KVQ_EINVAL;
   if ((int64_t)tq * gqa > (1 << 30)) return KVQ_EINVAL;
   if (st->quantized > 0 && (!cache->k_codes || !cache->v_codes || !cache->k_scale || !cache->v_scale ||
                             (g.G == 0 && !cache->seg_index)))
