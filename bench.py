@@ -134,7 +134,7 @@ def run_decode(args, log):
         "us_per_step": round(ms_step * 1e3, 3),
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "f32", "data": "synthetic",
+        "dtype": "i8 MFMA (i32 acc) + f32 softmax", "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "q_heads": w.q_heads,
                    "kv_heads": w.kv_heads, "head_dim": w.head_dim, "context": w.prefill,
                    "codes": f"int{w.code_bits}", "residual": w.residual, "group": w.group,
@@ -144,7 +144,7 @@ def run_decode(args, log):
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None,
-                     "kernel": "kvq_decode_attn = decode_mfma_kernel<128,4> + merge_kernel<128,4>"},
+                     "kernel": "kvq_decode_attn = decode_i8_kernel<128,4,4> + merge_kernel<128,4>"},
     }
     return res, (cfg, w)
 
