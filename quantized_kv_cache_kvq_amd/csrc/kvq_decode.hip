@@ -318,26 +318,30 @@ __device__ __forceinline__ void load_q(const DecodeArgs& a, int unit, float (*qs
 
 // Work of one wave: quantized tiles [t0, t1) and tail chunks [c0, c1).
 // Split s owns an equal share of the tiles and of the chunks (so the tail is
-// spread over the splits); its four waves share the concatenated list
+// spread over the splits).  Its four waves share the concatenated list
 // (tiles, then chunks) in contiguous runs, so a wave meets each Key segment
-// once.
+// once; a chunk counts as kChunkCost tiles when the runs are balanced.
 struct WaveWork {
   int t0, t1, c0, c1;
 };
+template <int kChunkCost>
 __device__ __forceinline__ WaveWork wave_work(const DecodeArgs& a, int split, int wave) {
   const int chunks = a.items - a.tiles_q;
   const int ts0 = (int)(((int64_t)a.tiles_q * split) / a.splits);
   const int ts1 = (int)(((int64_t)a.tiles_q * (split + 1)) / a.splits);
   const int cs0 = (int)(((int64_t)chunks * split) / a.splits);
   const int cs1 = (int)(((int64_t)chunks * (split + 1)) / a.splits);
-  const int n = (ts1 - ts0) + (cs1 - cs0);
-  const int lo = (n * wave) / kWaves, hi = (n * (wave + 1)) / kWaves;
-  const int nt = ts1 - ts0;
+  const int nt = ts1 - ts0, nc = cs1 - cs0;
+  const int cost = nt + kChunkCost * nc;
+  const int lo = (cost * wave) / kWaves, hi = (cost * (wave + 1)) / kWaves;
+  // position p in [0, cost): tiles occupy [0, nt), chunk j occupies [nt + j c, nt + (j + 1) c)
+  auto tiles_before = [&](int p) { return p < nt ? p : nt; };
+  auto chunks_before = [&](int p) { return p <= nt ? 0 : (p - nt + kChunkCost - 1) / kChunkCost; };
   WaveWork w;
-  w.t0 = ts0 + (lo < nt ? lo : nt);
-  w.t1 = ts0 + (hi < nt ? hi : nt);
-  w.c0 = cs0 + (lo > nt ? lo - nt : 0);
-  w.c1 = cs0 + (hi > nt ? hi - nt : 0);
+  w.t0 = ts0 + tiles_before(lo);
+  w.t1 = ts0 + tiles_before(hi);
+  w.c0 = cs0 + chunks_before(lo);
+  w.c1 = cs0 + chunks_before(hi);
   return w;
 }
 
@@ -376,7 +380,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     for (int k = 0; k < TCPL; ++k) acc_tail[k][h] = 0.0f;
   }
 
-  const WaveWork ww = wave_work(a, split, wave);
+  const WaveWork ww = wave_work<1>(a, split, wave);
   const uint8_t* kbase = a.k_codes + (int64_t)unit * g.code_stream;
   const uint8_t* vbase = a.v_codes + (int64_t)unit * g.code_stream;
   const uint16_t* ksbase = a.k_scale + (int64_t)unit * g.max_seg * D;
@@ -637,7 +641,8 @@ void decode_i8_kernel(DecodeArgs a) {
   auto chan = [](int p) { return (p & ~15) + F16::field(p & 15); };
 
 
-  const WaveWork ww = wave_work(a, split, wave);
+  // A 16-token bf16 tail chunk costs about three int4 tiles on this path.
+  const WaveWork ww = wave_work<3>(a, split, wave);
   const int w_begin = ww.t0, q_end = ww.t1;
   const uint8_t* kbase = a.k_codes + (int64_t)unit * g.code_stream;
   const uint8_t* vbase = a.v_codes + (int64_t)unit * g.code_stream;
