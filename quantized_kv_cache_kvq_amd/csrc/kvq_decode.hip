@@ -650,17 +650,14 @@ void decode_i8_kernel(DecodeArgs a) {
   const uint16_t* vsbase = a.v_scale + (int64_t)unit * g.C;
 
   // Per-lane constants: tokens T(gg, col) of the Key MFMAs, code byte offsets.
-  int tok[4];
-#pragma unroll
-  for (int gg = 0; gg < 4; ++gg) tok[gg] = 16 * (col / 4) + F16::field(4 * (col % 4) + gg);
-  int koff[4][MK];
-#pragma unroll
-  for (int gg = 0; gg < 4; ++gg)
-#pragma unroll
-    for (int mk = 0; mk < MK; ++mk) {
-      const int r0 = 8 * BITS * mk + 2 * BITS * q4;
-      koff[gg][mk] = (r0 / 16) * 1024 + tok[gg] * 16 + r0 % 16;
-    }
+  // Token of column col of Key MFMA gg (recomputed where used: no registers held).
+  auto tok = [&](int gg) { return 16 * (col / 4) + F16::field(4 * (col % 4) + gg); };
+  // Byte of a Key word: chunk (r0 / 16) of token tok[gg], byte r0 % 16 in it,
+  // r0 = 8 BITS mk + 2 BITS q4.
+  auto koff = [&](int gg, int mk) {
+    const int r0 = 8 * BITS * mk + 2 * BITS * q4;
+    return (r0 / 16) * 1024 + r0 % 16 + tok(gg) * 16;
+  };
   const int voff = col * (8 * BITS) + 2 * BITS * q4;
 
   // Online-softmax state: head 4 hg + q4 of this lane's row quad.
@@ -692,16 +689,21 @@ void decode_i8_kernel(DecodeArgs a) {
   struct TileRegs {
     raw_t kw[4][MK];
     raw_t vw[NV];
-    float vs[4];
-    uint16_t ks[RPL];     // Key scales (slot order lane * RPL + i) when the tile opens a segment
+    uint32_t vs[2];       // fp16 Value scales of tokens tok[0..3], two per word
+    uint32_t ks;          // fp16 Key scales of slots lane * RPL + 0..1 (RPL <= 2)
     bool new_seg;
   };
+  static_assert(RPL <= 2, "two Key-scale slots per lane at most");
+  // Every load of a tile is unconditional (the Key scales too), so the
+  // number of loads a wave has in flight does not depend on the path and
+  // the compiler can wait for exactly the ones it needs.
   auto load_tile = [&](int tile, TileRegs& r) {
     r.new_seg = tile == w_begin || tile % a.tiles_per_seg == 0;
-    if (r.new_seg) {
+    {
       const uint16_t* ks = ksbase + (tile / a.tiles_per_seg) * D;
-#pragma unroll
-      for (int i = 0; i < RPL; ++i) r.ks[i] = ks[chan(lane * RPL + i)];
+      uint32_t k2 = ks[chan(lane * RPL)];
+      if constexpr (RPL == 2) k2 |= (uint32_t)ks[chan(lane * RPL + 1)] << 16;
+      r.ks = k2;
     }
     const uint8_t* kt = kbase + (int64_t)tile * (kTile * W);
     const uint8_t* vt = vbase + (int64_t)tile * (kTile * W);
@@ -709,11 +711,11 @@ void decode_i8_kernel(DecodeArgs a) {
 #pragma unroll
     for (int gg = 0; gg < 4; ++gg)
 #pragma unroll
-      for (int mk = 0; mk < MK; ++mk) r.kw[gg][mk] = *reinterpret_cast<const raw_t*>(kt + koff[gg][mk]);
+      for (int mk = 0; mk < MK; ++mk) r.kw[gg][mk] = *reinterpret_cast<const raw_t*>(kt + koff(gg, mk));
 #pragma unroll
     for (int n = 0; n < NV; ++n) r.vw[n] = *reinterpret_cast<const raw_t*>(vt + n * 16 * (8 * BITS) + voff);
-#pragma unroll
-    for (int gg = 0; gg < 4; ++gg) r.vs[gg] = half_bits_to_f32(vst[tok[gg]]);
+    r.vs[0] = (uint32_t)vst[tok(0)] | ((uint32_t)vst[tok(1)] << 16);
+    r.vs[1] = (uint32_t)vst[tok(2)] | ((uint32_t)vst[tok(3)] << 16);
   };
 
   // Key operands of a segment: digit d of round(F a[head][c]) in row 4 h + d.
@@ -723,7 +725,7 @@ void decode_i8_kernel(DecodeArgs a) {
     float rkmax = 0.0f;
 #pragma unroll
     for (int i = 0; i < RPL; ++i) {
-      const float rk = fast_rcp(fmaxf(half_bits_to_f32(r.ks[i]), g.eps));
+      const float rk = fast_rcp(fmaxf(half_bits_to_f32((uint16_t)(r.ks >> (16 * i))), g.eps));
       rkP[wave][lane * RPL + i] = rk;
       rkmax = fmaxf(rkmax, rk);
     }
@@ -806,7 +808,8 @@ void decode_i8_kernel(DecodeArgs a) {
     }
     float vsrf[4];
 #pragma unroll
-    for (int gg = 0; gg < 4; ++gg) vsrf[gg] = fv * fast_rcp(fmaxf(r.vs[gg], g.eps));
+    for (int gg = 0; gg < 4; ++gg)
+      vsrf[gg] = fv * fast_rcp(fmaxf(half_bits_to_f32((uint16_t)(r.vs[gg / 2] >> (16 * (gg % 2)))), g.eps));
 #pragma unroll
     for (int hg = 0; hg < HG; ++hg) {
       uint32_t P[4];
@@ -834,35 +837,56 @@ void decode_i8_kernel(DecodeArgs a) {
     wave_lds_sync();      // pD is rewritten by the next tile
   };
 
-  // Every global load of the first two tiles (and the run's Value scales,
-  // which fix Fv) is issued before the query is read: one memory round trip.
+  // The query is read first, then the wave's first tile and its run's Value
+  // scales (which fix Fv): the tile index is clamped to an existing tile, so
+  // the loads are unconditional and writing the query to LDS waits for the
+  // query alone.  Later tiles are prefetched one ahead (a tile's loads are
+  // issued just before the previous tile is computed), so a wave starts
+  // computing as soon as its first tile lands instead of waiting behind a
+  // deep queue of its own loads.
+  constexpr int NQ = (GQA * D + kThreads - 1) / kThreads;
+  float qT[NQ], qP[NQ];
+  {
+    const int b = unit / g.H, kvh = unit % g.H;
+#pragma unroll
+    for (int k = 0; k < NQ; ++k) {
+      const int i = tid + k * kThreads;
+      const int ic = i < GQA * D ? i : 0;
+      const int h = ic / D, c = ic % D;
+      const int64_t row = ((int64_t)b * g.H * GQA + kvh * GQA + h) * D;
+      qT[k] = load_elem(a.q, row + c, g.dtype);
+      qP[k] = load_elem(a.q, row + chan(c), g.dtype);
+    }
+  }
   int tile = w_begin;
   TileRegs bufA, bufB;
+  const int last_tile = a.tiles_q - 1;          // >= 0: this kernel runs with a quantized prefix
+  load_tile(w_begin < last_tile ? w_begin : last_tile, bufA);
   float vs_run[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int t = (w_begin + k) * kTile + lane;
-    vs_run[k] = t < q_end * kTile ? half_bits_to_f32(vsbase[t]) : INFINITY;
+    const float v = half_bits_to_f32(vsbase[t < a.nq ? t : a.nq - 1]);
+    vs_run[k] = t < q_end * kTile ? v : INFINITY;
   }
-  if (tile < q_end) load_tile(tile, bufA);
-  if (tile + 1 < q_end) load_tile(tile + 1, bufB);
-  TailRegs<D, true> trA, trB;
-  if (ww.c0 < ww.c1) tail_load<D, true>(a, unit, ww.c0, trA);
-
-  {
-    const int b = unit / g.H, kvh = unit % g.H;
-    for (int i = tid; i < GQA * D; i += kThreads) {
-      const int h = i / D, c = i % D;
-      const int64_t row = ((int64_t)b * g.H * GQA + kvh * GQA + h) * D;
-      qsT[c][h] = load_elem(a.q, row + c, g.dtype) * a.qscale;
-      qsP[h][c] = load_elem(a.q, row + chan(c), g.dtype) * a.qscale;
+#pragma unroll
+  for (int k = 0; k < NQ; ++k) {
+    const int i = tid + k * kThreads;
+    if (i < GQA * D) {
+      qsT[i % D][i / D] = qT[k] * a.qscale;
+      qsP[i / D][i % D] = qP[k] * a.qscale;
     }
+  }
+  {
     uint4* z0 = reinterpret_cast<uint4*>(&qD[0][0][0][0][0][0]);
     for (int i = tid; i < (int)(sizeof(qD) / 16); i += kThreads) z0[i] = uint4{0u, 0u, 0u, 0u};
     uint4* z1 = reinterpret_cast<uint4*>(&pD[0][0][0][0][0]);
     for (int i = tid; i < (int)(sizeof(pD) / 16); i += kThreads) z1[i] = uint4{0u, 0u, 0u, 0u};
   }
   __syncthreads();
+  TailRegs<D, true> trA, trB;
+  const bool has_chunks = ww.c0 < ww.c1;
+  if (has_chunks) tail_load<D, true>(a, unit, ww.c0, trA);   // computed after the tiles
   init_state();
 
   if (tile < q_end) {
@@ -882,23 +906,25 @@ void decode_i8_kernel(DecodeArgs a) {
     }
     fv = kFixP / wave_max(vsr_max);
   }
-  // Quantized tiles, two in flight: while one is computed the other's loads
-  // are outstanding.  The int32 Value sums are folded into fp32 at least
-  // every 1024 tiles (no overflow).
+  // Quantized tiles: before a tile is computed (after its Key operands are
+  // built) the next one's loads are issued.  The int32 Value sums are folded into fp32 at least every 1024
+  // tiles (no overflow).
   int since_fold = 0;
-  while (tile < q_end) {
-    if (bufA.new_seg) build_key_operands(bufA);
-    compute_tile(bufA);
-    if (tile + 2 < q_end) load_tile(tile + 2, bufA);
-    if (++tile >= q_end) break;
-    if (bufB.new_seg) build_key_operands(bufB);
-    compute_tile(bufB);
-    if (tile + 2 < q_end) load_tile(tile + 2, bufB);
-    ++tile;
-    if ((since_fold += 2) >= 1024) {
-      since_fold = 0;
+  if (tile < q_end) {
+    while (true) {
+      if (bufA.new_seg) build_key_operands(bufA);
+      if (tile + 1 < q_end) load_tile(tile + 1, bufB);
+      compute_tile(bufA);
+      if (++tile >= q_end) break;
+      if (bufB.new_seg) build_key_operands(bufB);
+      if (tile + 1 < q_end) load_tile(tile + 1, bufA);
+      compute_tile(bufB);
+      if (++tile >= q_end) break;
+      if ((since_fold += 2) >= 1024) {
+        since_fold = 0;
 #pragma unroll
-      for (int hg = 0; hg < HG; ++hg) fold_int(hg, 1.0f);
+        for (int hg = 0; hg < HG; ++hg) fold_int(hg, 1.0f);
+      }
     }
   }
 #pragma unroll
@@ -937,8 +963,8 @@ void decode_i8_kernel(DecodeArgs a) {
   };
 
   // Tail chunks (bf16) after the quantized tiles of this wave; the first
-  // chunk's loads were issued with the tiles', each later one is loaded
-  // while the one before is computed.
+  // one's loads were issued at the start, each later one's while the one
+  // before is computed.
   for (int chunk = ww.c0; chunk < ww.c1; chunk += 2) {
     if (chunk + 1 < ww.c1) tail_load<D, true>(a, unit, chunk + 1, trB);
     tail_compute<D, GQA, true>(a, trA, qsT, pw[wave], mu, lu, alpha_u, acc_tail);
@@ -973,7 +999,7 @@ template <int D, int BITS, int GQA>
 void launch(const DecodeArgs& a, hipStream_t s) {
   dim3 grid(a.splits, a.g.B * a.g.H);
   if constexpr ((BITS == 4 || BITS == 2) && D >= 64) {
-    if (a.g.G > 0 && a.g.dtype == KVQ_BF16)
+    if (a.g.G > 0 && a.g.dtype == KVQ_BF16 && a.tiles_q > 0)
       hipLaunchKernelGGL((decode_i8_kernel<D, BITS, GQA>), grid, dim3(kThreads), 0, s, a);
     else
       hipLaunchKernelGGL((decode_kernel<D, BITS, GQA>), grid, dim3(kThreads), 0, s, a);
