@@ -216,6 +216,174 @@ def run_video_block(args, log):
     }
 
 
+def run_long_decode(args, log):
+    """One step = 32 sequential decode calls, one per layer cache of 131072 tokens."""
+    import torch
+
+    import kvq_synth as ks
+    from quantized_kv_cache_kvq_amd import KVCache, make_config
+
+    w = ks.LONG_CONTEXT
+    cfg = make_config(batch=w.batch, kv_heads=w.kv_heads, head_dim=w.head_dim,
+                      capacity=w.prefill + 256, code_bits=w.code_bits, qmax=w.qmax,
+                      residual=w.residual, group=w.group)
+    caches, qs = [], []
+    for layer in range(w.layers):
+        k, v = ks.device_kv_pair(w, w.prefill, seed=layer)
+        c = KVCache(cfg, zero=False)
+        c.append(k, v)
+        del k, v
+        caches.append(c)
+        qs.append(ks.device_queries(w, seed=layer))
+    torch.cuda.synchronize()
+    log(f"built {w.layers} layer caches of {w.prefill} tokens")
+    out = torch.empty(w.batch, w.q_heads, w.head_dim, device="cuda")
+    ws = caches[0].workspace(w.q_heads, 1)
+    stream = torch.cuda.current_stream()
+    steps, warmup = max(2, args.steps // 20), max(1, args.warmup // 10)
+
+    def step():
+        for layer, c in enumerate(caches):
+            c.decode_attn(qs[layer], out, ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    nbytes = sum(decode_bytes(cfg, c.state.quantized, c.state.tail, w.q_heads) for c in caches)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    log(f"long decode: {ms * 1e3:.1f} us per 32-layer step, {gbs:.0f} GB/s")
+    return {
+        "metric": "decode-attn effective KV GB/s, 32 layers of 131072 tokens, int4",
+        "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": round(ms, 4), "us_per_step": round(ms * 1e3, 2),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "i8 MFMA (i32 acc) + f32 softmax", "data": "synthetic (seeded, drawn on the device)",
+        "config": {"workload": w.name, "batch": w.batch, "q_heads": w.q_heads, "kv_heads": w.kv_heads,
+                   "head_dim": w.head_dim, "context": w.prefill, "layers": w.layers,
+                   "codes": f"int{w.code_bits}", "parallelism": "single-gpu"},
+        "bytes_per_step": int(nbytes),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "kvq_decode_attn = decode_i8_kernel<128,4,4> + merge_kernel<128,4>"},
+    }
+
+
+def append_bytes(cfg, st0, st1, n_new: int) -> int:
+    """Algorithmic bytes of one append: new tokens read, surviving tokens written to
+    the tail ring, flushed tokens read (old tail + new) and their codes and scales
+    written."""
+    units = cfg.batch * cfg.kv_heads
+    D, es = cfg.head_dim, 2 if cfg.kv_dtype == 0 else 4
+    W = D * cfg.code_bits // 8
+    flushed = st1.quantized - st0.quantized
+    kept_new = n_new - max(0, flushed - st0.tail)
+    nseg = st1.segments - st0.segments
+    per_unit = 2 * n_new * D * es                  # read K, V of the new tokens
+    per_unit += 2 * kept_new * D * es              # write them to the tail ring
+    per_unit += 2 * min(flushed, st0.tail) * D * es  # read the flushed tokens that sat in the tail
+    per_unit += 2 * flushed * W + flushed * 2 + nseg * D * 2   # codes, V scales, K scales
+    return units * per_unit
+
+
+def run_append(args, log, bits: int):
+    """128 appends of 16 tokens into 4096-token caches of 16 x 8 heads.
+
+    The 128 calls are captured once into a HIP graph (the host-side token
+    accounting runs at capture) and the graph is replayed: the replays time
+    the GPU work of the whole run without per-call host overhead.  Replays
+    rewrite the same buffers, so only the first pass leaves the exact cache
+    the calls describe; the timing does not depend on the values.  The eager
+    (host-driven) time per append is reported beside it.
+    """
+    import torch
+
+    import kvq_synth as ks
+    from quantized_kv_cache_kvq_amd import KVCache, make_config
+
+    w = ks.APPEND_INT8 if bits == 8 else ks.APPEND_INT4
+    total = w.prefill + w.steps * w.step_tokens
+    cfg = make_config(batch=w.batch, kv_heads=w.kv_heads, head_dim=w.head_dim, capacity=total,
+                      code_bits=w.code_bits, qmax=w.qmax, residual=w.residual, group=w.group)
+    k0, v0 = ks.device_kv_pair(w, w.prefill, seed=0)
+    kn, vn = ks.device_kv_pair(w, w.steps * w.step_tokens, seed=1)
+    chunks = [(kn[:, :, i * w.step_tokens:(i + 1) * w.step_tokens].contiguous(),
+               vn[:, :, i * w.step_tokens:(i + 1) * w.step_tokens].contiguous()) for i in range(w.steps)]
+
+    def fresh():
+        c = KVCache(cfg, zero=False)
+        c.append(k0, v0)
+        torch.cuda.synchronize()
+        return c
+
+    def snap(st):
+        return type("S", (), dict(quantized=st.quantized, tail=st.tail, total=st.total,
+                                  flushed_last=st.flushed_last, segments=st.segments))
+
+    # eager: host-driven calls, one event pair around the run
+    stream = torch.cuda.current_stream()
+    eager_ms = []
+    for r in range(2):
+        c = fresh()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for kc, vc in chunks:
+            c.append(kc, vc, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        eager_ms.append(e0.elapsed_time(e1))
+    # graph: capture the 128 calls once, replay
+    c = fresh()
+    graph = torch.cuda.CUDAGraph()
+    nbytes, nflush = 0, 0
+    cap = torch.cuda.Stream()
+    cap.wait_stream(stream)
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(graph, stream=cap):
+            for kc, vc in chunks:
+                st0 = snap(c.state)
+                c.append(kc, vc, cap)
+                nbytes += append_bytes(cfg, st0, c.state, w.step_tokens)
+                nflush += int(c.state.flushed_last > 0)
+    stream.wait_stream(cap)
+    runs = max(3, args.steps // 20)
+    for _ in range(2):
+        graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(runs):
+        graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / runs
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    log(f"append int{bits}: graph {ms * 1e3:.1f} us per {w.steps} appends ({nflush} with a flush), "
+        f"{gbs:.0f} GB/s; eager {min(eager_ms) * 1e3 / w.steps:.1f} us per append")
+    return {
+        "metric": f"append/quantize write path GB/s, int{bits}",
+        "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": w.steps, "warmup": 2,
+        "ms_per_step": round(ms / w.steps, 5), "us_per_append": round(ms * 1e3 / w.steps, 3),
+        "us_per_append_eager": round(min(eager_ms) * 1e3 / w.steps, 3), "flushes_per_run": nflush,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 in, f32 scale arithmetic, int codes", "data": "synthetic (seeded, drawn on the device)",
+        "config": {"workload": w.name, "batch": w.batch, "kv_heads": w.kv_heads, "head_dim": w.head_dim,
+                   "prefill": w.prefill, "appends": w.steps, "tokens_per_append": w.step_tokens,
+                   "codes": f"int{bits}", "residual": w.residual, "group": w.group,
+                   "parallelism": "single-gpu", "timing": "HIP graph of the 128 appends, replayed"},
+        "bytes_per_run": int(nbytes),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": f"kvq_append = flush_kernel<{bits}> + tail_kernel"},
+    }
+
+
 def cpu_baseline_decode(budget_s: float, log):
     """Time the CPU oracle's decode attention on a bounded sample of units."""
     import numpy as np
@@ -268,9 +436,12 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quiet", action="store_true")
-    ap.add_argument("--workload", choices=["llama3_decode", "video_block"], default="llama3_decode",
+    ap.add_argument("--workload", choices=["llama3_decode", "video_block", "long_decode", "append_int8",
+                                           "append_int4"], default="llama3_decode",
                     help="llama3_decode (default): the append + decode step; video_block: one "
-                         "1024-query causal block against the 432000-token int2 cache")
+                         "1024-query causal block against the 432000-token int2 cache; long_decode: "
+                         "32 layers of 131072-token caches; append_int8/int4: 128 appends of 16 "
+                         "tokens into 4096-token caches (16 x 8 heads)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build runs on a single MI355X and has no "
@@ -292,6 +463,10 @@ def main():
     kvq.load()
     if args.workload == "video_block":
         res = run_video_block(args, log)
+    elif args.workload == "long_decode":
+        res = run_long_decode(args, log)
+    elif args.workload.startswith("append_"):
+        res = run_append(args, log, 8 if args.workload == "append_int8" else 4)
     else:
         res, _ = run_decode(args, log)
         if not args.no_cpu_baseline:

@@ -150,3 +150,30 @@ def block_inputs(s: Stream, tq: int):
 def small(w: Workload, **changes) -> Workload:
     """A reduced copy of a workload (same dtype/codec), for CPU-sized parity."""
     return dataclasses.replace(w, **changes)
+
+
+def device_kv_pair(w: Workload, tokens: int, seed: int, device="cuda", outliers=None):
+    """(K, V) of shape [batch, kv_heads, tokens, head_dim] drawn on the device.
+
+    For benchmark-scale caches only: same distribution as ``kv_pair`` (float32
+    standard normals, the workload's outlier Key channels x10, cast to the
+    storage dtype) from a seeded torch generator, but not the same numbers as
+    the numpy draws the parity tests share with the oracle.
+    """
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed))
+    if outliers is None:
+        outliers = Stream(w, seed).outliers
+    shape = (w.batch, w.kv_heads, tokens, w.head_dim)
+    k = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+    k[..., torch.as_tensor(outliers, device=device)] *= w.outlier_gain
+    v = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+    dt = torch.bfloat16 if w.kv_dtype == "bf16" else torch.float32
+    return k.to(dt), v.to(dt)
+
+
+def device_queries(w: Workload, seed: int, device="cuda"):
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed) + 7919)
+    q = torch.randn((w.batch, w.q_heads, w.head_dim), generator=gen, device=device, dtype=torch.float32)
+    return q.to(torch.bfloat16 if w.kv_dtype == "bf16" else torch.float32)

@@ -10,9 +10,11 @@
 // clamp(rne(fp32(x) * scale16), -qmax, qmax), packed as b-bit fields.
 //
 // Device work of one append, in stream order:
-//   1. flush_kernel  -- one workgroup per (new segment, batch*head).  Tokens
-//      are read straight from the old tail ring or from the new input (the
-//      "concatenation" is virtual), reduced, scaled, rounded and packed.
+//   1. flush_kernel  -- grid (segments * (1 + value workgroups), batch*heads).
+//      Per segment one workgroup quantizes the Keys and a few quantize the
+//      Values, one group of 64-token tiles each.  Tokens are read straight
+//      from the old tail ring or from the new input (the "concatenation" is
+//      virtual), as 16-byte pieces of their rows.
 //   2. tail_kernel   -- copies the new tokens that stay in the window into
 //      their ring slots.  It runs after the flush because a ring slot being
 //      refilled may hold a token the flush is still reading.
@@ -22,7 +24,7 @@ namespace kvq {
 namespace {
 
 constexpr int kFlushThreads = 256;
-constexpr int kVChunk = 1024;  // tokens per Value-scale staging chunk (64-aligned)
+constexpr int kKeyBatch = 8;      // 16-byte pieces per thread in flight in the Key pass
 
 struct FlushArgs {
   Geom g;
@@ -37,21 +39,33 @@ struct FlushArgs {
   uint16_t* v_scale;
   int32_t* seg_index;
   int64_t nq_old, nt_old;  // accounting before this append
+  int nq_slot_old;         // nq_old % ring: ring slot of the oldest tail token
   int64_t seg_base;        // id of the first segment written by this launch
   int64_t seg_len;         // tokens per segment (G, or the whole flush when G == 0)
+  int pieces;              // 16-byte pieces per token row
+  int v_tiles_per_wg;      // 64-token tiles per Value workgroup
+  int v_wgs;               // Value workgroups per segment
 };
 
-// Token at absolute position p of stream bh, channel c: from the old tail
-// ring if it was already cached, else from the new input.
-__device__ __forceinline__ float flush_src(const FlushArgs& a, bool key, int bh, int64_t p, int c) {
+// Row (head_dim elements) of absolute position p of the flushed range: the
+// old tail ring if p was already cached, else the new input.
+__device__ __forceinline__ const uint8_t* flush_row(const FlushArgs& a, bool key, int bh, int64_t p) {
   const Geom& g = a.g;
+  const int row_bytes = a.pieces * 16;
   const int64_t old_end = a.nq_old + a.nt_old;
   if (p < old_end) {
-    const int64_t slot = p % g.ring;
-    return load_elem(key ? a.k_tail : a.v_tail, ((int64_t)bh * g.ring + slot) * g.D + c, g.dtype);
+    int slot = a.nq_slot_old + static_cast<int>(p - a.nq_old);   // p - nq_old < nt_old <= ring
+    if (slot >= g.ring) slot -= g.ring;
+    return static_cast<const uint8_t*>(key ? a.k_tail : a.v_tail) + ((int64_t)bh * g.ring + slot) * row_bytes;
   }
-  const int64_t i = p - old_end;
-  return load_elem(key ? a.k_new : a.v_new, ((int64_t)bh * a.n_new + i) * g.D + c, g.dtype);
+  return static_cast<const uint8_t*>(key ? a.k_new : a.v_new) + ((int64_t)bh * a.n_new + (p - old_end)) * row_bytes;
+}
+
+// Element e (0 .. 16/es - 1) of a 16-byte piece as fp32 (exact).
+__device__ __forceinline__ float piece_elem(const uint4& w, int e, bool bf16) {
+  const uint32_t v[4] = {w.x, w.y, w.z, w.w};
+  if (bf16) return bf16_bits_to_f32((v[e / 2] >> (16 * (e % 2))) & 0xFFFFu);
+  return __uint_as_float(v[e]);
 }
 
 __device__ __forceinline__ float scale_of(float absmax, int qmax, float eps) {
@@ -67,113 +81,180 @@ __device__ __forceinline__ uint32_t code_field(float x, float s, int qmax, uint3
   return static_cast<uint32_t>(static_cast<int>(cl)) & mask;
 }
 
+// Max over aligned groups of `width` consecutive lanes (width a power of two
+// <= 32, wave-uniform).  Every lane of a group ends with the group's max.
+__device__ __forceinline__ float lane_group_max(float v, int width) {
+  if (width >= 2) v = fmaxf(v, dpp_f<kDppQuadXor1>(v));
+  if (width >= 4) v = fmaxf(v, dpp_f<kDppQuadXor2>(v));
+  if (width >= 8) v = fmaxf(v, dpp_f<kDppRowHalfMirror>(v));
+  if (width >= 16) v = fmaxf(v, dpp_f<kDppRowMirror>(v));
+  if (width >= 32) v = fmaxf(v, __shfl_xor(v, 16));
+  return v;
+}
+
+// Keys of one segment.  Thread (row group rg, piece q) reads piece q of the
+// tokens p0 + rg + rows*i.  The per-channel absmax is reduced over the
+// lanes holding the same piece, then over the four waves in LDS; the codes
+// of a piece (epp fields) are stored as one 1..8-byte word of its token's
+// 16-byte chunk.
 template <int BITS>
-__global__ __launch_bounds__(kFlushThreads) void flush_kernel(FlushArgs a) {
-  constexpr int kPer = 8 / BITS;             // fields per byte
+__device__ __forceinline__ void flush_keys(const FlushArgs& a, int bh, int64_t seg, int64_t p0, int64_t p1,
+                                           float (*red)[128], float* sc) {
   constexpr uint32_t kMask = (1u << BITS) - 1u;
   const Geom& g = a.g;
-  const int D = g.D;
-  const int tid = threadIdx.x;
-  const int bh = blockIdx.y;
-  const int64_t seg = a.seg_base + blockIdx.x;
-  const int64_t p0 = a.nq_old + (int64_t)blockIdx.x * a.seg_len;
-  const int64_t p1 = p0 + a.seg_len;
-
-  __shared__ float red[kFlushThreads];
-  __shared__ float kscale[128];
-  __shared__ float vscale[kVChunk];
-
-  // ---- Keys: per-channel absmax over the segment's tokens -----------------------
-  {
-    const int c = tid % D;
-    const int nsub = kFlushThreads / D;
-    const int sub = tid / D;
-    float m = 0.0f;
-    for (int64_t p = p0 + sub; p < p1; p += nsub) m = fmaxf(m, fabsf(flush_src(a, true, bh, p, c)));
-    red[tid] = m;
-    __syncthreads();
-    if (tid < D) {
-      for (int k = 1; k < nsub; ++k) m = fmaxf(m, red[k * D + tid]);
-      const uint16_t h = f32_to_half_bits(scale_of(m, g.qmax, g.eps));
-      a.k_scale[((int64_t)bh * g.max_seg + seg) * D + tid] = h;
-      kscale[tid] = half_bits_to_f32(h);
+  const int D = g.D, tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const bool bf16 = g.dtype == KVQ_BF16;
+  const int epp = bf16 ? 8 : 4;                  // elements per 16-byte piece
+  const int P = a.pieces;
+  const int rows = kFlushThreads / P;
+  const int q = tid % P, rg = tid / P;
+  const int64_t per_batch = (int64_t)rows * kKeyBatch;
+  const int nb = static_cast<int>((p1 - p0 + per_batch - 1) / per_batch);
+  uint4 r[kKeyBatch];
+  auto load_batch = [&](int b) {
+#pragma unroll
+    for (int i = 0; i < kKeyBatch; ++i) {
+      int64_t p = p0 + b * per_batch + rg + (int64_t)rows * i;
+      p = p < p1 ? p : p1 - 1;                   // clamped: the loads stay unconditional
+      r[i] = *reinterpret_cast<const uint4*>(flush_row(a, true, bh, p) + q * 16);
     }
-    __syncthreads();
-  }
-
-  // ---- Key codes: one 16-byte chunk of one token row per thread ------------------
-  {
-    uint8_t* kc = a.k_codes + (int64_t)bh * g.code_stream;
-    const int chunks = g.W / 16;
-    const int64_t items = (p1 - p0) * chunks;
-    for (int64_t it = tid; it < items; it += kFlushThreads) {
-      const int64_t p = p0 + it / chunks;
-      const int j = static_cast<int>(it % chunks);
-      uint32_t w4[4];
+  };
+  float mx[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+  for (int b = 0; b < nb; ++b) {
+    load_batch(b);
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        uint32_t word = 0;
-        const int c0 = (j * 16 + w * 4) * kPer;
+    for (int i = 0; i < kKeyBatch; ++i) {
+      // a clamped duplicate of the last token leaves the max unchanged
 #pragma unroll
-        for (int f = 0; f < 4 * kPer; ++f) {
-          const int c = c0 + f;
-          word |= code_field(flush_src(a, true, bh, p, c), kscale[c], g.qmax, kMask) << (f * BITS);
-        }
-        w4[w] = word;
-      }
-      const int64_t off = (p / kTile) * kTile * g.W + (int64_t)j * 1024 + (p % kTile) * 16;
-      *reinterpret_cast<uint4*>(kc + off) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+      for (int e = 0; e < 8; ++e)
+        if (e < epp) mx[e] = fmaxf(mx[e], fabsf(piece_elem(r[i], e, bf16)));
     }
   }
+  for (int m = P; m < kWave; m <<= 1) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) mx[e] = fmaxf(mx[e], __shfl_xor(mx[e], m));
+  }
+  if (lane < P) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (e < epp) red[wave][q * epp + e] = mx[e];
+  }
+  __syncthreads();
+  if (tid < D) {
+    const float m = fmaxf(fmaxf(red[0][tid], red[1][tid]), fmaxf(red[2][tid], red[3][tid]));
+    const uint16_t h = f32_to_half_bits(scale_of(m, g.qmax, g.eps));
+    a.k_scale[((int64_t)bh * g.max_seg + seg) * D + tid] = h;
+    sc[tid] = half_bits_to_f32(h);
+  }
+  __syncthreads();
+  float s[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) s[e] = e < epp ? sc[q * epp + e] : 0.0f;
+  const int cpc = 128 / BITS;                    // channels per 16-byte chunk
+  const int j = (q * epp) / cpc;                 // chunk of the piece
+  const int byte_in_chunk = ((q * epp - j * cpc) * BITS) / 8;
+  const int bytes = epp * BITS / 8;              // 1, 2, 4 or 8
+  uint8_t* kc = a.k_codes + (int64_t)bh * g.code_stream + j * 1024 + byte_in_chunk;
+  for (int b = 0; b < nb; ++b) {
+    if (nb > 1) load_batch(b);                   // one batch: still in registers
+#pragma unroll
+    for (int i = 0; i < kKeyBatch; ++i) {
+      const int64_t p = p0 + b * per_batch + rg + (int64_t)rows * i;
+      if (p >= p1) continue;
+      uint64_t bits = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (e < epp) bits |= static_cast<uint64_t>(code_field(piece_elem(r[i], e, bf16), s[e], g.qmax, kMask)) << (e * BITS);
+      uint8_t* dst = kc + (p / kTile) * kTile * g.W + (p % kTile) * 16;
+      if (bytes == 8) *reinterpret_cast<uint2*>(dst) = make_uint2(static_cast<uint32_t>(bits), static_cast<uint32_t>(bits >> 32));
+      else if (bytes == 4) *reinterpret_cast<uint32_t*>(dst) = static_cast<uint32_t>(bits);
+      else if (bytes == 2) *reinterpret_cast<uint16_t*>(dst) = static_cast<uint16_t>(bits);
+      else *dst = static_cast<uint8_t>(bits);
+    }
+  }
+}
 
-  // ---- Values: per-token scales and codes, in 64-aligned chunks of tokens --------
+// Values of one group of 64-token tiles.  A packed word holds one channel
+// of 32/BITS consecutive tokens, so unit (tile, token group wj, piece q)
+// reads piece q of those tokens and builds the words of the piece's
+// channels in registers.  The units of a token group sit in `pieces`
+// consecutive lanes, which reduce the per-token absmax; every lane derives
+// the scale itself, the piece-0 lane stores it.
+template <int BITS>
+__device__ __forceinline__ void flush_values(const FlushArgs& a, int bh, int vw, int64_t p0, int64_t p1) {
+  constexpr uint32_t kMask = (1u << BITS) - 1u;
+  constexpr int kTok = 32 / BITS;                // tokens per packed word
+  constexpr int kGroups = kTile / kTok;          // words per channel in a tile
+  const Geom& g = a.g;
+  const bool bf16 = g.dtype == KVQ_BF16;
+  const int epp = bf16 ? 8 : 4;
+  const int P = a.pieces;
+  const int per_tile = kGroups * P;              // units per tile
+  const int units = a.v_tiles_per_wg * per_tile; // a multiple of the block size
   uint8_t* vc = a.v_codes + (int64_t)bh * g.code_stream;
-  const int wave = tid / kWave, lane = tid % kWave;
-  constexpr int kTokPerWord = 32 / BITS;
-  for (int64_t t0 = (p0 / kTile) * kTile; t0 < p1; t0 += kVChunk) {
-    const int64_t cs = t0 > p0 ? t0 : p0;
-    const int64_t ce = (t0 + kVChunk) < p1 ? (t0 + kVChunk) : p1;
-    __syncthreads();
-    for (int64_t p = cs + wave; p < ce; p += kFlushThreads / kWave) {
-      float m = 0.0f;
-      for (int c = lane; c < D; c += kWave) m = fmaxf(m, fabsf(flush_src(a, false, bh, p, c)));
-      m = wave_max(m);
-      if (lane == 0) {
-        const uint16_t h = f32_to_half_bits(scale_of(m, g.qmax, g.eps));
-        a.v_scale[(int64_t)bh * g.C + p] = h;
-        vscale[p - t0] = half_bits_to_f32(h);
-      }
-    }
-    __syncthreads();
-    // Words of kTokPerWord tokens of one channel; channel fastest so that the
-    // source reads of consecutive threads are contiguous.
-    const int64_t w_first = cs / kTokPerWord, w_last = (ce - 1) / kTokPerWord;
-    const int64_t items = (w_last - w_first + 1) * D;
-    for (int64_t it = tid; it < items; it += kFlushThreads) {
-      const int c = static_cast<int>(it % D);
-      const int64_t wt = (w_first + it / D) * kTokPerWord;   // first token of the word
-      const int64_t off = (wt / kTile) * kTile * g.W + (int64_t)c * 8 * BITS + ((wt % kTile) * BITS) / 8;
-      uint32_t* dst = reinterpret_cast<uint32_t*>(vc + off);
-      uint32_t word = 0;
-      if (wt < cs) {
-        // Only at an unaligned segment start (group == 0): keep the fields of
-        // the previous segment's tokens.
-        const int keep = static_cast<int>(cs - wt);
-        word = *dst & ((1u << (keep * BITS)) - 1u);
-      }
+  for (int u = threadIdx.x; u < units; u += kFlushThreads) {
+    const int q = u % P, wj = (u / P) % kGroups, tw = u / per_tile;
+    const int64_t t0 = (p0 / kTile + (int64_t)vw * a.v_tiles_per_wg + tw) * kTile;
+    const int64_t wt = t0 + wj * kTok;           // first token of the word
+    uint4 x[kTok];
 #pragma unroll
-      for (int f = 0; f < kTokPerWord; ++f) {
-        const int64_t t = wt + f;
-        if (t >= cs && t < ce)
-          word |= code_field(flush_src(a, false, bh, t, c), vscale[t - t0], g.qmax, kMask) << (f * BITS);
+    for (int i = 0; i < kTok; ++i) {
+      int64_t p = wt + i;
+      p = p < p0 ? p0 : (p < p1 ? p : p1 - 1);    // clamped: the loads stay unconditional
+      x[i] = *reinterpret_cast<const uint4*>(flush_row(a, false, bh, p) + q * 16);
+    }
+    float s[kTok];
+#pragma unroll
+    for (int i = 0; i < kTok; ++i) {
+      float m = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (e < epp) m = fmaxf(m, fabsf(piece_elem(x[i], e, bf16)));
+      m = lane_group_max(m, P);
+      const uint16_t h = f32_to_half_bits(scale_of(m, g.qmax, g.eps));
+      s[i] = half_bits_to_f32(h);
+      const int64_t t = wt + i;
+      if (q == 0 && t >= p0 && t < p1) a.v_scale[(int64_t)bh * g.C + t] = h;
+    }
+    if (wt + kTok <= p0 || wt >= p1) continue;   // no token of this word is flushed here
+    uint32_t keep_mask = 0;
+    if (wt < p0) keep_mask = (1u << ((p0 - wt) * BITS)) - 1u;   // unaligned start (group == 0)
+    uint32_t* dst = reinterpret_cast<uint32_t*>(vc + (t0 / kTile) * kTile * g.W + wj * 4);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if (e >= epp) continue;
+      const int c = q * epp + e;
+      uint32_t word = 0;
+#pragma unroll
+      for (int i = 0; i < kTok; ++i) {
+        const int64_t t = wt + i;
+        if (t >= p0 && t < p1) word |= code_field(piece_elem(x[i], e, bf16), s[i], g.qmax, kMask) << (i * BITS);
       }
-      *dst = word;
+      uint32_t* w = dst + c * 2 * BITS;          // channel c: 8*BITS bytes per tile
+      if (keep_mask) word |= *w & keep_mask;     // keep the previous segment's fields
+      *w = word;
     }
   }
+}
 
-  // ---- group == 0: record the segment id of every flushed token ------------------
-  if (g.G == 0 && bh == 0) {
-    for (int64_t p = p0 + tid; p < p1; p += kFlushThreads) a.seg_index[p] = static_cast<int32_t>(seg);
+template <int BITS>
+__global__ __launch_bounds__(kFlushThreads) void flush_kernel(FlushArgs a) {
+  const int bh = blockIdx.y;
+  const int per_seg = 1 + a.v_wgs;
+  const int64_t sl = blockIdx.x / per_seg;
+  const int role = blockIdx.x % per_seg;
+  const int64_t seg = a.seg_base + sl;
+  const int64_t p0 = a.nq_old + sl * a.seg_len;
+  const int64_t p1 = p0 + a.seg_len;
+  __shared__ float red[kFlushThreads / kWave][128];
+  __shared__ float sc[128];
+  if (role == 0) {
+    flush_keys<BITS>(a, bh, seg, p0, p1, red, sc);
+    // group == 0: record the segment id of every flushed token
+    if (a.g.G == 0 && bh == 0)
+      for (int64_t p = p0 + threadIdx.x; p < p1; p += kFlushThreads) a.seg_index[p] = static_cast<int32_t>(seg);
+  } else {
+    flush_values<BITS>(a, bh, role - 1, p0, p1);
   }
 }
 
@@ -183,31 +264,26 @@ struct TailArgs {
   uint8_t* k_tail;
   uint8_t* v_tail;
   int64_t n_new;      // tokens in the input
-  int64_t first;      // first input token that stays in the window
-  int64_t count;      // tokens that stay
-  int64_t pos0;       // absolute position of input token 0
+  int first;          // first input token that stays in the window
+  int count;          // tokens that stay (<= ring)
+  int slot0;          // ring slot of input token `first`
   int ring;
   int row16;          // 16-byte chunks per token row
-  int BH;
 };
 
+// grid (chunks of count * row16, batch*heads, 2 = K / V): one 16-byte copy per thread.
 __global__ __launch_bounds__(256) void tail_kernel(TailArgs a) {
-  const int64_t per_bh = a.count * a.row16;
-  const int64_t total = per_bh * a.BH * 2;
-  for (int64_t it = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; it < total;
-       it += (int64_t)gridDim.x * blockDim.x) {
-    const bool val = it >= per_bh * a.BH;
-    const int64_t r = val ? it - per_bh * a.BH : it;
-    const int64_t bh = r / per_bh;
-    const int64_t rem = r % per_bh;
-    const int64_t i = a.first + rem / a.row16;        // input token
-    const int64_t ch = rem % a.row16;
-    const int64_t slot = (a.pos0 + i) % a.ring;
-    const uint4* src = reinterpret_cast<const uint4*>(val ? a.v_new : a.k_new) +
-                       (bh * a.n_new + i) * a.row16 + ch;
-    uint4* dst = reinterpret_cast<uint4*>(val ? a.v_tail : a.k_tail) + (bh * a.ring + slot) * a.row16 + ch;
-    *dst = *src;
-  }
+  const int it = blockIdx.x * blockDim.x + threadIdx.x;
+  if (it >= a.count * a.row16) return;
+  const int bh = blockIdx.y;
+  const bool val = blockIdx.z == 1;
+  const int j = it / a.row16, ch = it % a.row16;
+  int slot = a.slot0 + j;
+  if (slot >= a.ring) slot -= a.ring;
+  const uint4* src = reinterpret_cast<const uint4*>(val ? a.v_new : a.k_new) +
+                     ((int64_t)bh * a.n_new + a.first + j) * a.row16 + ch;
+  uint4* dst = reinterpret_cast<uint4*>(val ? a.v_tail : a.k_tail) + ((int64_t)bh * a.ring + slot) * a.row16 + ch;
+  *dst = *src;
 }
 
 kvq_status check_state(const Geom& g, const kvq_state* st) {
@@ -287,10 +363,18 @@ extern "C" kvq_status kvq_append(const kvq_config* cfg, kvq_state* st, const kvq
     a.seg_index = static_cast<int32_t*>(cache->seg_index);
     a.nq_old = st->quantized;
     a.nt_old = st->tail;
+    a.nq_slot_old = static_cast<int>(st->quantized % g.ring);
     a.seg_base = st->segments;
     a.seg_len = g.G == 0 ? flush : g.G;
+    a.pieces = g.D * (g.dtype == KVQ_BF16 ? 2 : 4) / 16;
+    const int per_tile = (kTile / (32 / g.bits)) * a.pieces;   // Value units of one tile
+    a.v_tiles_per_wg = per_tile >= kFlushThreads ? 1 : kFlushThreads / per_tile;
+    // tiles touched by one segment (group > 0 segments are tile aligned)
+    const int64_t p0 = a.nq_old, p1 = a.nq_old + a.seg_len;
+    const int64_t seg_tiles = (p1 + kTile - 1) / kTile - p0 / kTile;
+    a.v_wgs = static_cast<int>((seg_tiles + a.v_tiles_per_wg - 1) / a.v_tiles_per_wg);
     const int64_t nseg = flush / a.seg_len;
-    dim3 grid(static_cast<unsigned>(nseg), static_cast<unsigned>(g.B * g.H));
+    dim3 grid(static_cast<unsigned>(nseg * (1 + a.v_wgs)), static_cast<unsigned>(g.B * g.H));
     switch (g.bits) {
       case 8: hipLaunchKernelGGL(flush_kernel<8>, grid, dim3(kFlushThreads), 0, hs, a); break;
       case 4: hipLaunchKernelGGL(flush_kernel<4>, grid, dim3(kFlushThreads), 0, hs, a); break;
@@ -308,16 +392,14 @@ extern "C" kvq_status kvq_append(const kvq_config* cfg, kvq_state* st, const kvq
     t.k_tail = static_cast<uint8_t*>(cache->k_tail);
     t.v_tail = static_cast<uint8_t*>(cache->v_tail);
     t.n_new = n_new;
-    t.first = first;
-    t.count = count;
-    t.pos0 = old_end;
+    t.first = static_cast<int>(first);
+    t.count = static_cast<int>(count);
+    t.slot0 = static_cast<int>((old_end + first) % g.ring);
     t.ring = g.ring;
     t.row16 = g.D * (g.dtype == KVQ_BF16 ? 2 : 4) / 16;
-    t.BH = g.B * g.H;
-    const int64_t total = count * t.row16 * t.BH * 2;
-    int64_t blocks = (total + 255) / 256;
-    if (blocks > 4096) blocks = 4096;
-    hipLaunchKernelGGL(tail_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, hs, t);
+    const int64_t items = count * t.row16;
+    dim3 tgrid(static_cast<unsigned>((items + 255) / 256), static_cast<unsigned>(g.B * g.H), 2);
+    hipLaunchKernelGGL(tail_kernel, tgrid, dim3(256), 0, hs, t);
   }
   if (hipGetLastError() != hipSuccess) return KVQ_EDEVICE;
   *st = next;
