@@ -71,6 +71,8 @@ struct DecodeArgs {
   float* part;           // [unit][split][gqa][D + 2]
   int splits;
   int tiles_q, items;    // quantized tiles; work items = tiles_q + tail chunks
+  int tq_div, tq_mod;    // tiles_q = splits * tq_div + tq_mod
+  int ch_div, ch_mod;    // tail chunks, likewise
 };
 
 
@@ -326,11 +328,11 @@ struct WaveWork {
 };
 template <int kChunkCost>
 __device__ __forceinline__ WaveWork wave_work(const DecodeArgs& a, int split, int wave) {
-  const int chunks = a.items - a.tiles_q;
-  const int ts0 = (int)(((int64_t)a.tiles_q * split) / a.splits);
-  const int ts1 = (int)(((int64_t)a.tiles_q * (split + 1)) / a.splits);
-  const int cs0 = (int)(((int64_t)chunks * split) / a.splits);
-  const int cs1 = (int)(((int64_t)chunks * (split + 1)) / a.splits);
+  // the first (count % splits) splits take one item more (no division here)
+  const int ts0 = split * a.tq_div + (split < a.tq_mod ? split : a.tq_mod);
+  const int ts1 = ts0 + a.tq_div + (split < a.tq_mod ? 1 : 0);
+  const int cs0 = split * a.ch_div + (split < a.ch_mod ? split : a.ch_mod);
+  const int cs1 = cs0 + a.ch_div + (split < a.ch_mod ? 1 : 0);
   const int nt = ts1 - ts0, nc = cs1 - cs0;
   const int cost = nt + kChunkCost * nc;
   const int lo = (cost * wave) / kWaves, hi = (cost * (wave + 1)) / kWaves;
@@ -558,6 +560,24 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
 // of one Value-operand dword and stores each digit with one 32-bit LDS write.
 
 typedef int i4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf8_t __attribute__((ext_vector_type(8)));
+typedef float f4_t __attribute__((ext_vector_type(4)));
+
+// bf16 bits of x, rounded to nearest even (x finite).
+__device__ __forceinline__ uint32_t bf16_rne(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// A 16-token chunk of the bf16 window as the matrix-core path reads it:
+// Keys as the B operand of the score MFMA (lane (q4, col): channels
+// 32 mk + 8 q4 .. + 8 of token col), Values by channel owner (TailMap).
+template <int D>
+struct ChunkRegs {
+  uint4 k[D / 32];
+  uint32_t v[kTailChunk];
+  int nvalid;
+};
 
 // Sixteen packed b-bit fields (one operand k-group) -> four dwords of int8
 // values 2^(8-b) * field; field(j) = the field held in operand slot j.
@@ -628,7 +648,7 @@ void decode_i8_kernel(DecodeArgs a) {
   const int unit = blockIdx.y;
   const int split = blockIdx.x;
 
-  __shared__ float qsT[D][GQA];                       // sigma log2e q (tail path)
+  __shared__ __attribute__((aligned(16))) float qsN[GQA][D];     // sigma log2e q (tail path)
   __shared__ __attribute__((aligned(16))) float qsP[GQA][D];     // same, channels in slot order
   __shared__ __attribute__((aligned(16))) float rkP[kWaves][D];  // 1 / kscale, slot order
   __shared__ __attribute__((aligned(16))) uint32_t qD[kWaves][HG][MK][16][4][4];  // Key operand digits
@@ -663,7 +683,6 @@ void decode_i8_kernel(DecodeArgs a) {
   // Online-softmax state: head 4 hg + q4 of this lane's row quad.
   float m[HG], lsum[HG], inv[HG], mq[HG];
   float acc_f[HG][NV];
-  i4_t acc_i[HG][NV];
   auto init_state = [&]() {
 #pragma unroll
     for (int hg = 0; hg < HG; ++hg) {
@@ -671,10 +690,7 @@ void decode_i8_kernel(DecodeArgs a) {
       lsum[hg] = 0.0f;
       inv[hg] = 0.0f;
 #pragma unroll
-      for (int n = 0; n < NV; ++n) {
-        acc_f[hg][n] = 0.0f;
-        acc_i[hg][n] = i4_t{0, 0, 0, 0};
-      }
+      for (int n = 0; n < NV; ++n) acc_f[hg][n] = 0.0f;
       // max |q| of head 4 hg + q4 (bounds the fixed-point query with max 1/kscale)
       const int h = 4 * hg + q4;
       float mx = 0.0f;
@@ -763,15 +779,6 @@ void decode_i8_kernel(DecodeArgs a) {
       for (int mk = 0; mk < MK; ++mk) qop[hg][mk] = *reinterpret_cast<const i4_t*>(&qD[wave][hg][mk][col][q4][0]);
   };
 
-  // int32 digit sums -> fp32 accumulator (before a rescale and at the end)
-  auto fold_int = [&](int hg, float scale) {
-#pragma unroll
-    for (int n = 0; n < NV; ++n) {
-      acc_f[hg][n] = (acc_f[hg][n] + digits_value(acc_i[hg][n])) * scale;
-      acc_i[hg][n] = i4_t{0, 0, 0, 0};
-    }
-  };
-
   float fv = 0.0f;        // Fv: P = fv * p / vscale
   auto compute_tile = [&](const TileRegs& r) {
     float x[HG][4];
@@ -790,21 +797,13 @@ void decode_i8_kernel(DecodeArgs a) {
       for (int hg = 0; hg < HG; ++hg) x[hg][gg] = digits_value(s[hg]) * inv[hg];
     }
     float alpha[HG];
-    bool moved = false;   // a running maximum moved (the first tile only sets it)
 #pragma unroll
     for (int hg = 0; hg < HG; ++hg) {
       const float tm = row16_max(fmaxf(fmaxf(x[hg][0], x[hg][1]), fmaxf(x[hg][2], x[hg][3])));
-      const float mn = fmaxf(m[hg], tm);
-      alpha[hg] = fast_exp2(m[hg] - mn);
-      moved |= alpha[hg] != 1.0f && m[hg] != -INFINITY;
+      const float mn = fmaxf(m[hg], tm);     // finite: every token of a tile is cached
+      alpha[hg] = fast_exp2(m[hg] - mn);     // exp2(-inf) = 0 on the first tile
       m[hg] = mn;
-    }
-    if (__any(moved)) {
-#pragma unroll
-      for (int hg = 0; hg < HG; ++hg) {
-        lsum[hg] *= alpha[hg];
-        fold_int(hg, alpha[hg]);
-      }
+      lsum[hg] *= alpha[hg];
     }
     float vsrf[4];
 #pragma unroll
@@ -828,11 +827,16 @@ void decode_i8_kernel(DecodeArgs a) {
     i4_t pop[HG];
 #pragma unroll
     for (int hg = 0; hg < HG; ++hg) pop[hg] = *reinterpret_cast<const i4_t*>(&pD[wave][hg][col][q4][0]);
+    // The tile's int32 digit sums start from zero and are folded into the
+    // fp32 accumulator at once: nothing integer is carried between tiles.
 #pragma unroll
     for (int n = 0; n < NV; ++n) {
       const i4_t vb = F16::unpack(r.vw[n]);
 #pragma unroll
-      for (int hg = 0; hg < HG; ++hg) acc_i[hg][n] = __builtin_amdgcn_mfma_i32_16x16x64_i8(pop[hg], vb, acc_i[hg][n], 0, 0, 0);
+      for (int hg = 0; hg < HG; ++hg) {
+        const i4_t d = __builtin_amdgcn_mfma_i32_16x16x64_i8(pop[hg], vb, i4_t{0, 0, 0, 0}, 0, 0, 0);
+        acc_f[hg][n] = fmaf(acc_f[hg][n], alpha[hg], digits_value(d));
+      }
     }
     wave_lds_sync();      // pD is rewritten by the next tile
   };
@@ -873,7 +877,7 @@ void decode_i8_kernel(DecodeArgs a) {
   for (int k = 0; k < NQ; ++k) {
     const int i = tid + k * kThreads;
     if (i < GQA * D) {
-      qsT[i % D][i / D] = qT[k] * a.qscale;
+      qsN[i / D][i % D] = qT[k] * a.qscale;
       qsP[i / D][i % D] = qP[k] * a.qscale;
     }
   }
@@ -884,9 +888,25 @@ void decode_i8_kernel(DecodeArgs a) {
     for (int i = tid; i < (int)(sizeof(pD) / 16); i += kThreads) z1[i] = uint4{0u, 0u, 0u, 0u};
   }
   __syncthreads();
-  TailRegs<D, true> trA, trB;
+  // Tail chunks: 32-bit offsets inside this unit's ring (ring * D < 2^28).
+  const uint16_t* ring_k = static_cast<const uint16_t*>(a.k_tail) + (int64_t)unit * g.ring * D;
+  const uint16_t* ring_v = static_cast<const uint16_t*>(a.v_tail) + (int64_t)unit * g.ring * D;
+  auto chunk_load = [&](int chunk, ChunkRegs<D>& r) {
+    const int tt0 = chunk * kTailChunk;
+    r.nvalid = a.nt - tt0 < kTailChunk ? a.nt - tt0 : kTailChunk;
+    const uint16_t* kr = ring_k + tail_slot(a, tt0 + (col < r.nvalid ? col : 0)) * D + 8 * q4;
+#pragma unroll
+    for (int mk = 0; mk < D / 32; ++mk) r.k[mk] = *reinterpret_cast<const uint4*>(kr + 32 * mk);
+#pragma unroll
+    for (int t = 0; t < kTailChunk; ++t) {
+      const uint16_t* vr = ring_v + tail_slot(a, tt0 + (t < r.nvalid ? t : 0)) * D;
+      if constexpr (TCPL == 2) r.v[t] = *reinterpret_cast<const uint32_t*>(vr + 2 * lane);
+      else r.v[t] = vr[lane];
+    }
+  };
+  ChunkRegs<D> crA, crB;
   const bool has_chunks = ww.c0 < ww.c1;
-  if (has_chunks) tail_load<D, true>(a, unit, ww.c0, trA);   // computed after the tiles
+  if (has_chunks) chunk_load(ww.c0, crA);   // computed after the tiles
   init_state();
 
   if (tile < q_end) {
@@ -907,9 +927,7 @@ void decode_i8_kernel(DecodeArgs a) {
     fv = kFixP / wave_max(vsr_max);
   }
   // Quantized tiles: before a tile is computed (after its Key operands are
-  // built) the next one's loads are issued.  The int32 Value sums are folded into fp32 at least every 1024
-  // tiles (no overflow).
-  int since_fold = 0;
+  // built) the next one's loads are issued.
   if (tile < q_end) {
     while (true) {
       if (bufA.new_seg) build_key_operands(bufA);
@@ -920,18 +938,94 @@ void decode_i8_kernel(DecodeArgs a) {
       if (tile + 1 < q_end) load_tile(tile + 1, bufA);
       compute_tile(bufB);
       if (++tile >= q_end) break;
-      if ((since_fold += 2) >= 1024) {
-        since_fold = 0;
-#pragma unroll
-        for (int hg = 0; hg < HG; ++hg) fold_int(hg, 1.0f);
-      }
     }
   }
+
+  // Tail chunks (bf16) after the quantized tiles.  Scores on the matrix
+  // cores: A = the query in two bf16 rows per head (4 h: high part, 4 h + 1:
+  // the rounding remainder, about 16 more bits), B = the chunk's Keys, so
+  // lane (q4, col) receives head q4's score for token col -- the layout of
+  // the tile scores, and the same online-softmax state.  Weighted Values on
+  // the vector ALUs, each lane owning TCPL channels of every head.
+  float acc_tail[TCPL][GQA];
 #pragma unroll
-  for (int hg = 0; hg < HG; ++hg) fold_int(hg, 1.0f);
+  for (int h = 0; h < GQA; ++h)
+#pragma unroll
+    for (int k = 0; k < TCPL; ++k) acc_tail[k][h] = 0.0f;
+  if (has_chunks) {
+    bf8_t qa[HG][D / 32];
+    {
+      const int hq = col / 4, part = col % 4;
+#pragma unroll
+      for (int hg = 0; hg < HG; ++hg) {
+        const int h = 4 * hg + hq;
+#pragma unroll
+        for (int mk = 0; mk < D / 32; ++mk) {
+          uint32_t w[4] = {0u, 0u, 0u, 0u};
+          if (h < GQA && part < 2) {
+            const float* src = &qsN[h][32 * mk + 8 * q4];
+            const float4 x0 = *reinterpret_cast<const float4*>(src);
+            const float4 x1 = *reinterpret_cast<const float4*>(src + 4);
+            const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              const uint32_t hb = bf16_rne(xs[j]);
+              const uint32_t b = part == 0 ? hb : bf16_rne(xs[j] - bf16_bits_to_f32(hb));
+              w[j / 2] |= b << (16 * (j % 2));
+            }
+          }
+          qa[hg][mk] = __builtin_bit_cast(bf8_t, make_uint4(w[0], w[1], w[2], w[3]));
+        }
+      }
+    }
+    auto chunk_compute = [&](const ChunkRegs<D>& r) {
+      float al_u[GQA];
+#pragma unroll
+      for (int hg = 0; hg < HG; ++hg) {
+        f4_t sc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int mk = 0; mk < D / 32; ++mk)
+          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[hg][mk], __builtin_bit_cast(bf8_t, r.k[mk]), sc, 0, 0, 0);
+        const float x = col < r.nvalid ? sc[0] + sc[1] : -INFINITY;
+        const float mn = fmaxf(m[hg], row16_max(x));     // finite: a chunk has a valid token
+        const float al = fast_exp2(m[hg] - mn);            // exp2(-inf) = 0 before the first token
+        m[hg] = mn;
+        const float pr = fast_exp2(x - mn);                // 0 for padding tokens
+        lsum[hg] = lsum[hg] * al + pr;
+#pragma unroll
+        for (int n = 0; n < NV; ++n) acc_f[hg][n] *= al;
+        if (4 * hg + q4 < GQA) pw[wave][col][4 * hg + q4] = pr;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (4 * hg + i < GQA) al_u[4 * hg + i] = lane_value(al, 16 * i);
+      }
+      wave_lds_sync();
+#pragma unroll
+      for (int t = 0; t < kTailChunk; ++t) {
+        float v[TCPL];
+        v[0] = bf16_lo(r.v[t]);
+        if constexpr (TCPL == 2) v[1] = bf16_hi(r.v[t]);
+#pragma unroll
+        for (int h = 0; h < GQA; ++h) {
+          const float pt = pw[wave][t][h];
+#pragma unroll
+          for (int k = 0; k < TCPL; ++k)
+            acc_tail[k][h] = fmaf(pt, v[k], t == 0 ? acc_tail[k][h] * al_u[h] : acc_tail[k][h]);
+        }
+      }
+      wave_lds_sync();      // pw is rewritten by the next chunk
+    };
+    for (int chunk = ww.c0; chunk < ww.c1; chunk += 2) {
+      if (chunk + 1 < ww.c1) chunk_load(chunk + 1, crB);
+      chunk_compute(crA);
+      if (chunk + 1 >= ww.c1) break;
+      if (chunk + 2 < ww.c1) chunk_load(chunk + 2, crA);
+      chunk_compute(crB);
+    }
+  }
 
   // Per-head state as wave-uniform values (head 4 hg + i lives in lanes 16 i..).
-  float mu[GQA], lu[GQA], alpha_u[GQA], acc_tail[TCPL][GQA];
+  float mu[GQA], lu[GQA];
 #pragma unroll
   for (int hg = 0; hg < HG; ++hg) {
     const float ls = row16_sum(lsum[hg]);
@@ -943,36 +1037,6 @@ void decode_i8_kernel(DecodeArgs a) {
         lu[h] = lane_value(ls, 16 * i);
       }
     }
-  }
-#pragma unroll
-  for (int h = 0; h < GQA; ++h)
-#pragma unroll
-    for (int k = 0; k < TCPL; ++k) acc_tail[k][h] = 0.0f;
-  // Rescale the quantized-tile accumulator of this lane's head by a tail
-  // chunk's alpha (wave-uniform per head).
-  auto rescale_tail = [&](const float* al_u) {
-#pragma unroll
-    for (int hg = 0; hg < HG; ++hg) {
-      float al = 1.0f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (4 * hg + i < GQA && q4 == i) al = al_u[4 * hg + i];
-#pragma unroll
-      for (int n = 0; n < NV; ++n) acc_f[hg][n] *= al;
-    }
-  };
-
-  // Tail chunks (bf16) after the quantized tiles of this wave; the first
-  // one's loads were issued at the start, each later one's while the one
-  // before is computed.
-  for (int chunk = ww.c0; chunk < ww.c1; chunk += 2) {
-    if (chunk + 1 < ww.c1) tail_load<D, true>(a, unit, chunk + 1, trB);
-    tail_compute<D, GQA, true>(a, trA, qsT, pw[wave], mu, lu, alpha_u, acc_tail);
-    rescale_tail(alpha_u);
-    if (chunk + 1 >= ww.c1) break;
-    if (chunk + 2 < ww.c1) tail_load<D, true>(a, unit, chunk + 2, trA);
-    tail_compute<D, GQA, true>(a, trB, qsT, pw[wave], mu, lu, alpha_u, acc_tail);
-    rescale_tail(alpha_u);
   }
 
   // ---- wave result into red[wave][channel][head] ----
@@ -1094,6 +1158,10 @@ extern "C" kvq_status kvq_decode_attn(const kvq_config* cfg, const kvq_state* st
   a.items = a.tiles_q + (a.nt + kTailChunk - 1) / kTailChunk;
   const int units = g.B * g.H;
   a.splits = num_splits > 0 ? num_splits : auto_splits(units, a.items);
+  a.tq_div = a.tiles_q / a.splits;
+  a.tq_mod = a.tiles_q % a.splits;
+  a.ch_div = (a.items - a.tiles_q) / a.splits;
+  a.ch_mod = (a.items - a.tiles_q) % a.splits;
   clear_stale_hip_error();
   if (!dispatch(a, gqa, static_cast<hipStream_t>(stream))) return KVQ_EINVAL;
   return hipGetLastError() == hipSuccess ? KVQ_OK : KVQ_EDEVICE;
