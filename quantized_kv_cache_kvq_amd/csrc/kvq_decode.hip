@@ -24,20 +24,13 @@
 // multiply integer codes by folded factors.
 //
 // Two kernels share this structure:
-//   * decode_mfma_kernel (int4 codes, head_dim 64/128, whole-group segments,
-//     bf16 tail):
-//     both contractions of a tile run on v_mfma_f32_16x16x32_f16.  A nibble
-//     field with its sign bit flipped (u = code + 8) becomes the fp16 value
-//     X = 1 + u/16 by masking it into the mantissa of 1.0 (one shift and one
-//     and-or per pair of fields); with the other operand a pre-scaled by 16,
-//     sum a X = sum (a/16) code + 1.5 sum a, so the exact per-head term
-//     1.5 sum a (summed from the same fp16 operands) is subtracted.  Query
-//     heads are the MFMA M dimension (GQA <= 16).
-//     The folded query is carried as two fp16 terms (hi + lo, about 22
-//     significant bits): one fp16 term alone shifts the logits of outlier-
-//     heavy Key channels by up to ~2e-3 of the output.
-//   * decode_kernel (every other shape): the same tiles on the vector ALUs.
-// Tail chunks (bf16 / fp32 values) run on the vector ALUs in both kernels.
+//   * decode_i8_kernel (int4 / int2 codes, head_dim 64 / 128, whole-group
+//     segments, bf16 window): both contractions of a quantized tile run on
+//     the integer matrix cores (v_mfma_i32_16x16x64_i8, see the comment
+//     above that kernel); window chunks score on v_mfma_f32_16x16x32_bf16.
+//   * decode_kernel (every other shape): the same work items on the vector
+//     ALUs.
+// A second, small kernel merges the split partials.
 // Hot-loop indexing is 32-bit; ring slots wrap with one subtraction.
 #include "kvq_internal.h"
 
@@ -550,9 +543,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
 // Value side: acc[head][c] += sum_t P[head][t] code[t][c] with
 // P = Fv p / vscale[t], p = exp2(logit - running max) <= 1 and Fv fixed for the
 // wave's run of tiles (from the largest 1 / vscale in it), so P is an unsigned
-// 21-bit integer; its three base-128 digits go in rows 4 h + d and the
-// products accumulate in int32 across tiles.  When a running maximum moves,
-// the int32 sums are folded into an fp32 accumulator and rescaled.
+// 21-bit integer; its three base-128 digits go in rows 4 h + d.  A tile's
+// int32 digit sums start from zero and are recombined into the fp32
+// accumulator at once (acc = acc * alpha + sums), so no integer state is
+// carried from tile to tile.
 //
 // Token order: slot j of the Value operand of k-group kg holds token
 // 16 kg + f(j) (f = field order of the unpacked word); column col of Key MFMA
@@ -661,8 +655,9 @@ void decode_i8_kernel(DecodeArgs a) {
   auto chan = [](int p) { return (p & ~15) + F16::field(p & 15); };
 
 
-  // A 16-token bf16 tail chunk costs about three int4 tiles on this path.
-  const WaveWork ww = wave_work<3>(a, split, wave);
+  // A 16-token bf16 tail chunk (scores on the matrix cores) costs about
+  // what an int4 tile does, and moves as many bytes.
+  const WaveWork ww = wave_work<1>(a, split, wave);
   const int w_begin = ww.t0, q_end = ww.t1;
   const uint8_t* kbase = a.k_codes + (int64_t)unit * g.code_stream;
   const uint8_t* vbase = a.v_codes + (int64_t)unit * g.code_stream;

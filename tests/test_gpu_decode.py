@@ -165,3 +165,32 @@ def test_decode_back_to_back_on_one_workspace(splits):
     for i, out in enumerate(outs):
         assert max_abs(out.cpu().numpy(), refs[i % 4]) <= TOL, i
     assert not ws[:64].any()
+
+
+@needs_gpu
+def test_decode_graph_replay_matches_eager():
+    """A decode call captured in a HIP graph reproduces the eager output on
+    every replay, with eager calls on the same workspace in between."""
+    w = ks.small(ks.LLAMA3_DECODE, batch=2, kv_heads=2, q_heads=8)
+    p, s = build(w, 1000)
+    q = ks.decode_query(s).cuda()
+    ws = p.cache.workspace(w.q_heads)
+    eager = torch.empty(w.batch, w.q_heads, w.head_dim, device="cuda")
+    p.cache.decode_attn(q, eager, ws)
+    torch.cuda.synchronize()
+    out = torch.zeros_like(eager)
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    note("decode graph capture")
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(graph, stream=cap):
+            p.cache.decode_attn(q, out, ws, stream=cap)
+    torch.cuda.current_stream().wait_stream(cap)
+    other = torch.empty_like(eager)
+    for r in range(3):
+        out.zero_()
+        p.cache.decode_attn(ks.decode_query(s).cuda(), other, ws)   # eager work between replays
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), r
