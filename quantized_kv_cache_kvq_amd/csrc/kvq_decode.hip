@@ -218,46 +218,54 @@ __device__ __forceinline__ void tail_compute(const DecodeArgs& a, const TailRegs
   }
 }
 
-// One workgroup per (batch, KV head): combine the splits' partials
-// (m, l, acc) and write the output.  Eight splits are read per round trip
-// and folded with an online maximum.
+// Merge of the split partials (m, l, acc) of one (batch, KV head, query
+// head): one workgroup, thread c owns output channel c.  Every thread issues
+// its splits' acc[c] loads (up to 32 in flight) together with the split
+// maxima and sums, so up to 32 splits cost one memory round trip; the
+// per-split weights exp2(m_s - M) are computed once into LDS.
+constexpr int kMergeBatch = 32;
+
 template <int D, int GQA>
-__global__ __launch_bounds__(kThreads) void merge_kernel(DecodeArgs a) {
-  const int unit = blockIdx.x;
+__global__ __launch_bounds__(D) void merge_kernel(DecodeArgs a) {
+  const int unit = blockIdx.x, h = blockIdx.y, c = threadIdx.x;
   const Geom& g = a.g;
-  const int b = unit / g.H, kvh = unit % g.H;
-  const float* pu = a.part + (int64_t)unit * a.splits * GQA * (D + 2);
-  for (int i = threadIdx.x; i < GQA * D; i += kThreads) {
-    const int h = i / D, c = i % D;
-    float M = -INFINITY, num = 0.0f, den = 0.0f;
-    for (int s0 = 0; s0 < a.splits; s0 += 8) {
-      float ms[8], ls[8], vs[8];
+  const int S = a.splits;
+  const int stride = GQA * (D + 2);                  // floats between splits
+  const float* pu = a.part + (int64_t)unit * S * stride + h * (D + 2);
+  __shared__ float ew[kMaxSplits], el[kMaxSplits];
+  float v[kMergeBatch];
+  auto load_batch = [&](int s0) {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int s = s0 + k < a.splits ? s0 + k : s0;
-        const float* ps = pu + (s * GQA + h) * (D + 2);
-        ms[k] = ps[D];
-        ls[k] = ps[D + 1];
-        vs[k] = ps[c];
-      }
-      float mx = M;
-#pragma unroll
-      for (int k = 0; k < 8; ++k)
-        if (s0 + k < a.splits) mx = fmaxf(mx, ms[k]);
-      if (mx == -INFINITY) continue;               // every split so far is empty
-      const float r = M == -INFINITY ? 0.0f : fast_exp2(M - mx);
-      num *= r;
-      den *= r;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const float e = (s0 + k < a.splits && ms[k] != -INFINITY) ? fast_exp2(ms[k] - mx) : 0.0f;
-        num = fmaf(vs[k], e, num);
-        den = fmaf(ls[k], e, den);
-      }
-      M = mx;
+    for (int k = 0; k < kMergeBatch; ++k) {
+      const int sk = s0 + k < S ? s0 + k : S - 1;   // clamped: unconditional loads
+      v[k] = pu[sk * stride + c];
     }
-    a.out[((int64_t)b * g.H * GQA + kvh * GQA + h) * D + c] = num / den;
+  };
+  load_batch(0);
+  for (int sk = c; sk < S; sk += D) {
+    ew[sk] = pu[sk * stride + D];
+    el[sk] = pu[sk * stride + D + 1];
   }
+  __syncthreads();
+  float M = -INFINITY;
+  for (int sk = 0; sk < S; ++sk) M = fmaxf(M, ew[sk]);   // finite: the cache holds a token
+  __syncthreads();
+  for (int sk = c; sk < S; sk += D) {
+    const float e = ew[sk] == -INFINITY ? 0.0f : fast_exp2(ew[sk] - M);   // empty split: weight 0
+    ew[sk] = e;
+    el[sk] *= e;
+  }
+  __syncthreads();
+  float num = 0.0f, den = 0.0f;
+  for (int s0 = 0; s0 < S; s0 += kMergeBatch) {
+    if (s0 > 0) load_batch(s0);
+#pragma unroll
+    for (int k = 0; k < kMergeBatch; ++k)
+      if (s0 + k < S) num = fmaf(v[k], ew[s0 + k], num);
+  }
+  for (int sk = 0; sk < S; ++sk) den += el[sk];
+  const int b = unit / g.H, kvh = unit % g.H;
+  a.out[((int64_t)b * g.H * GQA + kvh * GQA + h) * D + c] = num / den;
 }
 
 // Fold the four waves of a workgroup and write a partial (or, with a single
@@ -1066,7 +1074,7 @@ void launch(const DecodeArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((decode_kernel<D, BITS, GQA>), grid, dim3(kThreads), 0, s, a);
   }
   if (a.splits > 1)
-    hipLaunchKernelGGL((merge_kernel<D, GQA>), dim3(a.g.B * a.g.H), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((merge_kernel<D, GQA>), dim3(a.g.B * a.g.H, GQA), dim3(D), 0, s, a);
 }
 
 template <int D, int BITS>
