@@ -562,6 +562,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
 // of one Value-operand dword and stores each digit with one 32-bit LDS write.
 
 typedef int i4_t __attribute__((ext_vector_type(4)));
+
+// Buffer resources: word 3 of a raw (untyped, stride 0) buffer, and an
+// offset beyond every resource's size (such a load reads nothing).
+constexpr int kRsrcWord3 = 0x00020000;
+constexpr int kOutOfRange = (int)0x80000000u;
 typedef __bf16 bf8_t __attribute__((ext_vector_type(8)));
 typedef float f4_t __attribute__((ext_vector_type(4)));
 
@@ -653,8 +658,11 @@ void decode_i8_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) float qsN[GQA][D];     // sigma log2e q (tail path)
   __shared__ __attribute__((aligned(16))) float qsP[GQA][D];     // same, channels in slot order
   __shared__ __attribute__((aligned(16))) float rkP[kWaves][D];  // 1 / kscale, slot order
-  __shared__ __attribute__((aligned(16))) uint32_t qD[kWaves][HG][MK][16][4][4];  // Key operand digits
-  __shared__ __attribute__((aligned(16))) uint32_t pD[kWaves][HG][16][4][4];      // Value operand digits
+  // Operand digits, one row per MFMA row; rows padded to 20 dwords so that
+  // the 16-byte operand reads (lane col reads row col) spread over all banks.
+  constexpr int kRowPad = 20;
+  __shared__ __attribute__((aligned(16))) uint32_t qD[kWaves][HG][MK][16][kRowPad];  // Key operand digits
+  __shared__ __attribute__((aligned(16))) uint32_t pD[kWaves][HG][16][kRowPad];      // Value operand digits
   __shared__ float pw[kWaves][kTailChunk][GQA];
   __shared__ float red[kWaves][D][GQA];
   __shared__ float wml[kWaves][2][GQA];
@@ -708,33 +716,79 @@ void decode_i8_kernel(DecodeArgs a) {
   struct TileRegs {
     raw_t kw[4][MK];
     raw_t vw[NV];
-    uint32_t vs[2];       // fp16 Value scales of tokens tok[0..3], two per word
-    uint32_t ks;          // fp16 Key scales of slots lane * RPL + 0..1 (RPL <= 2)
+    // fp16 Value scales of tokens tok[0..3] and Key scales of slots
+    // lane * RPL + i, kept 16-bit: widening them at load time would make the
+    // wave wait for the loads it has just issued
+    uint16_t vs[4];
+    uint16_t ks[RPL];
     bool new_seg;
   };
   static_assert(RPL <= 2, "two Key-scale slots per lane at most");
-  // Every load of a tile is unconditional (the Key scales too), so the
-  // number of loads a wave has in flight does not depend on the path and
-  // the compiler can wait for exactly the ones it needs.
-  auto load_tile = [&](int tile, TileRegs& r) {
-    r.new_seg = tile == w_begin || tile % a.tiles_per_seg == 0;
-    {
-      const uint16_t* ks = ksbase + (tile / a.tiles_per_seg) * D;
-      uint32_t k2 = ks[chan(lane * RPL)];
-      if constexpr (RPL == 2) k2 |= (uint32_t)ks[chan(lane * RPL + 1)] << 16;
-      r.ks = k2;
-    }
-    const uint8_t* kt = kbase + (int64_t)tile * (kTile * W);
-    const uint8_t* vt = vbase + (int64_t)tile * (kTile * W);
-    const uint16_t* vst = vsbase + tile * kTile;
+  // Every load of a tile or window chunk is issued unconditionally through a
+  // buffer resource; the loads of an item past the wave's run get an offset
+  // beyond the resource's size, which the hardware drops (no memory access,
+  // zero data).  The number of loads in flight is then the same on every
+  // path and the compiler waits for exactly the ones an item needs.  No
+  // loaded register is touched before its item is computed (packing two
+  // scales into one register at load time would make the wave wait for the
+  // loads it has just issued).
+  const __amdgpu_buffer_rsrc_t rK = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, (int)g.code_stream, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rV = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, (int)g.code_stream, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rKS = __builtin_amdgcn_make_buffer_rsrc((void*)ksbase, (short)0, g.max_seg * D * 2, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rVS = __builtin_amdgcn_make_buffer_rsrc((void*)vsbase, (short)0, g.C * 2, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rNull = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, 0, kRsrcWord3);
+  // Per-lane byte offsets inside a tile (loop invariant); the tile's own
+  // offset travels in the scalar offset of each load, so a tile's loads need
+  // no per-tile vector arithmetic (and no temporaries that alias the
+  // destinations of loads still in flight).
+  int koffv[4], vsoffv[4], ksoffv[RPL];
+#pragma unroll
+  for (int gg = 0; gg < 4; ++gg) {
+    koffv[gg] = koff(gg, 0);
+    vsoffv[gg] = tok(gg) * 2;
+  }
+#pragma unroll
+  for (int i = 0; i < RPL; ++i) ksoffv[i] = chan(lane * RPL + i) * 2;
+  constexpr int kMkBytes = ((8 * BITS) / 16) * 1024;   // koff(gg, mk) - koff(gg, 0) per mk
+  auto ld_raw = [&](__amdgpu_buffer_rsrc_t rs, int voff_, int soff) -> raw_t {
+    if constexpr (sizeof(raw_t) == 8)
+      return __builtin_bit_cast(raw_t, __builtin_amdgcn_raw_buffer_load_b64(rs, voff_, soff, 0));
+    else
+      return __builtin_bit_cast(raw_t, __builtin_amdgcn_raw_buffer_load_b32(rs, voff_, soff, 0));
+  };
+  // Tiles are loaded in order: the segment of the next one is tracked with a
+  // counter (no division per tile); the first load sets it.
+  int ld_seg = 0, ld_pos = 0;
+  auto load_tile = [&](int tile_, TileRegs& r) {
+    // Loop counters are wave-uniform; taking them through readfirstlane first
+    // keeps the whole offset computation in scalar registers.
+    const int tile = __builtin_amdgcn_readfirstlane(tile_);
+    const int seg = __builtin_amdgcn_readfirstlane(ld_seg);
+    const bool ok = tile < q_end;              // past the run: a zero-size resource, nothing read
+    r.new_seg = tile == w_begin || ld_pos == 0;
+    // scales first: the code words, issued last, are what a wait for the
+    // newest loads has to cover
+    const __amdgpu_buffer_rsrc_t rks = ok ? rKS : rNull;
+    const __amdgpu_buffer_rsrc_t rvs = ok ? rVS : rNull;
+    const __amdgpu_buffer_rsrc_t rk = ok ? rK : rNull;
+    const __amdgpu_buffer_rsrc_t rv = ok ? rV : rNull;
+    const int kso = ok ? seg * (D * 2) : 0;
+    const int vso = ok ? tile * (kTile * 2) : 0;
+    const int to = ok ? tile * (kTile * W) : 0;
+#pragma unroll
+    for (int i = 0; i < RPL; ++i) r.ks[i] = __builtin_amdgcn_raw_buffer_load_b16(rks, ksoffv[i], kso, 0);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) r.vs[k] = __builtin_amdgcn_raw_buffer_load_b16(rvs, vsoffv[k], vso, 0);
 #pragma unroll
     for (int gg = 0; gg < 4; ++gg)
 #pragma unroll
-      for (int mk = 0; mk < MK; ++mk) r.kw[gg][mk] = *reinterpret_cast<const raw_t*>(kt + koff(gg, mk));
+      for (int mk = 0; mk < MK; ++mk) r.kw[gg][mk] = ld_raw(rk, koffv[gg] + mk * kMkBytes, to);
 #pragma unroll
-    for (int n = 0; n < NV; ++n) r.vw[n] = *reinterpret_cast<const raw_t*>(vt + n * 16 * (8 * BITS) + voff);
-    r.vs[0] = (uint32_t)vst[tok(0)] | ((uint32_t)vst[tok(1)] << 16);
-    r.vs[1] = (uint32_t)vst[tok(2)] | ((uint32_t)vst[tok(3)] << 16);
+    for (int n = 0; n < NV; ++n) r.vw[n] = ld_raw(rv, voff + n * 16 * (8 * BITS), to);
+    if (++ld_pos == a.tiles_per_seg) {
+      ld_pos = 0;
+      ++ld_seg;
+    }
   };
 
   // Key operands of a segment: digit d of round(F a[head][c]) in row 4 h + d.
@@ -744,7 +798,7 @@ void decode_i8_kernel(DecodeArgs a) {
     float rkmax = 0.0f;
 #pragma unroll
     for (int i = 0; i < RPL; ++i) {
-      const float rk = fast_rcp(fmaxf(half_bits_to_f32((uint16_t)(r.ks >> (16 * i))), g.eps));
+      const float rk = fast_rcp(fmaxf(half_bits_to_f32(r.ks[i]), g.eps));
       rkP[wave][lane * RPL + i] = rk;
       rkmax = fmaxf(rkmax, rk);
     }
@@ -754,8 +808,11 @@ void decode_i8_kernel(DecodeArgs a) {
 #pragma unroll
     for (int hg = 0; hg < HG; ++hg) {
       const int h = 4 * hg + q4;
-      const float F = kFixQ / fmaxf(mq[hg] * rkmax, 1e-30f);   // all-zero query: any finite F
-      inv[hg] = h < GQA ? 1.0f / (F * F16::kMul) : 0.0f;
+      // F only sets the fixed-point scale: the hardware reciprocal (about one
+      // ulp) keeps |round(a F)| below 2^20 thanks to the headroom in kFixQ,
+      // and inv undoes exactly the F used, up to one more ulp.
+      const float F = kFixQ * fast_rcp(fmaxf(mq[hg] * rkmax, 1e-30f));   // all-zero query: any finite F
+      inv[hg] = h < GQA ? fast_rcp(F * F16::kMul) : 0.0f;
       if (h < GQA) {
 #pragma unroll
         for (int mk = 0; mk < MK; ++mk) {
@@ -764,14 +821,14 @@ void decode_i8_kernel(DecodeArgs a) {
           const float4 rv = *reinterpret_cast<const float4*>(&rkP[wave][p0]);
           const uint32_t u[4] = {fixed_biased(qv.x * rv.x, F), fixed_biased(qv.y * rv.y, F),
                                  fixed_biased(qv.z * rv.z, F), fixed_biased(qv.w * rv.w, F)};
-          uint32_t* dst = &qD[wave][hg][mk][4 * q4][kgi][qi];
+          uint32_t* dst = &qD[wave][hg][mk][4 * q4][4 * kgi + qi];
           // balanced digits: (u & 127) - 64, ((u >> 7) & 127) - 64, (u >> 14) - 64
-          dst[0 * 16] = pack_bytes((u[0] >> 14) - 64u, (u[1] >> 14) - 64u, (u[2] >> 14) - 64u,
-                                   (u[3] >> 14) - 64u);
-          dst[1 * 16] = pack_bytes(((u[0] >> 7) & 127u) - 64u, ((u[1] >> 7) & 127u) - 64u,
-                                   ((u[2] >> 7) & 127u) - 64u, ((u[3] >> 7) & 127u) - 64u);
-          dst[2 * 16] = pack_bytes((u[0] & 127u) - 64u, (u[1] & 127u) - 64u, (u[2] & 127u) - 64u,
-                                   (u[3] & 127u) - 64u);
+          dst[0 * kRowPad] = pack_bytes((u[0] >> 14) - 64u, (u[1] >> 14) - 64u, (u[2] >> 14) - 64u,
+                                        (u[3] >> 14) - 64u);
+          dst[1 * kRowPad] = pack_bytes(((u[0] >> 7) & 127u) - 64u, ((u[1] >> 7) & 127u) - 64u,
+                                        ((u[2] >> 7) & 127u) - 64u, ((u[3] >> 7) & 127u) - 64u);
+          dst[2 * kRowPad] = pack_bytes((u[0] & 127u) - 64u, (u[1] & 127u) - 64u, (u[2] & 127u) - 64u,
+                                        (u[3] & 127u) - 64u);
         }
       }
     }
@@ -779,7 +836,7 @@ void decode_i8_kernel(DecodeArgs a) {
 #pragma unroll
     for (int hg = 0; hg < HG; ++hg)
 #pragma unroll
-      for (int mk = 0; mk < MK; ++mk) qop[hg][mk] = *reinterpret_cast<const i4_t*>(&qD[wave][hg][mk][col][q4][0]);
+      for (int mk = 0; mk < MK; ++mk) qop[hg][mk] = *reinterpret_cast<const i4_t*>(&qD[wave][hg][mk][col][4 * q4]);
   };
 
   float fv = 0.0f;        // Fv: P = fv * p / vscale
@@ -811,7 +868,7 @@ void decode_i8_kernel(DecodeArgs a) {
     float vsrf[4];
 #pragma unroll
     for (int gg = 0; gg < 4; ++gg)
-      vsrf[gg] = fv * fast_rcp(fmaxf(half_bits_to_f32((uint16_t)(r.vs[gg / 2] >> (16 * (gg % 2)))), g.eps));
+      vsrf[gg] = fv * fast_rcp(fmaxf(half_bits_to_f32(r.vs[gg]), g.eps));
 #pragma unroll
     for (int hg = 0; hg < HG; ++hg) {
       uint32_t P[4];
@@ -821,15 +878,15 @@ void decode_i8_kernel(DecodeArgs a) {
         lsum[hg] += p;
         P[gg] = (uint32_t)(p * vsrf[gg]);
       }
-      uint32_t* dst = &pD[wave][hg][4 * q4][col / 4][col % 4];
-      dst[0 * 16] = pack_bytes(P[0] >> 14, P[1] >> 14, P[2] >> 14, P[3] >> 14);
-      dst[1 * 16] = pack_bytes((P[0] >> 7) & 127u, (P[1] >> 7) & 127u, (P[2] >> 7) & 127u, (P[3] >> 7) & 127u);
-      dst[2 * 16] = pack_bytes(P[0] & 127u, P[1] & 127u, P[2] & 127u, P[3] & 127u);
+      uint32_t* dst = &pD[wave][hg][4 * q4][col];      // k-group col / 4, dword col % 4
+      dst[0 * kRowPad] = pack_bytes(P[0] >> 14, P[1] >> 14, P[2] >> 14, P[3] >> 14);
+      dst[1 * kRowPad] = pack_bytes((P[0] >> 7) & 127u, (P[1] >> 7) & 127u, (P[2] >> 7) & 127u, (P[3] >> 7) & 127u);
+      dst[2 * kRowPad] = pack_bytes(P[0] & 127u, P[1] & 127u, P[2] & 127u, P[3] & 127u);
     }
     wave_lds_sync();
     i4_t pop[HG];
 #pragma unroll
-    for (int hg = 0; hg < HG; ++hg) pop[hg] = *reinterpret_cast<const i4_t*>(&pD[wave][hg][col][q4][0]);
+    for (int hg = 0; hg < HG; ++hg) pop[hg] = *reinterpret_cast<const i4_t*>(&pD[wave][hg][col][4 * q4]);
     // The tile's int32 digit sums start from zero and are folded into the
     // fp32 accumulator at once: nothing integer is carried between tiles.
 #pragma unroll
@@ -867,8 +924,9 @@ void decode_i8_kernel(DecodeArgs a) {
   }
   int tile = w_begin;
   TileRegs bufA, bufB;
-  const int last_tile = a.tiles_q - 1;          // >= 0: this kernel runs with a quantized prefix
-  load_tile(w_begin < last_tile ? w_begin : last_tile, bufA);
+  ld_seg = w_begin / a.tiles_per_seg;
+  ld_pos = w_begin - ld_seg * a.tiles_per_seg;
+  load_tile(w_begin, bufA);                   // nothing is read if the wave has no tiles
   float vs_run[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
@@ -885,31 +943,41 @@ void decode_i8_kernel(DecodeArgs a) {
     }
   }
   {
-    uint4* z0 = reinterpret_cast<uint4*>(&qD[0][0][0][0][0][0]);
+    uint4* z0 = reinterpret_cast<uint4*>(&qD[0][0][0][0][0]);
     for (int i = tid; i < (int)(sizeof(qD) / 16); i += kThreads) z0[i] = uint4{0u, 0u, 0u, 0u};
-    uint4* z1 = reinterpret_cast<uint4*>(&pD[0][0][0][0][0]);
+    uint4* z1 = reinterpret_cast<uint4*>(&pD[0][0][0][0]);
     for (int i = tid; i < (int)(sizeof(pD) / 16); i += kThreads) z1[i] = uint4{0u, 0u, 0u, 0u};
   }
   __syncthreads();
-  // Tail chunks: 32-bit offsets inside this unit's ring (ring * D < 2^28).
+  // Window chunks: this unit's ring through buffer resources (byte offsets
+  // below ring * D * 2 < 2^29); a chunk past the wave's run reads nothing.
   const uint16_t* ring_k = static_cast<const uint16_t*>(a.k_tail) + (int64_t)unit * g.ring * D;
   const uint16_t* ring_v = static_cast<const uint16_t*>(a.v_tail) + (int64_t)unit * g.ring * D;
-  auto chunk_load = [&](int chunk, ChunkRegs<D>& r) {
+  const __amdgpu_buffer_rsrc_t rRK = __builtin_amdgcn_make_buffer_rsrc((void*)ring_k, (short)0, g.ring * D * 2, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rRV = __builtin_amdgcn_make_buffer_rsrc((void*)ring_v, (short)0, g.ring * D * 2, kRsrcWord3);
+  const int vlane = TCPL * lane * 2;          // this lane's Value channels in a ring row (bytes)
+  auto chunk_load = [&](int chunk_, ChunkRegs<D>& r) {
+    const int chunk = __builtin_amdgcn_readfirstlane(chunk_);
+    const bool ok = chunk < ww.c1;            // past the run: a zero-size resource, nothing read
+    const __amdgpu_buffer_rsrc_t rk = ok ? rRK : rNull;
+    const __amdgpu_buffer_rsrc_t rv = ok ? rRV : rNull;
     const int tt0 = chunk * kTailChunk;
-    r.nvalid = a.nt - tt0 < kTailChunk ? a.nt - tt0 : kTailChunk;
-    const uint16_t* kr = ring_k + tail_slot(a, tt0 + (col < r.nvalid ? col : 0)) * D + 8 * q4;
+    const int nv = a.nt - tt0 < kTailChunk ? a.nt - tt0 : kTailChunk;
+    r.nvalid = nv;
+    const int kro = (tail_slot(a, tt0 + (col < nv ? col : 0)) * D + 8 * q4) * 2;
 #pragma unroll
-    for (int mk = 0; mk < D / 32; ++mk) r.k[mk] = *reinterpret_cast<const uint4*>(kr + 32 * mk);
+    for (int mk = 0; mk < D / 32; ++mk)
+      r.k[mk] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, kro + 64 * mk, 0, 0));
 #pragma unroll
     for (int t = 0; t < kTailChunk; ++t) {
-      const uint16_t* vr = ring_v + tail_slot(a, tt0 + (t < r.nvalid ? t : 0)) * D;
-      if constexpr (TCPL == 2) r.v[t] = *reinterpret_cast<const uint32_t*>(vr + 2 * lane);
-      else r.v[t] = vr[lane];
+      const int row = __builtin_amdgcn_readfirstlane(tail_slot(a, tt0 + (t < nv ? t : 0)) * D * 2);
+      if constexpr (TCPL == 2) r.v[t] = __builtin_amdgcn_raw_buffer_load_b32(rv, vlane, row, 0);
+      else r.v[t] = __builtin_amdgcn_raw_buffer_load_b16(rv, vlane, row, 0);
     }
   };
   ChunkRegs<D> crA, crB;
   const bool has_chunks = ww.c0 < ww.c1;
-  if (has_chunks) chunk_load(ww.c0, crA);   // computed after the tiles
+  chunk_load(ww.c0, crA);                     // computed after the tiles; nothing read without chunks
   init_state();
 
   if (tile < q_end) {
@@ -929,18 +997,27 @@ void decode_i8_kernel(DecodeArgs a) {
     }
     fv = kFixP / wave_max(vsr_max);
   }
-  // Quantized tiles: before a tile is computed (after its Key operands are
-  // built) the next one's loads are issued.
+  // Quantized tiles, the next one's loads in flight while one is computed.
+  // The refill goes out first (its registers then hold loads in flight and
+  // are not reused as scratch by the operand build) and a scheduling barrier
+  // keeps it ahead of the compute.  The run's last tile is computed in a
+  // copy of its own, with nothing to refill, so every refill is a real load
+  // and the number in flight is the same on every path into a compute.
+  auto step = [&](TileRegs& cur, TileRegs& refill) {
+    if (tile + 1 >= q_end) {
+      if (cur.new_seg) build_key_operands(cur);
+      compute_tile(cur);
+      return false;
+    }
+    load_tile(tile + 1, refill);
+    __builtin_amdgcn_sched_barrier(0);
+    if (cur.new_seg) build_key_operands(cur);
+    compute_tile(cur);
+    ++tile;
+    return true;
+  };
   if (tile < q_end) {
-    while (true) {
-      if (bufA.new_seg) build_key_operands(bufA);
-      if (tile + 1 < q_end) load_tile(tile + 1, bufB);
-      compute_tile(bufA);
-      if (++tile >= q_end) break;
-      if (bufB.new_seg) build_key_operands(bufB);
-      if (tile + 1 < q_end) load_tile(tile + 1, bufA);
-      compute_tile(bufB);
-      if (++tile >= q_end) break;
+    while (step(bufA, bufB) && step(bufB, bufA)) {
     }
   }
 
@@ -1019,10 +1096,10 @@ void decode_i8_kernel(DecodeArgs a) {
       wave_lds_sync();      // pw is rewritten by the next chunk
     };
     for (int chunk = ww.c0; chunk < ww.c1; chunk += 2) {
-      if (chunk + 1 < ww.c1) chunk_load(chunk + 1, crB);
+      chunk_load(chunk + 1, crB);
       chunk_compute(crA);
       if (chunk + 1 >= ww.c1) break;
-      if (chunk + 2 < ww.c1) chunk_load(chunk + 2, crA);
+      chunk_load(chunk + 2, crA);
       chunk_compute(crB);
     }
   }
@@ -1066,7 +1143,10 @@ template <int D, int BITS, int GQA>
 void launch(const DecodeArgs& a, hipStream_t s) {
   dim3 grid(a.splits, a.g.B * a.g.H);
   if constexpr ((BITS == 4 || BITS == 2) && D >= 64) {
-    if (a.g.G > 0 && a.g.dtype == KVQ_BF16 && a.tiles_q > 0)
+    // The matrix-core kernel addresses a unit's streams with 32-bit buffer offsets.
+    const bool offsets32 = a.g.code_stream < (int64_t(1) << 31) &&
+                           (int64_t)a.g.max_seg * a.g.D * 2 < (int64_t(1) << 31);
+    if (a.g.G > 0 && a.g.dtype == KVQ_BF16 && a.tiles_q > 0 && offsets32)
       hipLaunchKernelGGL((decode_i8_kernel<D, BITS, GQA>), grid, dim3(kThreads), 0, s, a);
     else
       hipLaunchKernelGGL((decode_kernel<D, BITS, GQA>), grid, dim3(kThreads), 0, s, a);
