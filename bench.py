@@ -41,6 +41,19 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 
+# HBM bytes per decode call (decode_i8_kernel + merge_kernel), from separate
+# rocprofv3 --pmc passes of FETCH_SIZE and WRITE_SIZE over the same commands
+# bench.py runs, each scaled by what the counter reads for the hbm_copy
+# workload's known 256 MiB read + 256 MiB write (FETCH_SIZE x 2,
+# WRITE_SIZE x 1).  They describe the kernels in
+# profiles/decode_i8_*.md and are to be reset to None when those change.
+DECODE_CALL_TRAFFIC = 41_163_980     # 4096-token Llama-3-8B shape (algorithmic 38.04 MB)
+LONG_CALL_TRAFFIC = 142_926_848      # one 131072-token layer (algorithmic 138.8 MB)
+# Same measurement for the other workloads: 128 appends (16 flushes + 128
+# window copies) and one block-attention call (block_kernel + block_merge_kernel).
+APPEND_RUN_TRAFFIC = {4: 444212838, 8: 479005900}
+BLOCK_CALL_TRAFFIC = 2011507507        # the cache is streamed once per query tile
+
 
 def decode_bytes(cfg, nq: int, nt: int, q_heads: int) -> int:
     """Algorithmic bytes one decode call must read (codes, scales, tail, q)."""
@@ -180,7 +193,7 @@ def run_decode(args, log):
         "decode_bytes_per_step": int(bytes_step),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None,
+                     "traffic": DECODE_CALL_TRAFFIC,
                      "kernel": "kvq_decode_attn = decode_i8_kernel<128,4,4> + merge_kernel<128,4>"},
     }
     return res, (cfg, w)
@@ -238,7 +251,7 @@ def run_video_block(args, log):
                    "block_q": w.block_q, "codes": f"int{w.code_bits}", "parallelism": "single-gpu"},
         "flops_per_block": flops,
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": 2500.0,
-                     "unit": "TFLOP/s", "frac": round(tflops / 2500.0, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(tflops / 2500.0, 4), "traffic": BLOCK_CALL_TRAFFIC,
                      "kernel": "kvq_block_attn = block_kernel<128,2> + block_merge_kernel<128>"},
     }
 
@@ -297,7 +310,7 @@ def run_long_decode(args, log):
                    "codes": f"int{w.code_bits}", "parallelism": "single-gpu"},
         "bytes_per_step": int(nbytes),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": LONG_CALL_TRAFFIC,
                      "kernel": "kvq_decode_attn = decode_i8_kernel<128,4,4> + merge_kernel<128,4>"},
     }
 
@@ -406,7 +419,7 @@ def run_append(args, log, bits: int):
                    "parallelism": "single-gpu", "timing": "HIP graph of the 128 appends, replayed"},
         "bytes_per_run": int(nbytes),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": APPEND_RUN_TRAFFIC[bits],
                      "kernel": f"kvq_append = flush_kernel<{bits}> + tail_kernel"},
     }
 
@@ -454,6 +467,34 @@ def cpu_baseline_decode(budget_s: float, log):
             "cpu": platform.processor() or platform.machine()}
 
 
+def run_hbm_copy(args, log):
+    """A plain device-to-device copy of 256 MiB (the runtime's copy kernel),
+    ten times back to back: a reference read+write rate for this box, and a
+    kernel of known size for scaling the HBM traffic counters."""
+    import torch
+
+    nbytes = 256 << 20
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 10
+    e0.record(stream)
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    gbs = 2 * nbytes / (ms * 1e-3) / 1e9
+    log(f"hbm copy: {ms * 1e3:.1f} us per 256 MiB copy, {gbs:.0f} GB/s read + write")
+    return {"metric": "device copy GB/s (read + write)", "value": round(gbs, 2), "unit": "GB/s",
+            "n_gpus": 1, "steps": reps, "warmup": 1, "ms_per_step": round(ms, 5),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+            "data": "synthetic", "config": {"workload": "hbm_copy_256MiB", "bytes": nbytes}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -464,15 +505,17 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quiet", action="store_true")
     ap.add_argument("--workload", choices=["llama3_decode", "video_block", "long_decode", "append_int8",
-                                           "append_int4"], default="llama3_decode",
+                                           "append_int4", "hbm_copy"], default="llama3_decode",
                     help="llama3_decode (default): the append + decode step; video_block: one "
                          "1024-query causal block against the 432000-token int2 cache; long_decode: "
                          "32 layers of 131072-token caches; append_int8/int4: 128 appends of 16 "
-                         "tokens into 4096-token caches (16 x 8 heads)")
+                         "tokens into 4096-token caches (16 x 8 heads); hbm_copy: a plain 256 MiB "
+                         "device copy (reference rate, and the known-size kernel that scales the "
+                         "FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: this build runs on a single MI355X and has no "
-              "multi-GPU path; run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path; run with --gpus 1",
+              file=sys.stderr)
         sys.exit(2)
 
     def log(msg):
@@ -488,7 +531,9 @@ def main():
         import __graft_entry__
         __graft_entry__.build()
     kvq.load()
-    if args.workload == "video_block":
+    if args.workload == "hbm_copy":
+        res = run_hbm_copy(args, log)
+    elif args.workload == "video_block":
         res = run_video_block(args, log)
     elif args.workload == "long_decode":
         res = run_long_decode(args, log)
