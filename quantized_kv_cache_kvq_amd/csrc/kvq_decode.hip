@@ -655,7 +655,9 @@ void decode_i8_kernel(DecodeArgs a) {
   const int unit = blockIdx.y;
   const int split = blockIdx.x;
 
-  __shared__ __attribute__((aligned(16))) float qsN[GQA][D];     // sigma log2e q (tail path)
+  // sigma log2e q as a bf16 high part and the bf16 rounding of the remainder
+  // (the window-chunk score operand), split once by the whole workgroup
+  __shared__ __attribute__((aligned(16))) uint16_t qsHL[2][GQA][D];
   __shared__ __attribute__((aligned(16))) float qsP[GQA][D];     // same, channels in slot order
   __shared__ __attribute__((aligned(16))) float rkP[kWaves][D];  // 1 / kscale, slot order
   // Operand digits, one row per MFMA row; rows padded to 20 dwords so that
@@ -671,8 +673,9 @@ void decode_i8_kernel(DecodeArgs a) {
   auto chan = [](int p) { return (p & ~15) + F16::field(p & 15); };
 
 
-  // A 16-token bf16 tail chunk (scores on the matrix cores) costs about
-  // what an int4 tile does, and moves as many bytes.
+  // A 16-token bf16 window chunk moves as many bytes as an int4 tile and,
+  // with its scores on the matrix cores and the query split done in the
+  // prologue, costs about as much.
   const WaveWork ww = wave_work<1>(a, split, wave);
   const int w_begin = ww.t0, q_end = ww.t1;
   const uint8_t* kbase = a.k_codes + (int64_t)unit * g.code_stream;
@@ -938,7 +941,10 @@ void decode_i8_kernel(DecodeArgs a) {
   for (int k = 0; k < NQ; ++k) {
     const int i = tid + k * kThreads;
     if (i < GQA * D) {
-      qsN[i / D][i % D] = qT[k] * a.qscale;
+      const float x = qT[k] * a.qscale;
+      const uint32_t hb = bf16_rne(x);
+      qsHL[0][i / D][i % D] = (uint16_t)hb;
+      qsHL[1][i / D][i % D] = (uint16_t)bf16_rne(x - bf16_bits_to_f32(hb));
       qsP[i / D][i % D] = qP[k] * a.qscale;
     }
   }
@@ -1041,20 +1047,9 @@ void decode_i8_kernel(DecodeArgs a) {
         const int h = 4 * hg + hq;
 #pragma unroll
         for (int mk = 0; mk < D / 32; ++mk) {
-          uint32_t w[4] = {0u, 0u, 0u, 0u};
-          if (h < GQA && part < 2) {
-            const float* src = &qsN[h][32 * mk + 8 * q4];
-            const float4 x0 = *reinterpret_cast<const float4*>(src);
-            const float4 x1 = *reinterpret_cast<const float4*>(src + 4);
-            const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-              const uint32_t hb = bf16_rne(xs[j]);
-              const uint32_t b = part == 0 ? hb : bf16_rne(xs[j] - bf16_bits_to_f32(hb));
-              w[j / 2] |= b << (16 * (j % 2));
-            }
-          }
-          qa[hg][mk] = __builtin_bit_cast(bf8_t, make_uint4(w[0], w[1], w[2], w[3]));
+          uint4 w = make_uint4(0u, 0u, 0u, 0u);
+          if (h < GQA && part < 2) w = *reinterpret_cast<const uint4*>(&qsHL[part][h][32 * mk + 8 * q4]);
+          qa[hg][mk] = __builtin_bit_cast(bf8_t, w);
         }
       }
     }
