@@ -222,10 +222,9 @@ __device__ __forceinline__ void tail_compute(const DecodeArgs& a, const TailRegs
 // head): one workgroup, thread c owns output channel c.  Every thread issues
 // its splits' acc[c] loads (up to 32 in flight) together with the split
 // maxima and sums, so up to 32 splits cost one memory round trip; the
-// per-split weights exp2(m_s - M) are computed once into LDS.
-constexpr int kMergeBatch = 32;
-
-template <int D, int GQA>
+// per-split weights exp2(m_s - M) are computed once into LDS.  kBatch is 8
+// when the splits fit in it (no duplicate loads), 32 otherwise.
+template <int D, int GQA, int kBatch>
 __global__ __launch_bounds__(D) void merge_kernel(DecodeArgs a) {
   const int unit = blockIdx.x, h = blockIdx.y, c = threadIdx.x;
   const Geom& g = a.g;
@@ -233,10 +232,10 @@ __global__ __launch_bounds__(D) void merge_kernel(DecodeArgs a) {
   const int stride = GQA * (D + 2);                  // floats between splits
   const float* pu = a.part + (int64_t)unit * S * stride + h * (D + 2);
   __shared__ float ew[kMaxSplits], el[kMaxSplits];
-  float v[kMergeBatch];
+  float v[kBatch];
   auto load_batch = [&](int s0) {
 #pragma unroll
-    for (int k = 0; k < kMergeBatch; ++k) {
+    for (int k = 0; k < kBatch; ++k) {
       const int sk = s0 + k < S ? s0 + k : S - 1;   // clamped: unconditional loads
       v[k] = pu[sk * stride + c];
     }
@@ -257,10 +256,10 @@ __global__ __launch_bounds__(D) void merge_kernel(DecodeArgs a) {
   }
   __syncthreads();
   float num = 0.0f, den = 0.0f;
-  for (int s0 = 0; s0 < S; s0 += kMergeBatch) {
+  for (int s0 = 0; s0 < S; s0 += kBatch) {
     if (s0 > 0) load_batch(s0);
 #pragma unroll
-    for (int k = 0; k < kMergeBatch; ++k)
+    for (int k = 0; k < kBatch; ++k)
       if (s0 + k < S) num = fmaf(v[k], ew[s0 + k], num);
   }
   for (int sk = 0; sk < S; ++sk) den += el[sk];
@@ -1148,8 +1147,10 @@ void launch(const DecodeArgs& a, hipStream_t s) {
   } else {
     hipLaunchKernelGGL((decode_kernel<D, BITS, GQA>), grid, dim3(kThreads), 0, s, a);
   }
-  if (a.splits > 1)
-    hipLaunchKernelGGL((merge_kernel<D, GQA>), dim3(a.g.B * a.g.H, GQA), dim3(D), 0, s, a);
+  if (a.splits > 1 && a.splits <= 8)
+    hipLaunchKernelGGL((merge_kernel<D, GQA, 8>), dim3(a.g.B * a.g.H, GQA), dim3(D), 0, s, a);
+  else if (a.splits > 8)
+    hipLaunchKernelGGL((merge_kernel<D, GQA, 32>), dim3(a.g.B * a.g.H, GQA), dim3(D), 0, s, a);
 }
 
 template <int D, int BITS>
