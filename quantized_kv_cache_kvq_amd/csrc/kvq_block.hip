@@ -9,10 +9,11 @@
 // Strategies", Step 4 ``restore``); tail and block tokens are used as stored.
 //
 // Work: grid = (query row tiles, KV splits, batch * KV heads).  A workgroup
-// owns 128 query rows of one KV head -- a row is a (position, head) pair --
+// owns 256 (head_dim 128) or 128 query rows of one KV head -- a row is a
+// (position, head) pair --
 // and a contiguous range of 64-token KV tiles: quantized tiles, then tail
-// tiles (bf16 ring), then own-block tiles (bf16, causal).  Its 256 threads
-// restore each tile once into LDS, shared by the four waves (32 rows each):
+// tiles (bf16 ring), then own-block tiles (bf16, causal).  Its threads
+// restore each tile once into LDS, shared by its waves (32 rows each):
 //   Khi, Klo [token][channel]  bf16 hi + lo of code / kscale (tail and block
 //                              tokens: the stored value, lo = 0)
 //   V [channel][token]         fp16: the codes (exact), or the stored values
@@ -38,10 +39,18 @@ size_t workspace_counter_bytes(const Geom& g, int tq);
 
 namespace {
 
-constexpr int kBT = 256;                 // threads per workgroup
-constexpr int kBWaves = kBT / kWave;
 constexpr int kRowsWave = 32;            // two 16-row query blocks per wave
-constexpr int kRowsWG = kRowsWave * kBWaves;
+constexpr int kMergeThreads = 256;
+
+// Workgroup shape: eight waves (256 query rows) share each restored tile at
+// head_dim 128, four at head_dim 64 (where a thread's share of a Key row
+// would otherwise be narrower than the 32-bit words it loads).
+template <int D>
+struct BlockShape {
+  static constexpr int kThreads = D >= 128 ? 512 : 256;
+  static constexpr int kWaves = kThreads / kWave;
+  static constexpr int kRows = kRowsWave * kWaves;   // query rows per workgroup
+};
 constexpr int kBlockMaxSplits = 8;       // partial slots the workspace holds for tq > 1
 
 typedef __bf16 bf8_t __attribute__((ext_vector_type(8)));
@@ -73,9 +82,12 @@ struct BlockArgs {
 enum TileKind { kQuant = 0, kTail = 1, kOwn = 2 };
 
 template <int D, int BITS>
-__global__ __launch_bounds__(kBT) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(BlockShape<D>::kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void block_kernel(BlockArgs a) {
-  constexpr int CG = D / 4;                // channels per thread in the K fill
+  constexpr int kBT = BlockShape<D>::kThreads;
+  constexpr int kBWaves = BlockShape<D>::kWaves;
+  constexpr int kRowsWG = BlockShape<D>::kRows;
+  constexpr int CG = D / (kBT / kTile);    // channels per thread in the K fill
   constexpr int KROW = D + 8;              // LDS row pitch (bf16) of Khi / Klo: no bank conflicts
   constexpr int VROW = kTile + 4;          // LDS row pitch (fp16) of V: 34 banks, 16 rows of a
                                            // 64-bit operand read hit 32 distinct banks
@@ -440,11 +452,11 @@ void block_kernel(BlockArgs a) {
 
 // Combine the splits' partials of each query row: one thread per (row, channel).
 template <int D>
-__global__ __launch_bounds__(kBT) void block_merge_kernel(BlockArgs a) {
+__global__ __launch_bounds__(kMergeThreads) void block_merge_kernel(BlockArgs a) {
   const int unit = blockIdx.y;
   const int b = unit / a.g.H, kvh = unit % a.g.H;
   const int Hq = a.g.H * a.gqa;
-  const int64_t idx = (int64_t)blockIdx.x * kBT + threadIdx.x;
+  const int64_t idx = (int64_t)blockIdx.x * kMergeThreads + threadIdx.x;
   if (idx >= (int64_t)a.rows * D) return;
   const int r = (int)(idx / D), c = (int)(idx % D);
   float M = -INFINITY;
@@ -463,11 +475,12 @@ __global__ __launch_bounds__(kBT) void block_merge_kernel(BlockArgs a) {
 
 template <int D, int BITS>
 void launch_block(const BlockArgs& a, hipStream_t s) {
+  constexpr int kRowsWG = BlockShape<D>::kRows;
   dim3 grid((a.rows + kRowsWG - 1) / kRowsWG, a.splits, a.g.B * a.g.H);
-  hipLaunchKernelGGL((block_kernel<D, BITS>), grid, dim3(kBT), 0, s, a);
+  hipLaunchKernelGGL((block_kernel<D, BITS>), grid, dim3(BlockShape<D>::kThreads), 0, s, a);
   if (a.splits > 1) {
-    dim3 mg((unsigned)(((int64_t)a.rows * D + kBT - 1) / kBT), a.g.B * a.g.H);
-    hipLaunchKernelGGL((block_merge_kernel<D>), mg, dim3(kBT), 0, s, a);
+    dim3 mg((unsigned)(((int64_t)a.rows * D + kMergeThreads - 1) / kMergeThreads), a.g.B * a.g.H);
+    hipLaunchKernelGGL((block_merge_kernel<D>), mg, dim3(kMergeThreads), 0, s, a);
   }
 }
 
@@ -482,11 +495,12 @@ bool dispatch_block(const BlockArgs& a, hipStream_t s) {
   return false;
 }
 
-int block_auto_splits(int row_tiles, int units, int items) {
-  // Aim for about two workgroups per compute unit (256 CUs) and at least
-  // eight tiles per split.
+int block_auto_splits(int row_tiles, int units, int items, int threads) {
+  // Aim for about eight waves per compute unit (256 CUs) and at least eight
+  // tiles per split.
   const int64_t wgs = (int64_t)row_tiles * units;
-  int s = (int)((512 + wgs - 1) / wgs);
+  const int64_t target = 256 * 8 * kWave / threads;
+  int s = (int)((target + wgs - 1) / wgs);
   if (s > kBlockMaxSplits) s = kBlockMaxSplits;
   if (s > items / 8) s = items / 8;
   return s < 1 ? 1 : s;
@@ -545,9 +559,11 @@ extern "C" kvq_status kvq_block_attn(const kvq_config* cfg, const kvq_state* st,
   a.tiles_q = (a.nq + kTile - 1) / kTile;
   a.tiles_t = (a.nt + kTile - 1) / kTile;
   a.tiles_b = (tq + kTile - 1) / kTile;
-  const int row_tiles = (a.rows + kRowsWG - 1) / kRowsWG;
+  const int rows_wg = g.D >= 128 ? BlockShape<128>::kRows : BlockShape<64>::kRows;
+  const int threads = g.D >= 128 ? BlockShape<128>::kThreads : BlockShape<64>::kThreads;
+  const int row_tiles = (a.rows + rows_wg - 1) / rows_wg;
   const int items = a.tiles_q + a.tiles_t + a.tiles_b;
-  a.splits = num_splits > 0 ? num_splits : block_auto_splits(row_tiles, g.B * g.H, items);
+  a.splits = num_splits > 0 ? num_splits : block_auto_splits(row_tiles, g.B * g.H, items, threads);
   if (a.splits > items) a.splits = items;
   if (row_tiles > 65535) return KVQ_EINVAL;
   clear_stale_hip_error();
