@@ -81,6 +81,11 @@ struct BlockArgs {
 // Token a tile slot covers, and whether it exists (per tile kind).
 enum TileKind { kQuant = 0, kTail = 1, kOwn = 2 };
 
+template <int P>
+struct Par {                 // a compile-time flag passed to a generic lambda
+  static constexpr int value = P;
+};
+
 template <int D, int BITS>
 __global__ __launch_bounds__(BlockShape<D>::kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void block_kernel(BlockArgs a) {
@@ -288,29 +293,46 @@ void block_kernel(BlockArgs a) {
     if (next_q) load_qraw(item + 1, cur);    // cur's fill is done: its registers are free
 
     // ---- logits S^T[token][query] (token block tb, query block qb) ----
+    // The Key operands of k step ks + 1 are read from LDS while the MFMAs of
+    // k step ks run: scheduling barriers keep each batch of reads ahead of the
+    // previous batch's products (eight independent accumulators per k step).
     f4_t S[4][2];
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) S[tb][qb] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    // k step outermost: eight independent accumulators between dependent MFMAs
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb) {
-        const bf8_t ah = *reinterpret_cast<const bf8_t*>(&Khi[tb * 16 + col][32 * ks + 8 * q4]);
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) S[tb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, qop[qb][ks], S[tb][qb], 0, 0, 0);
-      }
-      if (kind == kQuant) {
+    auto logits = [&](auto with_lo) {
+      constexpr bool kLo = decltype(with_lo)::value != 0;
+      bf8_t kh[2][4], kl[2][4];
+      auto kread = [&](int ks, bf8_t (&h)[4], bf8_t (&l)[4]) {
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) {
-          const bf8_t al = *reinterpret_cast<const bf8_t*>(&Klo[tb * 16 + col][32 * ks + 8 * q4]);
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb) S[tb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, qop[qb][ks], S[tb][qb], 0, 0, 0);
+          h[tb] = *reinterpret_cast<const bf8_t*>(&Khi[tb * 16 + col][32 * ks + 8 * q4]);
+          if constexpr (kLo) l[tb] = *reinterpret_cast<const bf8_t*>(&Klo[tb * 16 + col][32 * ks + 8 * q4]);
         }
+      };
+      kread(0, kh[0], kl[0]);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        if (ks + 1 < KS) kread(ks + 1, kh[(ks + 1) & 1], kl[(ks + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb)
+            S[tb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh[ks & 1][tb], qop[qb][ks], S[tb][qb], 0, 0, 0);
+        if constexpr (kLo) {
+#pragma unroll
+          for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb)
+              S[tb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kl[ks & 1][tb], qop[qb][ks], S[tb][qb], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-    }
+    };
+    if (kind == kQuant) logits(Par<1>{});
+    else logits(Par<0>{});
 
     // ---- online softmax per query (lane's column col of block qb) ----
     // S[tb][qb][i]: token t0 + 16 tb + 4 q4 + i; the logit (log2 domain) is
@@ -383,17 +405,34 @@ void block_kernel(BlockArgs a) {
       wave_lds_sync();
     }
 
-    // ---- acc[query][channel] += P' . V (k step outermost) ----
+    // ---- acc[query][channel] += P' . V (k step outermost; the Value
+    // operands of k step 1 are read while the MFMAs of k step 0 run) ----
+    // Value operands in batches of four channel blocks, one batch ahead.
+    constexpr int kVB = 4;
+    constexpr int NVB = 2 * CB / kVB;     // batches (k step major)
+    h8_t vop[2][kVB];
+    auto vread = [&](int bi, h8_t (&v)[kVB]) {
+      const int ks = bi / (CB / kVB), cb0 = (bi % (CB / kVB)) * kVB;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb) {
+      for (int j = 0; j < kVB; ++j) {
+        const int cb = cb0 + j;
         const h4_t v0 = *reinterpret_cast<const h4_t*>(&Vs[16 * cb + col][32 * ks + 4 * q4]);
         const h4_t v1 = *reinterpret_cast<const h4_t*>(&Vs[16 * cb + col][32 * ks + 16 + 4 * q4]);
-        const h8_t vb = h8_t{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) acc[qb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[qb][ks], vb, acc[qb][cb], 0, 0, 0);
+        v[j] = h8_t{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
       }
+    };
+    vread(0, vop[0]);
+#pragma unroll
+    for (int bi = 0; bi < NVB; ++bi) {
+      if (bi + 1 < NVB) vread(bi + 1, vop[(bi + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      const int ks = bi / (CB / kVB), cb0 = (bi % (CB / kVB)) * kVB;
+#pragma unroll
+      for (int j = 0; j < kVB; ++j)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+          acc[qb][cb0 + j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[qb][ks], vop[bi & 1][j], acc[qb][cb0 + j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
     if (next_rk) rkL[(item + 1) & 1][tid] = rk_next;
     __syncthreads();      // the next tile overwrites the LDS tile

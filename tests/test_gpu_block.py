@@ -75,6 +75,26 @@ def test_block_short_caches(n):
 
 
 @needs_gpu
+@pytest.mark.parametrize("D", [64, 128])
+def test_block_overflow_only_segments(D):
+    """Per-append segments (one Key-scale row per flush, of any length)."""
+    w = ks.small(ks.TINY, batch=2, kv_heads=2, q_heads=8, head_dim=D, code_bits=4, qmax=7,
+                 residual=10, group=0, kv_dtype="bf16")
+    p = Pair(w, 1024)
+    s = ks.Stream(w)
+    for n in (100, 1, 7, 64, 3, 200, 65):
+        k, v = ks.kv_pair(s, n)
+        p.append(k, v)
+    q, kb, vb = ks.block_inputs(s, 37)
+    note(f"block overflow-only segments D={D}")
+    got = p.block(q, kb, vb)
+    ref = p.block_ref(q, kb, vb)
+    err = max_abs(got, ref)
+    note(f"block overflow-only segments D={D}: max-abs {err:.3e}")
+    assert err <= TOL
+
+
+@needs_gpu
 def test_block_of_one_equals_decode_after_append():
     """tq = 1: the block path equals appending the token, then decoding."""
     w = ks.small(ks.VIDEO_BLOCK, batch=2, kv_heads=2, q_heads=8, code_bits=4, qmax=7)
