@@ -52,7 +52,7 @@ LONG_CALL_TRAFFIC = 142_894_490      # one 131072-token layer (algorithmic 138.8
 # Same measurement for the other workloads: 128 appends (16 flushes + 128
 # window copies) and one block-attention call (block_kernel + block_merge_kernel).
 APPEND_RUN_TRAFFIC = {4: 444212838, 8: 479005900}
-BLOCK_CALL_TRAFFIC = None             # block_kernel changed since its counters were taken
+BLOCK_CALL_TRAFFIC = 2_008_315_085    # the cache is streamed once per query-row tile
 
 
 def decode_bytes(cfg, nq: int, nt: int, q_heads: int) -> int:
