@@ -176,6 +176,30 @@ kvq_status kvq_decode_attn(const kvq_config* cfg, const kvq_state* st, const kvq
                            int32_t num_splits, float* out, void* workspace,
                            size_t workspace_bytes, void* stream);
 
+/* One decode step: append n_new tokens, then attend with q over the whole
+ * cache including them -- the per-step order encode, append, attend of
+ * "KV Cache quantization and compression", section 02.  The result is that
+ * of kvq_append(cfg, st, cache, k_new, v_new, n_new, stream) followed by
+ * kvq_decode_attn(cfg, st, cache, q, ...): the same cache bytes and state,
+ * and attention outputs equal within float rounding.  When the append
+ * flushes nothing (1 <= n_new <= 16, kv_dtype bf16, a non-empty cache) the
+ * step runs without the append's own kernels: attention runs over the cache
+ * as it was, and the merge pass adds the new tokens as further softmax
+ * terms and writes them into their window slots (cutting the per-step
+ * kernel launches, "KV Cache and autoregressive video generation",
+ * section 05).  Otherwise it runs kvq_append, then kvq_decode_attn.
+ *   st           : host, advanced as kvq_plan_append says on KVQ_OK
+ *   k_new, v_new : device, kv_dtype [batch, kv_heads, n_new, head_dim]
+ *   q, out, softmax_scale, num_splits, workspace : as for kvq_decode_attn
+ * Every precondition of both calls is checked before anything is enqueued;
+ * on error *st is unchanged.
+ * Errors: KVQ_EINVAL, KVQ_ECAPACITY, KVQ_EWORKSPACE, KVQ_EDEVICE. */
+kvq_status kvq_decode_step(const kvq_config* cfg, kvq_state* st, const kvq_cache* cache,
+                           const void* k_new, const void* v_new, int64_t n_new,
+                           const void* q, int32_t q_heads, float softmax_scale,
+                           int32_t num_splits, float* out, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
 /* Causal attention of a block of tq new queries against the cache plus the
  * block's own keys/values (Attn = softmax(Q K^T sigma + M) V with
  * M_ij = -inf for j > i, "KV Cache and autoregressive video generation",

@@ -20,7 +20,8 @@ KVQ_OK, KVQ_EINVAL, KVQ_ECAPACITY, KVQ_EWORKSPACE, KVQ_EDEVICE = range(5)
 KVQ_BF16, KVQ_F32 = 0, 1
 
 EXPORTED = ("kvq_buffer_sizes", "kvq_plan_append", "kvq_append", "kvq_workspace_size",
-            "kvq_workspace_init", "kvq_decode_attn", "kvq_block_attn", "kvq_status_str")
+            "kvq_workspace_init", "kvq_decode_attn", "kvq_decode_step", "kvq_block_attn",
+            "kvq_status_str")
 
 
 class kvq_config(ctypes.Structure):
@@ -74,6 +75,8 @@ def load() -> ctypes.CDLL:
         "kvq_workspace_size": [P(kvq_config), i32, i32, P(sz)],
         "kvq_workspace_init": [vp, sz, vp],
         "kvq_decode_attn": [P(kvq_config), P(kvq_state), P(kvq_cache), vp, i32, f32, i32, vp, vp, sz, vp],
+        "kvq_decode_step": [P(kvq_config), P(kvq_state), P(kvq_cache), vp, vp, i64, vp, i32, f32, i32,
+                            vp, vp, sz, vp],
         "kvq_block_attn": [P(kvq_config), P(kvq_state), P(kvq_cache), vp, vp, vp, i32, i32, f32, i32,
                            vp, vp, sz, vp],
     }
@@ -159,6 +162,14 @@ def kvq_decode_attn(cfg, st, cache, q, q_heads, softmax_scale, num_splits, out, 
                                   ws.numel() * ws.element_size(), _stream(stream)), "kvq_decode_attn")
 
 
+def kvq_decode_step(cfg, st, cache, k_new, v_new, n_new, q, q_heads, softmax_scale, num_splits, out, ws,
+                    stream=None):
+    _check(load().kvq_decode_step(ctypes.byref(cfg), ctypes.byref(st), ctypes.byref(cache), _ptr(k_new),
+                                  _ptr(v_new), n_new, _ptr(q), q_heads, softmax_scale, num_splits,
+                                  _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
+                                  _stream(stream)), "kvq_decode_step")
+
+
 def kvq_block_attn(cfg, st, cache, q, k_blk, v_blk, tq, q_heads, softmax_scale, num_splits,
                    out, ws, stream=None):
     _check(load().kvq_block_attn(ctypes.byref(cfg), ctypes.byref(st), ctypes.byref(cache), _ptr(q),
@@ -207,6 +218,13 @@ class KVCache:
         D = self.cfg.head_dim
         s = 1.0 / math.sqrt(D) if softmax_scale is None else softmax_scale
         kvq_decode_attn(self.cfg, self.state, self.c, q, q.shape[1], s, num_splits, out, ws, stream)
+
+    def decode_step(self, k_new, v_new, q, out, ws, softmax_scale=None, num_splits=0, stream=None):
+        """Append k_new/v_new [B, Hkv, n, D], then attend with q (one call)."""
+        D = self.cfg.head_dim
+        s = 1.0 / math.sqrt(D) if softmax_scale is None else softmax_scale
+        kvq_decode_step(self.cfg, self.state, self.c, k_new, v_new, k_new.shape[2], q, q.shape[1], s,
+                        num_splits, out, ws, stream)
 
     def block_attn(self, q, k_blk, v_blk, out, ws, softmax_scale=None, num_splits=0, stream=None):
         D = self.cfg.head_dim

@@ -66,7 +66,18 @@ struct DecodeArgs {
   int tiles_q, items;    // quantized tiles; work items = tiles_q + tail chunks
   int tq_div, tq_mod;    // tiles_q = splits * tq_div + tq_mod
   int ch_div, ch_mod;    // tail chunks, likewise
+  int force_part;        // write partials even with one split (the merge runs)
+  // Tokens appended by the same call (kvq_decode_step), folded in by the
+  // merge: keys and values [unit][n_new][D] (bf16), and the window slot of
+  // the first one; the merge of query head 0 copies them into the window.
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  uint16_t* ring_k;
+  uint16_t* ring_v;
+  int n_new, new_slot0;
 };
+
+constexpr int kMaxStepNew = 16;   // appended tokens kvq_decode_step folds into the merge
 
 
 // ---- shared pieces ---------------------------------------------------------------
@@ -224,14 +235,22 @@ __device__ __forceinline__ void tail_compute(const DecodeArgs& a, const TailRegs
 // maxima and sums, so up to 32 splits cost one memory round trip; the
 // per-split weights exp2(m_s - M) are computed once into LDS.  kBatch is 8
 // when the splits fit in it (no duplicate loads), 32 otherwise.
-template <int D, int GQA, int kBatch>
+// kNew: the call also appended n_new tokens that the partials do not cover.
+// Each is one more term of the softmax: its logit q . k (log2 domain) is a
+// workgroup reduction, its value row is read directly, and the workgroup of
+// query head 0 copies the keys and values into their window slots.
+template <int D, int GQA, int kBatch, bool kNew>
 __global__ __launch_bounds__(D) void merge_kernel(DecodeArgs a) {
+  constexpr int W = D < kWave ? D : kWave;           // lanes of one reduction
+  constexpr int NW = D / W;
   const int unit = blockIdx.x, h = blockIdx.y, c = threadIdx.x;
   const Geom& g = a.g;
   const int S = a.splits;
   const int stride = GQA * (D + 2);                  // floats between splits
   const float* pu = a.part + (int64_t)unit * S * stride + h * (D + 2);
+  const int b = unit / g.H, kvh = unit % g.H;
   __shared__ float ew[kMaxSplits], el[kMaxSplits];
+  __shared__ float lgw[kNew ? kMaxStepNew : 1][NW];  // per-wave parts of the new logits
   float v[kBatch];
   auto load_batch = [&](int s0) {
 #pragma unroll
@@ -245,9 +264,27 @@ __global__ __launch_bounds__(D) void merge_kernel(DecodeArgs a) {
     ew[sk] = pu[sk * stride + D];
     el[sk] = pu[sk * stride + D + 1];
   }
+  if constexpr (kNew) {
+    const float qc = bf16_bits_to_f32(static_cast<const uint16_t*>(a.q)[((int64_t)b * g.H * GQA + kvh * GQA + h) * D + c]);
+    for (int t = 0; t < a.n_new; ++t) {
+      float x = qc * bf16_bits_to_f32(a.k_new[((int64_t)unit * a.n_new + t) * D + c]);
+#pragma unroll
+      for (int off = W / 2; off > 0; off >>= 1) x += __shfl_xor(x, off, W);
+      if (c % W == 0) lgw[t][c / W] = x;
+    }
+  }
   __syncthreads();
+  auto new_logit = [&](int t) {
+    float x = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) x += lgw[t][w];
+    return x * a.qscale;
+  };
   float M = -INFINITY;
-  for (int sk = 0; sk < S; ++sk) M = fmaxf(M, ew[sk]);   // finite: the cache holds a token
+  for (int sk = 0; sk < S; ++sk) M = fmaxf(M, ew[sk]);   // -inf only for empty splits
+  if constexpr (kNew) {
+    for (int t = 0; t < a.n_new; ++t) M = fmaxf(M, new_logit(t));
+  }
   __syncthreads();
   for (int sk = c; sk < S; sk += D) {
     const float e = ew[sk] == -INFINITY ? 0.0f : fast_exp2(ew[sk] - M);   // empty split: weight 0
@@ -263,7 +300,20 @@ __global__ __launch_bounds__(D) void merge_kernel(DecodeArgs a) {
       if (s0 + k < S) num = fmaf(v[k], ew[s0 + k], num);
   }
   for (int sk = 0; sk < S; ++sk) den += el[sk];
-  const int b = unit / g.H, kvh = unit % g.H;
+  if constexpr (kNew) {
+    for (int t = 0; t < a.n_new; ++t) {
+      const int64_t row = ((int64_t)unit * a.n_new + t) * D + c;
+      const float e = fast_exp2(new_logit(t) - M);
+      num = fmaf(e, bf16_bits_to_f32(a.v_new[row]), num);
+      den += e;
+      if (h == 0) {
+        int slot = a.new_slot0 + t;
+        slot = slot >= g.ring ? slot - g.ring : slot;
+        a.ring_k[((int64_t)unit * g.ring + slot) * D + c] = a.k_new[row];
+        a.ring_v[((int64_t)unit * g.ring + slot) * D + c] = a.v_new[row];
+      }
+    }
+  }
   a.out[((int64_t)b * g.H * GQA + kvh * GQA + h) * D + c] = num / den;
 }
 
@@ -295,7 +345,7 @@ __device__ __forceinline__ void fold_and_store(const DecodeArgs& a, int unit, in
       s += red[w][c][h] * e;
       L += wml[w][1][h] * e;
     }
-    if (a.splits == 1) {
+    if (a.splits == 1 && !a.force_part) {
       a.out[((int64_t)b * g.H * GQA + kvh * GQA + h) * D + c] = s / L;
     } else {
       float* part = a.part + ((int64_t)unit * a.splits + split) * GQA * (D + 2) + h * (D + 2);
@@ -1147,10 +1197,16 @@ void launch(const DecodeArgs& a, hipStream_t s) {
   } else {
     hipLaunchKernelGGL((decode_kernel<D, BITS, GQA>), grid, dim3(kThreads), 0, s, a);
   }
-  if (a.splits > 1 && a.splits <= 8)
-    hipLaunchKernelGGL((merge_kernel<D, GQA, 8>), dim3(a.g.B * a.g.H, GQA), dim3(D), 0, s, a);
-  else if (a.splits > 8)
-    hipLaunchKernelGGL((merge_kernel<D, GQA, 32>), dim3(a.g.B * a.g.H, GQA), dim3(D), 0, s, a);
+  if (a.splits > 1 || a.force_part) {
+    const dim3 mgrid(a.g.B * a.g.H, GQA);
+    if (a.n_new > 0) {
+      if (a.splits <= 8) hipLaunchKernelGGL((merge_kernel<D, GQA, 8, true>), mgrid, dim3(D), 0, s, a);
+      else hipLaunchKernelGGL((merge_kernel<D, GQA, 32, true>), mgrid, dim3(D), 0, s, a);
+    } else {
+      if (a.splits <= 8) hipLaunchKernelGGL((merge_kernel<D, GQA, 8, false>), mgrid, dim3(D), 0, s, a);
+      else hipLaunchKernelGGL((merge_kernel<D, GQA, 32, false>), mgrid, dim3(D), 0, s, a);
+    }
+  }
 }
 
 template <int D, int BITS>
@@ -1194,17 +1250,20 @@ int auto_splits(int units, int items) {
 
 using namespace kvq;
 
-extern "C" kvq_status kvq_decode_attn(const kvq_config* cfg, const kvq_state* st, const kvq_cache* cache,
-                                      const void* q, int32_t q_heads, float softmax_scale,
-                                      int32_t num_splits, float* out, void* workspace,
-                                      size_t workspace_size, void* stream) {
-  Geom g;
-  kvq_status s = validate_config(cfg, &g);
-  if (s != KVQ_OK) return s;
+namespace kvq {
+kvq_status plan_append(const Geom& g, const kvq_state* st, int64_t n_new, kvq_state* next);
+
+namespace {
+
+// Preconditions of attention over a cache in state `st` (every one checked
+// before anything is enqueued); sets the query-group size.
+kvq_status check_decode(const Geom& g, const kvq_state* st, const kvq_cache* cache, const void* q,
+                        int32_t q_heads, float softmax_scale, int32_t num_splits, const float* out,
+                        const void* workspace, size_t workspace_size, int* gqa) {
   if (!st || !cache || !q || !out) return KVQ_EINVAL;
   if (q_heads < 1 || q_heads % g.H != 0) return KVQ_EINVAL;
-  const int gqa = q_heads / g.H;
-  if (gqa != 1 && gqa != 2 && gqa != 4 && gqa != 8) return KVQ_EINVAL;
+  *gqa = q_heads / g.H;
+  if (*gqa != 1 && *gqa != 2 && *gqa != 4 && *gqa != 8) return KVQ_EINVAL;
   if (st->quantized < 0 || st->tail < 0 || st->total != st->quantized + st->tail || st->total < 1 ||
       st->quantized > g.C || st->tail > g.ring)
     return KVQ_EINVAL;
@@ -1215,7 +1274,12 @@ extern "C" kvq_status kvq_decode_attn(const kvq_config* cfg, const kvq_state* st
     return KVQ_EINVAL;
   if (st->tail > 0 && (!cache->k_tail || !cache->v_tail)) return KVQ_EINVAL;
   if (!workspace || workspace_size < workspace_bytes(g, q_heads, 1)) return KVQ_EWORKSPACE;
+  return KVQ_OK;
+}
 
+// Kernel arguments of attention over the cache in state `st`.
+DecodeArgs decode_args(const Geom& g, const kvq_state* st, const kvq_cache* cache, const void* q,
+                       float softmax_scale, int32_t num_splits, float* out, void* workspace) {
   DecodeArgs a;
   a.g = g;
   a.k_codes = static_cast<const uint8_t*>(cache->k_codes);
@@ -1241,7 +1305,75 @@ extern "C" kvq_status kvq_decode_attn(const kvq_config* cfg, const kvq_state* st
   a.tq_mod = a.tiles_q % a.splits;
   a.ch_div = (a.items - a.tiles_q) / a.splits;
   a.ch_mod = (a.items - a.tiles_q) % a.splits;
+  a.force_part = 0;
+  a.k_new = nullptr;
+  a.v_new = nullptr;
+  a.ring_k = nullptr;
+  a.ring_v = nullptr;
+  a.n_new = 0;
+  a.new_slot0 = 0;
+  return a;
+}
+
+}  // namespace
+}  // namespace kvq
+
+extern "C" kvq_status kvq_decode_attn(const kvq_config* cfg, const kvq_state* st, const kvq_cache* cache,
+                                      const void* q, int32_t q_heads, float softmax_scale,
+                                      int32_t num_splits, float* out, void* workspace,
+                                      size_t workspace_size, void* stream) {
+  Geom g;
+  kvq_status s = validate_config(cfg, &g);
+  if (s != KVQ_OK) return s;
+  int gqa = 0;
+  s = check_decode(g, st, cache, q, q_heads, softmax_scale, num_splits, out, workspace, workspace_size, &gqa);
+  if (s != KVQ_OK) return s;
+  const DecodeArgs a = decode_args(g, st, cache, q, softmax_scale, num_splits, out, workspace);
   clear_stale_hip_error();
   if (!dispatch(a, gqa, static_cast<hipStream_t>(stream))) return KVQ_EINVAL;
   return hipGetLastError() == hipSuccess ? KVQ_OK : KVQ_EDEVICE;
+}
+
+extern "C" kvq_status kvq_decode_step(const kvq_config* cfg, kvq_state* st, const kvq_cache* cache,
+                                      const void* k_new, const void* v_new, int64_t n_new,
+                                      const void* q, int32_t q_heads, float softmax_scale,
+                                      int32_t num_splits, float* out, void* workspace,
+                                      size_t workspace_size, void* stream) {
+  Geom g;
+  kvq_status s = validate_config(cfg, &g);
+  if (s != KVQ_OK) return s;
+  if (!st) return KVQ_EINVAL;
+  kvq_state next;
+  s = plan_append(g, st, n_new, &next);
+  if (s != KVQ_OK) return s;
+  int gqa = 0;
+  s = check_decode(g, &next, cache, q, q_heads, softmax_scale, num_splits, out, workspace, workspace_size, &gqa);
+  if (s != KVQ_OK) return s;
+  if (n_new > 0 && (!k_new || !v_new || !cache->k_codes || !cache->v_codes || !cache->k_scale ||
+                    !cache->v_scale || !cache->k_tail || !cache->v_tail || (g.G == 0 && !cache->seg_index)))
+    return KVQ_EINVAL;      // what kvq_append requires
+  // One pass when nothing is flushed: attention over the cache as it was,
+  // and the appended tokens folded in (and written to the window) by the
+  // merge.  Otherwise the append, then attention.
+  const bool fused = n_new >= 1 && n_new <= kMaxStepNew && next.flushed_last == 0 && st->total >= 1 &&
+                     g.dtype == KVQ_BF16;
+  if (!fused) {
+    s = kvq_append(cfg, st, cache, k_new, v_new, n_new, stream);
+    if (s != KVQ_OK) return s;
+    return kvq_decode_attn(cfg, st, cache, q, q_heads, softmax_scale, num_splits, out, workspace,
+                           workspace_size, stream);
+  }
+  DecodeArgs a = decode_args(g, st, cache, q, softmax_scale, num_splits, out, workspace);
+  a.force_part = 1;
+  a.k_new = static_cast<const uint16_t*>(k_new);
+  a.v_new = static_cast<const uint16_t*>(v_new);
+  a.ring_k = static_cast<uint16_t*>(cache->k_tail);
+  a.ring_v = static_cast<uint16_t*>(cache->v_tail);
+  a.n_new = static_cast<int>(n_new);
+  a.new_slot0 = static_cast<int>((st->quantized + st->tail) % g.ring);
+  clear_stale_hip_error();
+  if (!dispatch(a, gqa, static_cast<hipStream_t>(stream))) return KVQ_EINVAL;
+  if (hipGetLastError() != hipSuccess) return KVQ_EDEVICE;
+  *st = next;
+  return KVQ_OK;
 }

@@ -95,6 +95,17 @@ class Pair:
         torch.cuda.synchronize()
         return out.cpu().numpy(), ws
 
+    def step(self, k: torch.Tensor, v: torch.Tensor, q: torch.Tensor, num_splits: int = 0, ws=None):
+        """One kvq_decode_step (append k, v [B, H, n, D], then attend with q); the
+        oracle state is advanced with the same append."""
+        hq = q.shape[1]
+        ws = ws if ws is not None else self.cache.workspace(hq, 1)
+        out = torch.full((q.shape[0], hq, self.w.head_dim), float("nan"), device="cuda")
+        self.cache.decode_step(k.cuda(), v.cuda(), q.cuda(), out, ws, num_splits=num_splits)
+        torch.cuda.synchronize()
+        self.ost = self.oracle.append_and_partition(self.ost, f32(k), f32(v), self.w.residual)
+        return out.cpu().numpy(), ws
+
     def decode_ref(self, q: torch.Tensor, units=None):
         return oatt.decode_attention(self.ost, f32(q), 1.0 / math.sqrt(self.w.head_dim), units=units)
 
