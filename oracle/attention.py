@@ -15,7 +15,11 @@ and compression", section 02 pseudo-code: append, then attention).
 
 Block attention: query i of a block of Tq queries sits at absolute position
 N + i, after the N cached tokens; it sees all N cached tokens and the block's
-own (not yet appended) tokens 0..i.
+own (not yet appended) tokens 0..i.  With frames of F tokens ("KV Cache and
+autoregressive video generation", section 6.3: bidirectional inside a frame,
+causal across frames) it sees the block tokens j whose frame
+floor((N + j) / F) is not later than its own, floor((N + i) / F); F = 1 is
+the token-causal mask.
 
 ``sigma`` is a parameter: 1/sqrt(head_dim) in the workloads; the scalar worked
 example of "KV Cache quantization and compression" section 03 uses 1.
@@ -36,8 +40,9 @@ from .cache import key_scales, segment_of_tokens, stacked_codes, value_scales
 from .codec import restore
 
 
-def attention_rows(q_rows, K, V, sigma: float, visible=None) -> np.ndarray:
-    """softmax(sigma * q K^T) V for each row of q, row i seeing K[:visible[i]]."""
+def attention_rows(q_rows, K, V, sigma: float, visible=None, mask=None) -> np.ndarray:
+    """softmax(sigma * q K^T) V for each row of q, row i seeing K[:visible[i]],
+    or the keys where mask[i] is True."""
     q = np.asarray(q_rows, dtype=np.float64)
     K = np.asarray(K, dtype=np.float64)
     V = np.asarray(V, dtype=np.float64)
@@ -45,6 +50,8 @@ def attention_rows(q_rows, K, V, sigma: float, visible=None) -> np.ndarray:
     if visible is not None:
         visible = np.asarray(visible).reshape(-1, 1)
         scores = np.where(np.arange(K.shape[0])[None, :] < visible, scores, -np.inf)
+    if mask is not None:
+        scores = np.where(np.asarray(mask, bool), scores, -np.inf)
     scores = scores - scores.max(axis=1, keepdims=True)
     p = np.exp(scores)
     p = p / p.sum(axis=1, keepdims=True)
@@ -97,9 +104,21 @@ def decode_attention(state, q, sigma: float, eps: float = 1e-8, units=None) -> n
     return out
 
 
+def block_mask(n_cached: int, rows, tq: int, frame_tokens: int = 1) -> np.ndarray:
+    """Visibility [len(rows), n_cached + tq] of block attention: every cached
+    token, and block token j for query i iff floor((N + j) / F) <= floor((N + i) / F)."""
+    rows = np.asarray(rows)
+    frame_q = (n_cached + rows) // frame_tokens
+    frame_k = (n_cached + np.arange(tq)) // frame_tokens
+    own = frame_k[None, :] <= frame_q[:, None]
+    return np.concatenate((np.ones((rows.size, n_cached), bool), own), axis=1)
+
+
 def block_attention(state, q, k_blk, v_blk, sigma: float, eps: float = 1e-8,
-                    rows=None, heads=None) -> np.ndarray:
-    """Causal block attention.  q: [B, Tq, Hq, D]; k_blk, v_blk: [B, Tq, Hkv, D].
+                    rows=None, heads=None, frame_tokens: int = 1) -> np.ndarray:
+    """Block attention (causal across frames of ``frame_tokens`` positions,
+    bidirectional inside one; 1 = token-causal).  q: [B, Tq, Hq, D];
+    k_blk, v_blk: [B, Tq, Hkv, D].
 
     Returns [B, Tq, Hq, D]; with ``rows``/``heads`` only those query rows /
     query heads are computed (the others stay NaN).
@@ -118,9 +137,9 @@ def block_attention(state, q, k_blk, v_blk, sigma: float, eps: float = 1e-8,
             n_cached = K.shape[0]
             K_all = np.concatenate((K, np.asarray(k_blk[b, :, kh], np.float64)))
             V_all = np.concatenate((V, np.asarray(v_blk[b, :, kh], np.float64)))
-            visible = n_cached + rows + 1
+            mask = block_mask(n_cached, rows, Tq, frame_tokens)
             for h in heads:
                 if h // g != kh:
                     continue
-                out[b, rows, h] = attention_rows(q[b, rows, h], K_all, V_all, sigma, visible)
+                out[b, rows, h] = attention_rows(q[b, rows, h], K_all, V_all, sigma, mask=mask)
     return out

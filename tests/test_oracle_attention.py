@@ -117,3 +117,46 @@ def test_block_causal_visibility():
         st_, kb[:, :1].transpose(0, 2, 1, 3), vb[:, :1].transpose(0, 2, 1, 3), residual_length=N + 1)
     dec = attention.decode_attention(st2, q1[:, 0], sigma=0.4)
     assert np.allclose(blk[:, 0], dec, atol=1e-6)
+
+
+def test_frame_mask_matches_the_video_figure():
+    """"KV Cache and autoregressive video generation", section 6.3 figure:
+    5 frames of 12 tokens; a frame sees itself and every earlier frame (the
+    upper-right blocks are empty, the diagonal blocks full)."""
+    m = attention.block_mask(0, np.arange(60), 60, frame_tokens=12)
+    expect = np.kron(np.tril(np.ones((5, 5), bool)), np.ones((12, 12), bool))
+    assert np.array_equal(m, expect)
+    # frames of one token are the token-causal mask
+    assert np.array_equal(attention.block_mask(0, np.arange(7), 7, 1), np.tril(np.ones((7, 7), bool)))
+    # cached tokens are always visible
+    assert attention.block_mask(9, np.arange(3), 3, 2)[:, :9].all()
+
+
+def test_frame_mask_with_a_partly_cached_frame():
+    """N = 5 cached tokens, frames of 4: positions 5..7 close frame 1 (they see
+    block tokens 0..2), positions 8..11 form frame 2 (block tokens 0..6)."""
+    m = attention.block_mask(5, np.arange(7), 7, frame_tokens=4)
+    assert m[:, :5].all()
+    assert [int(r[5:].sum()) for r in m] == [3, 3, 3, 7, 7, 7, 7]
+
+
+def test_block_frames_bidirectional_inside_a_frame():
+    """One frame spanning the whole block: every query sees every block token,
+    so q = 0 returns the mean of all cached and block values for every row;
+    frame_tokens = 1 keeps the token-causal result."""
+    rng = np.random.default_rng(6)
+    B, H, N, D, g, Tq = 1, 2, 8, 4, 2, 6
+    k = rng.standard_normal((B, H, N, D)).astype(np.float32)
+    v = rng.standard_normal((B, H, N, D)).astype(np.float32)
+    st_ = KVQuantizationStrategies(group=0).append_and_partition(None, k, v, residual_length=N)
+    kb = rng.standard_normal((B, Tq, H, D))
+    vb = rng.standard_normal((B, Tq, H, D))
+    q0 = np.zeros((B, Tq, H * g, D))
+    out = attention.block_attention(st_, q0, kb, vb, sigma=1.0, frame_tokens=N + Tq)
+    for h in range(H * g):
+        allv = np.concatenate((v[0, h // g], vb[0, :, h // g]))
+        assert np.allclose(out[0, :, h], allv.mean(0), atol=1e-12)
+    q = rng.standard_normal((B, Tq, H * g, D))
+    a = attention.block_attention(st_, q, kb, vb, sigma=0.5)
+    b = attention.block_attention(st_, q, kb, vb, sigma=0.5, frame_tokens=1)
+    assert np.array_equal(a, b)
