@@ -200,16 +200,20 @@ kvq_status kvq_decode_step(const kvq_config* cfg, kvq_state* st, const kvq_cache
                            int32_t num_splits, float* out, void* workspace,
                            size_t workspace_bytes, void* stream);
 
-/* Causal attention of a block of tq new queries against the cache plus the
- * block's own keys/values (Attn = softmax(Q K^T sigma + M) V with
- * M_ij = -inf for j > i, "KV Cache and autoregressive video generation",
- * section 3.1).  Query i sits at absolute position N + i after the N cached
- * tokens: it sees all N cached tokens and block tokens 0..i.  The block's
- * own K/V are read as given and are not appended.  Matrix products run on
- * the MFMA units over tiles restored into LDS.  Supported: kv_dtype bf16 and
+/* Attention of a block of tq new queries against the cache plus the
+ * block's own keys/values (Attn = softmax(Q K^T sigma + M) V, "KV Cache and
+ * autoregressive video generation", section 3.1).  Query i sits at absolute
+ * position N + i after the N cached tokens: it sees all N cached tokens and
+ * the block tokens j in frames no later than its own, i.e.
+ * floor((N + j) / F) <= floor((N + i) / F) for frame_tokens = F --
+ * bidirectional inside a frame, causal across frames (section 6.3);
+ * F = 1 is the token-causal mask M_ij = -inf for j > i.  The block's own
+ * K/V are read as given and are not appended.  Matrix products run on the
+ * MFMA units over tiles restored into LDS.  Supported: kv_dtype bf16 and
  * head_dim 64 or 128 (other configurations return KVQ_EINVAL).
  *   q            : device, kv_dtype [batch, tq, q_heads, head_dim]
  *   k_blk, v_blk : device, kv_dtype [batch, tq, kv_heads, head_dim]
+ *   frame_tokens : F >= 1 (N + tq + F below 2^31)
  *   out          : device, float32 [batch, tq, q_heads, head_dim]
  *   softmax_scale: sigma > 0 (1/sqrt(head_dim) for standard attention)
  *   num_splits   : splits of the cached sequence, at most 8; 0 = library's choice
@@ -217,8 +221,9 @@ kvq_status kvq_decode_step(const kvq_config* cfg, kvq_state* st, const kvq_cache
  * Errors: KVQ_EINVAL, KVQ_EWORKSPACE, KVQ_EDEVICE. */
 kvq_status kvq_block_attn(const kvq_config* cfg, const kvq_state* st, const kvq_cache* cache,
                           const void* q, const void* k_blk, const void* v_blk, int32_t tq,
-                          int32_t q_heads, float softmax_scale, int32_t num_splits,
-                          float* out, void* workspace, size_t workspace_bytes, void* stream);
+                          int32_t q_heads, int32_t frame_tokens, float softmax_scale,
+                          int32_t num_splits, float* out, void* workspace, size_t workspace_bytes,
+                          void* stream);
 
 /* Static string naming a status code. */
 const char* kvq_status_str(kvq_status s);

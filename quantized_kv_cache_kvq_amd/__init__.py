@@ -77,8 +77,8 @@ def load() -> ctypes.CDLL:
         "kvq_decode_attn": [P(kvq_config), P(kvq_state), P(kvq_cache), vp, i32, f32, i32, vp, vp, sz, vp],
         "kvq_decode_step": [P(kvq_config), P(kvq_state), P(kvq_cache), vp, vp, i64, vp, i32, f32, i32,
                             vp, vp, sz, vp],
-        "kvq_block_attn": [P(kvq_config), P(kvq_state), P(kvq_cache), vp, vp, vp, i32, i32, f32, i32,
-                           vp, vp, sz, vp],
+        "kvq_block_attn": [P(kvq_config), P(kvq_state), P(kvq_cache), vp, vp, vp, i32, i32, i32, f32,
+                           i32, vp, vp, sz, vp],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -170,11 +170,11 @@ def kvq_decode_step(cfg, st, cache, k_new, v_new, n_new, q, q_heads, softmax_sca
                                   _stream(stream)), "kvq_decode_step")
 
 
-def kvq_block_attn(cfg, st, cache, q, k_blk, v_blk, tq, q_heads, softmax_scale, num_splits,
-                   out, ws, stream=None):
+def kvq_block_attn(cfg, st, cache, q, k_blk, v_blk, tq, q_heads, frame_tokens, softmax_scale,
+                   num_splits, out, ws, stream=None):
     _check(load().kvq_block_attn(ctypes.byref(cfg), ctypes.byref(st), ctypes.byref(cache), _ptr(q),
-                                 _ptr(k_blk), _ptr(v_blk), tq, q_heads, softmax_scale, num_splits,
-                                 _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
+                                 _ptr(k_blk), _ptr(v_blk), tq, q_heads, frame_tokens, softmax_scale,
+                                 num_splits, _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
                                  _stream(stream)), "kvq_block_attn")
 
 
@@ -226,8 +226,11 @@ class KVCache:
         kvq_decode_step(self.cfg, self.state, self.c, k_new, v_new, k_new.shape[2], q, q.shape[1], s,
                         num_splits, out, ws, stream)
 
-    def block_attn(self, q, k_blk, v_blk, out, ws, softmax_scale=None, num_splits=0, stream=None):
+    def block_attn(self, q, k_blk, v_blk, out, ws, softmax_scale=None, num_splits=0, stream=None,
+                   frame_tokens=1):
+        """frame_tokens = F: bidirectional inside frames of F positions, causal
+        across frames; 1 = token-causal."""
         D = self.cfg.head_dim
         s = 1.0 / math.sqrt(D) if softmax_scale is None else softmax_scale
-        kvq_block_attn(self.cfg, self.state, self.c, q, k_blk, v_blk, q.shape[1], q.shape[2], s,
-                       num_splits, out, ws, stream)
+        kvq_block_attn(self.cfg, self.state, self.c, q, k_blk, v_blk, q.shape[1], q.shape[2],
+                       frame_tokens, s, num_splits, out, ws, stream)

@@ -76,6 +76,8 @@ struct BlockArgs {
   int tq, gqa, rows;        // rows = tq * gqa query rows per KV head
   float qscale;             // sigma * log2(e)
   int tiles_q, tiles_t, tiles_b, splits;
+  int frame;                // frame length F (1 = token-causal)
+  int cached;               // N = nq + nt: absolute position of the block's first query
 };
 
 // Token a tile slot covers, and whether it exists (per tile kind).
@@ -123,12 +125,19 @@ void block_kernel(BlockArgs a) {
   // ---- this wave's query rows: operand B of S^T = Khat . Q^T ----
   bf8_t qop[2][KS];
   int qpos[2];        // position of query row col of block qb (or -1 past the end)
+  // Last block token each of those rows sees: the end of its frame
+  // floor((N + pos) / F), clipped to the block.
+  auto own_limit = [&](int pos) {
+    return min(a.tq - 1, ((a.cached + pos) / a.frame + 1) * a.frame - 1 - a.cached);
+  };
+  int qlim[2];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const int r = r0 + wave * kRowsWave + qb * 16 + col;
     const bool ok = r < a.rows;
     const int pos = ok ? r / a.gqa : 0, h = ok ? r % a.gqa : 0;
     qpos[qb] = ok ? pos : -1;
+    qlim[qb] = own_limit(pos);
     const uint16_t* qrow = a.q + (((int64_t)b * a.tq + pos) * Hq + kvh * a.gqa + h) * D;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -136,7 +145,8 @@ void block_kernel(BlockArgs a) {
       qop[qb][ks] = __builtin_bit_cast(bf8_t, w);
     }
   }
-  const int pos_hi = (min(r0 + kRowsWG, a.rows) - 1) / a.gqa;   // last position in the workgroup
+  // last block token any row of the workgroup sees
+  const int lim_hi = own_limit((min(r0 + kRowsWG, a.rows) - 1) / a.gqa);
 
   float m[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.0f, 0.0f};
   f4_t acc[2][CB];
@@ -190,7 +200,7 @@ void block_kernel(BlockArgs a) {
     const int kind = item < a.tiles_q ? kQuant : (item < a.tiles_q + a.tiles_t ? kTail : kOwn);
     const int tile = kind == kQuant ? item : (kind == kTail ? item - a.tiles_q : item - a.tiles_q - a.tiles_t);
     const int t0 = tile * kTile;
-    if (kind == kOwn && t0 > pos_hi) break;   // later block tiles are masked for every row here
+    if (kind == kOwn && t0 > lim_hi) break;   // later block tiles are masked for every row here
     const int count = kind == kQuant ? min(kTile, a.nq - t0)
                                      : (kind == kTail ? min(kTile, a.nt - t0) : min(kTile, a.tq - t0));
 
@@ -356,7 +366,7 @@ void block_kernel(BlockArgs a) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int tt = 16 * tb + 4 * q4 + i;
-            const bool vis = tt < count && qpos[qb] >= 0 && (kind != kOwn || t0 + tt <= qpos[qb]);
+            const bool vis = tt < count && qpos[qb] >= 0 && (kind != kOwn || t0 + tt <= qlim[qb]);
             S[tb][qb][i] = vis ? S[tb][qb][i] : -INFINITY;
           }
       }
@@ -552,8 +562,9 @@ using namespace kvq;
 
 extern "C" kvq_status kvq_block_attn(const kvq_config* cfg, const kvq_state* st, const kvq_cache* cache,
                                      const void* q, const void* k_blk, const void* v_blk, int32_t tq,
-                                     int32_t q_heads, float softmax_scale, int32_t num_splits,
-                                     float* out, void* workspace, size_t workspace_size, void* stream) {
+                                     int32_t q_heads, int32_t frame_tokens, float softmax_scale,
+                                     int32_t num_splits, float* out, void* workspace,
+                                     size_t workspace_size, void* stream) {
   Geom g;
   kvq_status s = validate_config(cfg, &g);
   if (s != KVQ_OK) return s;
@@ -568,6 +579,7 @@ extern "C" kvq_status kvq_block_attn(const kvq_config* cfg, const kvq_state* st,
   if (g.G > 0 && st->quantized % g.G != 0) return KVQ_EINVAL;
   if (!(softmax_scale > 0.0f) || num_splits < 0 || num_splits > kBlockMaxSplits) return KVQ_EINVAL;
   if ((int64_t)tq * gqa > (1 << 30)) return KVQ_EINVAL;
+  if (frame_tokens < 1 || st->total + (int64_t)tq + frame_tokens > (int64_t(1) << 31) - 1) return KVQ_EINVAL;
   if (st->quantized > 0 && (!cache->k_codes || !cache->v_codes || !cache->k_scale || !cache->v_scale ||
                             (g.G == 0 && !cache->seg_index)))
     return KVQ_EINVAL;
@@ -598,6 +610,8 @@ extern "C" kvq_status kvq_block_attn(const kvq_config* cfg, const kvq_state* st,
   a.tiles_q = (a.nq + kTile - 1) / kTile;
   a.tiles_t = (a.nt + kTile - 1) / kTile;
   a.tiles_b = (tq + kTile - 1) / kTile;
+  a.frame = frame_tokens;
+  a.cached = static_cast<int>(st->total);
   const int rows_wg = g.D >= 128 ? BlockShape<128>::kRows : BlockShape<64>::kRows;
   const int threads = g.D >= 128 ? BlockShape<128>::kThreads : BlockShape<64>::kThreads;
   const int row_tiles = (a.rows + rows_wg - 1) / rows_wg;

@@ -110,18 +110,20 @@ class Pair:
         return oatt.decode_attention(self.ost, f32(q), 1.0 / math.sqrt(self.w.head_dim), units=units)
 
     def block(self, q: torch.Tensor, k_blk: torch.Tensor, v_blk: torch.Tensor, num_splits: int = 0,
-              ws=None):
+              ws=None, frame_tokens: int = 1):
         """q [B, tq, Hq, D], k_blk / v_blk [B, tq, Hkv, D] (CPU) -> output [B, tq, Hq, D]."""
         B, tq, hq, D = q.shape
         ws = ws if ws is not None else self.cache.workspace(hq, tq)
         out = torch.full((B, tq, hq, D), float("nan"), device="cuda")
-        self.cache.block_attn(q.cuda(), k_blk.cuda(), v_blk.cuda(), out, ws, num_splits=num_splits)
+        self.cache.block_attn(q.cuda(), k_blk.cuda(), v_blk.cuda(), out, ws, num_splits=num_splits,
+                              frame_tokens=frame_tokens)
         torch.cuda.synchronize()
         return out.cpu().numpy()
 
-    def block_ref(self, q, k_blk, v_blk, rows=None, heads=None):
+    def block_ref(self, q, k_blk, v_blk, rows=None, heads=None, frame_tokens: int = 1):
         return oatt.block_attention(self.ost, f32(q), f32(k_blk), f32(v_blk),
-                                    1.0 / math.sqrt(self.w.head_dim), rows=rows, heads=heads)
+                                    1.0 / math.sqrt(self.w.head_dim), rows=rows, heads=heads,
+                                    frame_tokens=frame_tokens)
 
 
 def _first_diff(a, b):

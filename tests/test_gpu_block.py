@@ -95,6 +95,38 @@ def test_block_overflow_only_segments(D):
 
 
 @needs_gpu
+@pytest.mark.parametrize("frame,n,tq,splits", [
+    (4, 1000, 100, 0),       # frames straddle the cache end (N = 1000 is not a multiple of 4 * 64)
+    (100, 1000, 300, 0),     # N a whole number of frames
+    (64, 900, 200, 3),
+    (37, 777, 150, 1),       # odd frame length, ragged tiles
+    (1300, 1000, 256, 0),    # one frame spans the block: bidirectional
+])
+def test_block_frames(frame, n, tq, splits):
+    """Frames of F positions: bidirectional inside a frame, causal across
+    frames ("KV Cache and autoregressive video generation", section 6.3)."""
+    w = ks.small(ks.VIDEO_BLOCK, batch=1, kv_heads=2, q_heads=8)
+    p, s = build(w, n)
+    q, kb, vb = ks.block_inputs(s, tq)
+    note(f"block frames F={frame} n={n} tq={tq} splits={splits}")
+    got = p.block(q, kb, vb, num_splits=splits, frame_tokens=frame)
+    ref = p.block_ref(q, kb, vb, frame_tokens=frame)
+    err = max_abs(got, ref)
+    note(f"block frames F={frame}: max-abs {err:.3e}")
+    assert err <= TOL
+
+
+@needs_gpu
+def test_block_frame_of_one_is_token_causal():
+    w = ks.small(ks.VIDEO_BLOCK, batch=1, kv_heads=2, q_heads=8, code_bits=4, qmax=7)
+    p, s = build(w, 700)
+    q, kb, vb = ks.block_inputs(s, 90)
+    assert np.array_equal(p.block(q, kb, vb), p.block(q, kb, vb, frame_tokens=1))
+    with pytest.raises(Exception):
+        p.block(q, kb, vb, frame_tokens=0)
+
+
+@needs_gpu
 def test_block_of_one_equals_decode_after_append():
     """tq = 1: the block path equals appending the token, then decoding."""
     w = ks.small(ks.VIDEO_BLOCK, batch=2, kv_heads=2, q_heads=8, code_bits=4, qmax=7)
@@ -120,8 +152,11 @@ def test_block_rejects_unsupported():
 
 
 @needs_gpu
-def test_block_video_full_size_sampled_rows():
-    """The video block at full size: 432000 int2 tokens, 1024 causal queries.
+@pytest.mark.parametrize("frame", [1, 14400])
+def test_block_video_full_size_sampled_rows(frame):
+    """The video block at full size: 432000 int2 tokens, 1024 queries, token-
+    causal or in frames of 14400 positions (the block then lies inside one
+    frame and is bidirectional).
 
     The fp64 oracle computes a sample of rows (first, last, and a seeded
     spread) for the query heads of two KV heads; the kernel computes all.
@@ -129,13 +164,13 @@ def test_block_video_full_size_sampled_rows():
     w = ks.VIDEO_BLOCK
     p, s = build(w, w.prefill)
     q, kb, vb = ks.block_inputs(s, w.block_q)
-    note("block video full size")
-    got = p.block(q, kb, vb)
+    note(f"block video full size frames={frame}")
+    got = p.block(q, kb, vb, frame_tokens=frame)
     assert np.isfinite(got).all()
     rng = np.random.default_rng(5)
     rows = np.unique(np.concatenate(([0, 1, 511, w.block_q - 1], rng.choice(w.block_q, 8, replace=False))))
     heads = [0, 3, 20, 23]                     # KV heads 0 and 5
-    ref = p.block_ref(q, kb, vb, rows=rows, heads=heads)
+    ref = p.block_ref(q, kb, vb, rows=rows, heads=heads, frame_tokens=frame)
     err = max_abs(got[:, rows][:, :, heads], ref[:, rows][:, :, heads])
-    note(f"block video full size: max-abs {err:.3e}")
+    note(f"block video full size frames={frame}: max-abs {err:.3e}")
     assert err <= TOL
