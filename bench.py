@@ -214,6 +214,98 @@ def run_decode(args, log):
     return res, (cfg, w)
 
 
+def run_decode_paths(args, log):
+    """Read path (i) against the fused one on the Llama-3-8B int4 decode shape
+    ("KV Cache quantization and compression", section 06): restore the whole
+    quantized history into a dense bf16 buffer in HBM (kvq_restore), copy the
+    window after it, and attend over the dense history (kvq_decode_attn on a
+    cache whose window holds every token), against kvq_decode_attn on the
+    quantized cache."""
+    import torch
+
+    import kvq_synth as ks
+    from quantized_kv_cache_kvq_amd import KVCache, make_config
+
+    w = ks.LLAMA3_DECODE
+    n_caches = args.caches
+    cfg, caches = build_caches(w, n_caches, w.prefill + 64, log)
+    total = caches[0].state.total
+    nq, nt = caches[0].state.quantized, caches[0].state.tail
+    # One dense history (a per-layer temporary of path (i)): every token in the
+    # bf16 window, nothing quantized.
+    dcfg = make_config(batch=w.batch, kv_heads=w.kv_heads, head_dim=w.head_dim, capacity=64,
+                       code_bits=w.code_bits, qmax=w.qmax, residual=total, group=w.group)
+    dense = KVCache(dcfg, zero=False)
+    dense.state.quantized, dense.state.tail, dense.state.total = 0, total, total
+    ring = caches[0].sizes.ring
+    slots = torch.tensor([(nq + i) % ring for i in range(nt)], device="cuda")
+    s = ks.Stream(w, seed=20_000)
+    q = ks.decode_query(s).cuda()
+    out_f = torch.empty(w.batch, w.q_heads, w.head_dim, device="cuda")
+    out_d = torch.empty_like(out_f)
+    ws = caches[0].workspace(w.q_heads, 1)
+    dws = dense.workspace(w.q_heads, 1)
+    stream = torch.cuda.current_stream()
+    reps = max(4, args.steps // n_caches)
+
+    def timed(fn):
+        for c in caches[:2]:
+            fn(c)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            for c in caches:
+                fn(c)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / (reps * n_caches)
+
+    def restore(c):
+        c.restore(dense.k_tail, dense.v_tail)
+
+    def window(c):
+        dense.k_tail[:, :, nq:total] = c.k_tail[:, :, slots]
+        dense.v_tail[:, :, nq:total] = c.v_tail[:, :, slots]
+
+    def path_i(c):
+        restore(c)
+        window(c)
+        dense.decode_attn(q, out_d, dws)
+
+    fused_us = timed(lambda c: c.decode_attn(q, out_f, ws))
+    restore_us = timed(restore)
+    window_us = timed(window)
+    dense_us = timed(lambda c: dense.decode_attn(q, out_d, dws))
+    path_us = timed(path_i)
+    caches[-1].decode_attn(q, out_f, ws)
+    path_i(caches[-1])
+    torch.cuda.synchronize()
+    diff = float((out_f - out_d).abs().max())
+    units = w.batch * w.kv_heads
+    fused_bytes = decode_bytes(cfg, nq, nt, w.q_heads)
+    restored = 2 * units * nq * w.head_dim * 2                 # bf16 keys and values written
+    dense_read = 2 * units * total * w.head_dim * 2 + w.batch * w.q_heads * w.head_dim * 2
+    path_bytes = (fused_bytes - 2 * units * nt * w.head_dim * 2) + restored + 2 * (2 * units * nt * w.head_dim * 2) + dense_read
+    log(f"fused decode {fused_us:.2f} us; restore-to-HBM path {path_us:.2f} us (restore {restore_us:.2f}, "
+        f"window copy {window_us:.2f}, dense attention {dense_us:.2f}); max |fused - path| {diff:.2e}")
+    return {
+        "metric": "decode call time by read path, Llama-3-8B shape int4 (restore to HBM + dense attention vs fused)",
+        "value": round(path_us, 3), "unit": "us", "n_gpus": 1, "steps": reps * n_caches, "warmup": 2,
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 dense history / int4 fused", "data": "synthetic",
+        "config": {"workload": w.name + "_read_paths", "batch": w.batch, "q_heads": w.q_heads,
+                   "kv_heads": w.kv_heads, "head_dim": w.head_dim, "context": total,
+                   "codes": f"int{w.code_bits}", "caches_rotated": n_caches, "parallelism": "single-gpu"},
+        "fused_us": round(fused_us, 3),
+        "restore_us": round(restore_us, 3),
+        "window_copy_us": round(window_us, 3),
+        "dense_attention_us": round(dense_us, 3),
+        "max_abs_fused_vs_path": diff,
+        "algorithmic_bytes": {"fused": int(fused_bytes), "restore_path": int(path_bytes)},
+    }
+
+
 def block_flops(nq_total: int, tq: int, q_heads: int, head_dim: int, batch: int = 1,
                 frame_tokens: int = 1) -> float:
     """Algorithmic FLOPs of one block: QK^T and PV over N cached tokens plus the
@@ -530,13 +622,15 @@ def main():
     ap.add_argument("--frame-tokens", type=int, default=1,
                     help="video_block: frame length of the block mask (1 = token-causal)")
     ap.add_argument("--workload", choices=["llama3_decode", "video_block", "long_decode", "append_int8",
-                                           "append_int4", "hbm_copy"], default="llama3_decode",
+                                           "append_int4", "hbm_copy", "decode_paths"],
+                    default="llama3_decode",
                     help="llama3_decode (default): the append + decode step; video_block: one "
                          "1024-query causal block against the 432000-token int2 cache; long_decode: "
                          "32 layers of 131072-token caches; append_int8/int4: 128 appends of 16 "
                          "tokens into 4096-token caches (16 x 8 heads); hbm_copy: a plain 256 MiB "
                          "device copy (reference rate, and the known-size kernel that scales the "
-                         "FETCH_SIZE / WRITE_SIZE counters)")
+                         "FETCH_SIZE / WRITE_SIZE counters); decode_paths: the decode call by "
+                         "restore-to-HBM + dense attention against the fused kernel")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the library has no multi-GPU path; run with --gpus 1",
@@ -562,6 +656,8 @@ def main():
         res = run_video_block(args, log)
     elif args.workload == "long_decode":
         res = run_long_decode(args, log)
+    elif args.workload == "decode_paths":
+        res = run_decode_paths(args, log)
     elif args.workload.startswith("append_"):
         res = run_append(args, log, 8 if args.workload == "append_int8" else 4)
     else:

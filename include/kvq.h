@@ -142,6 +142,23 @@ kvq_status kvq_plan_append(const kvq_config* cfg, const kvq_state* st, int64_t n
 kvq_status kvq_append(const kvq_config* cfg, kvq_state* st, const kvq_cache* cache,
                       const void* k_new, const void* v_new, int64_t n_new, void* stream);
 
+/* Restore of the quantized prefix into dense arrays: for every quantized
+ * token t and channel c, k = code / max(kscale[segment(t)][c], eps) and
+ * v = code / max(vscale[t], eps) ("KV Cache Quantization Strategies",
+ * Step 4 restore), computed as an IEEE fp32 division and stored as fp32 or
+ * rounded once to bf16.  This is the first half of the "restore the whole
+ * history to HBM, then ordinary attention" read path ("KV Cache
+ * quantization and compression", section 06); the attention calls of this
+ * library restore inside their kernels instead.
+ *   k_out, v_out : device, out_dtype [batch, kv_heads, ld, head_dim]; rows
+ *                  0 .. quantized - 1 of each (batch, head) are written
+ *   out_dtype    : KVQ_F32 or KVQ_BF16
+ *   ld           : rows per (batch, head) of the outputs, >= st->quantized
+ * The tail is not touched (it is stored as given).  An empty prefix is a
+ * valid no-op.  Errors: KVQ_EINVAL, KVQ_EDEVICE. */
+kvq_status kvq_restore(const kvq_config* cfg, const kvq_state* st, const kvq_cache* cache,
+                       void* k_out, void* v_out, int32_t out_dtype, int64_t ld, void* stream);
+
 /* Bytes of device workspace needed by kvq_decode_attn (tq = 1) or
  * kvq_block_attn (tq = query block length) for q_heads query heads.
  * Errors: KVQ_EINVAL. */

@@ -21,7 +21,7 @@ KVQ_BF16, KVQ_F32 = 0, 1
 
 EXPORTED = ("kvq_buffer_sizes", "kvq_plan_append", "kvq_append", "kvq_workspace_size",
             "kvq_workspace_init", "kvq_decode_attn", "kvq_decode_step", "kvq_block_attn",
-            "kvq_status_str")
+            "kvq_restore", "kvq_status_str")
 
 
 class kvq_config(ctypes.Structure):
@@ -73,6 +73,7 @@ def load() -> ctypes.CDLL:
         "kvq_plan_append": [P(kvq_config), P(kvq_state), i64, P(kvq_state)],
         "kvq_append": [P(kvq_config), P(kvq_state), P(kvq_cache), vp, vp, i64, vp],
         "kvq_workspace_size": [P(kvq_config), i32, i32, P(sz)],
+        "kvq_restore": [P(kvq_config), P(kvq_state), P(kvq_cache), vp, vp, i32, i64, vp],
         "kvq_workspace_init": [vp, sz, vp],
         "kvq_decode_attn": [P(kvq_config), P(kvq_state), P(kvq_cache), vp, i32, f32, i32, vp, vp, sz, vp],
         "kvq_decode_step": [P(kvq_config), P(kvq_state), P(kvq_cache), vp, vp, i64, vp, i32, f32, i32,
@@ -144,6 +145,11 @@ def kvq_append(cfg, st, cache: kvq_cache, k_new, v_new, n_new: int, stream=None)
                              _ptr(k_new), _ptr(v_new), n_new, _stream(stream)), "kvq_append")
 
 
+def kvq_restore(cfg, st, cache, k_out, v_out, out_dtype: int, ld: int, stream=None):
+    _check(load().kvq_restore(ctypes.byref(cfg), ctypes.byref(st), ctypes.byref(cache), _ptr(k_out),
+                              _ptr(v_out), out_dtype, ld, _stream(stream)), "kvq_restore")
+
+
 def kvq_workspace_size(cfg, q_heads: int, tq: int) -> int:
     n = ctypes.c_size_t()
     _check(load().kvq_workspace_size(ctypes.byref(cfg), q_heads, tq, ctypes.byref(n)),
@@ -206,6 +212,12 @@ class KVCache:
 
     def append(self, k_new, v_new, stream=None):
         kvq_append(self.cfg, self.state, self.c, k_new, v_new, k_new.shape[2], stream)
+
+    def restore(self, k_out, v_out, stream=None):
+        """Restored quantized prefix into k_out / v_out [B, Hkv, ld, D] (fp32 or bf16)."""
+        import torch
+        dt = KVQ_BF16 if k_out.dtype == torch.bfloat16 else KVQ_F32
+        kvq_restore(self.cfg, self.state, self.c, k_out, v_out, dt, k_out.shape[2], stream)
 
     def workspace(self, q_heads: int, tq: int = 1, stream=None):
         import torch
