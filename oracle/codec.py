@@ -26,10 +26,16 @@ fp16 half-to-even, and to compute the codes with the *stored* fp16 scale so
 that restore uses exactly the scale the codes were made with.  Clamping only
 lowers a scale, so no element clips beyond half a step.
 
+Same-axis grouping (``quantize_grouped_per_token``): the Step 2 table's
+third row, one fixed-size local group, as in section 5.1's setting (groups
+of 64 along head_dim for both K and V): steps 1-4 with the absmax taken over
+each run of ``group`` consecutive channels of one token.
+
 Parity: pinned by tests/test_oracle_codec.py (worked grid examples of "KV
 Cache quantization and compression" section 03, the round-half-even tie
 vector, the all-zero range contract, the per-element error bound, fp16
-conversion against numpy's own float16 cast).
+conversion against numpy's own float16 cast; grouping over the whole of
+head_dim equals the per-token quantizer).
 """
 from __future__ import annotations
 
@@ -86,3 +92,26 @@ def restore(codes, scale, eps: float = 1e-8, dtype=None) -> np.ndarray:
     dt = np.dtype(dtype) if dtype is not None else s.dtype
     floor = np.asarray(np.float32(eps)).astype(dt)
     return np.asarray(codes).astype(dt) / np.maximum(s.astype(dt), floor)
+
+
+def quantize_grouped_per_token(x, group: int, qmax: int = 7, eps: float = 1e-8, storage: str = "fp32"):
+    """Same-axis codes: absmax over each run of ``group`` consecutive channels
+    of a token; scale [..., tokens, head_dim // group, 1]."""
+    _check4(x, "x")
+    a = np.asarray(x, dtype=np.float32)
+    B, H, T, D = a.shape
+    if group < 1 or D % group:
+        raise ValueError("group must divide head_dim")
+    runs = a.reshape(B, H, T, D // group, group)
+    absmax = np.abs(runs).max(axis=-1, keepdims=True)
+    scale = scale_from_absmax(absmax, qmax, eps, storage)
+    return quantize_with_scale(runs, scale, qmax).reshape(B, H, T, D), scale
+
+
+def restore_grouped_per_token(codes, scale, eps: float = 1e-8, dtype=np.float64) -> np.ndarray:
+    """codes / max(scale, eps) for ``quantize_grouped_per_token`` codes."""
+    c = np.asarray(codes)
+    B, H, T, D = c.shape
+    G = np.shape(scale)[-2]
+    runs = c.reshape(B, H, T, G, D // G)
+    return restore(runs, scale, eps, dtype).reshape(B, H, T, D)

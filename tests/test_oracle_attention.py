@@ -160,3 +160,22 @@ def test_block_frames_bidirectional_inside_a_frame():
     a = attention.block_attention(st_, q, kb, vb, sigma=0.5)
     b = attention.block_attention(st_, q, kb, vb, sigma=0.5, frame_tokens=1)
     assert np.array_equal(a, b)
+
+
+def test_axis_study_outlier_channels_favour_per_channel_keys():
+    """Keys with channels ten times larger (the synthetic workloads' outliers):
+    a per-channel Key range restores the other channels far better than runs
+    of 64 channels that contain an outlier; Values are per token in both."""
+    from oracle import axis_study
+    rng = np.random.default_rng(13)
+    B, H, T, D = 1, 2, 256, 128
+    k = rng.standard_normal((B, H, T, D))
+    k[..., [5, 70]] *= 10
+    v = rng.standard_normal((B, H, T, D))
+    q = rng.standard_normal((B, 4, D))
+    r = axis_study.compare(k, v, q, qmax=7, segment=128, group=64)
+    assert r["kivi"]["k_rms"] < 0.6 * r["same_axis"]["k_rms"]
+    assert r["kivi"]["attn_rms"] < r["same_axis"]["attn_rms"]
+    # with one scale over all of head_dim and no outliers, Values are the same in both
+    r0 = axis_study.compare(rng.standard_normal((B, H, T, D)), v, q, qmax=7, segment=128, group=128)
+    assert abs(r0["kivi"]["v_rms"] - r0["same_axis"]["v_rms"]) < 1e-12

@@ -131,3 +131,32 @@ def test_uniform_quantizer_bounds(x, qmax, storage, axis):
     unsaturated = np.broadcast_to(scale.astype(np.float64) < 65504, x.shape)
     hit = np.abs(codes.astype(np.int32)) == qmax
     assert np.all(hit[is_max & unsaturated])
+
+
+def test_grouped_over_all_of_head_dim_is_the_per_token_quantizer():
+    x = np.random.default_rng(11).standard_normal((2, 3, 17, 64)).astype(np.float32) * 3
+    for storage in ("fp32", "fp16"):
+        c1, s1 = codec.quantize_grouped_per_token(x, 64, 7, 1e-8, storage)
+        c2, s2 = codec.quantize_value_per_token(x, 7, 1e-8, storage)
+        assert np.array_equal(c1, c2)
+        assert np.array_equal(s1[..., 0, :], s2)
+
+
+def test_grouped_runs_are_independent_and_bounded():
+    """Each run of `group` channels has its own range: scaling one run leaves
+    the others' codes unchanged; the run's absmax element reaches +-qmax and
+    every element restores within half a step."""
+    rng = np.random.default_rng(12)
+    x = rng.standard_normal((1, 2, 9, 128)).astype(np.float32)
+    c, s = codec.quantize_grouped_per_token(x, 32, 7)
+    y = x.copy()
+    y[..., 32:64] *= 10
+    c2, _ = codec.quantize_grouped_per_token(y, 32, 7)
+    keep = np.r_[0:32, 64:128]
+    assert np.array_equal(c[..., keep], c2[..., keep])
+    runs = np.abs(x).reshape(1, 2, 9, 4, 32)
+    hit = np.abs(c.astype(np.int32)).reshape(1, 2, 9, 4, 32) == 7
+    assert np.all(hit[runs == runs.max(axis=-1, keepdims=True)])
+    xr = codec.restore_grouped_per_token(c, s)
+    step = np.repeat(1.0 / s.astype(np.float64)[..., 0], 32, axis=-1)
+    assert np.all(np.abs(xr - x) <= 0.5 * step * (1 + 1e-6))
