@@ -24,6 +24,10 @@ What it computes, and from where:
   specification (the pages do not fix a packing; see the docstring there).
 * ``ledger``    -- byte budgets ("KV Cache quantization and compression",
   sections 01 and 05; page 1 ``compare``).
+* ``axis_study`` -- asymmetric-axis against same-axis grouped quantization
+  (page 1, Step 2 table and section 5.1), measured on the synthetic
+  workloads; the block-attention frame mask lives in ``attention``
+  ("KV Cache and autoregressive video generation", section 6.3).
 
 Parity status of every function is stated in its module header.
 """
