@@ -362,9 +362,15 @@ template <int D, int GQA>
 __device__ __forceinline__ void load_q(const DecodeArgs& a, int unit, float (*qsT)[GQA]) {
   const Geom& g = a.g;
   const int b = unit / g.H, kvh = unit % g.H;
-  for (int i = threadIdx.x; i < GQA * D; i += kThreads) {
-    const int h = i / D, c = i % D;
-    qsT[c][h] = load_elem(a.q, ((int64_t)b * g.H * GQA + kvh * GQA + h) * D + c, g.dtype) * a.qscale;
+  const int64_t row = ((int64_t)b * g.H * GQA + kvh * GQA) * D;
+  // The dtype test stays outside the loops, so that the loads of a thread
+  // are unconditional and in flight together.
+  if (g.dtype == KVQ_BF16) {
+    const uint16_t* q = static_cast<const uint16_t*>(a.q) + row;
+    for (int i = threadIdx.x; i < GQA * D; i += kThreads) qsT[i % D][i / D] = bf16_bits_to_f32(q[i]) * a.qscale;
+  } else {
+    const float* q = static_cast<const float*>(a.q) + row;
+    for (int i = threadIdx.x; i < GQA * D; i += kThreads) qsT[i % D][i / D] = q[i] * a.qscale;
   }
 }
 
@@ -970,10 +976,16 @@ void decode_i8_kernel(DecodeArgs a) {
       const int ic = i < GQA * D ? i : 0;
       const int h = ic / D, c = ic % D;
       const int64_t row = ((int64_t)b * g.H * GQA + kvh * GQA + h) * D;
-      qT[k] = load_elem(a.q, row + c, g.dtype);
-      qP[k] = load_elem(a.q, row + chan(c), g.dtype);
+      // bf16 only (the launch requires it): unconditional loads, so that the
+      // query's round trip overlaps the first tile's instead of preceding it
+      const uint16_t* qb = static_cast<const uint16_t*>(a.q);
+      qT[k] = bf16_bits_to_f32(qb[row + c]);
+      qP[k] = bf16_bits_to_f32(qb[row + chan(c)]);
     }
   }
+  // Every query load goes out before the tile's: waiting for the query then
+  // leaves the tile loads in flight.
+  __builtin_amdgcn_sched_barrier(0);
   int tile = w_begin;
   TileRegs bufA, bufB;
   ld_seg = w_begin / a.tiles_per_seg;
