@@ -986,18 +986,22 @@ void decode_i8_kernel(DecodeArgs a) {
   // Every query load goes out before the tile's: waiting for the query then
   // leaves the tile loads in flight.
   __builtin_amdgcn_sched_barrier(0);
+  // Value scales of the run's first kRunScan tiles (for the P scale fv),
+  // also ahead of the tile loads so that their wait leaves those in flight.
+  constexpr int kRunScan = 8;
+  float vs_run[kRunScan];
+#pragma unroll
+  for (int k = 0; k < kRunScan; ++k) {
+    const int t = (w_begin + k) * kTile + lane;
+    const float v = half_bits_to_f32(vsbase[t < a.nq ? t : a.nq - 1]);
+    vs_run[k] = t < q_end * kTile ? v : INFINITY;
+  }
+  __builtin_amdgcn_sched_barrier(0);
   int tile = w_begin;
   TileRegs bufA, bufB;
   ld_seg = w_begin / a.tiles_per_seg;
   ld_pos = w_begin - ld_seg * a.tiles_per_seg;
   load_tile(w_begin, bufA);                   // nothing is read if the wave has no tiles
-  float vs_run[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int t = (w_begin + k) * kTile + lane;
-    const float v = half_bits_to_f32(vsbase[t < a.nq ? t : a.nq - 1]);
-    vs_run[k] = t < q_end * kTile ? v : INFINITY;
-  }
 #pragma unroll
   for (int k = 0; k < NQ; ++k) {
     const int i = tid + k * kThreads;
@@ -1051,13 +1055,14 @@ void decode_i8_kernel(DecodeArgs a) {
     // Fv from the largest 1 / vscale of the run.
     float vsr_max = 0.0f;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) vsr_max = fmaxf(vsr_max, fast_rcp(fmaxf(vs_run[k], g.eps)));
-    for (int t0 = (w_begin + 4) * kTile; t0 < q_end * kTile; t0 += 4 * kTile) {
+    for (int k = 0; k < kRunScan; ++k) vsr_max = fmaxf(vsr_max, fast_rcp(fmaxf(vs_run[k], g.eps)));
+    for (int t0 = (w_begin + kRunScan) * kTile; t0 < q_end * kTile; t0 += 4 * kTile) {
       float vs4[4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
+      for (int k = 0; k < 4; ++k) {     // clamped index: four unconditional loads in flight together
         const int t = t0 + k * kTile + lane;
-        vs4[k] = t < q_end * kTile ? half_bits_to_f32(vsbase[t]) : INFINITY;
+        const float v = half_bits_to_f32(vsbase[t < a.nq ? t : a.nq - 1]);
+        vs4[k] = t < q_end * kTile ? v : INFINITY;
       }
 #pragma unroll
       for (int k = 0; k < 4; ++k) vsr_max = fmaxf(vsr_max, fast_rcp(fmaxf(vs4[k], g.eps)));
