@@ -260,18 +260,38 @@ __global__ __launch_bounds__(D) void merge_kernel(DecodeArgs a) {
     }
   };
   load_batch(0);
-  for (int sk = c; sk < S; sk += D) {
-    ew[sk] = pu[sk * stride + D];
-    el[sk] = pu[sk * stride + D + 1];
-  }
+  // split maxima and sums: thread c reads split c (clamped, unconditional, in
+  // flight with the partials); splits beyond D are read further down
+  const int sk0 = c < S ? c : S - 1;
+  const float m0 = pu[sk0 * stride + D], l0 = pu[sk0 * stride + D + 1];
+  // The first kPreNew appended tokens' key and value elements are loaded with
+  // the partials (clamped indices, unconditional), so one round trip covers
+  // the merge; further tokens (up to kMaxStepNew) are read where used.
+  constexpr int kPreNew = 4;
+  uint16_t kn[kPreNew], vn[kPreNew];
   if constexpr (kNew) {
     const float qc = bf16_bits_to_f32(static_cast<const uint16_t*>(a.q)[((int64_t)b * g.H * GQA + kvh * GQA + h) * D + c]);
+#pragma unroll
+    for (int t = 0; t < kPreNew; ++t) {
+      const int64_t row = ((int64_t)unit * a.n_new + (t < a.n_new ? t : a.n_new - 1)) * D + c;
+      kn[t] = a.k_new[row];
+      vn[t] = a.v_new[row];
+    }
     for (int t = 0; t < a.n_new; ++t) {
-      float x = qc * bf16_bits_to_f32(a.k_new[((int64_t)unit * a.n_new + t) * D + c]);
+      const uint16_t kb = t < kPreNew ? kn[t < kPreNew ? t : 0] : a.k_new[((int64_t)unit * a.n_new + t) * D + c];
+      float x = qc * bf16_bits_to_f32(kb);
 #pragma unroll
       for (int off = W / 2; off > 0; off >>= 1) x += __shfl_xor(x, off, W);
       if (c % W == 0) lgw[t][c / W] = x;
     }
+  }
+  if (c < S) {
+    ew[c] = m0;
+    el[c] = l0;
+  }
+  for (int sk = c + D; sk < S; sk += D) {
+    ew[sk] = pu[sk * stride + D];
+    el[sk] = pu[sk * stride + D + 1];
   }
   __syncthreads();
   auto new_logit = [&](int t) {
@@ -301,17 +321,23 @@ __global__ __launch_bounds__(D) void merge_kernel(DecodeArgs a) {
   }
   for (int sk = 0; sk < S; ++sk) den += el[sk];
   if constexpr (kNew) {
-    for (int t = 0; t < a.n_new; ++t) {
-      const int64_t row = ((int64_t)unit * a.n_new + t) * D + c;
+    auto fold_new = [&](int t, uint16_t kb, uint16_t vb) {
       const float e = fast_exp2(new_logit(t) - M);
-      num = fmaf(e, bf16_bits_to_f32(a.v_new[row]), num);
+      num = fmaf(e, bf16_bits_to_f32(vb), num);
       den += e;
       if (h == 0) {
         int slot = a.new_slot0 + t;
         slot = slot >= g.ring ? slot - g.ring : slot;
-        a.ring_k[((int64_t)unit * g.ring + slot) * D + c] = a.k_new[row];
-        a.ring_v[((int64_t)unit * g.ring + slot) * D + c] = a.v_new[row];
+        a.ring_k[((int64_t)unit * g.ring + slot) * D + c] = kb;
+        a.ring_v[((int64_t)unit * g.ring + slot) * D + c] = vb;
       }
+    };
+#pragma unroll
+    for (int t = 0; t < kPreNew; ++t)
+      if (t < a.n_new) fold_new(t, kn[t], vn[t]);
+    for (int t = kPreNew; t < a.n_new; ++t) {
+      const int64_t row = ((int64_t)unit * a.n_new + t) * D + c;
+      fold_new(t, a.k_new[row], a.v_new[row]);
     }
   }
   a.out[((int64_t)b * g.H * GQA + kvh * GQA + h) * D + c] = num / den;
