@@ -53,6 +53,7 @@ LONG_CALL_TRAFFIC = 143_058_125      # one 131072-token layer (algorithmic 138.8
 # window copies) and one block-attention call (block_kernel + block_merge_kernel).
 APPEND_RUN_TRAFFIC = {4: 444212838, 8: 479005900}
 BLOCK_CALL_TRAFFIC = 2_008_319_181    # the cache is streamed once per query-row tile
+PAGED_CALL_TRAFFIC = None             # paged decode, ragged lengths: not yet counted
 
 
 def decode_bytes(cfg, nq: int, nt: int, q_heads: int) -> int:
@@ -303,6 +304,114 @@ def run_decode_paths(args, log):
         "dense_attention_us": round(dense_us, 3),
         "max_abs_fused_vs_path": diff,
         "algorithmic_bytes": {"fused": int(fused_bytes), "restore_path": int(path_bytes)},
+    }
+
+
+def paged_decode_bytes(cfg, states, q_heads: int) -> int:
+    """Algorithmic bytes of one paged decode call: each sequence's codes,
+    scales and window at its own length, plus the queries."""
+    H, D = cfg.kv_heads, cfg.head_dim
+    W = D * cfg.code_bits // 8
+    es = 2 if cfg.kv_dtype == 0 else 4
+    total = 0
+    for st in states:
+        nq, nt = st.quantized, st.tail
+        total += H * (2 * nq * W + nq * 2 + (nq // cfg.group) * D * 2 + 2 * nt * D * es)
+    return total + cfg.batch * q_heads * D * es
+
+
+def run_paged_decode(args, log):
+    """Decode over paged caches (block table + per-sequence lengths) on the
+    Llama-3-8B int4 shape: ragged lengths, and all sequences at 4096 beside
+    the uniform cache's decode for the cost of paging."""
+    import numpy as np
+    import torch
+
+    import kvq_synth as ks
+    from quantized_kv_cache_kvq_amd import PagedKVCache, make_config
+
+    w = ks.LLAMA3_DECODE
+    n_caches = args.caches
+    ragged = [int(x) for x in np.random.default_rng(4096).integers(256, 7937, size=w.batch)]
+    stream = torch.cuda.current_stream()
+    out = torch.empty(w.batch, w.q_heads, w.head_dim, device="cuda")
+
+    def build(lengths, seed0):
+        stride = max(lengths) // 64 + 4
+        cfg = make_config(batch=w.batch, kv_heads=w.kv_heads, head_dim=w.head_dim, capacity=stride * 64,
+                          code_bits=w.code_bits, qmax=w.qmax, residual=w.residual, group=w.group)
+        caches, qs = [], []
+        for i in range(n_caches):
+            n_pages = w.batch * stride + 8
+            perm = np.random.default_rng(seed0 + i).permutation(n_pages)[:w.batch * stride]
+            table = torch.from_numpy(perm.reshape(w.batch, stride).astype(np.int32)).cuda()
+            c = PagedKVCache(cfg, n_pages, table)
+            k, v = ks.device_kv_pair(w, max(lengths), seed=seed0 + i)
+            c.append(k, v, lengths)
+            del k, v
+            caches.append(c)
+            qs.append(ks.device_queries(w, seed=seed0 + i))
+        torch.cuda.synchronize()
+        return cfg, caches, qs
+
+    def graph_time(calls):
+        graph = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(graph, stream=cap):
+                for fn in calls:
+                    fn(cap)
+        stream.wait_stream(cap)
+        replays = max(2, args.steps // len(calls))
+        for _ in range(2):
+            graph.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(replays):
+            graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / (replays * len(calls)), replays * len(calls)
+
+    results = {}
+    for name, lengths in (("ragged", ragged), ("uniform", [w.prefill] * w.batch)):
+        cfg, caches, qs = build(lengths, 30_000 if name == "ragged" else 40_000)
+        ws = caches[0].workspace(w.q_heads)
+        calls = [(lambda st, c=c, q=q: c.decode_attn(q, out, ws, stream=st)) for c, q in zip(caches, qs)]
+        us, n = graph_time(calls)
+        nbytes = paged_decode_bytes(cfg, caches[0].states, w.q_heads)
+        results[name] = (us, nbytes, n)
+        log(f"paged decode ({name} {lengths}): {us:.2f} us per call, {nbytes / (us * 1e-6) / 1e9:.0f} GB/s")
+        del caches, qs
+        torch.cuda.empty_cache()
+    # the uniform cache at the same shape (matrix-core decode kernel)
+    cfg, dense = build_caches(w, n_caches, w.prefill + 64, log)
+    dq = [ks.device_queries(w, seed=50_000 + i) for i in range(n_caches)]
+    dws = dense[0].workspace(w.q_heads, 1)
+    dense_us, _ = graph_time([(lambda st, c=c, q=q: c.decode_attn(q, out, dws, stream=st))
+                              for c, q in zip(dense, dq)])
+    us, nbytes, n = results["ragged"]
+    gbs = nbytes / (us * 1e-6) / 1e9
+    log(f"uniform cache decode {dense_us:.2f} us per call")
+    return {
+        "metric": "paged decode-attn effective KV GB/s, Llama-3-8B shape int4, ragged lengths",
+        "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": n, "warmup": 2,
+        "ms_per_step": round(us * 1e-3, 5), "us_per_call": round(us, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32 VALU dot products + f32 softmax", "data": "synthetic (seeded, drawn on the device)",
+        "config": {"workload": "llama3_8b_paged_decode_b8_ragged_int4", "batch": w.batch,
+                   "q_heads": w.q_heads, "kv_heads": w.kv_heads, "head_dim": w.head_dim,
+                   "lengths": ragged, "page_tokens": 64, "codes": f"int{w.code_bits}",
+                   "caches_rotated": n_caches, "parallelism": "single-gpu"},
+        "bytes_per_call": int(nbytes),
+        "uniform_4096_paged_us": round(results["uniform"][0], 3),
+        "uniform_4096_paged_gbs": round(results["uniform"][1] / (results["uniform"][0] * 1e-6) / 1e9, 2),
+        "uniform_4096_unpaged_us": round(dense_us, 3),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": PAGED_CALL_TRAFFIC,
+                     "kernel": "kvq_paged_decode_attn = decode_kernel<128,4,4,paged> + merge_kernel<128,4,8>"},
     }
 
 
@@ -622,7 +731,7 @@ def main():
     ap.add_argument("--frame-tokens", type=int, default=1,
                     help="video_block: frame length of the block mask (1 = token-causal)")
     ap.add_argument("--workload", choices=["llama3_decode", "video_block", "long_decode", "append_int8",
-                                           "append_int4", "hbm_copy", "decode_paths"],
+                                           "append_int4", "hbm_copy", "decode_paths", "paged_decode"],
                     default="llama3_decode",
                     help="llama3_decode (default): the append + decode step; video_block: one "
                          "1024-query causal block against the 432000-token int2 cache; long_decode: "
@@ -630,7 +739,8 @@ def main():
                          "tokens into 4096-token caches (16 x 8 heads); hbm_copy: a plain 256 MiB "
                          "device copy (reference rate, and the known-size kernel that scales the "
                          "FETCH_SIZE / WRITE_SIZE counters); decode_paths: the decode call by "
-                         "restore-to-HBM + dense attention against the fused kernel")
+                         "restore-to-HBM + dense attention against the fused kernel; paged_decode: "
+                         "decode over paged caches (block table, ragged per-sequence lengths)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the library has no multi-GPU path; run with --gpus 1",
@@ -658,6 +768,8 @@ def main():
         res = run_long_decode(args, log)
     elif args.workload == "decode_paths":
         res = run_decode_paths(args, log)
+    elif args.workload == "paged_decode":
+        res = run_paged_decode(args, log)
     elif args.workload.startswith("append_"):
         res = run_append(args, log, 8 if args.workload == "append_int8" else 4)
     else:

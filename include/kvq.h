@@ -242,6 +242,62 @@ kvq_status kvq_block_attn(const kvq_config* cfg, const kvq_state* st, const kvq_
                           int32_t num_splits, float* out, void* workspace, size_t workspace_bytes,
                           void* stream);
 
+/* ---- Paged caches: per-sequence lengths and a block table -----------------
+ * The step after uniform lengths ("KV Cache quantization and compression",
+ * section 02: appending also means maintaining valid lengths and paged
+ * addresses; section 07: paging must cover the low-bit data and its
+ * metadata together; "KV Cache and autoregressive video generation",
+ * section 05: a block table maps each request's logical blocks to physical
+ * blocks).  The quantized prefix of every sequence lives in pages of 64
+ * tokens taken from one pool.  A page holds, for each KV head, in order:
+ *   Key codes   64 * W bytes (the tile layout of the dense cache)
+ *   Value codes 64 * W bytes
+ *   Value scales 64 fp16 (one per token)
+ *   Key scales   head_dim fp16 (the row of the segment the tile belongs to;
+ *                every page of a segment holds the same row)
+ * so kvq_paged_page_bytes = kv_heads * (128 * W + 128 + 2 * head_dim).
+ * Logical tile j of sequence b (tokens 64 j .. 64 j + 63 of its prefix) is
+ * page block_table[b * table_stride + j].  The bf16/fp32 window stays dense
+ * per sequence: k_tail / v_tail as sized by kvq_buffer_sizes.  Every
+ * sequence has its own kvq_state.  Supported: group > 0 (whole pages per
+ * segment), batch <= 64; cfg->capacity is the per-sequence limit of the
+ * prefix and must not exceed 64 * table_stride.
+ * The caller owns the pool and the table (device memory) and maps the tiles
+ * a call may write: those below ceil(quantized / 64) after it.  Page numbers
+ * outside 0 .. n_pages - 1 are clamped (wrong results, no access outside
+ * the pool). */
+typedef struct kvq_paged_cache {
+  void* pool;                 /* n_pages * kvq_paged_page_bytes bytes           */
+  int64_t n_pages;
+  const int32_t* block_table; /* device, int32 [batch, table_stride]             */
+  int32_t table_stride;
+  void* k_tail;               /* dense window, as in kvq_cache                   */
+  void* v_tail;
+} kvq_paged_cache;
+
+/* Bytes of one page.  Errors: KVQ_EINVAL. */
+kvq_status kvq_paged_page_bytes(const kvq_config* cfg, size_t* bytes);
+
+/* Append n_new[b] tokens to sequence b (host array of batch counts, each
+ * >= 0) with the same accounting as kvq_append, per sequence: each
+ * sequence flushes its own overflow into its own pages.
+ *   st           : host, kvq_state[batch], each advanced on KVQ_OK
+ *   k_new, v_new : device, kv_dtype [batch, kv_heads, max_n, head_dim],
+ *                  max_n = max(n_new); sequence b uses its first n_new[b] rows
+ * Errors: KVQ_EINVAL, KVQ_ECAPACITY, KVQ_EDEVICE; on error no state changes. */
+kvq_status kvq_paged_append(const kvq_config* cfg, kvq_state* st, const kvq_paged_cache* cache,
+                            const void* k_new, const void* v_new, const int64_t* n_new,
+                            void* stream);
+
+/* Decode attention of every sequence over its own paged cache (the same
+ * computation as kvq_decode_attn, with per-sequence lengths).  Every
+ * sequence must hold at least one token.  Arguments as kvq_decode_attn; st
+ * is kvq_state[batch]; the workspace is kvq_workspace_size(cfg, q_heads, 1).
+ * Errors: KVQ_EINVAL, KVQ_EWORKSPACE, KVQ_EDEVICE. */
+kvq_status kvq_paged_decode_attn(const kvq_config* cfg, const kvq_state* st, const kvq_paged_cache* cache,
+                                 const void* q, int32_t q_heads, float softmax_scale, int32_t num_splits,
+                                 float* out, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static string naming a status code. */
 const char* kvq_status_str(kvq_status s);
 

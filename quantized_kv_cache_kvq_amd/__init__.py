@@ -21,7 +21,8 @@ KVQ_BF16, KVQ_F32 = 0, 1
 
 EXPORTED = ("kvq_buffer_sizes", "kvq_plan_append", "kvq_append", "kvq_workspace_size",
             "kvq_workspace_init", "kvq_decode_attn", "kvq_decode_step", "kvq_block_attn",
-            "kvq_restore", "kvq_status_str")
+            "kvq_restore", "kvq_paged_page_bytes", "kvq_paged_append", "kvq_paged_decode_attn",
+            "kvq_status_str")
 
 
 class kvq_config(ctypes.Structure):
@@ -40,6 +41,11 @@ class kvq_state(ctypes.Structure):
 class kvq_cache(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "k_codes", "v_codes", "k_scale", "v_scale", "k_tail", "v_tail", "seg_index")]
+
+
+class kvq_paged_cache(ctypes.Structure):
+    _fields_ = [("pool", ctypes.c_void_p), ("n_pages", ctypes.c_int64), ("block_table", ctypes.c_void_p),
+                ("table_stride", ctypes.c_int32), ("k_tail", ctypes.c_void_p), ("v_tail", ctypes.c_void_p)]
 
 
 class kvq_sizes(ctypes.Structure):
@@ -74,6 +80,10 @@ def load() -> ctypes.CDLL:
         "kvq_append": [P(kvq_config), P(kvq_state), P(kvq_cache), vp, vp, i64, vp],
         "kvq_workspace_size": [P(kvq_config), i32, i32, P(sz)],
         "kvq_restore": [P(kvq_config), P(kvq_state), P(kvq_cache), vp, vp, i32, i64, vp],
+        "kvq_paged_page_bytes": [P(kvq_config), P(sz)],
+        "kvq_paged_append": [P(kvq_config), P(kvq_state), P(kvq_paged_cache), vp, vp, P(i64), vp],
+        "kvq_paged_decode_attn": [P(kvq_config), P(kvq_state), P(kvq_paged_cache), vp, i32, f32, i32, vp, vp,
+                                  sz, vp],
         "kvq_workspace_init": [vp, sz, vp],
         "kvq_decode_attn": [P(kvq_config), P(kvq_state), P(kvq_cache), vp, i32, f32, i32, vp, vp, sz, vp],
         "kvq_decode_step": [P(kvq_config), P(kvq_state), P(kvq_cache), vp, vp, i64, vp, i32, f32, i32,
@@ -148,6 +158,27 @@ def kvq_append(cfg, st, cache: kvq_cache, k_new, v_new, n_new: int, stream=None)
 def kvq_restore(cfg, st, cache, k_out, v_out, out_dtype: int, ld: int, stream=None):
     _check(load().kvq_restore(ctypes.byref(cfg), ctypes.byref(st), ctypes.byref(cache), _ptr(k_out),
                               _ptr(v_out), out_dtype, ld, _stream(stream)), "kvq_restore")
+
+
+def kvq_paged_page_bytes(cfg) -> int:
+    n = ctypes.c_size_t()
+    _check(load().kvq_paged_page_bytes(ctypes.byref(cfg), ctypes.byref(n)), "kvq_paged_page_bytes")
+    return n.value
+
+
+def kvq_paged_append(cfg, states, pcache, k_new, v_new, n_new, stream=None):
+    if len(n_new) != cfg.batch or len(states) != cfg.batch:
+        raise KVQError(KVQ_EINVAL, f"kvq_paged_append: need one count and one state per sequence ({cfg.batch})")
+    counts = (ctypes.c_int64 * len(n_new))(*n_new)
+    _check(load().kvq_paged_append(ctypes.byref(cfg), states, ctypes.byref(pcache), _ptr(k_new), _ptr(v_new),
+                                   counts, _stream(stream)), "kvq_paged_append")
+
+
+def kvq_paged_decode_attn(cfg, states, pcache, q, q_heads, softmax_scale, num_splits, out, ws, stream=None):
+    _check(load().kvq_paged_decode_attn(ctypes.byref(cfg), states, ctypes.byref(pcache), _ptr(q), q_heads,
+                                        softmax_scale, num_splits, _ptr(out), _ptr(ws),
+                                        ws.numel() * ws.element_size(), _stream(stream)),
+           "kvq_paged_decode_attn")
 
 
 def kvq_workspace_size(cfg, q_heads: int, tq: int) -> int:
@@ -246,3 +277,41 @@ class KVCache:
         s = 1.0 / math.sqrt(D) if softmax_scale is None else softmax_scale
         kvq_block_attn(self.cfg, self.state, self.c, q, k_blk, v_blk, q.shape[1], q.shape[2],
                        frame_tokens, s, num_splits, out, ws, stream)
+
+
+class PagedKVCache:
+    """Caller-side owner of a paged cache: the page pool, the block table
+    (int32 [batch, table_stride], device, filled by the caller) and the dense
+    windows, plus one kvq_state per sequence."""
+
+    def __init__(self, cfg: kvq_config, n_pages: int, block_table, device="cuda"):
+        import torch
+        self.cfg = cfg
+        self.page_bytes = kvq_paged_page_bytes(cfg)
+        self.pool = torch.zeros(n_pages * self.page_bytes, dtype=torch.uint8, device=device)
+        self.table = block_table
+        sizes = kvq_buffer_sizes(cfg)
+        tdt = torch.bfloat16 if cfg.kv_dtype == KVQ_BF16 else torch.float32
+        B, H, D = cfg.batch, cfg.kv_heads, cfg.head_dim
+        self.k_tail = torch.zeros(B, H, sizes.ring, D, dtype=tdt, device=device)
+        self.v_tail = torch.zeros(B, H, sizes.ring, D, dtype=tdt, device=device)
+        self.ring = sizes.ring
+        self.states = (kvq_state * B)()
+        self.c = kvq_paged_cache(_ptr(self.pool), n_pages, _ptr(block_table), block_table.shape[1],
+                                 _ptr(self.k_tail), _ptr(self.v_tail))
+
+    def append(self, k_new, v_new, n_new, stream=None):
+        """k_new, v_new [B, Hkv, max_n, D]; sequence b appends its first n_new[b] rows."""
+        kvq_paged_append(self.cfg, self.states, self.c, k_new, v_new, list(n_new), stream)
+
+    def workspace(self, q_heads: int, stream=None):
+        import torch
+        n = kvq_workspace_size(self.cfg, q_heads, 1)
+        ws = torch.empty(n // 4, dtype=torch.int32, device=self.pool.device)
+        kvq_workspace_init(ws, stream)
+        return ws
+
+    def decode_attn(self, q, out, ws, softmax_scale=None, num_splits=0, stream=None):
+        D = self.cfg.head_dim
+        s = 1.0 / math.sqrt(D) if softmax_scale is None else softmax_scale
+        kvq_paged_decode_attn(self.cfg, self.states, self.c, q, q.shape[1], s, num_splits, out, ws, stream)

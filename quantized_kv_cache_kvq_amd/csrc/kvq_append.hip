@@ -45,7 +45,23 @@ struct FlushArgs {
   int pieces;              // 16-byte pieces per token row
   int v_tiles_per_wg;      // 64-token tiles per Value workgroup
   int v_wgs;               // Value workgroups per segment
+  // Paged caches (pool != null): tile j's codes and scales go to page
+  // table[j] of this sequence; grid.y runs over its KV heads.
+  uint8_t* pool;
+  const int32_t* table;    // the sequence's row of the block table
+  int64_t n_pages;
+  int64_t page_bytes;
+  int head_bytes;          // 128 W + 128 + 2 D
+  int seq;                 // sequence index (window and input rows: seq * H + head)
 };
+
+// Base of KV head h's part of the page holding tile `tile` (paged caches);
+// out-of-range page numbers are clamped into the pool.
+__device__ __forceinline__ uint8_t* page_head(const FlushArgs& a, int h, int64_t tile) {
+  int64_t pg = a.table[tile];
+  pg = pg < 0 ? 0 : (pg >= a.n_pages ? a.n_pages - 1 : pg);
+  return a.pool + pg * a.page_bytes + (int64_t)h * a.head_bytes;
+}
 
 // Row (head_dim elements) of absolute position p of the flushed range: the
 // old tail ring if p was already cached, else the new input.
@@ -143,7 +159,12 @@ __device__ __forceinline__ void flush_keys(const FlushArgs& a, int bh, int64_t s
   if (tid < D) {
     const float m = fmaxf(fmaxf(red[0][tid], red[1][tid]), fmaxf(red[2][tid], red[3][tid]));
     const uint16_t h = f32_to_half_bits(scale_of(m, g.qmax, g.eps));
-    a.k_scale[((int64_t)bh * g.max_seg + seg) * D + tid] = h;
+    if (a.pool) {          // the segment's row in each of its pages
+      for (int64_t tl = p0 / kTile; tl < (p1 + kTile - 1) / kTile; ++tl)
+        reinterpret_cast<uint16_t*>(page_head(a, bh % g.H, tl) + 2 * kTile * g.W + 2 * kTile)[tid] = h;
+    } else {
+      a.k_scale[((int64_t)bh * g.max_seg + seg) * D + tid] = h;
+    }
     sc[tid] = half_bits_to_f32(h);
   }
   __syncthreads();
@@ -154,7 +175,7 @@ __device__ __forceinline__ void flush_keys(const FlushArgs& a, int bh, int64_t s
   const int j = (q * epp) / cpc;                 // chunk of the piece
   const int byte_in_chunk = ((q * epp - j * cpc) * BITS) / 8;
   const int bytes = epp * BITS / 8;              // 1, 2, 4 or 8
-  uint8_t* kc = a.k_codes + (int64_t)bh * g.code_stream + j * 1024 + byte_in_chunk;
+  uint8_t* kc = a.pool ? nullptr : a.k_codes + (int64_t)bh * g.code_stream + j * 1024 + byte_in_chunk;
   for (int b = 0; b < nb; ++b) {
     if (nb > 1) load_batch(b);                   // one batch: still in registers
 #pragma unroll
@@ -165,7 +186,8 @@ __device__ __forceinline__ void flush_keys(const FlushArgs& a, int bh, int64_t s
 #pragma unroll
       for (int e = 0; e < 8; ++e)
         if (e < epp) bits |= static_cast<uint64_t>(code_field(piece_elem(r[i], e, bf16), s[e], g.qmax, kMask)) << (e * BITS);
-      uint8_t* dst = kc + (p / kTile) * kTile * g.W + (p % kTile) * 16;
+      uint8_t* dst = a.pool ? page_head(a, bh % g.H, p / kTile) + j * 1024 + byte_in_chunk + (p % kTile) * 16
+                            : kc + (p / kTile) * kTile * g.W + (p % kTile) * 16;
       if (bytes == 8) *reinterpret_cast<uint2*>(dst) = make_uint2(static_cast<uint32_t>(bits), static_cast<uint32_t>(bits >> 32));
       else if (bytes == 4) *reinterpret_cast<uint32_t*>(dst) = static_cast<uint32_t>(bits);
       else if (bytes == 2) *reinterpret_cast<uint16_t*>(dst) = static_cast<uint16_t>(bits);
@@ -191,7 +213,7 @@ __device__ __forceinline__ void flush_values(const FlushArgs& a, int bh, int vw,
   const int P = a.pieces;
   const int per_tile = kGroups * P;              // units per tile
   const int units = a.v_tiles_per_wg * per_tile; // a multiple of the block size
-  uint8_t* vc = a.v_codes + (int64_t)bh * g.code_stream;
+  uint8_t* vc = a.pool ? nullptr : a.v_codes + (int64_t)bh * g.code_stream;
   for (int u = threadIdx.x; u < units; u += kFlushThreads) {
     const int q = u % P, wj = (u / P) % kGroups, tw = u / per_tile;
     const int64_t t0 = (p0 / kTile + (int64_t)vw * a.v_tiles_per_wg + tw) * kTile;
@@ -214,12 +236,16 @@ __device__ __forceinline__ void flush_values(const FlushArgs& a, int bh, int vw,
       const uint16_t h = f32_to_half_bits(scale_of(m, g.qmax, g.eps));
       s[i] = half_bits_to_f32(h);
       const int64_t t = wt + i;
-      if (q == 0 && t >= p0 && t < p1) a.v_scale[(int64_t)bh * g.C + t] = h;
+      if (q == 0 && t >= p0 && t < p1) {
+        if (a.pool) reinterpret_cast<uint16_t*>(page_head(a, bh % g.H, t / kTile) + 2 * kTile * g.W)[t % kTile] = h;
+        else a.v_scale[(int64_t)bh * g.C + t] = h;
+      }
     }
     if (wt + kTok <= p0 || wt >= p1) continue;   // no token of this word is flushed here
     uint32_t keep_mask = 0;
     if (wt < p0) keep_mask = (1u << ((p0 - wt) * BITS)) - 1u;   // unaligned start (group == 0)
-    uint32_t* dst = reinterpret_cast<uint32_t*>(vc + (t0 / kTile) * kTile * g.W + wj * 4);
+    uint32_t* dst = reinterpret_cast<uint32_t*>(
+        (a.pool ? page_head(a, bh % g.H, t0 / kTile) + kTile * g.W : vc + (t0 / kTile) * kTile * g.W) + wj * 4);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       if (e >= epp) continue;
@@ -239,7 +265,7 @@ __device__ __forceinline__ void flush_values(const FlushArgs& a, int bh, int vw,
 
 template <int BITS>
 __global__ __launch_bounds__(kFlushThreads) void flush_kernel(FlushArgs a) {
-  const int bh = blockIdx.y;
+  const int bh = a.pool ? a.seq * a.g.H + (int)blockIdx.y : (int)blockIdx.y;
   const int per_seg = 1 + a.v_wgs;
   const int64_t sl = blockIdx.x / per_seg;
   const int role = blockIdx.x % per_seg;
@@ -282,6 +308,57 @@ __global__ __launch_bounds__(256) void tail_kernel(TailArgs a) {
   if (slot >= a.ring) slot -= a.ring;
   const uint4* src = reinterpret_cast<const uint4*>(val ? a.v_new : a.k_new) +
                      ((int64_t)bh * a.n_new + a.first + j) * a.row16 + ch;
+  uint4* dst = reinterpret_cast<uint4*>(val ? a.v_tail : a.k_tail) + ((int64_t)bh * a.ring + slot) * a.row16 + ch;
+  *dst = *src;
+}
+
+// Segment geometry of a flush of `flush` tokens after nq_old, and the launch
+// (grid.y: the (batch, head) units, or a paged sequence's heads).
+void launch_flush(const Geom& g, FlushArgs& a, int64_t flush, unsigned grid_y, hipStream_t hs) {
+  a.seg_len = g.G == 0 ? flush : g.G;
+  a.pieces = g.D * (g.dtype == KVQ_BF16 ? 2 : 4) / 16;
+  const int per_tile = (kTile / (32 / g.bits)) * a.pieces;   // Value units of one tile
+  a.v_tiles_per_wg = per_tile >= kFlushThreads ? 1 : kFlushThreads / per_tile;
+  // tiles touched by one segment (group > 0 segments are tile aligned)
+  const int64_t p0 = a.nq_old, p1 = a.nq_old + a.seg_len;
+  const int64_t seg_tiles = (p1 + kTile - 1) / kTile - p0 / kTile;
+  a.v_wgs = static_cast<int>((seg_tiles + a.v_tiles_per_wg - 1) / a.v_tiles_per_wg);
+  const int64_t nseg = flush / a.seg_len;
+  dim3 grid(static_cast<unsigned>(nseg * (1 + a.v_wgs)), grid_y);
+  switch (g.bits) {
+    case 8: hipLaunchKernelGGL(flush_kernel<8>, grid, dim3(kFlushThreads), 0, hs, a); break;
+    case 4: hipLaunchKernelGGL(flush_kernel<4>, grid, dim3(kFlushThreads), 0, hs, a); break;
+    default: hipLaunchKernelGGL(flush_kernel<2>, grid, dim3(kFlushThreads), 0, hs, a); break;
+  }
+}
+
+constexpr int kMaxPagedSeqs = 64;
+
+struct PagedTailArgs {
+  const uint8_t* k_new;
+  const uint8_t* v_new;
+  uint8_t* k_tail;
+  uint8_t* v_tail;
+  int64_t max_n;      // rows per (sequence, head) of the input
+  int ring;
+  int row16;          // 16-byte chunks per token row
+  int H;
+  int first[kMaxPagedSeqs];   // per sequence: first input token that stays in the window,
+  int count[kMaxPagedSeqs];   // how many stay,
+  int slot0[kMaxPagedSeqs];   // and the window slot of the first
+};
+
+// grid (chunks of max count * row16, batch*heads, 2 = K / V): one 16-byte copy per thread.
+__global__ __launch_bounds__(256) void paged_tail_kernel(PagedTailArgs a) {
+  const int bh = blockIdx.y, b = bh / a.H;
+  const int it = blockIdx.x * blockDim.x + threadIdx.x;
+  if (it >= a.count[b] * a.row16) return;
+  const bool val = blockIdx.z == 1;
+  const int j = it / a.row16, ch = it % a.row16;
+  int slot = a.slot0[b] + j;
+  if (slot >= a.ring) slot -= a.ring;
+  const uint4* src = reinterpret_cast<const uint4*>(val ? a.v_new : a.k_new) +
+                     ((int64_t)bh * a.max_n + a.first[b] + j) * a.row16 + ch;
   uint4* dst = reinterpret_cast<uint4*>(val ? a.v_tail : a.k_tail) + ((int64_t)bh * a.ring + slot) * a.row16 + ch;
   *dst = *src;
 }
@@ -365,21 +442,13 @@ extern "C" kvq_status kvq_append(const kvq_config* cfg, kvq_state* st, const kvq
     a.nt_old = st->tail;
     a.nq_slot_old = static_cast<int>(st->quantized % g.ring);
     a.seg_base = st->segments;
-    a.seg_len = g.G == 0 ? flush : g.G;
-    a.pieces = g.D * (g.dtype == KVQ_BF16 ? 2 : 4) / 16;
-    const int per_tile = (kTile / (32 / g.bits)) * a.pieces;   // Value units of one tile
-    a.v_tiles_per_wg = per_tile >= kFlushThreads ? 1 : kFlushThreads / per_tile;
-    // tiles touched by one segment (group > 0 segments are tile aligned)
-    const int64_t p0 = a.nq_old, p1 = a.nq_old + a.seg_len;
-    const int64_t seg_tiles = (p1 + kTile - 1) / kTile - p0 / kTile;
-    a.v_wgs = static_cast<int>((seg_tiles + a.v_tiles_per_wg - 1) / a.v_tiles_per_wg);
-    const int64_t nseg = flush / a.seg_len;
-    dim3 grid(static_cast<unsigned>(nseg * (1 + a.v_wgs)), static_cast<unsigned>(g.B * g.H));
-    switch (g.bits) {
-      case 8: hipLaunchKernelGGL(flush_kernel<8>, grid, dim3(kFlushThreads), 0, hs, a); break;
-      case 4: hipLaunchKernelGGL(flush_kernel<4>, grid, dim3(kFlushThreads), 0, hs, a); break;
-      default: hipLaunchKernelGGL(flush_kernel<2>, grid, dim3(kFlushThreads), 0, hs, a); break;
-    }
+    a.pool = nullptr;
+    a.table = nullptr;
+    a.n_pages = 0;
+    a.page_bytes = 0;
+    a.head_bytes = 0;
+    a.seq = 0;
+    launch_flush(g, a, flush, static_cast<unsigned>(g.B * g.H), hs);
   }
   // New tokens at absolute positions >= next.quantized stay in the window.
   const int64_t old_end = st->quantized + st->tail;
@@ -403,5 +472,103 @@ extern "C" kvq_status kvq_append(const kvq_config* cfg, kvq_state* st, const kvq
   }
   if (hipGetLastError() != hipSuccess) return KVQ_EDEVICE;
   *st = next;
+  return KVQ_OK;
+}
+
+// ---- paged caches ------------------------------------------------------------------
+
+extern "C" kvq_status kvq_paged_page_bytes(const kvq_config* cfg, size_t* bytes) {
+  Geom g;
+  kvq_status s = validate_config(cfg, &g);
+  if (s != KVQ_OK) return s;
+  if (!bytes) return KVQ_EINVAL;
+  *bytes = static_cast<size_t>(g.H) * (2 * kTile * g.W + 2 * kTile + 2 * g.D);
+  return KVQ_OK;
+}
+
+extern "C" kvq_status kvq_paged_append(const kvq_config* cfg, kvq_state* st, const kvq_paged_cache* cache,
+                                       const void* k_new, const void* v_new, const int64_t* n_new,
+                                       void* stream) {
+  Geom g;
+  kvq_status s = validate_config(cfg, &g);
+  if (s != KVQ_OK) return s;
+  if (!st || !cache || !n_new) return KVQ_EINVAL;
+  if (g.G <= 0 || g.B > kMaxPagedSeqs) return KVQ_EINVAL;
+  if (!cache->pool || !cache->block_table || cache->n_pages < 1 || cache->table_stride < 1 ||
+      (int64_t)cache->table_stride * kTile < g.C || !cache->k_tail || !cache->v_tail)
+    return KVQ_EINVAL;
+  const int64_t page_bytes = static_cast<int64_t>(g.H) * (2 * kTile * g.W + 2 * kTile + 2 * g.D);
+  kvq_state next[kMaxPagedSeqs];
+  int64_t max_n = 0;
+  for (int b = 0; b < g.B; ++b) {
+    s = plan_append(g, &st[b], n_new[b], &next[b]);
+    if (s != KVQ_OK) return s;
+    max_n = n_new[b] > max_n ? n_new[b] : max_n;
+  }
+  if (max_n == 0) {
+    for (int b = 0; b < g.B; ++b) st[b] = next[b];
+    return KVQ_OK;
+  }
+  if (!k_new || !v_new) return KVQ_EINVAL;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  clear_stale_hip_error();
+  // each sequence flushes its own overflow into its own pages
+  for (int b = 0; b < g.B; ++b) {
+    const int64_t flush = next[b].flushed_last;
+    if (flush == 0) continue;
+    FlushArgs a;
+    a.g = g;
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.n_new = max_n;
+    a.k_tail = cache->k_tail;
+    a.v_tail = cache->v_tail;
+    a.k_codes = nullptr;
+    a.v_codes = nullptr;
+    a.k_scale = nullptr;
+    a.v_scale = nullptr;
+    a.seg_index = nullptr;
+    a.nq_old = st[b].quantized;
+    a.nt_old = st[b].tail;
+    a.nq_slot_old = static_cast<int>(st[b].quantized % g.ring);
+    a.seg_base = st[b].segments;
+    a.pool = static_cast<uint8_t*>(cache->pool);
+    a.table = cache->block_table + (int64_t)b * cache->table_stride;
+    a.n_pages = cache->n_pages;
+    a.page_bytes = page_bytes;
+    a.head_bytes = 2 * kTile * g.W + 2 * kTile + 2 * g.D;
+    a.seq = b;
+    launch_flush(g, a, flush, static_cast<unsigned>(g.H), hs);
+  }
+  // then the tokens that stay in each window
+  PagedTailArgs t;
+  t.k_new = static_cast<const uint8_t*>(k_new);
+  t.v_new = static_cast<const uint8_t*>(v_new);
+  t.k_tail = static_cast<uint8_t*>(cache->k_tail);
+  t.v_tail = static_cast<uint8_t*>(cache->v_tail);
+  t.max_n = max_n;
+  t.ring = g.ring;
+  t.row16 = g.D * (g.dtype == KVQ_BF16 ? 2 : 4) / 16;
+  t.H = g.H;
+  int max_count = 0;
+  for (int b = 0; b < kMaxPagedSeqs; ++b) {
+    t.first[b] = t.count[b] = t.slot0[b] = 0;
+    if (b >= g.B) continue;
+    const int64_t old_end = st[b].quantized + st[b].tail;
+    const int64_t first = next[b].quantized > old_end ? next[b].quantized - old_end : 0;
+    const int64_t count = n_new[b] - first;
+    if (count <= 0) continue;
+    t.first[b] = static_cast<int>(first);
+    t.count[b] = static_cast<int>(count);
+    t.slot0[b] = static_cast<int>((old_end + first) % g.ring);
+    max_count = t.count[b] > max_count ? t.count[b] : max_count;
+  }
+  if (max_count > 0) {
+    const int64_t items = (int64_t)max_count * t.row16;
+    dim3 tgrid(static_cast<unsigned>((items + 255) / 256), static_cast<unsigned>(g.B * g.H), 2);
+    hipLaunchKernelGGL(paged_tail_kernel, tgrid, dim3(256), 0, hs, t);
+  }
+  if (hipGetLastError() != hipSuccess) return KVQ_EDEVICE;
+  for (int b = 0; b < g.B; ++b) st[b] = next[b];
   return KVQ_OK;
 }

@@ -78,6 +78,21 @@ struct DecodeArgs {
 };
 
 constexpr int kMaxStepNew = 16;   // appended tokens kvq_decode_step folds into the merge
+constexpr int kMaxPagedSeqs = 64;
+
+// Paged caches: per-sequence lengths and the page of each tile.  A page
+// holds, per KV head: Key codes (64 W bytes), Value codes (64 W), Value
+// scales (64 fp16), the segment's Key-scale row (D fp16).
+struct PagedDecode {
+  const uint8_t* pool;
+  const int32_t* table;     // [batch, stride]
+  int64_t n_pages;
+  int64_t page_bytes;
+  int head_bytes;
+  int stride;
+  int nq[kMaxPagedSeqs];
+  int nt[kMaxPagedSeqs];
+};
 
 
 // ---- shared pieces ---------------------------------------------------------------
@@ -431,18 +446,34 @@ __device__ __forceinline__ WaveWork wave_work(const DecodeArgs& a, int split, in
 
 // ---- vector-ALU kernel (every shape) ------------------------------------------------
 
-template <int D, int BITS, int GQA>
-__global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
+template <int D, int BITS, int GQA, bool kPaged = false>
+__global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a0, PagedDecode pd) {
   constexpr int W = D * BITS / 8;        // bytes per token row
   constexpr int NSLOT = W / 16;          // 16-byte units per lane per tile
   constexpr int TPU = 128 / BITS;        // tokens per Value unit
   constexpr int FPW = 32 / BITS;         // fields per 32-bit word
   constexpr int TCPL = TailMap<D>::TCPL;
-  const Geom& g = a.g;
+  const Geom& g = a0.g;
   const int tid = threadIdx.x, lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int unit = blockIdx.y;
   const int split = blockIdx.x;
+  // Paged caches: this sequence's lengths and work split (uniform caches:
+  // the arguments as given).
+  DecodeArgs pa = a0;
+  if constexpr (kPaged) {
+    const int b = unit / a0.g.H;
+    pa.nq = pd.nq[b];
+    pa.nt = pd.nt[b];
+    pa.nq_slot = pa.nq % a0.g.ring;
+    pa.tiles_q = (pa.nq + kTile - 1) / kTile;
+    pa.items = pa.tiles_q + (pa.nt + kTailChunk - 1) / kTailChunk;
+    pa.tq_div = pa.tiles_q / pa.splits;
+    pa.tq_mod = pa.tiles_q % pa.splits;
+    pa.ch_div = (pa.items - pa.tiles_q) / pa.splits;
+    pa.ch_mod = (pa.items - pa.tiles_q) % pa.splits;
+  }
+  const DecodeArgs& a = pa;
 
   __shared__ float qsT[D][GQA];
   __shared__ float aq[kWaves][D][GQA];
@@ -483,15 +514,30 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   for (int tile = ww.t0; tile < ww.t1; ++tile) {
     const int t = tile * kTile + lane;
     const bool valid = t < a.nq;
-    const uint8_t* kt = kbase + (int64_t)tile * (kTile * W);
-    const uint8_t* vt = vbase + (int64_t)tile * (kTile * W);
+    const uint8_t* kt;
+    const uint8_t* vt;
+    const uint16_t* vs_tile;     // Value scales of the tile's tokens
+    const uint16_t* ks_page;     // the tile's Key-scale row (paged)
+    if constexpr (kPaged) {
+      int64_t pg = pd.table[(int64_t)(unit / g.H) * pd.stride + tile];
+      pg = pg < 0 ? 0 : (pg >= pd.n_pages ? pd.n_pages - 1 : pg);   // clamped into the pool
+      kt = pd.pool + pg * pd.page_bytes + (int64_t)(unit % g.H) * pd.head_bytes;
+      vt = kt + kTile * W;
+      vs_tile = reinterpret_cast<const uint16_t*>(kt + 2 * kTile * W);
+      ks_page = vs_tile + kTile;
+    } else {
+      kt = kbase + (int64_t)tile * (kTile * W);
+      vt = vbase + (int64_t)tile * (kTile * W);
+      vs_tile = vsbase + tile * kTile;
+      ks_page = nullptr;
+    }
     // Issue every load of the tile before any arithmetic.
     uint4 kc[NSLOT], vc[NSLOT];
 #pragma unroll
     for (int j = 0; j < NSLOT; ++j) kc[j] = *reinterpret_cast<const uint4*>(kt + j * 1024 + lane * 16);
 #pragma unroll
     for (int k = 0; k < NSLOT; ++k) vc[k] = *reinterpret_cast<const uint4*>(vt + (k * kWave + lane) * 16);
-    const float vs = valid ? half_bits_to_f32(vsbase[t]) : 1.0f;
+    const float vs = valid ? half_bits_to_f32(vs_tile[lane]) : 1.0f;
     float logit[GQA];
 #pragma unroll
     for (int h = 0; h < GQA; ++h) logit[h] = 0.0f;
@@ -500,7 +546,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
       const int seg = tile / a.tiles_per_seg;
       if (seg != cur_seg) {
         cur_seg = seg;
-        const uint16_t* ks = ksbase + seg * D;
+        const uint16_t* ks = kPaged ? ks_page : ksbase + seg * D;
         wave_lds_sync();
         for (int c = lane; c < D; c += kWave) {
           const float r = fast_rcp(fmaxf(half_bits_to_f32(ks[c]), g.eps));
@@ -1227,18 +1273,20 @@ void decode_i8_kernel(DecodeArgs a) {
 }
 
 template <int D, int BITS, int GQA>
-void launch(const DecodeArgs& a, hipStream_t s) {
+void launch(const DecodeArgs& a, const PagedDecode* pd, hipStream_t s) {
   dim3 grid(a.splits, a.g.B * a.g.H);
-  if constexpr ((BITS == 4 || BITS == 2) && D >= 64) {
+  if (pd) {
+    hipLaunchKernelGGL((decode_kernel<D, BITS, GQA, true>), grid, dim3(kThreads), 0, s, a, *pd);
+  } else if constexpr ((BITS == 4 || BITS == 2) && D >= 64) {
     // The matrix-core kernel addresses a unit's streams with 32-bit buffer offsets.
     const bool offsets32 = a.g.code_stream < (int64_t(1) << 31) &&
                            (int64_t)a.g.max_seg * a.g.D * 2 < (int64_t(1) << 31);
     if (a.g.G > 0 && a.g.dtype == KVQ_BF16 && a.tiles_q > 0 && offsets32)
       hipLaunchKernelGGL((decode_i8_kernel<D, BITS, GQA>), grid, dim3(kThreads), 0, s, a);
     else
-      hipLaunchKernelGGL((decode_kernel<D, BITS, GQA>), grid, dim3(kThreads), 0, s, a);
+      hipLaunchKernelGGL((decode_kernel<D, BITS, GQA>), grid, dim3(kThreads), 0, s, a, PagedDecode{});
   } else {
-    hipLaunchKernelGGL((decode_kernel<D, BITS, GQA>), grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((decode_kernel<D, BITS, GQA>), grid, dim3(kThreads), 0, s, a, PagedDecode{});
   }
   if (a.splits > 1 || a.force_part) {
     const dim3 mgrid(a.g.B * a.g.H, GQA);
@@ -1253,27 +1301,27 @@ void launch(const DecodeArgs& a, hipStream_t s) {
 }
 
 template <int D, int BITS>
-bool dispatch_gqa(const DecodeArgs& a, int gqa, hipStream_t s) {
+bool dispatch_gqa(const DecodeArgs& a, int gqa, const PagedDecode* pd, hipStream_t s) {
   switch (gqa) {
-    case 1: launch<D, BITS, 1>(a, s); return true;
-    case 2: launch<D, BITS, 2>(a, s); return true;
-    case 4: launch<D, BITS, 4>(a, s); return true;
-    case 8: launch<D, BITS, 8>(a, s); return true;
+    case 1: launch<D, BITS, 1>(a, pd, s); return true;
+    case 2: launch<D, BITS, 2>(a, pd, s); return true;
+    case 4: launch<D, BITS, 4>(a, pd, s); return true;
+    case 8: launch<D, BITS, 8>(a, pd, s); return true;
   }
   return false;
 }
 
-bool dispatch(const DecodeArgs& a, int gqa, hipStream_t s) {
+bool dispatch(const DecodeArgs& a, int gqa, hipStream_t s, const PagedDecode* pd = nullptr) {
   const int D = a.g.D, bits = a.g.bits;
-  if (D == 16 && bits == 8) return dispatch_gqa<16, 8>(a, gqa, s);
-  if (D == 32 && bits == 8) return dispatch_gqa<32, 8>(a, gqa, s);
-  if (D == 32 && bits == 4) return dispatch_gqa<32, 4>(a, gqa, s);
-  if (D == 64 && bits == 8) return dispatch_gqa<64, 8>(a, gqa, s);
-  if (D == 64 && bits == 4) return dispatch_gqa<64, 4>(a, gqa, s);
-  if (D == 64 && bits == 2) return dispatch_gqa<64, 2>(a, gqa, s);
-  if (D == 128 && bits == 8) return dispatch_gqa<128, 8>(a, gqa, s);
-  if (D == 128 && bits == 4) return dispatch_gqa<128, 4>(a, gqa, s);
-  if (D == 128 && bits == 2) return dispatch_gqa<128, 2>(a, gqa, s);
+  if (D == 16 && bits == 8) return dispatch_gqa<16, 8>(a, gqa, pd, s);
+  if (D == 32 && bits == 8) return dispatch_gqa<32, 8>(a, gqa, pd, s);
+  if (D == 32 && bits == 4) return dispatch_gqa<32, 4>(a, gqa, pd, s);
+  if (D == 64 && bits == 8) return dispatch_gqa<64, 8>(a, gqa, pd, s);
+  if (D == 64 && bits == 4) return dispatch_gqa<64, 4>(a, gqa, pd, s);
+  if (D == 64 && bits == 2) return dispatch_gqa<64, 2>(a, gqa, pd, s);
+  if (D == 128 && bits == 8) return dispatch_gqa<128, 8>(a, gqa, pd, s);
+  if (D == 128 && bits == 4) return dispatch_gqa<128, 4>(a, gqa, pd, s);
+  if (D == 128 && bits == 2) return dispatch_gqa<128, 2>(a, gqa, pd, s);
   return false;
 }
 
@@ -1419,4 +1467,54 @@ extern "C" kvq_status kvq_decode_step(const kvq_config* cfg, kvq_state* st, cons
   if (hipGetLastError() != hipSuccess) return KVQ_EDEVICE;
   *st = next;
   return KVQ_OK;
+}
+
+extern "C" kvq_status kvq_paged_decode_attn(const kvq_config* cfg, const kvq_state* st,
+                                            const kvq_paged_cache* cache, const void* q, int32_t q_heads,
+                                            float softmax_scale, int32_t num_splits, float* out,
+                                            void* workspace, size_t workspace_size, void* stream) {
+  Geom g;
+  kvq_status s = validate_config(cfg, &g);
+  if (s != KVQ_OK) return s;
+  if (!st || !cache || !q || !out) return KVQ_EINVAL;
+  if (g.G <= 0 || g.B > kMaxPagedSeqs) return KVQ_EINVAL;
+  if (!cache->pool || !cache->block_table || cache->n_pages < 1 || cache->table_stride < 1 ||
+      (int64_t)cache->table_stride * kTile < g.C)
+    return KVQ_EINVAL;
+  if (q_heads < 1 || q_heads % g.H != 0) return KVQ_EINVAL;
+  const int gqa = q_heads / g.H;
+  if (gqa != 1 && gqa != 2 && gqa != 4 && gqa != 8) return KVQ_EINVAL;
+  if (!(softmax_scale == softmax_scale) || num_splits < 0 || num_splits > kMaxSplits) return KVQ_EINVAL;
+  if (!workspace || workspace_size < workspace_bytes(g, q_heads, 1)) return KVQ_EWORKSPACE;
+  PagedDecode pd;
+  pd.pool = static_cast<const uint8_t*>(cache->pool);
+  pd.table = cache->block_table;
+  pd.n_pages = cache->n_pages;
+  pd.head_bytes = 2 * kTile * g.W + 2 * kTile + 2 * g.D;
+  pd.page_bytes = static_cast<int64_t>(g.H) * pd.head_bytes;
+  pd.stride = cache->table_stride;
+  int max_items = 1;
+  bool any_tail = false;
+  for (int b = 0; b < kMaxPagedSeqs; ++b) {
+    pd.nq[b] = pd.nt[b] = 0;
+    if (b >= g.B) continue;
+    const kvq_state& x = st[b];
+    if (x.quantized < 0 || x.tail < 0 || x.total != x.quantized + x.tail || x.total < 1 || x.quantized > g.C ||
+        x.tail > g.ring || x.quantized % g.G != 0)
+      return KVQ_EINVAL;
+    pd.nq[b] = static_cast<int>(x.quantized);
+    pd.nt[b] = static_cast<int>(x.tail);
+    any_tail |= x.tail > 0;
+    const int items = static_cast<int>((x.quantized + kTile - 1) / kTile + (x.tail + kTailChunk - 1) / kTailChunk);
+    max_items = items > max_items ? items : max_items;
+  }
+  if (any_tail && (!cache->k_tail || !cache->v_tail)) return KVQ_EINVAL;
+  // Uniform fields from the first sequence; the kernel replaces the
+  // per-sequence ones.
+  kvq_cache dense = {nullptr, nullptr, nullptr, nullptr, cache->k_tail, cache->v_tail, nullptr};
+  DecodeArgs a = decode_args(g, &st[0], &dense, q, softmax_scale, num_splits, out, workspace);
+  a.splits = num_splits > 0 ? num_splits : auto_splits(g.B * g.H, max_items);
+  clear_stale_hip_error();
+  if (!dispatch(a, gqa, static_cast<hipStream_t>(stream), &pd)) return KVQ_EINVAL;
+  return hipGetLastError() == hipSuccess ? KVQ_OK : KVQ_EDEVICE;
 }

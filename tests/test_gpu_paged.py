@@ -1,0 +1,157 @@
+"""GPU parity of the paged cache: per-sequence lengths and a block table.
+
+Every sequence of a paged cache must behave exactly like a cache of its own
+(the same codes, scales, window and counters as the oracle run on that
+sequence alone), with its 64-token tiles in the pages its row of the block
+table names ("KV Cache and autoregressive video generation", section 05: a
+block table maps logical blocks to physical ones; "KV Cache quantization and
+compression", section 07: the low-bit data and its metadata are paged
+together).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import kvq_synth as ks
+import quantized_kv_cache_kvq_amd as kvq
+from harness import f32, max_abs, note
+from oracle import attention as oatt
+from oracle import layout as olay
+from oracle.cache import KVQuantizationStrategies, key_scales, stacked_codes, value_scales
+
+pytestmark = pytest.mark.gpu
+needs_gpu = pytest.mark.skipif(not torch.cuda.is_available(), reason="no GPU")
+
+TOL = 2e-3
+
+
+class PagedPair:
+    """A paged device cache and one oracle state per sequence."""
+
+    def __init__(self, w, stride, spare=7, seed=0):
+        self.w = w
+        self.stride = stride
+        self.cfg = kvq.make_config(batch=w.batch, kv_heads=w.kv_heads, head_dim=w.head_dim,
+                                   capacity=stride * 64, code_bits=w.code_bits, qmax=w.qmax,
+                                   residual=w.residual, group=w.group)
+        self.n_pages = w.batch * stride + spare
+        perm = np.random.default_rng(seed).permutation(self.n_pages)[:w.batch * stride]
+        self.table_np = perm.reshape(w.batch, stride).astype(np.int32)     # shuffled pages
+        self.cache = kvq.PagedKVCache(self.cfg, self.n_pages, torch.from_numpy(self.table_np).cuda())
+        self.oracle = KVQuantizationStrategies(qmax=w.qmax, eps=1e-8, scale_storage="fp16", group=w.group)
+        self.ost = [None] * w.batch
+
+    def append(self, k, v, lens):
+        """k, v: CPU [B, H, max_n, D]; sequence b takes its first lens[b] rows."""
+        self.cache.append(k.cuda(), v.cuda(), lens)
+        for b, n in enumerate(lens):
+            self.ost[b] = self.oracle.append_and_partition(
+                self.ost[b], f32(k[b:b + 1, :, :n]), f32(v[b:b + 1, :, :n]), self.w.residual)
+
+    def decode(self, q, num_splits=0):
+        hq = q.shape[1]
+        ws = self.cache.workspace(hq)
+        out = torch.full((q.shape[0], hq, self.w.head_dim), float("nan"), device="cuda")
+        self.cache.decode_attn(q.cuda(), out, ws, num_splits=num_splits)
+        torch.cuda.synchronize()
+        return out.cpu().numpy()
+
+    def decode_ref(self, q):
+        sigma = 1.0 / math.sqrt(self.w.head_dim)
+        return np.concatenate([oatt.decode_attention(o, f32(q[b:b + 1]), sigma) for b, o in enumerate(self.ost)])
+
+    def check(self):
+        torch.cuda.synchronize()
+        w, H, D = self.w, self.w.kv_heads, self.w.head_dim
+        W = D * w.code_bits // 8
+        head = 128 * W + 128 + 2 * D
+        pool = self.cache.pool.cpu().numpy().reshape(self.n_pages, H, head)
+        k_tail = f32(self.cache.k_tail)
+        v_tail = f32(self.cache.v_tail)
+        for b, o in enumerate(self.ost):
+            st = self.cache.states[b]
+            assert (st.quantized, st.tail, st.total, st.segments) == (
+                o["quantized_tokens"], o["key_residual"].shape[-2], o["total_tokens"], len(o["key_q_segments"]))
+            nq, nt = st.quantized, st.tail
+            cap = self.stride * 64
+            ek = olay.pack_cache(stacked_codes(o, "key"), w.code_bits, cap, "key")[0]     # [H, stream]
+            ev = olay.pack_cache(stacked_codes(o, "value"), w.code_bits, cap, "value")[0]
+            eks = key_scales(o).astype(np.float16).view(np.uint16)[0]                     # [H, nseg, D]
+            evs = value_scales(o).astype(np.float16).view(np.uint16)[0]                   # [H, nq]
+            for j in range((nq + 63) // 64):
+                page = pool[self.table_np[b, j]]                                          # [H, head]
+                assert np.array_equal(page[:, :64 * W], ek[:, j * 64 * W:(j + 1) * 64 * W]), (b, j, "key codes")
+                assert np.array_equal(page[:, 64 * W:128 * W], ev[:, j * 64 * W:(j + 1) * 64 * W]), (b, j, "values")
+                n = min(64, nq - 64 * j)
+                vs = page[:, 128 * W:128 * W + 128].copy().view(np.uint16)[:, :n]
+                assert np.array_equal(vs, evs[:, 64 * j:64 * j + n]), (b, j, "value scales")
+                ksr = page[:, 128 * W + 128:].copy().view(np.uint16)
+                assert np.array_equal(ksr, eks[:, (64 * j) // w.group]), (b, j, "key scales")
+            slots = olay.ring_positions(nq, nt, self.cache.ring)
+            assert np.array_equal(k_tail[b][:, slots], o["key_residual"][0])
+            assert np.array_equal(v_tail[b][:, slots], o["value_residual"][0])
+
+
+@needs_gpu
+@pytest.mark.parametrize("bits,qmax", [(4, 7), (2, 1), (8, 127)])
+def test_paged_ragged_prefill_decode_steps(bits, qmax):
+    w = ks.small(ks.LLAMA3_DECODE, batch=3, kv_heads=2, q_heads=8, code_bits=bits, qmax=qmax)
+    p = PagedPair(w, stride=24, seed=bits)
+    s = ks.Stream(w)
+    lens = [300, 1000, 129]
+    k, v = ks.kv_pair(s, max(lens))
+    note(f"paged bits={bits} prefill {lens}")
+    p.append(k, v, lens)
+    p.check()
+    worst = 0.0
+    nq0 = [p.cache.states[b].quantized for b in range(3)]
+    for step in range(30):                 # sequence 1 reaches residual + group tokens at step 24
+        q = ks.decode_query(s)
+        got = p.decode(q)
+        worst = max(worst, max_abs(got, p.decode_ref(q)))
+        k1, v1 = ks.kv_pair(s, 1)
+        p.append(k1, v1, [1, 1, 1])
+    p.check()
+    assert p.cache.states[1].quantized > nq0[1]    # a flush inside the decode steps
+    note(f"paged bits={bits}: max-abs {worst:.3e}")
+    assert worst <= TOL
+
+
+@needs_gpu
+def test_paged_uneven_appends_flush_per_sequence():
+    """Sequences append different counts (0 included); each flushes on its own."""
+    w = ks.small(ks.LLAMA3_DECODE, batch=4, kv_heads=2, q_heads=4, head_dim=64, code_bits=4, qmax=7)
+    p = PagedPair(w, stride=20, seed=9)
+    s = ks.Stream(w)
+    plan = [[200, 0, 130, 1], [5, 90, 0, 1], [128, 128, 256, 0], [1, 1, 1, 300], [0, 60, 3, 17]]
+    for lens in plan:
+        k, v = ks.kv_pair(s, max(lens))
+        note(f"paged uneven {lens}")
+        p.append(k, v, lens)
+    p.check()
+    for splits in (0, 1, 5):
+        q = ks.decode_query(s)
+        assert max_abs(p.decode(q, num_splits=splits), p.decode_ref(q)) <= TOL
+
+
+@needs_gpu
+def test_paged_rejects_bad_calls():
+    w = ks.small(ks.LLAMA3_DECODE, batch=2, kv_heads=2, q_heads=8)
+    p = PagedPair(w, stride=4)
+    s = ks.Stream(w)
+    k, v = ks.kv_pair(s, 300)
+    big_k, big_v = ks.kv_pair(s, 600)
+    with pytest.raises(kvq.KVQError):          # sequence 0 would quantize 512 tokens into 4 pages of 64
+        p.cache.append(big_k.cuda(), big_v.cuda(), [600, 10])
+    assert all(p.cache.states[b].total == 0 for b in range(2))
+    p.append(k, v, [300, 10])
+    q = ks.decode_query(s).cuda()
+    out = torch.empty(2, 8, w.head_dim, device="cuda")
+    ws = p.cache.workspace(8)
+    with pytest.raises(kvq.KVQError):          # q_heads not a multiple of kv_heads
+        kvq.kvq_paged_decode_attn(p.cfg, p.cache.states, p.cache.c, q, 7, 0.1, 0, out, ws)
+    with pytest.raises(kvq.KVQError):          # workspace too small
+        kvq.kvq_paged_decode_attn(p.cfg, p.cache.states, p.cache.c, q, 8, 0.1, 0, out, ws[:8])
+    p.check()
