@@ -46,14 +46,15 @@ HBM_PEAK_GBS = 8000.0
 # bench.py runs, each scaled by what the counter reads for the hbm_copy
 # workload's known 256 MiB read + 256 MiB write (FETCH_SIZE x 2,
 # WRITE_SIZE x 1).  They describe the kernels in
-# profiles/decode_i8_*.md and are to be reset to None when those change.
+# profiles/decode_i8_*.md (paged: profiles/paged_decode_*.md) and are to be
+# reset to None when those change.
 DECODE_CALL_TRAFFIC = 41_417_523     # 4096-token Llama-3-8B shape (algorithmic 38.04 MB)
 LONG_CALL_TRAFFIC = 143_058_125      # one 131072-token layer (algorithmic 138.8 MB)
 # Same measurement for the other workloads: 128 appends (16 flushes + 128
 # window copies) and one block-attention call (block_kernel + block_merge_kernel).
 APPEND_RUN_TRAFFIC = {4: 444212838, 8: 479005900}
 BLOCK_CALL_TRAFFIC = 2_008_319_181    # the cache is streamed once per query-row tile
-PAGED_CALL_TRAFFIC = None             # paged decode, ragged lengths: not yet counted
+PAGED_CALL_TRAFFIC = 44_977_562       # paged decode, ragged lengths (algorithmic 41.42 MB)
 
 
 def decode_bytes(cfg, nq: int, nt: int, q_heads: int) -> int:
@@ -400,7 +401,7 @@ def run_paged_decode(args, log):
         "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": n, "warmup": 2,
         "ms_per_step": round(us * 1e-3, 5), "us_per_call": round(us, 3),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "f32 VALU dot products + f32 softmax", "data": "synthetic (seeded, drawn on the device)",
+        "dtype": "i8 MFMA (i32 acc) + f32 softmax", "data": "synthetic (seeded, drawn on the device)",
         "config": {"workload": "llama3_8b_paged_decode_b8_ragged_int4", "batch": w.batch,
                    "q_heads": w.q_heads, "kv_heads": w.kv_heads, "head_dim": w.head_dim,
                    "lengths": ragged, "page_tokens": 64, "codes": f"int{w.code_bits}",
@@ -411,7 +412,7 @@ def run_paged_decode(args, log):
         "uniform_4096_unpaged_us": round(dense_us, 3),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": PAGED_CALL_TRAFFIC,
-                     "kernel": "kvq_paged_decode_attn = decode_kernel<128,4,4,paged> + merge_kernel<128,4,8>"},
+                     "kernel": "kvq_paged_decode_attn = decode_i8_kernel<128,4,4,paged> + merge_kernel<128,4,32,paged>"},
     }
 
 

@@ -293,6 +293,9 @@ kvq_status kvq_paged_append(const kvq_config* cfg, kvq_state* st, const kvq_page
  * computation as kvq_decode_attn, with per-sequence lengths).  Every
  * sequence must hold at least one token.  Arguments as kvq_decode_attn; st
  * is kvq_state[batch]; the workspace is kvq_workspace_size(cfg, q_heads, 1).
+ * Splits follow the work: a sequence takes splits in proportion to its
+ * length; num_splits = 0 chooses the size of a split, num_splits > 0 is the
+ * split count of the longest sequence.
  * Errors: KVQ_EINVAL, KVQ_EWORKSPACE, KVQ_EDEVICE. */
 kvq_status kvq_paged_decode_attn(const kvq_config* cfg, const kvq_state* st, const kvq_paged_cache* cache,
                                  const void* q, int32_t q_heads, float softmax_scale, int32_t num_splits,

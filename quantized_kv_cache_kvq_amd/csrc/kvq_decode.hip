@@ -90,9 +90,48 @@ struct PagedDecode {
   int64_t page_bytes;
   int head_bytes;
   int stride;
+  int per_split;            // work items per split: a sequence takes ceil(items / per_split) splits
   int nq[kMaxPagedSeqs];
   int nt[kMaxPagedSeqs];
+  int wg_end[kMaxPagedSeqs];  // workgroups of sequences 0..b (H times each one's split count)
 };
+struct NoPaging {};         // uniform caches: no page table
+
+// Paged caches launch only workgroups with work, on a 1-D grid: sequence b
+// owns ids [wg_end[b - 1], wg_end[b]), H units of ws splits each, consecutive
+// ids on consecutive splits of one unit (so every XCD gets its share of
+// every unit).
+struct PagedUnit {
+  int unit, split, ws;
+};
+__device__ __forceinline__ PagedUnit paged_unit(const PagedDecode& pd, int H, int batch, int id) {
+  int b = 0;
+  while (b < batch - 1 && id >= pd.wg_end[b]) ++b;
+  const int start = b > 0 ? pd.wg_end[b - 1] : 0;
+  PagedUnit u;
+  u.ws = (pd.wg_end[b] - start) / H;
+  const int local = id - start;
+  u.unit = b * H + local / u.ws;
+  u.split = local % u.ws;
+  return u;
+}
+
+// A paged sequence's lengths and its division of work into ws splits.  The
+// partials keep the layout of the largest split count (a.splits).
+__device__ __forceinline__ DecodeArgs paged_args(const DecodeArgs& a0, const PagedDecode& pd, int unit, int ws) {
+  DecodeArgs pa = a0;
+  const int b = unit / a0.g.H;
+  pa.nq = pd.nq[b];
+  pa.nt = pd.nt[b];
+  pa.nq_slot = pa.nq % a0.g.ring;
+  pa.tiles_q = (pa.nq + kTile - 1) / kTile;
+  pa.items = pa.tiles_q + (pa.nt + kTailChunk - 1) / kTailChunk;
+  pa.tq_div = pa.tiles_q / ws;
+  pa.tq_mod = pa.tiles_q % ws;
+  pa.ch_div = (pa.items - pa.tiles_q) / ws;
+  pa.ch_mod = (pa.items - pa.tiles_q) % ws;
+  return pa;
+}
 
 
 // ---- shared pieces ---------------------------------------------------------------
@@ -254,16 +293,17 @@ __device__ __forceinline__ void tail_compute(const DecodeArgs& a, const TailRegs
 // Each is one more term of the softmax: its logit q . k (log2 domain) is a
 // workgroup reduction, its value row is read directly, and the workgroup of
 // query head 0 copies the keys and values into their window slots.
-template <int D, int GQA, int kBatch, bool kNew>
-__global__ __launch_bounds__(D) void merge_kernel(DecodeArgs a) {
+template <int D, int GQA, int kBatch, bool kNew, typename PD = NoPaging>
+__global__ __launch_bounds__(D) void merge_kernel(DecodeArgs a, PD pd) {
   constexpr int W = D < kWave ? D : kWave;           // lanes of one reduction
   constexpr int NW = D / W;
   const int unit = blockIdx.x, h = blockIdx.y, c = threadIdx.x;
   const Geom& g = a.g;
-  const int S = a.splits;
-  const int stride = GQA * (D + 2);                  // floats between splits
-  const float* pu = a.part + (int64_t)unit * S * stride + h * (D + 2);
   const int b = unit / g.H, kvh = unit % g.H;
+  const int stride = GQA * (D + 2);                  // floats between splits
+  const float* pu = a.part + (int64_t)unit * a.splits * stride + h * (D + 2);
+  int S = a.splits;                                  // paged: the sequence's own split count
+  if constexpr (!__is_same(PD, NoPaging)) S = (pd.wg_end[b] - (b > 0 ? pd.wg_end[b - 1] : 0)) / g.H;
   __shared__ float ew[kMaxSplits], el[kMaxSplits];
   __shared__ float lgw[kNew ? kMaxStepNew : 1][NW];  // per-wave parts of the new logits
   float v[kBatch];
@@ -456,22 +496,16 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a0, PagedDe
   const Geom& g = a0.g;
   const int tid = threadIdx.x, lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int unit = blockIdx.y;
-  const int split = blockIdx.x;
+  int unit = blockIdx.y;
+  int split = blockIdx.x;
   // Paged caches: this sequence's lengths and work split (uniform caches:
   // the arguments as given).
   DecodeArgs pa = a0;
   if constexpr (kPaged) {
-    const int b = unit / a0.g.H;
-    pa.nq = pd.nq[b];
-    pa.nt = pd.nt[b];
-    pa.nq_slot = pa.nq % a0.g.ring;
-    pa.tiles_q = (pa.nq + kTile - 1) / kTile;
-    pa.items = pa.tiles_q + (pa.nt + kTailChunk - 1) / kTailChunk;
-    pa.tq_div = pa.tiles_q / pa.splits;
-    pa.tq_mod = pa.tiles_q % pa.splits;
-    pa.ch_div = (pa.items - pa.tiles_q) / pa.splits;
-    pa.ch_mod = (pa.items - pa.tiles_q) % pa.splits;
+    const PagedUnit pu = paged_unit(pd, a0.g.H, a0.g.B, blockIdx.x);
+    unit = pu.unit;
+    split = pu.split;
+    pa = paged_args(a0, pd, unit, pu.ws);
   }
   const DecodeArgs& a = pa;
 
@@ -762,9 +796,10 @@ __device__ __forceinline__ float digits_value(const i4_t s) {
 
 // Two waves per SIMD (<= 256 registers); eight heads per KV head need the
 // register file of one wave per SIMD.
-template <int D, int BITS, int GQA>
+template <int D, int BITS, int GQA, typename PD = NoPaging>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(GQA > 4 ? 1 : 2)))
-void decode_i8_kernel(DecodeArgs a) {
+void decode_i8_kernel(DecodeArgs a0, PD pd) {
+  constexpr bool kPaged = !__is_same(PD, NoPaging);
   using F16 = Fields16<BITS>;
   using raw_t = typename F16::raw_t;
   constexpr int W = D * BITS / 8;         // bytes per token row
@@ -775,12 +810,20 @@ void decode_i8_kernel(DecodeArgs a) {
   constexpr int RPL = D / 64;             // Key-scale slots per lane in the operand build
   constexpr float kFixQ = 1047552.0f;     // 2^20 (1 - 2^-10): |round(a F)| <= 2^20
   constexpr float kFixP = 2097150.0f;     // P < 2^21: top digit <= 127
-  const Geom& g = a.g;
+  const Geom& g = a0.g;
   const int tid = threadIdx.x, lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int q4 = lane / 16, col = lane % 16;
-  const int unit = blockIdx.y;
-  const int split = blockIdx.x;
+  int unit = blockIdx.y;
+  int split = blockIdx.x;
+  DecodeArgs pa = a0;
+  if constexpr (kPaged) {
+    const PagedUnit pu = paged_unit(pd, a0.g.H, a0.g.B, blockIdx.x);
+    unit = pu.unit;
+    split = pu.split;
+    pa = paged_args(a0, pd, unit, pu.ws);
+  }
+  const DecodeArgs& a = pa;
 
   // sigma log2e q as a bf16 high part and the bf16 rounding of the remainder
   // (the window-chunk score operand), split once by the whole workgroup
@@ -867,6 +910,30 @@ void decode_i8_kernel(DecodeArgs a) {
   const __amdgpu_buffer_rsrc_t rKS = __builtin_amdgcn_make_buffer_rsrc((void*)ksbase, (short)0, g.max_seg * D * 2, kRsrcWord3);
   const __amdgpu_buffer_rsrc_t rVS = __builtin_amdgcn_make_buffer_rsrc((void*)vsbase, (short)0, g.C * 2, kRsrcWord3);
   const __amdgpu_buffer_rsrc_t rNull = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, 0, kRsrcWord3);
+  // Paged caches: lane i holds the page of the run's tile w_begin + i (a run
+  // is at most 64 tiles: the launch keeps per_split <= 4 * 64), loaded before
+  // anything else; a tile's loads go through a resource over its page's part
+  // for this KV head: Key codes at 0, Value codes at 64 W, Value scales at
+  // 128 W, the segment's Key-scale row at 128 W + 128.
+  constexpr int kPgV = kTile * W, kPgVS = 2 * kTile * W, kPgKS = 2 * kTile * W + 2 * kTile;
+  int tpages = 0;
+  if constexpr (kPaged) {
+    const int ti = w_begin + lane < pd.stride ? w_begin + lane : pd.stride - 1;
+    tpages = pd.table[(int64_t)(unit / g.H) * pd.stride + ti];
+  }
+  __builtin_amdgcn_sched_barrier(0);          // the page numbers go out first
+  auto page_rsrc = [&](int tile_, bool ok) -> __amdgpu_buffer_rsrc_t {
+    if constexpr (kPaged) {
+      int k = __builtin_amdgcn_readfirstlane(tile_ - w_begin);
+      k = k < 0 ? 0 : (k > kWave - 1 ? kWave - 1 : k);
+      int64_t pg = __builtin_amdgcn_readlane(tpages, k);
+      pg = pg < 0 ? 0 : (pg >= pd.n_pages ? pd.n_pages - 1 : pg);    // clamped into the pool
+      const uint8_t* base = pd.pool + pg * pd.page_bytes + (int64_t)(unit % g.H) * pd.head_bytes;
+      return ok ? __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, pd.head_bytes, kRsrcWord3) : rNull;
+    } else {
+      return rNull;
+    }
+  };
   // Per-lane byte offsets inside a tile (loop invariant); the tile's own
   // offset travels in the scalar offset of each load, so a tile's loads need
   // no per-tile vector arithmetic (and no temporaries that alias the
@@ -898,13 +965,24 @@ void decode_i8_kernel(DecodeArgs a) {
     r.new_seg = tile == w_begin || ld_pos == 0;
     // scales first: the code words, issued last, are what a wait for the
     // newest loads has to cover
-    const __amdgpu_buffer_rsrc_t rks = ok ? rKS : rNull;
-    const __amdgpu_buffer_rsrc_t rvs = ok ? rVS : rNull;
-    const __amdgpu_buffer_rsrc_t rk = ok ? rK : rNull;
-    const __amdgpu_buffer_rsrc_t rv = ok ? rV : rNull;
-    const int kso = ok ? seg * (D * 2) : 0;
-    const int vso = ok ? tile * (kTile * 2) : 0;
-    const int to = ok ? tile * (kTile * W) : 0;
+    __amdgpu_buffer_rsrc_t rks, rvs, rk, rv;
+    int kso, vso, to, vto;
+    if constexpr (kPaged) {
+      rks = rvs = rk = rv = page_rsrc(tile, ok);
+      kso = kPgKS;
+      vso = kPgVS;
+      to = 0;
+      vto = kPgV;
+    } else {
+      rks = ok ? rKS : rNull;
+      rvs = ok ? rVS : rNull;
+      rk = ok ? rK : rNull;
+      rv = ok ? rV : rNull;
+      kso = ok ? seg * (D * 2) : 0;
+      vso = ok ? tile * (kTile * 2) : 0;
+      to = ok ? tile * (kTile * W) : 0;
+      vto = to;
+    }
 #pragma unroll
     for (int i = 0; i < RPL; ++i) r.ks[i] = __builtin_amdgcn_raw_buffer_load_b16(rks, ksoffv[i], kso, 0);
 #pragma unroll
@@ -914,7 +992,7 @@ void decode_i8_kernel(DecodeArgs a) {
 #pragma unroll
       for (int mk = 0; mk < MK; ++mk) r.kw[gg][mk] = ld_raw(rk, koffv[gg] + mk * kMkBytes, to);
 #pragma unroll
-    for (int n = 0; n < NV; ++n) r.vw[n] = ld_raw(rv, voff + n * 16 * (8 * BITS), to);
+    for (int n = 0; n < NV; ++n) r.vw[n] = ld_raw(rv, voff + n * 16 * (8 * BITS), vto);
     if (++ld_pos == a.tiles_per_seg) {
       ld_pos = 0;
       ++ld_seg;
@@ -1065,7 +1143,13 @@ void decode_i8_kernel(DecodeArgs a) {
 #pragma unroll
   for (int k = 0; k < kRunScan; ++k) {
     const int t = (w_begin + k) * kTile + lane;
-    const float v = half_bits_to_f32(vsbase[t < a.nq ? t : a.nq - 1]);
+    float v;
+    if constexpr (kPaged) {     // pages hold whole tiles
+      v = half_bits_to_f32(__builtin_amdgcn_raw_buffer_load_b16(page_rsrc(w_begin + k, w_begin + k < q_end),
+                                                                lane * 2, kPgVS, 0));
+    } else {
+      v = half_bits_to_f32(vsbase[t < a.nq ? t : a.nq - 1]);
+    }
     vs_run[k] = t < q_end * kTile ? v : INFINITY;
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -1133,7 +1217,13 @@ void decode_i8_kernel(DecodeArgs a) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) {     // clamped index: four unconditional loads in flight together
         const int t = t0 + k * kTile + lane;
-        const float v = half_bits_to_f32(vsbase[t < a.nq ? t : a.nq - 1]);
+        float v;
+        if constexpr (kPaged) {
+          const int tl = t0 / kTile + k;
+          v = half_bits_to_f32(__builtin_amdgcn_raw_buffer_load_b16(page_rsrc(tl, tl < q_end), lane * 2, kPgVS, 0));
+        } else {
+          v = half_bits_to_f32(vsbase[t < a.nq ? t : a.nq - 1]);
+        }
         vs4[k] = t < q_end * kTile ? v : INFINITY;
       }
 #pragma unroll
@@ -1276,13 +1366,25 @@ template <int D, int BITS, int GQA>
 void launch(const DecodeArgs& a, const PagedDecode* pd, hipStream_t s) {
   dim3 grid(a.splits, a.g.B * a.g.H);
   if (pd) {
-    hipLaunchKernelGGL((decode_kernel<D, BITS, GQA, true>), grid, dim3(kThreads), 0, s, a, *pd);
+    grid = dim3(pd->wg_end[a.g.B - 1], 1);   // the workgroups with work, 1-D
+    // Matrix-core kernel: a wave's run of tiles must fit its 64-lane page
+    // list.  A split holds at most per_split + 2 items (rounding of tiles and
+    // chunks), a wave at most a quarter of that, rounded up.
+    bool i8 = false;
+    if constexpr ((BITS == 4 || BITS == 2) && D >= 64)
+      i8 = a.g.dtype == KVQ_BF16 && pd->per_split + 2 <= kWaves * kWave;
+    if (i8) {
+      if constexpr ((BITS == 4 || BITS == 2) && D >= 64)
+        hipLaunchKernelGGL((decode_i8_kernel<D, BITS, GQA, PagedDecode>), grid, dim3(kThreads), 0, s, a, *pd);
+    } else {
+      hipLaunchKernelGGL((decode_kernel<D, BITS, GQA, true>), grid, dim3(kThreads), 0, s, a, *pd);
+    }
   } else if constexpr ((BITS == 4 || BITS == 2) && D >= 64) {
     // The matrix-core kernel addresses a unit's streams with 32-bit buffer offsets.
     const bool offsets32 = a.g.code_stream < (int64_t(1) << 31) &&
                            (int64_t)a.g.max_seg * a.g.D * 2 < (int64_t(1) << 31);
     if (a.g.G > 0 && a.g.dtype == KVQ_BF16 && a.tiles_q > 0 && offsets32)
-      hipLaunchKernelGGL((decode_i8_kernel<D, BITS, GQA>), grid, dim3(kThreads), 0, s, a);
+      hipLaunchKernelGGL((decode_i8_kernel<D, BITS, GQA>), grid, dim3(kThreads), 0, s, a, NoPaging{});
     else
       hipLaunchKernelGGL((decode_kernel<D, BITS, GQA>), grid, dim3(kThreads), 0, s, a, PagedDecode{});
   } else {
@@ -1290,12 +1392,15 @@ void launch(const DecodeArgs& a, const PagedDecode* pd, hipStream_t s) {
   }
   if (a.splits > 1 || a.force_part) {
     const dim3 mgrid(a.g.B * a.g.H, GQA);
-    if (a.n_new > 0) {
-      if (a.splits <= 8) hipLaunchKernelGGL((merge_kernel<D, GQA, 8, true>), mgrid, dim3(D), 0, s, a);
-      else hipLaunchKernelGGL((merge_kernel<D, GQA, 32, true>), mgrid, dim3(D), 0, s, a);
+    if (pd) {
+      if (a.splits <= 8) hipLaunchKernelGGL((merge_kernel<D, GQA, 8, false, PagedDecode>), mgrid, dim3(D), 0, s, a, *pd);
+      else hipLaunchKernelGGL((merge_kernel<D, GQA, 32, false, PagedDecode>), mgrid, dim3(D), 0, s, a, *pd);
+    } else if (a.n_new > 0) {
+      if (a.splits <= 8) hipLaunchKernelGGL((merge_kernel<D, GQA, 8, true>), mgrid, dim3(D), 0, s, a, NoPaging{});
+      else hipLaunchKernelGGL((merge_kernel<D, GQA, 32, true>), mgrid, dim3(D), 0, s, a, NoPaging{});
     } else {
-      if (a.splits <= 8) hipLaunchKernelGGL((merge_kernel<D, GQA, 8, false>), mgrid, dim3(D), 0, s, a);
-      else hipLaunchKernelGGL((merge_kernel<D, GQA, 32, false>), mgrid, dim3(D), 0, s, a);
+      if (a.splits <= 8) hipLaunchKernelGGL((merge_kernel<D, GQA, 8, false>), mgrid, dim3(D), 0, s, a, NoPaging{});
+      else hipLaunchKernelGGL((merge_kernel<D, GQA, 32, false>), mgrid, dim3(D), 0, s, a, NoPaging{});
     }
   }
 }
@@ -1494,6 +1599,7 @@ extern "C" kvq_status kvq_paged_decode_attn(const kvq_config* cfg, const kvq_sta
   pd.page_bytes = static_cast<int64_t>(g.H) * pd.head_bytes;
   pd.stride = cache->table_stride;
   int max_items = 1;
+  int64_t sum_items = 0;
   bool any_tail = false;
   for (int b = 0; b < kMaxPagedSeqs; ++b) {
     pd.nq[b] = pd.nt[b] = 0;
@@ -1507,13 +1613,46 @@ extern "C" kvq_status kvq_paged_decode_attn(const kvq_config* cfg, const kvq_sta
     any_tail |= x.tail > 0;
     const int items = static_cast<int>((x.quantized + kTile - 1) / kTile + (x.tail + kTailChunk - 1) / kTailChunk);
     max_items = items > max_items ? items : max_items;
+    sum_items += (int64_t)items * g.H;
   }
   if (any_tail && (!cache->k_tail || !cache->v_tail)) return KVQ_EINVAL;
   // Uniform fields from the first sequence; the kernel replaces the
   // per-sequence ones.
   kvq_cache dense = {nullptr, nullptr, nullptr, nullptr, cache->k_tail, cache->v_tail, nullptr};
   DecodeArgs a = decode_args(g, &st[0], &dense, q, softmax_scale, num_splits, out, workspace);
-  a.splits = num_splits > 0 ? num_splits : auto_splits(g.B * g.H, max_items);
+  // Splits sized by work: every split of every sequence gets about per_split
+  // items (window chunks count as tiles), so a long sequence takes more
+  // splits instead of setting the time for the batch.  Auto: about two
+  // workgroups per compute unit, at least four items each.
+  int per_split;
+  if (num_splits > 0) {
+    per_split = (max_items + num_splits - 1) / num_splits;
+  } else {
+    // Each sequence rounds its split count up: grow per_split until the
+    // workgroups with work fit in one round of two per compute unit.
+    const int64_t target = (sum_items + 2 * 256 - 1) / (2 * 256);
+    per_split = static_cast<int>(target < 4 ? 4 : target);
+    for (;;) {
+      int64_t wgs = 0;
+      for (int b = 0; b < g.B; ++b) {
+        const int items = static_cast<int>((st[b].quantized + kTile - 1) / kTile + (st[b].tail + kTailChunk - 1) / kTailChunk);
+        wgs += (int64_t)g.H * ((items + per_split - 1) / per_split);
+      }
+      if (wgs <= 2 * 256 || per_split >= max_items) break;
+      ++per_split;
+    }
+  }
+  if ((max_items + per_split - 1) / per_split > kMaxSplits) per_split = (max_items + kMaxSplits - 1) / kMaxSplits;
+  pd.per_split = per_split;
+  a.splits = (max_items + per_split - 1) / per_split;
+  int wg = 0;
+  for (int b = 0; b < kMaxPagedSeqs; ++b) {
+    if (b < g.B) {
+      const int items = static_cast<int>((st[b].quantized + kTile - 1) / kTile + (st[b].tail + kTailChunk - 1) / kTailChunk);
+      wg += g.H * ((items + per_split - 1) / per_split);
+    }
+    pd.wg_end[b] = wg;
+  }
   clear_stale_hip_error();
   if (!dispatch(a, gqa, static_cast<hipStream_t>(stream), &pd)) return KVQ_EINVAL;
   return hipGetLastError() == hipSuccess ? KVQ_OK : KVQ_EDEVICE;
