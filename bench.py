@@ -48,8 +48,8 @@ HBM_PEAK_GBS = 8000.0
 # WRITE_SIZE x 1).  They describe the kernels in
 # profiles/decode_i8_*.md (paged: profiles/paged_decode_*.md) and are to be
 # reset to None when those change.
-DECODE_CALL_TRAFFIC = 41_417_523     # 4096-token Llama-3-8B shape (algorithmic 38.04 MB)
-LONG_CALL_TRAFFIC = 143_058_125      # one 131072-token layer (algorithmic 138.8 MB)
+DECODE_CALL_TRAFFIC = 41_405_030     # 4096-token Llama-3-8B shape (algorithmic 38.04 MB)
+LONG_CALL_TRAFFIC = 143_074_304      # one 131072-token layer (algorithmic 138.8 MB)
 # Same measurement for the other workloads: 128 appends (16 flushes + 128
 # window copies) and one block-attention call (block_kernel + block_merge_kernel).
 APPEND_RUN_TRAFFIC = {4: 444212838, 8: 479005900}

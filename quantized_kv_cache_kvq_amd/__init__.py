@@ -217,6 +217,33 @@ def kvq_block_attn(cfg, st, cache, q, k_blk, v_blk, tq, q_heads, frame_tokens, s
 
 # ---- device buffers (plumbing) -----------------------------------------------------
 
+def _need(t, shape, dtypes, what: str):
+    """Check a tensor handed to the library: on the device, contiguous, of the
+    given shape (None = any extent) and dtype.  The C ABI takes bare pointers
+    and trusts these sizes, so a mismatch here is an error, not a guess.  The
+    common case is one comparison chain: these checks sit in the decode loop."""
+    try:
+        if t.is_cuda and t.dtype in dtypes and t.shape == shape and t.is_contiguous():
+            return
+    except (AttributeError, TypeError):
+        pass
+    bad = None
+    if not getattr(t, "is_cuda", False):
+        bad = "a device tensor"
+    elif not t.is_contiguous():
+        bad = "contiguous"
+    elif t.dim() != len(shape) or any(e is not None and e != n for e, n in zip(shape, t.shape)):
+        bad = f"of shape {tuple('*' if e is None else e for e in shape)}, got {tuple(t.shape)}"
+    elif t.dtype not in dtypes:
+        bad = f"of dtype {' or '.join(str(d) for d in dtypes)}, got {t.dtype}"
+    if bad:
+        raise KVQError(KVQ_EINVAL, f"{what} must be {bad}")
+
+
+def _check_ws(ws, i32):
+    _need(ws, (ws.numel(),), i32, "workspace")
+
+
 class KVCache:
     """Caller-side owner of one cache's device buffers and host state."""
 
@@ -232,6 +259,7 @@ class KVCache:
         self.k_scale = alloc(B, H, cfg.max_segments, D, dtype=torch.float16, device=device)
         self.v_scale = alloc(B, H, cfg.capacity, dtype=torch.float16, device=device)
         tdt = torch.bfloat16 if cfg.kv_dtype == KVQ_BF16 else torch.float32
+        self._kvdt, self._f32, self._i32 = (tdt,), (torch.float32,), (torch.int32,)
         self.k_tail = alloc(B, H, self.sizes.ring, D, dtype=tdt, device=device)
         self.v_tail = alloc(B, H, self.sizes.ring, D, dtype=tdt, device=device)
         self.seg_index = (alloc(max(cfg.capacity, 1), dtype=torch.int32, device=device)
@@ -241,12 +269,30 @@ class KVCache:
                                                self.v_scale, self.k_tail, self.v_tail,
                                                self.seg_index)])
 
+    def _kv(self, k_new, v_new, what):
+        cfg = self.cfg
+        shape = (cfg.batch, cfg.kv_heads, k_new.shape[2] if k_new.dim() == 4 else None, cfg.head_dim)
+        _need(k_new, shape, self._kvdt, what + " keys")
+        _need(v_new, shape, self._kvdt, what + " values")
+
+    def _q_out(self, q, out, ws, what):
+        cfg = self.cfg
+        shape = (cfg.batch, q.shape[1] if q.dim() == 3 else None, cfg.head_dim)
+        _need(q, shape, self._kvdt, what + " queries")
+        _need(out, shape, self._f32, what + " output")
+        _check_ws(ws, self._i32)
+
     def append(self, k_new, v_new, stream=None):
+        self._kv(k_new, v_new, "append")
         kvq_append(self.cfg, self.state, self.c, k_new, v_new, k_new.shape[2], stream)
 
     def restore(self, k_out, v_out, stream=None):
         """Restored quantized prefix into k_out / v_out [B, Hkv, ld, D] (fp32 or bf16)."""
         import torch
+        B, H, D = self.cfg.batch, self.cfg.kv_heads, self.cfg.head_dim
+        shape = (B, H, k_out.shape[2] if k_out.dim() == 4 else None, D)
+        _need(k_out, shape, (torch.float32, torch.bfloat16), "restore keys")
+        _need(v_out, shape, (k_out.dtype,), "restore values")
         dt = KVQ_BF16 if k_out.dtype == torch.bfloat16 else KVQ_F32
         kvq_restore(self.cfg, self.state, self.c, k_out, v_out, dt, k_out.shape[2], stream)
 
@@ -260,12 +306,15 @@ class KVCache:
     def decode_attn(self, q, out, ws, softmax_scale=None, num_splits=0, stream=None):
         D = self.cfg.head_dim
         s = 1.0 / math.sqrt(D) if softmax_scale is None else softmax_scale
+        self._q_out(q, out, ws, "decode")
         kvq_decode_attn(self.cfg, self.state, self.c, q, q.shape[1], s, num_splits, out, ws, stream)
 
     def decode_step(self, k_new, v_new, q, out, ws, softmax_scale=None, num_splits=0, stream=None):
         """Append k_new/v_new [B, Hkv, n, D], then attend with q (one call)."""
         D = self.cfg.head_dim
         s = 1.0 / math.sqrt(D) if softmax_scale is None else softmax_scale
+        self._kv(k_new, v_new, "decode step")
+        self._q_out(q, out, ws, "decode step")
         kvq_decode_step(self.cfg, self.state, self.c, k_new, v_new, k_new.shape[2], q, q.shape[1], s,
                         num_splits, out, ws, stream)
 
@@ -275,6 +324,15 @@ class KVCache:
         across frames; 1 = token-causal."""
         D = self.cfg.head_dim
         s = 1.0 / math.sqrt(D) if softmax_scale is None else softmax_scale
+        B, H = self.cfg.batch, self.cfg.kv_heads
+        ok4 = q.dim() == 4
+        qshape = (B, q.shape[1] if ok4 else None, q.shape[2] if ok4 else None, D)
+        kshape = (B, qshape[1], H, D)
+        _need(q, qshape, self._kvdt, "block queries")
+        _need(k_blk, kshape, self._kvdt, "block keys")
+        _need(v_blk, kshape, self._kvdt, "block values")
+        _need(out, qshape, self._f32, "block output")
+        _check_ws(ws, self._i32)
         kvq_block_attn(self.cfg, self.state, self.c, q, k_blk, v_blk, q.shape[1], q.shape[2],
                        frame_tokens, s, num_splits, out, ws, stream)
 
@@ -287,11 +345,14 @@ class PagedKVCache:
     def __init__(self, cfg: kvq_config, n_pages: int, block_table, device="cuda"):
         import torch
         self.cfg = cfg
+        _need(block_table, (cfg.batch, block_table.shape[-1] if block_table.dim() == 2 else None),
+              (torch.int32,), "block table")
         self.page_bytes = kvq_paged_page_bytes(cfg)
         self.pool = torch.zeros(n_pages * self.page_bytes, dtype=torch.uint8, device=device)
         self.table = block_table
         sizes = kvq_buffer_sizes(cfg)
         tdt = torch.bfloat16 if cfg.kv_dtype == KVQ_BF16 else torch.float32
+        self._kvdt, self._f32, self._i32 = (tdt,), (torch.float32,), (torch.int32,)
         B, H, D = cfg.batch, cfg.kv_heads, cfg.head_dim
         self.k_tail = torch.zeros(B, H, sizes.ring, D, dtype=tdt, device=device)
         self.v_tail = torch.zeros(B, H, sizes.ring, D, dtype=tdt, device=device)
@@ -302,6 +363,13 @@ class PagedKVCache:
 
     def append(self, k_new, v_new, n_new, stream=None):
         """k_new, v_new [B, Hkv, max_n, D]; sequence b appends its first n_new[b] rows."""
+        cfg = self.cfg
+        n_new = list(n_new)
+        shape = (cfg.batch, cfg.kv_heads, k_new.shape[2] if k_new.dim() == 4 else None, cfg.head_dim)
+        _need(k_new, shape, self._kvdt, "paged append keys")
+        _need(v_new, shape, self._kvdt, "paged append values")
+        if n_new and max(n_new) > k_new.shape[2]:
+            raise KVQError(KVQ_EINVAL, f"paged append: a count exceeds the {k_new.shape[2]} rows given")
         kvq_paged_append(self.cfg, self.states, self.c, k_new, v_new, list(n_new), stream)
 
     def workspace(self, q_heads: int, stream=None):
@@ -314,4 +382,8 @@ class PagedKVCache:
     def decode_attn(self, q, out, ws, softmax_scale=None, num_splits=0, stream=None):
         D = self.cfg.head_dim
         s = 1.0 / math.sqrt(D) if softmax_scale is None else softmax_scale
+        shape = (self.cfg.batch, q.shape[1] if q.dim() == 3 else None, D)
+        _need(q, shape, self._kvdt, "paged decode queries")
+        _need(out, shape, self._f32, "paged decode output")
+        _check_ws(ws, self._i32)
         kvq_paged_decode_attn(self.cfg, self.states, self.c, q, q.shape[1], s, num_splits, out, ws, stream)

@@ -35,7 +35,8 @@ class PagedPair:
         self.stride = stride
         self.cfg = kvq.make_config(batch=w.batch, kv_heads=w.kv_heads, head_dim=w.head_dim,
                                    capacity=stride * 64, code_bits=w.code_bits, qmax=w.qmax,
-                                   residual=w.residual, group=w.group)
+                                   residual=w.residual, group=w.group,
+                                   kv_dtype=kvq.KVQ_BF16 if w.kv_dtype == "bf16" else kvq.KVQ_F32)
         self.n_pages = w.batch * stride + spare
         perm = np.random.default_rng(seed).permutation(self.n_pages)[:w.batch * stride]
         self.table_np = perm.reshape(w.batch, stride).astype(np.int32)     # shuffled pages
@@ -146,6 +147,10 @@ def test_paged_rejects_bad_calls():
     with pytest.raises(kvq.KVQError):          # sequence 0 would quantize 512 tokens into 4 pages of 64
         p.cache.append(big_k.cuda(), big_v.cuda(), [600, 10])
     assert all(p.cache.states[b].total == 0 for b in range(2))
+    with pytest.raises(kvq.KVQError):          # fp32 rows for a bf16 cache
+        p.cache.append(k.float().cuda(), v.float().cuda(), [300, 10])
+    with pytest.raises(kvq.KVQError):          # a count beyond the rows given
+        p.cache.append(k.cuda(), v.cuda(), [301, 10])
     p.append(k, v, [300, 10])
     q = ks.decode_query(s).cuda()
     out = torch.empty(2, 8, w.head_dim, device="cuda")
@@ -154,4 +159,46 @@ def test_paged_rejects_bad_calls():
         kvq.kvq_paged_decode_attn(p.cfg, p.cache.states, p.cache.c, q, 7, 0.1, 0, out, ws)
     with pytest.raises(kvq.KVQError):          # workspace too small
         kvq.kvq_paged_decode_attn(p.cfg, p.cache.states, p.cache.c, q, 8, 0.1, 0, out, ws[:8])
+    p.check()
+
+
+@needs_gpu
+@pytest.mark.parametrize("D,bits,qmax,gqa,group,kv_dtype", [
+    (64, 4, 7, 2, 64, "f32"),       # fp32 windows: the vector-ALU paged kernel
+    (64, 2, 1, 8, 128, "bf16"),     # int2, eight query heads per KV head (matrix-core kernel)
+    (32, 8, 127, 4, 64, "bf16"),    # head_dim 32 int8 (vector-ALU kernel)
+])
+def test_paged_other_shapes(D, bits, qmax, gqa, group, kv_dtype):
+    w = ks.small(ks.LLAMA3_DECODE, batch=3, kv_heads=2, q_heads=2 * gqa, head_dim=D, code_bits=bits,
+                 qmax=qmax, group=group, kv_dtype=kv_dtype)
+    p = PagedPair(w, stride=12, seed=D + bits)
+    s = ks.Stream(w)
+    lens = [500, 70, 333]
+    k, v = ks.kv_pair(s, max(lens))
+    note(f"paged D={D} bits={bits} gqa={gqa} {kv_dtype}")
+    p.append(k, v, lens)
+    for step in range(3):
+        q = ks.decode_query(s)
+        assert max_abs(p.decode(q), p.decode_ref(q)) <= TOL
+        k1, v1 = ks.kv_pair(s, 5)
+        p.append(k1, v1, [5, 0, 3])
+    p.check()
+
+
+@needs_gpu
+def test_paged_long_sequence_one_split():
+    """One split over more than 64 tiles per wave takes the vector-ALU kernel
+    (the matrix-core kernel keeps a wave's page numbers in its 64 lanes); the
+    automatic split count takes the matrix-core kernel.  Both match the oracle."""
+    w = ks.small(ks.LLAMA3_DECODE, batch=2, kv_heads=1, q_heads=4, head_dim=64)
+    p = PagedPair(w, stride=300, seed=5)
+    s = ks.Stream(w)
+    lens = [17000, 2000]
+    k, v = ks.kv_pair(s, max(lens))
+    note("paged long sequence, one split")
+    p.append(k, v, lens)
+    q = ks.decode_query(s)
+    ref = p.decode_ref(q)
+    for splits in (1, 0, 2, 40):
+        assert max_abs(p.decode(q, num_splits=splits), ref) <= TOL, splits
     p.check()

@@ -132,3 +132,32 @@ def test_plan_append_matches_oracle_accounting(R, G, sizes):
         assert nxt.flushed_last == ost["flushed_tokens"]
         assert nxt.segments == len(ost["key_q_segments"])
         st_ = nxt
+
+
+def test_binding_checks_tensors_before_the_call():
+    """The classes hand bare pointers to the library, so they check every
+    tensor's device, contiguity, shape and dtype first (no GPU needed: a host
+    tensor is refused before anything else)."""
+    import torch
+    need = kvq._need
+    with pytest.raises(kvq.KVQError, match="device tensor"):
+        need(torch.zeros(2, 3), (2, 3), (torch.float32,), "x")
+    # shape and dtype rules, checked on host tensors by skipping the device test
+    class Dev:
+        def __init__(self, t):
+            self.t = t
+            self.is_cuda = True
+            self.shape, self.dtype = t.shape, t.dtype
+
+        def is_contiguous(self):
+            return self.t.is_contiguous()
+
+        def dim(self):
+            return self.t.dim()
+    need(Dev(torch.zeros(2, 5, 3)), (2, None, 3), (torch.float32,), "x")
+    with pytest.raises(kvq.KVQError, match="contiguous"):
+        need(Dev(torch.zeros(3, 2).t()), (2, 3), (torch.float32,), "x")
+    with pytest.raises(kvq.KVQError, match="shape"):
+        need(Dev(torch.zeros(2, 5, 4)), (2, None, 3), (torch.float32,), "x")
+    with pytest.raises(kvq.KVQError, match="dtype"):
+        need(Dev(torch.zeros(2, 5, 3, dtype=torch.bfloat16)), (2, None, 3), (torch.float32,), "x")
