@@ -1399,8 +1399,10 @@ void launch(const DecodeArgs& a, const PagedDecode* pd, hipStream_t s) {
       if (a.splits <= 8) hipLaunchKernelGGL((merge_kernel<D, GQA, 8, true>), mgrid, dim3(D), 0, s, a, NoPaging{});
       else hipLaunchKernelGGL((merge_kernel<D, GQA, 32, true>), mgrid, dim3(D), 0, s, a, NoPaging{});
     } else {
+      // one round trip for the partials of up to 8, 32 or 64 splits
       if (a.splits <= 8) hipLaunchKernelGGL((merge_kernel<D, GQA, 8, false>), mgrid, dim3(D), 0, s, a, NoPaging{});
-      else hipLaunchKernelGGL((merge_kernel<D, GQA, 32, false>), mgrid, dim3(D), 0, s, a, NoPaging{});
+      else if (a.splits <= 32) hipLaunchKernelGGL((merge_kernel<D, GQA, 32, false>), mgrid, dim3(D), 0, s, a, NoPaging{});
+      else hipLaunchKernelGGL((merge_kernel<D, GQA, 64, false>), mgrid, dim3(D), 0, s, a, NoPaging{});
     }
   }
 }

@@ -59,7 +59,7 @@ def test_decode_shapes(D, bits, qmax, g):
 
 
 @needs_gpu
-@pytest.mark.parametrize("splits", [1, 2, 3, 7, 16, 40])
+@pytest.mark.parametrize("splits", [1, 2, 3, 7, 16, 40, 64, 100, 256])
 def test_decode_split_invariance(splits):
     w = ks.small(ks.LLAMA3_DECODE, batch=2, kv_heads=2, q_heads=8)
     p, s = build(w, 1500)
