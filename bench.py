@@ -385,6 +385,34 @@ def run_paged_decode(args, log):
         nbytes = paged_decode_bytes(cfg, caches[0].states, w.q_heads)
         results[name] = (us, nbytes, n)
         log(f"paged decode ({name} {lengths}): {us:.2f} us per call, {nbytes / (us * 1e-6) / 1e9:.0f} GB/s")
+        if name == "ragged":
+            # Decode steps (append one token to every sequence, attend with it
+            # visible), eager, rotating over the caches: one
+            # kvq_paged_decode_step per step, then the same as two calls.
+            s = ks.Stream(w, seed=60_000)
+            nk, nv = (t.cuda() for t in ks.kv_pair(s, 1))
+            ones = [1] * w.batch
+            for i in range(2 * len(caches)):
+                caches[i % len(caches)].decode_step(nk, nv, ones, qs[i % len(caches)], out, ws)
+            steps_k = args.steps
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(steps_k):
+                caches[i % len(caches)].decode_step(nk, nv, ones, qs[i % len(caches)], out, ws)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            step_us = e0.elapsed_time(e1) * 1e3 / steps_k
+            e0.record(stream)
+            for i in range(steps_k):
+                c = caches[i % len(caches)]
+                c.append(nk, nv, ones)
+                c.decode_attn(qs[i % len(caches)], out, ws)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            two_us = e0.elapsed_time(e1) * 1e3 / steps_k
+            results["step"] = (step_us, two_us)
+            log(f"paged decode step (ragged): {step_us:.2f} us, {two_us:.2f} us as append + decode")
         del caches, qs
         torch.cuda.empty_cache()
     # the uniform cache at the same shape (matrix-core decode kernel)
@@ -410,6 +438,8 @@ def run_paged_decode(args, log):
         "uniform_4096_paged_us": round(results["uniform"][0], 3),
         "uniform_4096_paged_gbs": round(results["uniform"][1] / (results["uniform"][0] * 1e-6) / 1e9, 2),
         "uniform_4096_unpaged_us": round(dense_us, 3),
+        "ragged_step_us": round(results["step"][0], 3),
+        "ragged_step_us_two_calls": round(results["step"][1], 3),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": PAGED_CALL_TRAFFIC,
                      "kernel": "kvq_paged_decode_attn = decode_i8_kernel<128,4,4,paged> + merge_kernel<128,4,32,paged>"},

@@ -301,6 +301,28 @@ kvq_status kvq_paged_decode_attn(const kvq_config* cfg, const kvq_state* st, con
                                  const void* q, int32_t q_heads, float softmax_scale, int32_t num_splits,
                                  float* out, void* workspace, size_t workspace_bytes, void* stream);
 
+/* One decode step of every sequence of a paged cache: append n_new[b]
+ * tokens to sequence b, then attend with q over each whole cache including
+ * them (kvq_decode_step for paged caches).  The result is that of
+ * kvq_paged_append followed by kvq_paged_decode_attn: the same pages,
+ * windows and states, and outputs equal within float rounding.  When no
+ * sequence flushes, every sequence already holds a token, each n_new[b] is
+ * at most 16 (at least one above 0) and kv_dtype is bf16, the step runs
+ * without the append's kernels: attention over the caches as they were,
+ * and the merge adds each sequence's new tokens as further softmax terms
+ * and writes them into its window.  Otherwise it runs the two calls.
+ *   st, k_new, v_new, n_new : as for kvq_paged_append
+ *   q, q_heads, softmax_scale, num_splits, out, workspace : as for
+ *                 kvq_paged_decode_attn
+ * Every precondition of both calls is checked before anything is enqueued;
+ * on error no state changes.
+ * Errors: KVQ_EINVAL, KVQ_ECAPACITY, KVQ_EWORKSPACE, KVQ_EDEVICE. */
+kvq_status kvq_paged_decode_step(const kvq_config* cfg, kvq_state* st, const kvq_paged_cache* cache,
+                                 const void* k_new, const void* v_new, const int64_t* n_new,
+                                 const void* q, int32_t q_heads, float softmax_scale,
+                                 int32_t num_splits, float* out, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
 /* Static string naming a status code. */
 const char* kvq_status_str(kvq_status s);
 

@@ -22,7 +22,7 @@ KVQ_BF16, KVQ_F32 = 0, 1
 EXPORTED = ("kvq_buffer_sizes", "kvq_plan_append", "kvq_append", "kvq_workspace_size",
             "kvq_workspace_init", "kvq_decode_attn", "kvq_decode_step", "kvq_block_attn",
             "kvq_restore", "kvq_paged_page_bytes", "kvq_paged_append", "kvq_paged_decode_attn",
-            "kvq_status_str")
+            "kvq_paged_decode_step", "kvq_status_str")
 
 
 class kvq_config(ctypes.Structure):
@@ -84,6 +84,8 @@ def load() -> ctypes.CDLL:
         "kvq_paged_append": [P(kvq_config), P(kvq_state), P(kvq_paged_cache), vp, vp, P(i64), vp],
         "kvq_paged_decode_attn": [P(kvq_config), P(kvq_state), P(kvq_paged_cache), vp, i32, f32, i32, vp, vp,
                                   sz, vp],
+        "kvq_paged_decode_step": [P(kvq_config), P(kvq_state), P(kvq_paged_cache), vp, vp, P(i64), vp, i32, f32,
+                                  i32, vp, vp, sz, vp],
         "kvq_workspace_init": [vp, sz, vp],
         "kvq_decode_attn": [P(kvq_config), P(kvq_state), P(kvq_cache), vp, i32, f32, i32, vp, vp, sz, vp],
         "kvq_decode_step": [P(kvq_config), P(kvq_state), P(kvq_cache), vp, vp, i64, vp, i32, f32, i32,
@@ -179,6 +181,16 @@ def kvq_paged_decode_attn(cfg, states, pcache, q, q_heads, softmax_scale, num_sp
                                         softmax_scale, num_splits, _ptr(out), _ptr(ws),
                                         ws.numel() * ws.element_size(), _stream(stream)),
            "kvq_paged_decode_attn")
+
+
+def kvq_paged_decode_step(cfg, states, pcache, k_new, v_new, n_new, q, q_heads, softmax_scale, num_splits, out,
+                          ws, stream=None):
+    if len(n_new) != cfg.batch or len(states) != cfg.batch:
+        raise KVQError(KVQ_EINVAL, f"kvq_paged_decode_step: need one count and one state per sequence ({cfg.batch})")
+    counts = (ctypes.c_int64 * len(n_new))(*n_new)
+    _check(load().kvq_paged_decode_step(ctypes.byref(cfg), states, ctypes.byref(pcache), _ptr(k_new), _ptr(v_new),
+                                        counts, _ptr(q), q_heads, softmax_scale, num_splits, _ptr(out), _ptr(ws),
+                                        ws.numel() * ws.element_size(), _stream(stream)), "kvq_paged_decode_step")
 
 
 def kvq_workspace_size(cfg, q_heads: int, tq: int) -> int:
@@ -387,3 +399,22 @@ class PagedKVCache:
         _need(out, shape, self._f32, "paged decode output")
         _check_ws(ws, self._i32)
         kvq_paged_decode_attn(self.cfg, self.states, self.c, q, q.shape[1], s, num_splits, out, ws, stream)
+
+    def decode_step(self, k_new, v_new, n_new, q, out, ws, softmax_scale=None, num_splits=0, stream=None):
+        """Append sequence b's first n_new[b] rows of k_new / v_new [B, Hkv, max_n, D],
+        then attend with q [B, Hq, D] over every cache (one call)."""
+        cfg = self.cfg
+        D = cfg.head_dim
+        n_new = list(n_new)
+        shape = (cfg.batch, cfg.kv_heads, k_new.shape[2] if k_new.dim() == 4 else None, D)
+        _need(k_new, shape, self._kvdt, "paged step keys")
+        _need(v_new, shape, self._kvdt, "paged step values")
+        if n_new and max(n_new) > k_new.shape[2]:
+            raise KVQError(KVQ_EINVAL, f"paged step: a count exceeds the {k_new.shape[2]} rows given")
+        qshape = (cfg.batch, q.shape[1] if q.dim() == 3 else None, D)
+        _need(q, qshape, self._kvdt, "paged step queries")
+        _need(out, qshape, self._f32, "paged step output")
+        _check_ws(ws, self._i32)
+        s = 1.0 / math.sqrt(D) if softmax_scale is None else softmax_scale
+        kvq_paged_decode_step(cfg, self.states, self.c, k_new, v_new, n_new, q, q.shape[1], s, num_splits, out, ws,
+                              stream)

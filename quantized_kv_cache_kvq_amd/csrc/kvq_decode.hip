@@ -94,6 +94,8 @@ struct PagedDecode {
   int nq[kMaxPagedSeqs];
   int nt[kMaxPagedSeqs];
   int wg_end[kMaxPagedSeqs];  // workgroups of sequences 0..b (H times each one's split count)
+  int n_new[kMaxPagedSeqs];   // decode step: tokens appended to sequence b (rows of k_new / v_new)
+  int new_slot0[kMaxPagedSeqs];  // ... and the window slot of its first one
 };
 struct NoPaging {};         // uniform caches: no page table
 
@@ -303,7 +305,16 @@ __global__ __launch_bounds__(D) void merge_kernel(DecodeArgs a, PD pd) {
   const int stride = GQA * (D + 2);                  // floats between splits
   const float* pu = a.part + (int64_t)unit * a.splits * stride + h * (D + 2);
   int S = a.splits;                                  // paged: the sequence's own split count
-  if constexpr (!__is_same(PD, NoPaging)) S = (pd.wg_end[b] - (b > 0 ? pd.wg_end[b - 1] : 0)) / g.H;
+  int nn = a.n_new;                                  // appended tokens folded in (paged: this sequence's)
+  int slot0 = a.new_slot0;
+  if constexpr (!__is_same(PD, NoPaging)) {
+    S = (pd.wg_end[b] - (b > 0 ? pd.wg_end[b - 1] : 0)) / g.H;
+    if constexpr (kNew) {
+      nn = pd.n_new[b];
+      slot0 = pd.new_slot0[b];
+    }
+  }
+  const int nst = a.n_new;                           // rows per unit in k_new / v_new
   __shared__ float ew[kMaxSplits], el[kMaxSplits];
   __shared__ float lgw[kNew ? kMaxStepNew : 1][NW];  // per-wave parts of the new logits
   float v[kBatch];
@@ -328,12 +339,13 @@ __global__ __launch_bounds__(D) void merge_kernel(DecodeArgs a, PD pd) {
     const float qc = bf16_bits_to_f32(static_cast<const uint16_t*>(a.q)[((int64_t)b * g.H * GQA + kvh * GQA + h) * D + c]);
 #pragma unroll
     for (int t = 0; t < kPreNew; ++t) {
-      const int64_t row = ((int64_t)unit * a.n_new + (t < a.n_new ? t : a.n_new - 1)) * D + c;
+      const int tc = t < nn ? t : (nn > 0 ? nn - 1 : 0);
+      const int64_t row = ((int64_t)unit * nst + tc) * D + c;
       kn[t] = a.k_new[row];
       vn[t] = a.v_new[row];
     }
-    for (int t = 0; t < a.n_new; ++t) {
-      const uint16_t kb = t < kPreNew ? kn[t < kPreNew ? t : 0] : a.k_new[((int64_t)unit * a.n_new + t) * D + c];
+    for (int t = 0; t < nn; ++t) {
+      const uint16_t kb = t < kPreNew ? kn[t < kPreNew ? t : 0] : a.k_new[((int64_t)unit * nst + t) * D + c];
       float x = qc * bf16_bits_to_f32(kb);
 #pragma unroll
       for (int off = W / 2; off > 0; off >>= 1) x += __shfl_xor(x, off, W);
@@ -358,7 +370,7 @@ __global__ __launch_bounds__(D) void merge_kernel(DecodeArgs a, PD pd) {
   float M = -INFINITY;
   for (int sk = 0; sk < S; ++sk) M = fmaxf(M, ew[sk]);   // -inf only for empty splits
   if constexpr (kNew) {
-    for (int t = 0; t < a.n_new; ++t) M = fmaxf(M, new_logit(t));
+    for (int t = 0; t < nn; ++t) M = fmaxf(M, new_logit(t));
   }
   __syncthreads();
   for (int sk = c; sk < S; sk += D) {
@@ -381,7 +393,7 @@ __global__ __launch_bounds__(D) void merge_kernel(DecodeArgs a, PD pd) {
       num = fmaf(e, bf16_bits_to_f32(vb), num);
       den += e;
       if (h == 0) {
-        int slot = a.new_slot0 + t;
+        int slot = slot0 + t;
         slot = slot >= g.ring ? slot - g.ring : slot;
         a.ring_k[((int64_t)unit * g.ring + slot) * D + c] = kb;
         a.ring_v[((int64_t)unit * g.ring + slot) * D + c] = vb;
@@ -389,9 +401,9 @@ __global__ __launch_bounds__(D) void merge_kernel(DecodeArgs a, PD pd) {
     };
 #pragma unroll
     for (int t = 0; t < kPreNew; ++t)
-      if (t < a.n_new) fold_new(t, kn[t], vn[t]);
-    for (int t = kPreNew; t < a.n_new; ++t) {
-      const int64_t row = ((int64_t)unit * a.n_new + t) * D + c;
+      if (t < nn) fold_new(t, kn[t], vn[t]);
+    for (int t = kPreNew; t < nn; ++t) {
+      const int64_t row = ((int64_t)unit * nst + t) * D + c;
       fold_new(t, a.k_new[row], a.v_new[row]);
     }
   }
@@ -1392,9 +1404,13 @@ void launch(const DecodeArgs& a, const PagedDecode* pd, hipStream_t s) {
   }
   if (a.splits > 1 || a.force_part) {
     const dim3 mgrid(a.g.B * a.g.H, GQA);
-    if (pd) {
+    if (pd && a.n_new > 0) {
+      if (a.splits <= 8) hipLaunchKernelGGL((merge_kernel<D, GQA, 8, true, PagedDecode>), mgrid, dim3(D), 0, s, a, *pd);
+      else hipLaunchKernelGGL((merge_kernel<D, GQA, 32, true, PagedDecode>), mgrid, dim3(D), 0, s, a, *pd);
+    } else if (pd) {
       if (a.splits <= 8) hipLaunchKernelGGL((merge_kernel<D, GQA, 8, false, PagedDecode>), mgrid, dim3(D), 0, s, a, *pd);
-      else hipLaunchKernelGGL((merge_kernel<D, GQA, 32, false, PagedDecode>), mgrid, dim3(D), 0, s, a, *pd);
+      else if (a.splits <= 32) hipLaunchKernelGGL((merge_kernel<D, GQA, 32, false, PagedDecode>), mgrid, dim3(D), 0, s, a, *pd);
+      else hipLaunchKernelGGL((merge_kernel<D, GQA, 64, false, PagedDecode>), mgrid, dim3(D), 0, s, a, *pd);
     } else if (a.n_new > 0) {
       if (a.splits <= 8) hipLaunchKernelGGL((merge_kernel<D, GQA, 8, true>), mgrid, dim3(D), 0, s, a, NoPaging{});
       else hipLaunchKernelGGL((merge_kernel<D, GQA, 32, true>), mgrid, dim3(D), 0, s, a, NoPaging{});
@@ -1576,13 +1592,15 @@ extern "C" kvq_status kvq_decode_step(const kvq_config* cfg, kvq_state* st, cons
   return KVQ_OK;
 }
 
-extern "C" kvq_status kvq_paged_decode_attn(const kvq_config* cfg, const kvq_state* st,
-                                            const kvq_paged_cache* cache, const void* q, int32_t q_heads,
-                                            float softmax_scale, int32_t num_splits, float* out,
-                                            void* workspace, size_t workspace_size, void* stream) {
-  Geom g;
-  kvq_status s = validate_config(cfg, &g);
-  if (s != KVQ_OK) return s;
+namespace kvq {
+namespace {
+
+// Checks of a paged decode over states st[0 .. batch) and its launch
+// arguments: per-sequence lengths, work-sized splits, workgroup ranges.
+kvq_status paged_decode_setup(const Geom& g, const kvq_state* st, const kvq_paged_cache* cache, const void* q,
+                              int32_t q_heads, float softmax_scale, int32_t num_splits, float* out,
+                              void* workspace, size_t workspace_size, DecodeArgs* a_out, PagedDecode* pd_out,
+                              int* gqa_out) {
   if (!st || !cache || !q || !out) return KVQ_EINVAL;
   if (g.G <= 0 || g.B > kMaxPagedSeqs) return KVQ_EINVAL;
   if (!cache->pool || !cache->block_table || cache->n_pages < 1 || cache->table_stride < 1 ||
@@ -1591,9 +1609,10 @@ extern "C" kvq_status kvq_paged_decode_attn(const kvq_config* cfg, const kvq_sta
   if (q_heads < 1 || q_heads % g.H != 0) return KVQ_EINVAL;
   const int gqa = q_heads / g.H;
   if (gqa != 1 && gqa != 2 && gqa != 4 && gqa != 8) return KVQ_EINVAL;
+  *gqa_out = gqa;
   if (!(softmax_scale == softmax_scale) || num_splits < 0 || num_splits > kMaxSplits) return KVQ_EINVAL;
   if (!workspace || workspace_size < workspace_bytes(g, q_heads, 1)) return KVQ_EWORKSPACE;
-  PagedDecode pd;
+  PagedDecode& pd = *pd_out;
   pd.pool = static_cast<const uint8_t*>(cache->pool);
   pd.table = cache->block_table;
   pd.n_pages = cache->n_pages;
@@ -1604,7 +1623,7 @@ extern "C" kvq_status kvq_paged_decode_attn(const kvq_config* cfg, const kvq_sta
   int64_t sum_items = 0;
   bool any_tail = false;
   for (int b = 0; b < kMaxPagedSeqs; ++b) {
-    pd.nq[b] = pd.nt[b] = 0;
+    pd.nq[b] = pd.nt[b] = pd.n_new[b] = pd.new_slot0[b] = 0;
     if (b >= g.B) continue;
     const kvq_state& x = st[b];
     if (x.quantized < 0 || x.tail < 0 || x.total != x.quantized + x.tail || x.total < 1 || x.quantized > g.C ||
@@ -1621,7 +1640,8 @@ extern "C" kvq_status kvq_paged_decode_attn(const kvq_config* cfg, const kvq_sta
   // Uniform fields from the first sequence; the kernel replaces the
   // per-sequence ones.
   kvq_cache dense = {nullptr, nullptr, nullptr, nullptr, cache->k_tail, cache->v_tail, nullptr};
-  DecodeArgs a = decode_args(g, &st[0], &dense, q, softmax_scale, num_splits, out, workspace);
+  DecodeArgs& a = *a_out;
+  a = decode_args(g, &st[0], &dense, q, softmax_scale, num_splits, out, workspace);
   // Splits sized by work: every split of every sequence gets about per_split
   // items (window chunks count as tiles), so a long sequence takes more
   // splits instead of setting the time for the batch.  Auto: about two
@@ -1655,7 +1675,85 @@ extern "C" kvq_status kvq_paged_decode_attn(const kvq_config* cfg, const kvq_sta
     }
     pd.wg_end[b] = wg;
   }
+  return KVQ_OK;
+}
+
+}  // namespace
+}  // namespace kvq
+
+extern "C" kvq_status kvq_paged_decode_attn(const kvq_config* cfg, const kvq_state* st,
+                                            const kvq_paged_cache* cache, const void* q, int32_t q_heads,
+                                            float softmax_scale, int32_t num_splits, float* out,
+                                            void* workspace, size_t workspace_size, void* stream) {
+  Geom g;
+  kvq_status s = validate_config(cfg, &g);
+  if (s != KVQ_OK) return s;
+  DecodeArgs a;
+  PagedDecode pd;
+  int gqa = 0;
+  s = paged_decode_setup(g, st, cache, q, q_heads, softmax_scale, num_splits, out, workspace, workspace_size, &a,
+                         &pd, &gqa);
+  if (s != KVQ_OK) return s;
   clear_stale_hip_error();
   if (!dispatch(a, gqa, static_cast<hipStream_t>(stream), &pd)) return KVQ_EINVAL;
   return hipGetLastError() == hipSuccess ? KVQ_OK : KVQ_EDEVICE;
+}
+
+extern "C" kvq_status kvq_paged_decode_step(const kvq_config* cfg, kvq_state* st, const kvq_paged_cache* cache,
+                                            const void* k_new, const void* v_new, const int64_t* n_new,
+                                            const void* q, int32_t q_heads, float softmax_scale,
+                                            int32_t num_splits, float* out, void* workspace,
+                                            size_t workspace_size, void* stream) {
+  Geom g;
+  kvq_status s = validate_config(cfg, &g);
+  if (s != KVQ_OK) return s;
+  if (!st || !cache || !n_new) return KVQ_EINVAL;
+  if (g.G <= 0 || g.B > kMaxPagedSeqs) return KVQ_EINVAL;
+  kvq_state next[kMaxPagedSeqs];
+  int64_t max_n = 0;
+  bool fused = g.dtype == KVQ_BF16;
+  for (int b = 0; b < g.B; ++b) {
+    s = plan_append(g, &st[b], n_new[b], &next[b]);
+    if (s != KVQ_OK) return s;
+    max_n = n_new[b] > max_n ? n_new[b] : max_n;
+    fused = fused && n_new[b] <= kMaxStepNew && next[b].flushed_last == 0 && st[b].total >= 1;
+  }
+  fused = fused && max_n >= 1;
+  // Every precondition of the attention over the post-append states, and
+  // of the append, before anything is enqueued.
+  DecodeArgs a;
+  PagedDecode pd;
+  int gqa = 0;
+  s = paged_decode_setup(g, next, cache, q, q_heads, softmax_scale, num_splits, out, workspace, workspace_size, &a,
+                         &pd, &gqa);
+  if (s != KVQ_OK) return s;
+  if (max_n > 0 && (!k_new || !v_new || !cache->k_tail || !cache->v_tail)) return KVQ_EINVAL;
+  if (!fused) {
+    s = kvq_paged_append(cfg, st, cache, k_new, v_new, n_new, stream);
+    if (s != KVQ_OK) return s;
+    return kvq_paged_decode_attn(cfg, st, cache, q, q_heads, softmax_scale, num_splits, out, workspace,
+                                 workspace_size, stream);
+  }
+  // One pass: attention over the caches as they were (every sequence holds a
+  // token, none flushes), the appended tokens folded in and written to the
+  // windows by the merge.
+  s = paged_decode_setup(g, st, cache, q, q_heads, softmax_scale, num_splits, out, workspace, workspace_size, &a,
+                         &pd, &gqa);
+  if (s != KVQ_OK) return s;
+  a.force_part = 1;
+  a.k_new = static_cast<const uint16_t*>(k_new);
+  a.v_new = static_cast<const uint16_t*>(v_new);
+  a.ring_k = static_cast<uint16_t*>(cache->k_tail);
+  a.ring_v = static_cast<uint16_t*>(cache->v_tail);
+  a.n_new = static_cast<int>(max_n);
+  a.new_slot0 = 0;
+  for (int b = 0; b < g.B; ++b) {
+    pd.n_new[b] = static_cast<int>(n_new[b]);
+    pd.new_slot0[b] = static_cast<int>((st[b].quantized + st[b].tail) % g.ring);
+  }
+  clear_stale_hip_error();
+  if (!dispatch(a, gqa, static_cast<hipStream_t>(stream), &pd)) return KVQ_EINVAL;
+  if (hipGetLastError() != hipSuccess) return KVQ_EDEVICE;
+  for (int b = 0; b < g.B; ++b) st[b] = next[b];
+  return KVQ_OK;
 }

@@ -59,6 +59,18 @@ class PagedPair:
         torch.cuda.synchronize()
         return out.cpu().numpy()
 
+    def step(self, k, v, lens, q, num_splits=0):
+        """One kvq_paged_decode_step; the oracle states advance with the same append."""
+        hq = q.shape[1]
+        ws = self.cache.workspace(hq)
+        out = torch.full((q.shape[0], hq, self.w.head_dim), float("nan"), device="cuda")
+        self.cache.decode_step(k.cuda(), v.cuda(), lens, q.cuda(), out, ws, num_splits=num_splits)
+        torch.cuda.synchronize()
+        for b, n in enumerate(lens):
+            self.ost[b] = self.oracle.append_and_partition(
+                self.ost[b], f32(k[b:b + 1, :, :n]), f32(v[b:b + 1, :, :n]), self.w.residual)
+        return out.cpu().numpy()
+
     def decode_ref(self, q):
         sigma = 1.0 / math.sqrt(self.w.head_dim)
         return np.concatenate([oatt.decode_attention(o, f32(q[b:b + 1]), sigma) for b, o in enumerate(self.ost)])
@@ -201,4 +213,70 @@ def test_paged_long_sequence_one_split():
     ref = p.decode_ref(q)
     for splits in (1, 0, 2, 40):
         assert max_abs(p.decode(q, num_splits=splits), ref) <= TOL, splits
+    p.check()
+
+
+@needs_gpu
+@pytest.mark.parametrize("bits,qmax,num_splits", [(4, 7, 0), (2, 1, 0), (4, 7, 3)])
+def test_paged_decode_step(bits, qmax, num_splits):
+    """kvq_paged_decode_step against the oracle and against kvq_paged_append +
+    kvq_paged_decode_attn on a second cache with another page shuffle: mixed
+    per-sequence counts (zeros included), steps that flush (two calls inside),
+    an all-zero step."""
+    w = ks.small(ks.LLAMA3_DECODE, batch=4, kv_heads=2, q_heads=8, code_bits=bits, qmax=qmax)
+    fused = PagedPair(w, stride=24, seed=11)
+    split = PagedPair(w, stride=24, seed=12)
+    s = ks.Stream(w)
+    lens = [300, 1000, 129, 200]
+    k, v = ks.kv_pair(s, max(lens))
+    fused.append(k, v, lens)
+    split.append(k, v, lens)
+    plan = [[1, 1, 1, 1], [0, 2, 1, 3], [16, 1, 0, 5], [1, 0, 0, 0], [0, 0, 0, 0], [3, 3, 3, 3]]
+    worst = worst_pair = 0.0
+    one_pass = flush_steps = 0
+    for i in range(36):
+        ns = plan[i % len(plan)]
+        nxt = [kvq.kvq_plan_append(fused.cfg, fused.cache.states[b], ns[b]) for b in range(4)]
+        if any(x.flushed_last for x in nxt):
+            flush_steps += 1
+        elif max(ns) > 0:
+            one_pass += 1
+        k1, v1 = ks.kv_pair(s, max(ns))
+        q = ks.decode_query(s)
+        note(f"paged step {i} bits={bits} n={ns}")
+        got = fused.step(k1, v1, ns, q, num_splits=num_splits)
+        split.append(k1, v1, ns)
+        ref2 = split.decode(q, num_splits=num_splits)
+        worst = max(worst, max_abs(got, fused.decode_ref(q)))
+        worst_pair = max(worst_pair, max_abs(got, ref2))
+    fused.check()
+    split.check()
+    note(f"paged step bits={bits}: max-abs {worst:.3e}, vs two calls {worst_pair:.3e}, "
+         f"{one_pass} one-pass steps, {flush_steps} flush steps")
+    assert worst <= TOL and worst_pair <= 1e-4
+    assert one_pass >= 20 and flush_steps >= 1
+
+
+@needs_gpu
+def test_paged_decode_step_errors_leave_states_unchanged():
+    w = ks.small(ks.LLAMA3_DECODE, batch=2, kv_heads=2, q_heads=8)
+    p = PagedPair(w, stride=8)
+    s = ks.Stream(w)
+    k, v = ks.kv_pair(s, 200)
+    p.append(k, v, [200, 150])
+    before = [(x.quantized, x.tail, x.total) for x in p.cache.states]
+    k1, v1 = ks.kv_pair(s, 1)
+    q = ks.decode_query(s).cuda()
+    out = torch.empty(2, 8, w.head_dim, device="cuda")
+    ws = p.cache.workspace(8)
+    with pytest.raises(kvq.KVQError):          # q_heads not a multiple of kv_heads
+        kvq.kvq_paged_decode_step(p.cfg, p.cache.states, p.cache.c, k1.cuda(), v1.cuda(), [1, 1], q, 7, 0.1, 0,
+                                  out, ws)
+    with pytest.raises(kvq.KVQError):          # workspace too small
+        kvq.kvq_paged_decode_step(p.cfg, p.cache.states, p.cache.c, k1.cuda(), v1.cuda(), [1, 1], q, 8, 0.1, 0,
+                                  out, ws[:8])
+    big_k, big_v = ks.kv_pair(s, 600)
+    with pytest.raises(kvq.KVQError):          # capacity: sequence 0 would quantize 640 tokens into 8 pages of 64
+        p.cache.decode_step(big_k.cuda(), big_v.cuda(), [600, 1], q, out, ws)
+    assert [(x.quantized, x.tail, x.total) for x in p.cache.states] == before
     p.check()
