@@ -301,6 +301,20 @@ kvq_status kvq_paged_decode_attn(const kvq_config* cfg, const kvq_state* st, con
                                  const void* q, int32_t q_heads, float softmax_scale, int32_t num_splits,
                                  float* out, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Block attention over paged caches (kvq_block_attn with per-sequence
+ * lengths): every sequence b gets a block of tq queries at positions
+ * N_b .. N_b + tq - 1 after its own N_b cached tokens, with the same
+ * frame mask.  Arguments as kvq_block_attn; st is kvq_state[batch] and the
+ * cache a kvq_paged_cache.  Every sequence uses the same split count (the
+ * longest sets it).  Supported: kv_dtype bf16, head_dim 64 or 128,
+ * group > 0, batch <= 64.
+ * Errors: KVQ_EINVAL, KVQ_EWORKSPACE, KVQ_EDEVICE. */
+kvq_status kvq_paged_block_attn(const kvq_config* cfg, const kvq_state* st, const kvq_paged_cache* cache,
+                                const void* q, const void* k_blk, const void* v_blk, int32_t tq,
+                                int32_t q_heads, int32_t frame_tokens, float softmax_scale,
+                                int32_t num_splits, float* out, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
 /* One decode step of every sequence of a paged cache: append n_new[b]
  * tokens to sequence b, then attend with q over each whole cache including
  * them (kvq_decode_step for paged caches).  The result is that of

@@ -22,7 +22,7 @@ KVQ_BF16, KVQ_F32 = 0, 1
 EXPORTED = ("kvq_buffer_sizes", "kvq_plan_append", "kvq_append", "kvq_workspace_size",
             "kvq_workspace_init", "kvq_decode_attn", "kvq_decode_step", "kvq_block_attn",
             "kvq_restore", "kvq_paged_page_bytes", "kvq_paged_append", "kvq_paged_decode_attn",
-            "kvq_paged_decode_step", "kvq_status_str")
+            "kvq_paged_decode_step", "kvq_paged_block_attn", "kvq_status_str")
 
 
 class kvq_config(ctypes.Structure):
@@ -84,6 +84,8 @@ def load() -> ctypes.CDLL:
         "kvq_paged_append": [P(kvq_config), P(kvq_state), P(kvq_paged_cache), vp, vp, P(i64), vp],
         "kvq_paged_decode_attn": [P(kvq_config), P(kvq_state), P(kvq_paged_cache), vp, i32, f32, i32, vp, vp,
                                   sz, vp],
+        "kvq_paged_block_attn": [P(kvq_config), P(kvq_state), P(kvq_paged_cache), vp, vp, vp, i32, i32, i32, f32,
+                                 i32, vp, vp, sz, vp],
         "kvq_paged_decode_step": [P(kvq_config), P(kvq_state), P(kvq_paged_cache), vp, vp, P(i64), vp, i32, f32,
                                   i32, vp, vp, sz, vp],
         "kvq_workspace_init": [vp, sz, vp],
@@ -181,6 +183,16 @@ def kvq_paged_decode_attn(cfg, states, pcache, q, q_heads, softmax_scale, num_sp
                                         softmax_scale, num_splits, _ptr(out), _ptr(ws),
                                         ws.numel() * ws.element_size(), _stream(stream)),
            "kvq_paged_decode_attn")
+
+
+def kvq_paged_block_attn(cfg, states, pcache, q, k_blk, v_blk, tq, q_heads, frame_tokens, softmax_scale,
+                         num_splits, out, ws, stream=None):
+    if len(states) != cfg.batch:
+        raise KVQError(KVQ_EINVAL, f"kvq_paged_block_attn: need one state per sequence ({cfg.batch})")
+    _check(load().kvq_paged_block_attn(ctypes.byref(cfg), states, ctypes.byref(pcache), _ptr(q), _ptr(k_blk),
+                                       _ptr(v_blk), tq, q_heads, frame_tokens, softmax_scale, num_splits,
+                                       _ptr(out), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "kvq_paged_block_attn")
 
 
 def kvq_paged_decode_step(cfg, states, pcache, k_new, v_new, n_new, q, q_heads, softmax_scale, num_splits, out,
@@ -384,9 +396,9 @@ class PagedKVCache:
             raise KVQError(KVQ_EINVAL, f"paged append: a count exceeds the {k_new.shape[2]} rows given")
         kvq_paged_append(self.cfg, self.states, self.c, k_new, v_new, list(n_new), stream)
 
-    def workspace(self, q_heads: int, stream=None):
+    def workspace(self, q_heads: int, tq: int = 1, stream=None):
         import torch
-        n = kvq_workspace_size(self.cfg, q_heads, 1)
+        n = kvq_workspace_size(self.cfg, q_heads, tq)
         ws = torch.empty(n // 4, dtype=torch.int32, device=self.pool.device)
         kvq_workspace_init(ws, stream)
         return ws
@@ -399,6 +411,24 @@ class PagedKVCache:
         _need(out, shape, self._f32, "paged decode output")
         _check_ws(ws, self._i32)
         kvq_paged_decode_attn(self.cfg, self.states, self.c, q, q.shape[1], s, num_splits, out, ws, stream)
+
+    def block_attn(self, q, k_blk, v_blk, out, ws, softmax_scale=None, num_splits=0, stream=None,
+                   frame_tokens=1):
+        """q [B, tq, Hq, D], k_blk / v_blk [B, tq, Hkv, D]: each sequence's block of tq
+        queries after its own cached tokens (frame mask as for KVCache.block_attn)."""
+        cfg = self.cfg
+        D, B, H = cfg.head_dim, cfg.batch, cfg.kv_heads
+        ok4 = q.dim() == 4
+        qshape = (B, q.shape[1] if ok4 else None, q.shape[2] if ok4 else None, D)
+        kshape = (B, qshape[1], H, D)
+        _need(q, qshape, self._kvdt, "paged block queries")
+        _need(k_blk, kshape, self._kvdt, "paged block keys")
+        _need(v_blk, kshape, self._kvdt, "paged block values")
+        _need(out, qshape, self._f32, "paged block output")
+        _check_ws(ws, self._i32)
+        s = 1.0 / math.sqrt(D) if softmax_scale is None else softmax_scale
+        kvq_paged_block_attn(cfg, self.states, self.c, q, k_blk, v_blk, q.shape[1], q.shape[2], frame_tokens, s,
+                             num_splits, out, ws, stream)
 
     def decode_step(self, k_new, v_new, n_new, q, out, ws, softmax_scale=None, num_splits=0, stream=None):
         """Append sequence b's first n_new[b] rows of k_new / v_new [B, Hkv, max_n, D],

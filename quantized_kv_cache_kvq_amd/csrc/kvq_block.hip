@@ -80,6 +80,23 @@ struct BlockArgs {
   int cached;               // N = nq + nt: absolute position of the block's first query
 };
 
+// Paged caches (the page layout of kvq_paged_cache): per-sequence lengths
+// and the page of each 64-token tile.  A page holds, per KV head: Key codes
+// (64 W bytes), Value codes (64 W), Value scales (64 fp16), the segment's
+// Key-scale row (D fp16).
+constexpr int kMaxBlockSeqs = 64;
+struct PagedBlock {
+  const uint8_t* pool;
+  const int32_t* table;     // [batch, stride]
+  int64_t n_pages;
+  int64_t page_bytes;
+  int head_bytes;
+  int stride;
+  int nq[kMaxBlockSeqs];
+  int nt[kMaxBlockSeqs];
+};
+struct NoPagedBlock {};     // uniform caches
+
 // Token a tile slot covers, and whether it exists (per tile kind).
 enum TileKind { kQuant = 0, kTail = 1, kOwn = 2 };
 
@@ -88,9 +105,10 @@ struct Par {                 // a compile-time flag passed to a generic lambda
   static constexpr int value = P;
 };
 
-template <int D, int BITS>
+template <int D, int BITS, typename PB = NoPagedBlock>
 __global__ __launch_bounds__(BlockShape<D>::kThreads) __attribute__((amdgpu_waves_per_eu(2)))
-void block_kernel(BlockArgs a) {
+void block_kernel(BlockArgs a0, PB pb) {
+  constexpr bool kPaged = !__is_same(PB, NoPagedBlock);
   constexpr int kBT = BlockShape<D>::kThreads;
   constexpr int kBWaves = BlockShape<D>::kWaves;
   constexpr int kRowsWG = BlockShape<D>::kRows;
@@ -104,13 +122,35 @@ void block_kernel(BlockArgs a) {
   constexpr int NTV = kTile / TPC;         // tokens per thread in the V fill
   constexpr int KW = (CG * BITS + 31) / 32;   // code words per thread (K fill)
   constexpr int VW = (NTV * BITS + 31) / 32;  // code words per thread (V fill)
-  const Geom& g = a.g;
+  const Geom& g = a0.g;
   const int tid = threadIdx.x, lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int q4 = lane / 16, col = lane % 16;
   const int unit = blockIdx.z;
   const int split = blockIdx.y;
   const int b = unit / g.H, kvh = unit % g.H;
+  // Paged caches: this sequence's own lengths (uniform caches: as given).
+  BlockArgs pa = a0;
+  if constexpr (kPaged) {
+    pa.nq = pb.nq[b];
+    pa.nt = pb.nt[b];
+    pa.nq_slot = pa.nq % g.ring;
+    pa.cached = pa.nq + pa.nt;
+    pa.tiles_q = (pa.nq + kTile - 1) / kTile;
+    pa.tiles_t = (pa.nt + kTile - 1) / kTile;
+  }
+  const BlockArgs& a = pa;
+  // Base of this KV head's part of the page of quantized tile `item`
+  // (paged); page numbers outside the pool are clamped into it.
+  auto page_head = [&](int item) -> const uint8_t* {
+    if constexpr (kPaged) {
+      int64_t pg = pb.table[(int64_t)b * pb.stride + item];
+      pg = pg < 0 ? 0 : (pg >= pb.n_pages ? pb.n_pages - 1 : pg);
+      return pb.pool + pg * pb.page_bytes + (int64_t)kvh * pb.head_bytes;
+    } else {
+      return nullptr;
+    }
+  };
   const int r0 = blockIdx.x * kRowsWG;
   const int Hq = g.H * a.gqa;
 
@@ -163,7 +203,9 @@ void block_kernel(BlockArgs a) {
   // With whole-group segments every token of a tile shares one Key-scale row:
   // its reciprocals are computed once per tile (one per thread) into rkL.
   auto seg_rk = [&](int item) {
-    const float r = fast_rcp(fmaxf(half_bits_to_f32(kscale_unit[(item * kTile / g.G) * D + tid]), g.eps));
+    const uint16_t* ksrow = kPaged ? reinterpret_cast<const uint16_t*>(page_head(item) + 2 * kTile * g.W + 2 * kTile)
+                                   : kscale_unit + (item * kTile / g.G) * D;
+    const float r = fast_rcp(fmaxf(half_bits_to_f32(ksrow[tid]), g.eps));
     const float hi = (float)(__bf16)r;
     return float2{hi, (float)(__bf16)(r - hi)};
   };
@@ -179,7 +221,7 @@ void block_kernel(BlockArgs a) {
     const int t0 = item * kTile;
     const int count = min(kTile, a.nq - t0);
     const int i = tid % kTile, grp = tid / kTile;
-    const uint8_t* kt = a.k_codes + stream + (int64_t)item * (kTile * g.W);
+    const uint8_t* kt = kPaged ? page_head(item) : a.k_codes + stream + (int64_t)item * (kTile * g.W);
     const int rb = grp * CG * BITS / 8;
 #pragma unroll
     for (int k = 0; k < KW; ++k) {
@@ -187,10 +229,13 @@ void block_kernel(BlockArgs a) {
       r.w[k] = i < count ? *reinterpret_cast<const uint32_t*>(kt + (rr / 16) * 1024 + i * 16 + rr % 16) : 0u;
     }
     const int c = tid % D, vt0 = (tid / D) * NTV;
-    const uint8_t* vt = a.v_codes + stream + (int64_t)item * (kTile * g.W) + c * (8 * BITS) + vt0 * BITS / 8;
+    const uint8_t* vt = (kPaged ? kt + kTile * g.W : a.v_codes + stream + (int64_t)item * (kTile * g.W)) +
+                        c * (8 * BITS) + vt0 * BITS / 8;
 #pragma unroll
     for (int k = 0; k < VW; ++k) r.vw[k] = *reinterpret_cast<const uint32_t*>(vt + 4 * k);
-    r.vs = tid < count ? a.v_scale[(int64_t)unit * g.C + t0 + tid] : (uint16_t)0;
+    const uint16_t* vsrow = kPaged ? reinterpret_cast<const uint16_t*>(kt + 2 * kTile * g.W)
+                                   : a.v_scale + (int64_t)unit * g.C + t0;
+    r.vs = tid < count ? vsrow[tid] : (uint16_t)0;
   };
   QRaw cur;
   if (i0 < i1 && i0 < a.tiles_q) load_qraw(i0, cur);
@@ -523,24 +568,27 @@ __global__ __launch_bounds__(kMergeThreads) void block_merge_kernel(BlockArgs a)
 }
 
 template <int D, int BITS>
-void launch_block(const BlockArgs& a, hipStream_t s) {
+void launch_block(const BlockArgs& a, const PagedBlock* pb, hipStream_t s) {
   constexpr int kRowsWG = BlockShape<D>::kRows;
   dim3 grid((a.rows + kRowsWG - 1) / kRowsWG, a.splits, a.g.B * a.g.H);
-  hipLaunchKernelGGL((block_kernel<D, BITS>), grid, dim3(BlockShape<D>::kThreads), 0, s, a);
+  if (pb)
+    hipLaunchKernelGGL((block_kernel<D, BITS, PagedBlock>), grid, dim3(BlockShape<D>::kThreads), 0, s, a, *pb);
+  else
+    hipLaunchKernelGGL((block_kernel<D, BITS>), grid, dim3(BlockShape<D>::kThreads), 0, s, a, NoPagedBlock{});
   if (a.splits > 1) {
     dim3 mg((unsigned)(((int64_t)a.rows * D + kMergeThreads - 1) / kMergeThreads), a.g.B * a.g.H);
     hipLaunchKernelGGL((block_merge_kernel<D>), mg, dim3(kMergeThreads), 0, s, a);
   }
 }
 
-bool dispatch_block(const BlockArgs& a, hipStream_t s) {
+bool dispatch_block(const BlockArgs& a, hipStream_t s, const PagedBlock* pb = nullptr) {
   const int D = a.g.D, bits = a.g.bits;
-  if (D == 128 && bits == 2) { launch_block<128, 2>(a, s); return true; }
-  if (D == 128 && bits == 4) { launch_block<128, 4>(a, s); return true; }
-  if (D == 128 && bits == 8) { launch_block<128, 8>(a, s); return true; }
-  if (D == 64 && bits == 2) { launch_block<64, 2>(a, s); return true; }
-  if (D == 64 && bits == 4) { launch_block<64, 4>(a, s); return true; }
-  if (D == 64 && bits == 8) { launch_block<64, 8>(a, s); return true; }
+  if (D == 128 && bits == 2) { launch_block<128, 2>(a, pb, s); return true; }
+  if (D == 128 && bits == 4) { launch_block<128, 4>(a, pb, s); return true; }
+  if (D == 128 && bits == 8) { launch_block<128, 8>(a, pb, s); return true; }
+  if (D == 64 && bits == 2) { launch_block<64, 2>(a, pb, s); return true; }
+  if (D == 64 && bits == 4) { launch_block<64, 4>(a, pb, s); return true; }
+  if (D == 64 && bits == 8) { launch_block<64, 8>(a, pb, s); return true; }
   return false;
 }
 
@@ -621,5 +669,92 @@ extern "C" kvq_status kvq_block_attn(const kvq_config* cfg, const kvq_state* st,
   if (row_tiles > 65535) return KVQ_EINVAL;
   clear_stale_hip_error();
   if (!dispatch_block(a, static_cast<hipStream_t>(stream))) return KVQ_EINVAL;
+  return hipGetLastError() == hipSuccess ? KVQ_OK : KVQ_EDEVICE;
+}
+
+extern "C" kvq_status kvq_paged_block_attn(const kvq_config* cfg, const kvq_state* st,
+                                           const kvq_paged_cache* cache, const void* q, const void* k_blk,
+                                           const void* v_blk, int32_t tq, int32_t q_heads, int32_t frame_tokens,
+                                           float softmax_scale, int32_t num_splits, float* out, void* workspace,
+                                           size_t workspace_size, void* stream) {
+  Geom g;
+  kvq_status s = validate_config(cfg, &g);
+  if (s != KVQ_OK) return s;
+  if (!st || !cache || !q || !k_blk || !v_blk || !out) return KVQ_EINVAL;
+  if (g.dtype != KVQ_BF16 || (g.D != 64 && g.D != 128)) return KVQ_EINVAL;
+  if (g.G <= 0 || g.B > kMaxBlockSeqs) return KVQ_EINVAL;
+  if (!cache->pool || !cache->block_table || cache->n_pages < 1 || cache->table_stride < 1 ||
+      (int64_t)cache->table_stride * kTile < g.C)
+    return KVQ_EINVAL;
+  if (tq < 1 || q_heads < 1 || q_heads % g.H != 0) return KVQ_EINVAL;
+  const int gqa = q_heads / g.H;
+  if (gqa != 1 && gqa != 2 && gqa != 4 && gqa != 8) return KVQ_EINVAL;
+  if (!(softmax_scale > 0.0f) || num_splits < 0 || num_splits > kBlockMaxSplits) return KVQ_EINVAL;
+  if ((int64_t)tq * gqa > (1 << 30)) return KVQ_EINVAL;
+  if (frame_tokens < 1) return KVQ_EINVAL;
+  PagedBlock pb;
+  pb.pool = static_cast<const uint8_t*>(cache->pool);
+  pb.table = cache->block_table;
+  pb.n_pages = cache->n_pages;
+  pb.head_bytes = 2 * kTile * g.W + 2 * kTile + 2 * g.D;
+  pb.page_bytes = static_cast<int64_t>(g.H) * pb.head_bytes;
+  pb.stride = cache->table_stride;
+  int max_items = 1;
+  bool any_tail = false;
+  for (int b = 0; b < kMaxBlockSeqs; ++b) {
+    pb.nq[b] = pb.nt[b] = 0;
+    if (b >= g.B) continue;
+    const kvq_state& x = st[b];
+    if (x.quantized < 0 || x.tail < 0 || x.total != x.quantized + x.tail || x.quantized > g.C ||
+        x.tail > g.ring || x.quantized % g.G != 0)
+      return KVQ_EINVAL;
+    if (x.total + (int64_t)tq + frame_tokens > (int64_t(1) << 31) - 1) return KVQ_EINVAL;
+    pb.nq[b] = static_cast<int>(x.quantized);
+    pb.nt[b] = static_cast<int>(x.tail);
+    any_tail |= x.tail > 0;
+    const int items = static_cast<int>((x.quantized + kTile - 1) / kTile + (x.tail + kTile - 1) / kTile +
+                                       (tq + kTile - 1) / kTile);
+    max_items = items > max_items ? items : max_items;
+  }
+  if (any_tail && (!cache->k_tail || !cache->v_tail)) return KVQ_EINVAL;
+  if (!workspace || workspace_size < workspace_bytes(g, q_heads, tq)) return KVQ_EWORKSPACE;
+
+  // Uniform fields; the kernel takes each sequence's lengths from pb.
+  BlockArgs a;
+  a.g = g;
+  a.k_codes = nullptr;
+  a.v_codes = nullptr;
+  a.k_scale = nullptr;
+  a.v_scale = nullptr;
+  a.k_tail = static_cast<const uint16_t*>(cache->k_tail);
+  a.v_tail = static_cast<const uint16_t*>(cache->v_tail);
+  a.seg_index = nullptr;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k_blk = static_cast<const uint16_t*>(k_blk);
+  a.v_blk = static_cast<const uint16_t*>(v_blk);
+  a.out = out;
+  a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + workspace_counter_bytes(g, tq));
+  a.nq = 0;
+  a.nt = 0;
+  a.nq_slot = 0;
+  a.tq = tq;
+  a.gqa = gqa;
+  a.rows = tq * gqa;
+  a.qscale = softmax_scale * 1.4426950408889634f;
+  a.tiles_q = 0;
+  a.tiles_t = 0;
+  a.tiles_b = (tq + kTile - 1) / kTile;
+  a.frame = frame_tokens;
+  a.cached = 0;
+  const int rows_wg = g.D >= 128 ? BlockShape<128>::kRows : BlockShape<64>::kRows;
+  const int threads = g.D >= 128 ? BlockShape<128>::kThreads : BlockShape<64>::kThreads;
+  const int row_tiles = (a.rows + rows_wg - 1) / rows_wg;
+  // one split count for every sequence (the longest sets it); shorter
+  // sequences leave some splits empty, which the merge weighs as zero
+  a.splits = num_splits > 0 ? num_splits : block_auto_splits(row_tiles, g.B * g.H, max_items, threads);
+  if (a.splits > max_items) a.splits = max_items;
+  if (row_tiles > 65535) return KVQ_EINVAL;
+  clear_stale_hip_error();
+  if (!dispatch_block(a, static_cast<hipStream_t>(stream), &pb)) return KVQ_EINVAL;
   return hipGetLastError() == hipSuccess ? KVQ_OK : KVQ_EDEVICE;
 }

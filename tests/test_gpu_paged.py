@@ -280,3 +280,34 @@ def test_paged_decode_step_errors_leave_states_unchanged():
         p.cache.decode_step(big_k.cuda(), big_v.cuda(), [600, 1], q, out, ws)
     assert [(x.quantized, x.tail, x.total) for x in p.cache.states] == before
     p.check()
+
+
+@needs_gpu
+@pytest.mark.parametrize("bits,qmax,frame,num_splits", [(4, 7, 1, 0), (2, 1, 16, 0), (4, 7, 1, 4), (8, 127, 7, 2)])
+def test_paged_block_attn(bits, qmax, frame, num_splits):
+    """Block attention over paged caches: each sequence's block of tq queries
+    sits after its own cached tokens; compared with the oracle run on each
+    sequence alone (a sequence with an empty prefix included)."""
+    w = ks.small(ks.LLAMA3_DECODE, batch=3, kv_heads=2, q_heads=8, code_bits=bits, qmax=qmax)
+    p = PagedPair(w, stride=24, seed=21 + bits)
+    s = ks.Stream(w)
+    lens = [700, 90, 1300]
+    k, v = ks.kv_pair(s, max(lens))
+    p.append(k, v, lens)
+    tq = 100
+    q, kb, vb = ks.block_inputs(s, tq)
+    ws = p.cache.workspace(w.q_heads, tq)
+    out = torch.full((w.batch, tq, w.q_heads, w.head_dim), float("nan"), device="cuda")
+    note(f"paged block bits={bits} F={frame} splits={num_splits}")
+    p.cache.block_attn(q.cuda(), kb.cuda(), vb.cuda(), out, ws, num_splits=num_splits, frame_tokens=frame)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    sigma = 1.0 / math.sqrt(w.head_dim)
+    worst = 0.0
+    for b, o in enumerate(p.ost):
+        ref = oatt.block_attention(o, f32(q[b:b + 1]), f32(kb[b:b + 1]), f32(vb[b:b + 1]), sigma,
+                                   frame_tokens=frame)
+        worst = max(worst, max_abs(got[b:b + 1], ref))
+    note(f"paged block bits={bits}: max-abs {worst:.3e}")
+    assert worst <= TOL
+    p.check()
