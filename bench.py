@@ -53,7 +53,7 @@ LONG_CALL_TRAFFIC = 143_130_419      # one 131072-token layer (algorithmic 138.8
 # Same measurement for the other workloads: 128 appends (16 flushes + 128
 # window copies) and one block-attention call (block_kernel + block_merge_kernel).
 APPEND_RUN_TRAFFIC = {4: 444212838, 8: 479005900}
-BLOCK_CALL_TRAFFIC = 2_009_368_985    # the cache is streamed once per query-row tile
+BLOCK_CALL_TRAFFIC = 2_009_669_018    # the cache is streamed once per query-row tile
 PAGED_CALL_TRAFFIC = 44_977_562       # paged decode, ragged lengths (algorithmic 41.42 MB)
 
 
