@@ -311,3 +311,27 @@ def test_paged_block_attn(bits, qmax, frame, num_splits):
     note(f"paged block bits={bits}: max-abs {worst:.3e}")
     assert worst <= TOL
     p.check()
+
+
+@needs_gpu
+def test_paged_decode_llama3_full_size_ragged():
+    """The paged workload the benchmark times: Llama-3-8B shape (batch 8, 32 / 8
+    heads, head_dim 128, int4), lengths 494 .. 7845 from the benchmark's seeded
+    draw, a shuffled page table, the automatic split choice; every output
+    against the oracle, then one decode step (one token per sequence)."""
+    w = ks.LLAMA3_DECODE
+    lens = [int(x) for x in np.random.default_rng(4096).integers(256, 7937, size=w.batch)]
+    p = PagedPair(w, stride=max(lens) // 64 + 4, seed=4096)
+    s = ks.Stream(w)
+    k, v = ks.kv_pair(s, max(lens))
+    note(f"paged full size {lens}")
+    p.append(k, v, lens)
+    del k, v
+    q = ks.decode_query(s)
+    err = max_abs(p.decode(q), p.decode_ref(q))
+    k1, v1 = ks.kv_pair(s, 1)
+    q1 = ks.decode_query(s)
+    err1 = max_abs(p.step(k1, v1, [1] * w.batch, q1), p.decode_ref(q1))
+    note(f"paged full size: max-abs {err:.3e}, step {err1:.3e}")
+    assert err <= TOL and err1 <= TOL
+    p.check()
