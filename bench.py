@@ -55,6 +55,7 @@ LONG_CALL_TRAFFIC = 143_130_419      # one 131072-token layer (algorithmic 138.8
 APPEND_RUN_TRAFFIC = {4: 444212838, 8: 479005900}
 BLOCK_CALL_TRAFFIC = 2_009_669_018    # the cache is streamed once per query-row tile
 PAGED_CALL_TRAFFIC = 44_977_562       # paged decode, ragged lengths (algorithmic 41.42 MB)
+PAGED_BLOCK_CALL_TRAFFIC = 2_067_186_586   # the video block over a paged cache
 
 
 def decode_bytes(cfg, nq: int, nt: int, q_heads: int) -> int:
@@ -511,6 +512,71 @@ def run_video_block(args, log):
     }
 
 
+def run_paged_block(args, log):
+    """The video block (1024 causal queries, 432000-token int2 cache) with the
+    cache in 64-token pages behind a shuffled block table, timed beside the
+    same block on the uniform cache."""
+    import numpy as np
+    import torch
+
+    import kvq_synth as ks
+    from quantized_kv_cache_kvq_amd import KVCache, PagedKVCache, make_config
+
+    w = ks.VIDEO_BLOCK
+    cap = w.prefill + 128
+    stride = (cap + 63) // 64
+    cfg = make_config(batch=w.batch, kv_heads=w.kv_heads, head_dim=w.head_dim, capacity=stride * 64,
+                      code_bits=w.code_bits, qmax=w.qmax, residual=w.residual, group=w.group)
+    s = ks.Stream(w, seed=0)
+    k, v = (t.cuda() for t in ks.kv_pair(s, w.prefill))
+    c = KVCache(cfg, zero=False)
+    c.append(k, v)
+    n_pages = w.batch * stride + 16
+    perm = np.random.default_rng(432000).permutation(n_pages)[:w.batch * stride]
+    pc = PagedKVCache(cfg, n_pages, torch.from_numpy(perm.reshape(w.batch, stride).astype(np.int32)).cuda())
+    pc.append(k, v, [w.prefill] * w.batch)
+    del k, v
+    q, kb, vb = (t.cuda() for t in ks.block_inputs(s, w.block_q))
+    out = torch.empty(w.batch, w.block_q, w.q_heads, w.head_dim, device="cuda")
+    ws = c.workspace(w.q_heads, w.block_q)
+    stream = torch.cuda.current_stream()
+    steps, warmup = max(1, args.steps // 20), max(1, args.warmup // 10)
+    F = args.frame_tokens
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for i in range(steps):
+            ev[i][0].record(stream)
+            fn()
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in ev) / steps
+
+    paged_ms = timed(lambda: pc.block_attn(q, kb, vb, out, ws, frame_tokens=F))
+    dense_ms = timed(lambda: c.block_attn(q, kb, vb, out, ws, frame_tokens=F))
+    flops = block_flops(c.state.total, w.block_q, w.q_heads, w.head_dim, w.batch, F)
+    tflops = flops / (paged_ms * 1e-3) / 1e12
+    log(f"paged video block: {paged_ms:.3f} ms ({tflops:.1f} TFLOP/s); uniform cache {dense_ms:.3f} ms")
+    return {
+        "metric": "block attention over a paged quantized cache, ms per block",
+        "value": round(paged_ms, 4), "unit": "ms", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16/f16 MFMA, f32 accumulate", "data": "synthetic",
+        "config": {"workload": w.name + "_paged", "batch": w.batch, "q_heads": w.q_heads,
+                   "kv_heads": w.kv_heads, "head_dim": w.head_dim, "cached": c.state.total,
+                   "block_q": w.block_q, "frame_tokens": F, "codes": f"int{w.code_bits}", "page_tokens": 64,
+                   "parallelism": "single-gpu"},
+        "uniform_cache_ms": round(dense_ms, 4),
+        "flops_per_block": flops,
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": 2500.0, "unit": "TFLOP/s",
+                     "frac": round(tflops / 2500.0, 4), "traffic": PAGED_BLOCK_CALL_TRAFFIC,
+                     "kernel": "kvq_paged_block_attn = block_kernel<128,2,PagedBlock> + block_merge_kernel<128>"},
+    }
+
+
 def run_long_decode(args, log):
     """One step = 32 sequential decode calls, one per layer cache of 131072 tokens."""
     import torch
@@ -762,7 +828,7 @@ def main():
     ap.add_argument("--frame-tokens", type=int, default=1,
                     help="video_block: frame length of the block mask (1 = token-causal)")
     ap.add_argument("--workload", choices=["llama3_decode", "video_block", "long_decode", "append_int8",
-                                           "append_int4", "hbm_copy", "decode_paths", "paged_decode"],
+                                           "append_int4", "hbm_copy", "decode_paths", "paged_decode", "paged_block"],
                     default="llama3_decode",
                     help="llama3_decode (default): the append + decode step; video_block: one "
                          "1024-query causal block against the 432000-token int2 cache; long_decode: "
@@ -771,7 +837,8 @@ def main():
                          "device copy (reference rate, and the known-size kernel that scales the "
                          "FETCH_SIZE / WRITE_SIZE counters); decode_paths: the decode call by "
                          "restore-to-HBM + dense attention against the fused kernel; paged_decode: "
-                         "decode over paged caches (block table, ragged per-sequence lengths)")
+                         "decode over paged caches (block table, ragged per-sequence lengths); paged_block: "
+                         "the video block over a paged cache, beside the uniform cache")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the library has no multi-GPU path; run with --gpus 1",
@@ -801,6 +868,8 @@ def main():
         res = run_decode_paths(args, log)
     elif args.workload == "paged_decode":
         res = run_paged_decode(args, log)
+    elif args.workload == "paged_block":
+        res = run_paged_block(args, log)
     elif args.workload.startswith("append_"):
         res = run_append(args, log, 8 if args.workload == "append_int8" else 4)
     else:
