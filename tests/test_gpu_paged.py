@@ -6,7 +6,11 @@ sequence alone), with its 64-token tiles in the pages its row of the block
 table names ("KV Cache and autoregressive video generation", section 05: a
 block table maps logical blocks to physical ones; "KV Cache quantization and
 compression", section 07: the low-bit data and its metadata are paged
-together).
+together).  Covered: kvq_paged_append (ragged and uneven counts, flushes per
+sequence), kvq_paged_decode_attn (shapes, split choices, the benchmarked
+size), kvq_paged_decode_step (against the oracle and against the two calls)
+and kvq_paged_block_attn (frames, splits, an empty prefix); error paths leave
+every state unchanged.
 """
 import math
 
