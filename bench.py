@@ -52,7 +52,7 @@ DECODE_CALL_TRAFFIC = 41_405_030     # 4096-token Llama-3-8B shape (algorithmic 
 LONG_CALL_TRAFFIC = 143_130_419      # one 131072-token layer (algorithmic 138.8 MB)
 # Same measurement for the other workloads: 128 appends (16 flushes + 128
 # window copies) and one block-attention call (block_kernel + block_merge_kernel).
-APPEND_RUN_TRAFFIC = {4: 444212838, 8: 479005900}
+APPEND_RUN_TRAFFIC = {4: 444219392, 8: 478773248}
 BLOCK_CALL_TRAFFIC = 2_009_669_018    # the cache is streamed once per query-row tile
 PAGED_CALL_TRAFFIC = 44_977_562       # paged decode, ragged lengths (algorithmic 41.42 MB)
 PAGED_BLOCK_CALL_TRAFFIC = 2_067_186_586   # the video block over a paged cache

@@ -113,7 +113,7 @@ __device__ __forceinline__ float lane_group_max(float v, int width) {
 // lanes holding the same piece, then over the four waves in LDS; the codes
 // of a piece (epp fields) are stored as one 1..8-byte word of its token's
 // 16-byte chunk.
-template <int BITS>
+template <int BITS, bool kPaged>
 __device__ __forceinline__ void flush_keys(const FlushArgs& a, int bh, int64_t seg, int64_t p0, int64_t p1,
                                            float (*red)[128], float* sc) {
   constexpr uint32_t kMask = (1u << BITS) - 1u;
@@ -159,7 +159,7 @@ __device__ __forceinline__ void flush_keys(const FlushArgs& a, int bh, int64_t s
   if (tid < D) {
     const float m = fmaxf(fmaxf(red[0][tid], red[1][tid]), fmaxf(red[2][tid], red[3][tid]));
     const uint16_t h = f32_to_half_bits(scale_of(m, g.qmax, g.eps));
-    if (a.pool) {          // the segment's row in each of its pages
+    if constexpr (kPaged) {    // the segment's row in each of its pages
       for (int64_t tl = p0 / kTile; tl < (p1 + kTile - 1) / kTile; ++tl)
         reinterpret_cast<uint16_t*>(page_head(a, bh % g.H, tl) + 2 * kTile * g.W + 2 * kTile)[tid] = h;
     } else {
@@ -175,7 +175,7 @@ __device__ __forceinline__ void flush_keys(const FlushArgs& a, int bh, int64_t s
   const int j = (q * epp) / cpc;                 // chunk of the piece
   const int byte_in_chunk = ((q * epp - j * cpc) * BITS) / 8;
   const int bytes = epp * BITS / 8;              // 1, 2, 4 or 8
-  uint8_t* kc = a.pool ? nullptr : a.k_codes + (int64_t)bh * g.code_stream + j * 1024 + byte_in_chunk;
+  uint8_t* kc = kPaged ? nullptr : a.k_codes + (int64_t)bh * g.code_stream + j * 1024 + byte_in_chunk;
   for (int b = 0; b < nb; ++b) {
     if (nb > 1) load_batch(b);                   // one batch: still in registers
 #pragma unroll
@@ -186,7 +186,7 @@ __device__ __forceinline__ void flush_keys(const FlushArgs& a, int bh, int64_t s
 #pragma unroll
       for (int e = 0; e < 8; ++e)
         if (e < epp) bits |= static_cast<uint64_t>(code_field(piece_elem(r[i], e, bf16), s[e], g.qmax, kMask)) << (e * BITS);
-      uint8_t* dst = a.pool ? page_head(a, bh % g.H, p / kTile) + j * 1024 + byte_in_chunk + (p % kTile) * 16
+      uint8_t* dst = kPaged ? page_head(a, bh % g.H, p / kTile) + j * 1024 + byte_in_chunk + (p % kTile) * 16
                             : kc + (p / kTile) * kTile * g.W + (p % kTile) * 16;
       if (bytes == 8) *reinterpret_cast<uint2*>(dst) = make_uint2(static_cast<uint32_t>(bits), static_cast<uint32_t>(bits >> 32));
       else if (bytes == 4) *reinterpret_cast<uint32_t*>(dst) = static_cast<uint32_t>(bits);
@@ -202,7 +202,7 @@ __device__ __forceinline__ void flush_keys(const FlushArgs& a, int bh, int64_t s
 // channels in registers.  The units of a token group sit in `pieces`
 // consecutive lanes, which reduce the per-token absmax; every lane derives
 // the scale itself, the piece-0 lane stores it.
-template <int BITS>
+template <int BITS, bool kPaged>
 __device__ __forceinline__ void flush_values(const FlushArgs& a, int bh, int vw, int64_t p0, int64_t p1) {
   constexpr uint32_t kMask = (1u << BITS) - 1u;
   constexpr int kTok = 32 / BITS;                // tokens per packed word
@@ -213,7 +213,7 @@ __device__ __forceinline__ void flush_values(const FlushArgs& a, int bh, int vw,
   const int P = a.pieces;
   const int per_tile = kGroups * P;              // units per tile
   const int units = a.v_tiles_per_wg * per_tile; // a multiple of the block size
-  uint8_t* vc = a.pool ? nullptr : a.v_codes + (int64_t)bh * g.code_stream;
+  uint8_t* vc = kPaged ? nullptr : a.v_codes + (int64_t)bh * g.code_stream;
   for (int u = threadIdx.x; u < units; u += kFlushThreads) {
     const int q = u % P, wj = (u / P) % kGroups, tw = u / per_tile;
     const int64_t t0 = (p0 / kTile + (int64_t)vw * a.v_tiles_per_wg + tw) * kTile;
@@ -237,7 +237,7 @@ __device__ __forceinline__ void flush_values(const FlushArgs& a, int bh, int vw,
       s[i] = half_bits_to_f32(h);
       const int64_t t = wt + i;
       if (q == 0 && t >= p0 && t < p1) {
-        if (a.pool) reinterpret_cast<uint16_t*>(page_head(a, bh % g.H, t / kTile) + 2 * kTile * g.W)[t % kTile] = h;
+        if constexpr (kPaged) reinterpret_cast<uint16_t*>(page_head(a, bh % g.H, t / kTile) + 2 * kTile * g.W)[t % kTile] = h;
         else a.v_scale[(int64_t)bh * g.C + t] = h;
       }
     }
@@ -245,7 +245,7 @@ __device__ __forceinline__ void flush_values(const FlushArgs& a, int bh, int vw,
     uint32_t keep_mask = 0;
     if (wt < p0) keep_mask = (1u << ((p0 - wt) * BITS)) - 1u;   // unaligned start (group == 0)
     uint32_t* dst = reinterpret_cast<uint32_t*>(
-        (a.pool ? page_head(a, bh % g.H, t0 / kTile) + kTile * g.W : vc + (t0 / kTile) * kTile * g.W) + wj * 4);
+        (kPaged ? page_head(a, bh % g.H, t0 / kTile) + kTile * g.W : vc + (t0 / kTile) * kTile * g.W) + wj * 4);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       if (e >= epp) continue;
@@ -263,9 +263,10 @@ __device__ __forceinline__ void flush_values(const FlushArgs& a, int bh, int vw,
   }
 }
 
-template <int BITS>
+// kPaged: codes and scales go to the sequence's pages (a.pool, a.table).
+template <int BITS, bool kPaged>
 __global__ __launch_bounds__(kFlushThreads) void flush_kernel(FlushArgs a) {
-  const int bh = a.pool ? a.seq * a.g.H + (int)blockIdx.y : (int)blockIdx.y;
+  const int bh = kPaged ? a.seq * a.g.H + (int)blockIdx.y : (int)blockIdx.y;
   const int per_seg = 1 + a.v_wgs;
   const int64_t sl = blockIdx.x / per_seg;
   const int role = blockIdx.x % per_seg;
@@ -275,12 +276,12 @@ __global__ __launch_bounds__(kFlushThreads) void flush_kernel(FlushArgs a) {
   __shared__ float red[kFlushThreads / kWave][128];
   __shared__ float sc[128];
   if (role == 0) {
-    flush_keys<BITS>(a, bh, seg, p0, p1, red, sc);
+    flush_keys<BITS, kPaged>(a, bh, seg, p0, p1, red, sc);
     // group == 0: record the segment id of every flushed token
     if (a.g.G == 0 && bh == 0)
       for (int64_t p = p0 + threadIdx.x; p < p1; p += kFlushThreads) a.seg_index[p] = static_cast<int32_t>(seg);
   } else {
-    flush_values<BITS>(a, bh, role - 1, p0, p1);
+    flush_values<BITS, kPaged>(a, bh, role - 1, p0, p1);
   }
 }
 
@@ -325,10 +326,20 @@ void launch_flush(const Geom& g, FlushArgs& a, int64_t flush, unsigned grid_y, h
   a.v_wgs = static_cast<int>((seg_tiles + a.v_tiles_per_wg - 1) / a.v_tiles_per_wg);
   const int64_t nseg = flush / a.seg_len;
   dim3 grid(static_cast<unsigned>(nseg * (1 + a.v_wgs)), grid_y);
+  const bool paged = a.pool != nullptr;
   switch (g.bits) {
-    case 8: hipLaunchKernelGGL(flush_kernel<8>, grid, dim3(kFlushThreads), 0, hs, a); break;
-    case 4: hipLaunchKernelGGL(flush_kernel<4>, grid, dim3(kFlushThreads), 0, hs, a); break;
-    default: hipLaunchKernelGGL(flush_kernel<2>, grid, dim3(kFlushThreads), 0, hs, a); break;
+    case 8:
+      if (paged) hipLaunchKernelGGL((flush_kernel<8, true>), grid, dim3(kFlushThreads), 0, hs, a);
+      else hipLaunchKernelGGL((flush_kernel<8, false>), grid, dim3(kFlushThreads), 0, hs, a);
+      break;
+    case 4:
+      if (paged) hipLaunchKernelGGL((flush_kernel<4, true>), grid, dim3(kFlushThreads), 0, hs, a);
+      else hipLaunchKernelGGL((flush_kernel<4, false>), grid, dim3(kFlushThreads), 0, hs, a);
+      break;
+    default:
+      if (paged) hipLaunchKernelGGL((flush_kernel<2, true>), grid, dim3(kFlushThreads), 0, hs, a);
+      else hipLaunchKernelGGL((flush_kernel<2, false>), grid, dim3(kFlushThreads), 0, hs, a);
+      break;
   }
 }
 
