@@ -124,10 +124,21 @@ def _ptr(t) -> Optional[int]:
     return t.data_ptr()
 
 
+_raw_stream = None
+
+
 def _stream(stream) -> Optional[int]:
-    import torch
-    s = stream if stream is not None else torch.cuda.current_stream()
-    return s.cuda_stream
+    """HIP stream handle: the given torch stream's, else the current one's
+    (through torch's raw query where it exists: no Stream object per call)."""
+    global _raw_stream
+    if stream is not None:
+        return stream.cuda_stream
+    if _raw_stream is None:
+        import torch
+        raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+        _raw_stream = ((lambda: raw(torch.cuda.current_device())) if raw is not None
+                       else (lambda: torch.cuda.current_stream().cuda_stream))
+    return _raw_stream()
 
 
 def make_config(batch, kv_heads, head_dim, capacity, code_bits, qmax, residual, group,
