@@ -161,3 +161,56 @@ def test_binding_checks_tensors_before_the_call():
         need(Dev(torch.zeros(2, 5, 4)), (2, None, 3), (torch.float32,), "x")
     with pytest.raises(kvq.KVQError, match="dtype"):
         need(Dev(torch.zeros(2, 5, 3, dtype=torch.bfloat16)), (2, None, 3), (torch.float32,), "x")
+
+
+def test_paged_entry_points_validate_before_device_work():
+    """Paged calls: every check happens before anything is enqueued, so these
+    run without a GPU (fake non-null addresses are never dereferenced)."""
+    lib = kvq.load()
+    c = kvq.make_config(batch=2, kv_heads=2, head_dim=64, capacity=512, code_bits=4, qmax=7, residual=128,
+                        group=128)
+    W = 64 * 4 // 8
+    assert kvq.kvq_paged_page_bytes(c) == 2 * (128 * W + 128 + 2 * 64)
+    states = (kvq.kvq_state * 2)()
+    fake = 4096
+    pc = kvq.kvq_paged_cache(fake, 16, fake, 8, fake, fake)       # 8 pages of 64 per sequence = 512 tokens
+    # every call below fails its checks, so nothing is ever launched
+    counts = (ctypes.c_int64 * 2)(10**6, 0)
+    assert lib.kvq_paged_append(ctypes.byref(c), states, ctypes.byref(pc), fake, fake, counts,
+                                None) == kvq.KVQ_ECAPACITY
+    assert all(s.total == 0 for s in states)
+    counts[0] = -1
+    assert lib.kvq_paged_append(ctypes.byref(c), states, ctypes.byref(pc), fake, fake, counts,
+                                None) == kvq.KVQ_EINVAL
+    # the table must cover the capacity, the pool must exist, G must be > 0
+    short = kvq.kvq_paged_cache(fake, 16, fake, 7, fake, fake)
+    counts[0] = 0
+    assert lib.kvq_paged_append(ctypes.byref(c), states, ctypes.byref(short), fake, fake, counts,
+                                None) == kvq.KVQ_EINVAL
+    nopool = kvq.kvq_paged_cache(None, 16, fake, 8, fake, fake)
+    assert lib.kvq_paged_append(ctypes.byref(c), states, ctypes.byref(nopool), fake, fake, counts,
+                                None) == kvq.KVQ_EINVAL
+    g0 = kvq.make_config(batch=2, kv_heads=2, head_dim=64, capacity=512, code_bits=4, qmax=7, residual=128,
+                         group=0, max_segments=512)
+    assert lib.kvq_paged_append(ctypes.byref(g0), states, ctypes.byref(pc), fake, fake, counts,
+                                None) == kvq.KVQ_EINVAL
+    # decode over empty sequences, a bad head count, a short workspace
+    one = (kvq.kvq_state * 2)(kvq.kvq_state(0, 1, 1, 0, 0), kvq.kvq_state(0, 1, 1, 0, 0))
+    out = ctypes.c_void_p(fake)
+    ws_bytes = kvq.kvq_workspace_size(c, 8, 1)
+    assert lib.kvq_paged_decode_attn(ctypes.byref(c), states, ctypes.byref(pc), fake, 8, 0.1, 0, out, fake,
+                                     ws_bytes, None) == kvq.KVQ_EINVAL
+    assert lib.kvq_paged_decode_attn(ctypes.byref(c), one, ctypes.byref(pc), fake, 6, 0.1, 0, out, fake,
+                                     ws_bytes, None) == kvq.KVQ_EINVAL
+    assert lib.kvq_paged_decode_attn(ctypes.byref(c), one, ctypes.byref(pc), fake, 8, 0.1, 0, out, fake,
+                                     ws_bytes - 4, None) == kvq.KVQ_EWORKSPACE
+    # a step that would overflow leaves the states unchanged
+    counts[0], counts[1] = 10**6, 1
+    assert lib.kvq_paged_decode_step(ctypes.byref(c), one, ctypes.byref(pc), fake, fake, counts, fake, 8, 0.1,
+                                     0, out, fake, ws_bytes, None) == kvq.KVQ_ECAPACITY
+    assert [(s.quantized, s.tail, s.total) for s in one] == [(0, 1, 1), (0, 1, 1)]
+    # block attention: tq >= 1, a workspace of the block's size
+    assert lib.kvq_paged_block_attn(ctypes.byref(c), one, ctypes.byref(pc), fake, fake, fake, 0, 8, 1, 0.1, 0,
+                                    out, fake, ws_bytes, None) == kvq.KVQ_EINVAL
+    assert lib.kvq_paged_block_attn(ctypes.byref(c), one, ctypes.byref(pc), fake, fake, fake, 64, 8, 1, 0.1, 0,
+                                    out, fake, ws_bytes, None) == kvq.KVQ_EWORKSPACE
