@@ -4,8 +4,11 @@ Argument marshalling only: every step of append, decode attention and block
 attention runs in the HIP kernels of ``libkvq.so`` behind the C ABI declared
 in ``include/kvq.h``.  The functions below carry the C names and take torch
 tensors for device buffers (PyTorch supplies device memory and streams).
-There is no CPU fallback: if the library is not built, or no GPU is present,
-the calls raise.
+``KVCache`` owns the buffers of one uniform cache, ``PagedKVCache`` a page
+pool, a caller-filled block table and one state per sequence; both check
+every tensor's device, contiguity, shape and dtype before a call.  There is
+no CPU fallback: if the library is not built, or no GPU is present, the
+calls raise.
 """
 from __future__ import annotations
 
