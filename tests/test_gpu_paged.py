@@ -339,3 +339,35 @@ def test_paged_decode_llama3_full_size_ragged():
     note(f"paged full size: max-abs {err:.3e}, step {err1:.3e}")
     assert err <= TOL and err1 <= TOL
     p.check()
+
+
+@needs_gpu
+def test_paged_maximum_batch_of_64_sequences():
+    """64 sequences (the most a paged call takes: every per-sequence array of
+    the kernel arguments full), ragged lengths including a one-token sequence:
+    append, decode, one fused step and block attention against the oracle."""
+    w = ks.small(ks.LLAMA3_DECODE, batch=64, kv_heads=1, q_heads=4, head_dim=64)
+    p = PagedPair(w, stride=6, seed=64)
+    s = ks.Stream(w)
+    lens = [int(x) for x in np.random.default_rng(64).integers(1, 330, size=64)]
+    lens[0], lens[1] = 1, 329
+    k, v = ks.kv_pair(s, max(lens))
+    note("paged batch 64")
+    p.append(k, v, lens)
+    q = ks.decode_query(s)
+    assert max_abs(p.decode(q), p.decode_ref(q)) <= TOL
+    k1, v1 = ks.kv_pair(s, 2)
+    q1 = ks.decode_query(s)
+    assert max_abs(p.step(k1, v1, [2] * 64, q1), p.decode_ref(q1)) <= TOL
+    tq = 20
+    qb, kb, vb = ks.block_inputs(s, tq)
+    ws = p.cache.workspace(w.q_heads, tq)
+    out = torch.full((64, tq, w.q_heads, w.head_dim), float("nan"), device="cuda")
+    p.cache.block_attn(qb.cuda(), kb.cuda(), vb.cuda(), out, ws)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    sigma = 1.0 / math.sqrt(w.head_dim)
+    for b in (0, 1, 17, 63):
+        ref = oatt.block_attention(p.ost[b], f32(qb[b:b + 1]), f32(kb[b:b + 1]), f32(vb[b:b + 1]), sigma)
+        assert max_abs(got[b:b + 1], ref) <= TOL, b
+    p.check()
