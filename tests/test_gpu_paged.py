@@ -371,3 +371,21 @@ def test_paged_maximum_batch_of_64_sequences():
         ref = oatt.block_attention(p.ost[b], f32(qb[b:b + 1]), f32(kb[b:b + 1]), f32(vb[b:b + 1]), sigma)
         assert max_abs(got[b:b + 1], ref) <= TOL, b
     p.check()
+
+
+@needs_gpu
+def test_paged_decode_step_fp32_takes_the_two_calls():
+    """fp32 windows: every step runs kvq_paged_append then kvq_paged_decode_attn
+    inside the one call; outputs and states still match the oracle."""
+    w = ks.small(ks.LLAMA3_DECODE, batch=3, kv_heads=2, q_heads=4, head_dim=64, group=64, kv_dtype="f32")
+    p = PagedPair(w, stride=12, seed=32)
+    s = ks.Stream(w)
+    lens = [150, 400, 70]
+    k, v = ks.kv_pair(s, max(lens))
+    p.append(k, v, lens)
+    for ns in ([1, 1, 1], [0, 3, 1], [2, 0, 0], [70, 1, 1]):
+        k1, v1 = ks.kv_pair(s, max(ns))
+        q = ks.decode_query(s)
+        note(f"paged fp32 step n={ns}")
+        assert max_abs(p.step(k1, v1, ns, q), p.decode_ref(q)) <= TOL
+    p.check()
