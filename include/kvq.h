@@ -315,6 +315,14 @@ kvq_status kvq_paged_block_attn(const kvq_config* cfg, const kvq_state* st, cons
                                 int32_t num_splits, float* out, void* workspace, size_t workspace_bytes,
                                 void* stream);
 
+/* Restore of every sequence's quantized prefix from a paged cache
+ * (kvq_restore for paged caches): sequence b's rows 0 .. quantized_b - 1 of
+ * k_out / v_out [batch, kv_heads, ld, head_dim] are written, ld >= the
+ * longest prefix; other rows are not touched.  group > 0, batch <= 64.
+ * Errors: KVQ_EINVAL, KVQ_EDEVICE. */
+kvq_status kvq_paged_restore(const kvq_config* cfg, const kvq_state* st, const kvq_paged_cache* cache,
+                             void* k_out, void* v_out, int32_t out_dtype, int64_t ld, void* stream);
+
 /* One decode step of every sequence of a paged cache: append n_new[b]
  * tokens to sequence b, then attend with q over each whole cache including
  * them (kvq_decode_step for paged caches).  The result is that of

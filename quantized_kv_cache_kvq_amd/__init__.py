@@ -25,7 +25,7 @@ KVQ_BF16, KVQ_F32 = 0, 1
 EXPORTED = ("kvq_buffer_sizes", "kvq_plan_append", "kvq_append", "kvq_workspace_size",
             "kvq_workspace_init", "kvq_decode_attn", "kvq_decode_step", "kvq_block_attn",
             "kvq_restore", "kvq_paged_page_bytes", "kvq_paged_append", "kvq_paged_decode_attn",
-            "kvq_paged_decode_step", "kvq_paged_block_attn", "kvq_status_str")
+            "kvq_paged_decode_step", "kvq_paged_block_attn", "kvq_paged_restore", "kvq_status_str")
 
 
 class kvq_config(ctypes.Structure):
@@ -87,6 +87,7 @@ def load() -> ctypes.CDLL:
         "kvq_paged_append": [P(kvq_config), P(kvq_state), P(kvq_paged_cache), vp, vp, P(i64), vp],
         "kvq_paged_decode_attn": [P(kvq_config), P(kvq_state), P(kvq_paged_cache), vp, i32, f32, i32, vp, vp,
                                   sz, vp],
+        "kvq_paged_restore": [P(kvq_config), P(kvq_state), P(kvq_paged_cache), vp, vp, i32, i64, vp],
         "kvq_paged_block_attn": [P(kvq_config), P(kvq_state), P(kvq_paged_cache), vp, vp, vp, i32, i32, i32, f32,
                                  i32, vp, vp, sz, vp],
         "kvq_paged_decode_step": [P(kvq_config), P(kvq_state), P(kvq_paged_cache), vp, vp, P(i64), vp, i32, f32,
@@ -197,6 +198,13 @@ def kvq_paged_decode_attn(cfg, states, pcache, q, q_heads, softmax_scale, num_sp
                                         softmax_scale, num_splits, _ptr(out), _ptr(ws),
                                         ws.numel() * ws.element_size(), _stream(stream)),
            "kvq_paged_decode_attn")
+
+
+def kvq_paged_restore(cfg, states, pcache, k_out, v_out, out_dtype: int, ld: int, stream=None):
+    if len(states) != cfg.batch:
+        raise KVQError(KVQ_EINVAL, f"kvq_paged_restore: need one state per sequence ({cfg.batch})")
+    _check(load().kvq_paged_restore(ctypes.byref(cfg), states, ctypes.byref(pcache), _ptr(k_out), _ptr(v_out),
+                                    out_dtype, ld, _stream(stream)), "kvq_paged_restore")
 
 
 def kvq_paged_block_attn(cfg, states, pcache, q, k_blk, v_blk, tq, q_heads, frame_tokens, softmax_scale,
@@ -425,6 +433,16 @@ class PagedKVCache:
         _need(out, shape, self._f32, "paged decode output")
         _check_ws(ws, self._i32)
         kvq_paged_decode_attn(self.cfg, self.states, self.c, q, q.shape[1], s, num_splits, out, ws, stream)
+
+    def restore(self, k_out, v_out, stream=None):
+        """Every sequence's restored prefix into k_out / v_out [B, Hkv, ld, D] (fp32 or bf16)."""
+        import torch
+        cfg = self.cfg
+        shape = (cfg.batch, cfg.kv_heads, k_out.shape[2] if k_out.dim() == 4 else None, cfg.head_dim)
+        _need(k_out, shape, (torch.float32, torch.bfloat16), "paged restore keys")
+        _need(v_out, shape, (k_out.dtype,), "paged restore values")
+        dt = KVQ_BF16 if k_out.dtype == torch.bfloat16 else KVQ_F32
+        kvq_paged_restore(cfg, self.states, self.c, k_out, v_out, dt, k_out.shape[2], stream)
 
     def block_attn(self, q, k_blk, v_blk, out, ws, softmax_scale=None, num_splits=0, stream=None,
                    frame_tokens=1):

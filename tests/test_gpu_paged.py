@@ -9,8 +9,8 @@ compression", section 07: the low-bit data and its metadata are paged
 together).  Covered: kvq_paged_append (ragged and uneven counts, flushes per
 sequence), kvq_paged_decode_attn (shapes, split choices, the benchmarked
 size), kvq_paged_decode_step (against the oracle and against the two calls)
-and kvq_paged_block_attn (frames, splits, an empty prefix); error paths leave
-every state unchanged.
+kvq_paged_block_attn (frames, splits, an empty prefix) and kvq_paged_restore
+(bit-exact); error paths leave every state unchanged.
 """
 import math
 
@@ -389,3 +389,40 @@ def test_paged_decode_step_fp32_takes_the_two_calls():
         note(f"paged fp32 step n={ns}")
         assert max_abs(p.step(k1, v1, ns, q), p.decode_ref(q)) <= TOL
     p.check()
+
+
+@needs_gpu
+@pytest.mark.parametrize("bits,qmax,dtype", [(4, 7, torch.float32), (2, 1, torch.bfloat16), (8, 127, torch.float32)])
+def test_paged_restore_bit_exact(bits, qmax, dtype):
+    """kvq_paged_restore: each sequence's prefix equals the oracle's restore
+    (fp32 division, or that rounded once to bf16); rows past a sequence's
+    prefix are not written (an empty prefix included)."""
+    from oracle.cache import segment_of_tokens
+    from oracle.codec import restore
+    w = ks.small(ks.LLAMA3_DECODE, batch=3, kv_heads=2, q_heads=4, code_bits=bits, qmax=qmax)
+    p = PagedPair(w, stride=16, seed=7 + bits)
+    s = ks.Stream(w)
+    lens = [900, 100, 530]
+    k, v = ks.kv_pair(s, max(lens))
+    p.append(k, v, lens)
+    nq = [p.cache.states[b].quantized for b in range(3)]
+    ld = max(nq) + 3
+    ko = torch.full((3, w.kv_heads, ld, w.head_dim), float("nan"), dtype=dtype, device="cuda")
+    vo = torch.full_like(ko, float("nan"))
+    note(f"paged restore bits={bits} {dtype} nq={nq}")
+    p.cache.restore(ko, vo)
+    torch.cuda.synchronize()
+    ko, vo = ko.float().cpu().numpy(), vo.float().cpu().numpy()
+    for b, o in enumerate(p.ost):
+        n = nq[b]
+        assert np.isnan(ko[b, :, n:]).all() and np.isnan(vo[b, :, n:]).all(), b
+        if n == 0:
+            continue
+        seg = segment_of_tokens(o)
+        ek = restore(stacked_codes(o, "key"), key_scales(o).astype(np.float32)[:, :, seg], 1e-8, np.float32)[0]
+        ev = restore(stacked_codes(o, "value"), value_scales(o).astype(np.float32)[:, :, :, None], 1e-8,
+                     np.float32)[0]
+        if dtype == torch.bfloat16:
+            ek = torch.from_numpy(ek).to(torch.bfloat16).float().numpy()
+            ev = torch.from_numpy(ev).to(torch.bfloat16).float().numpy()
+        assert np.array_equal(ko[b, :, :n], ek) and np.array_equal(vo[b, :, :n], ev), b
