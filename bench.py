@@ -816,6 +816,139 @@ def run_hbm_copy(args, log):
             "data": "synthetic", "config": {"workload": "hbm_copy_256MiB", "bytes": nbytes}}
 
 
+def _graph_us(launches, replays: int, log=None) -> float:
+    """Average µs of one launch: the launches captured once into a HIP graph
+    on a side stream, the graph replayed back to back, one HIP event pair on
+    the current stream around the replays."""
+    import torch
+
+    stream = torch.cuda.current_stream()
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(stream)
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(graph, stream=cap):
+            for fn in launches:
+                fn(cap)
+    stream.wait_stream(cap)
+    for _ in range(2):
+        graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(replays):
+        graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (replays * len(launches))
+
+
+def run_hbm_read(args, log):
+    """Read-only HBM stream with the probe kernel (128-bit loads, one word
+    stored per workgroup): at the decode call's size, rotating over 16
+    buffers so that nothing is served from the 256 MB Infinity Cache, and at
+    1 GiB; swept over workgroup counts and loads in flight per thread.  An
+    empty kernel gives the launch floor."""
+    import torch
+
+    import kvq_synth as ks
+    from quantized_kv_cache_kvq_amd import make_config, probes
+
+    probes.load()
+    w = ks.LLAMA3_DECODE
+    cfg = make_config(batch=w.batch, kv_heads=w.kv_heads, head_dim=w.head_dim, capacity=w.prefill,
+                      code_bits=w.code_bits, qmax=w.qmax, residual=w.residual, group=w.group)
+    dec = decode_bytes(cfg, w.prefill - w.residual, w.residual, w.q_heads)
+    dec = (dec + 15) // 16 * 16
+    n_buf = 16
+    bufs = [torch.ones(dec // 4, dtype=torch.int32, device="cuda") for _ in range(n_buf)]
+    sink = torch.zeros(1 << 16, dtype=torch.int32, device="cuda")
+    reps = max(4, args.steps // 10)
+    small = {}
+    for wgs in (256, 512, 1024, 2048, 4096):
+        for depth in (1, 2, 4, 8, 16):
+            us = _graph_us([(lambda st, b=b: probes.stream_read(b, wgs, depth, sink, st)) for b in bufs], reps)
+            small[f"{wgs}x{depth}"] = round(us, 3)
+            log(f"hbm read {dec} B, {wgs} workgroups, depth {depth}: {us:.2f} us, {dec / us / 1e3:.0f} GB/s")
+    del bufs
+    torch.cuda.empty_cache()
+    big_bytes = 1 << 30
+    big = torch.ones(big_bytes // 4, dtype=torch.int32, device="cuda")
+    large = {}
+    for wgs in (512, 1024, 2048, 4096, 8192, 16384):
+        for depth in (4, 8, 16):
+            us = _graph_us([(lambda st: probes.stream_read(big, wgs, depth, sink, st))], max(4, reps // 4))
+            large[f"{wgs}x{depth}"] = round(us, 2)
+            log(f"hbm read 1 GiB, {wgs} workgroups, depth {depth}: {us:.1f} us, {big_bytes / us / 1e3:.0f} GB/s")
+    del big
+    empty = {}
+    for wgs in (512, 2048):
+        empty[str(wgs)] = round(_graph_us([(lambda st: probes.empty(wgs, st))] * 16, reps), 3)
+        log(f"empty kernel, {wgs} workgroups: {empty[str(wgs)]:.2f} us per launch")
+    best_small = min(small.items(), key=lambda kv: kv[1])
+    best_large = min(large.items(), key=lambda kv: kv[1])
+    at512 = min((v, k) for k, v in small.items() if k.startswith("512x"))
+    return {
+        "metric": "read-only HBM stream GB/s (probe kernel)",
+        "value": round(big_bytes / best_large[1] / 1e3, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": reps, "warmup": 2, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "u32x4 loads", "data": "synthetic",
+        "config": {"workload": "hbm_read_stream", "small_bytes": dec, "small_buffers": n_buf,
+                   "large_bytes": big_bytes},
+        "small_best_us": best_small[1], "small_best_shape": best_small[0],
+        "small_best_gbs": round(dec / best_small[1] / 1e3, 2),
+        "small_512wg_us": at512[0], "small_512wg_shape": at512[1],
+        "small_512wg_gbs": round(dec / at512[0] / 1e3, 2),
+        "large_best_shape": best_large[0],
+        "small_us_by_shape": small, "large_us_by_shape": large, "empty_kernel_us": empty,
+        "roofline": {"bound": "hbm", "achieved": round(big_bytes / best_large[1] / 1e3, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(big_bytes / best_large[1] / 1e3 / HBM_PEAK_GBS, 4),
+                     "traffic": None, "kernel": "stream_read_kernel"},
+    }
+
+
+def run_mfma_peak(args, log):
+    """Matrix-core throughput of the probe loop (eight independent chains per
+    wave, register operands), per instruction kind, at two and four waves per
+    SIMD."""
+    import torch
+
+    from quantized_kv_cache_kvq_amd import probes
+
+    probes.load()
+    sink = torch.zeros(1 << 16, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    iters = 4000
+    res = {}
+    for kind, (name, ops) in probes.MFMA_KINDS.items():
+        for wgs in (512, 1024):
+            for _ in range(2):
+                probes.mfma(kind, wgs, iters, sink)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            n = 5
+            e0.record(stream)
+            for _ in range(n):
+                probes.mfma(kind, wgs, iters, sink)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / n
+            work = wgs * 4 * iters * 8 * ops
+            tf = work / (ms * 1e-3) / 1e12
+            res[f"{name}@{wgs}"] = round(tf, 1)
+            log(f"{name}, {wgs} workgroups: {ms:.3f} ms, {tf:.0f} T(FL)OP/s")
+    bf16 = max(v for k, v in res.items() if "bf16" in k)
+    return {
+        "metric": "matrix-core throughput, probe loop (TFLOP/s; i8 in TOP/s)",
+        "value": bf16, "unit": "TFLOP/s", "n_gpus": 1, "steps": 5, "warmup": 2,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16 / f16 / i8",
+        "data": "synthetic", "config": {"workload": "mfma_peak", "iters": iters},
+        "by_kind": res,
+        "roofline": {"bound": "mfma", "achieved": bf16, "peak": 2500.0, "unit": "TFLOP/s",
+                     "frac": round(bf16 / 2500.0, 4), "traffic": None, "kernel": "mfma_kernel<bf16>"},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -828,7 +961,8 @@ def main():
     ap.add_argument("--frame-tokens", type=int, default=1,
                     help="video_block: frame length of the block mask (1 = token-causal)")
     ap.add_argument("--workload", choices=["llama3_decode", "video_block", "long_decode", "append_int8",
-                                           "append_int4", "hbm_copy", "decode_paths", "paged_decode", "paged_block"],
+                                           "append_int4", "hbm_copy", "decode_paths", "paged_decode", "paged_block",
+                                           "hbm_read", "mfma_peak"],
                     default="llama3_decode",
                     help="llama3_decode (default): the append + decode step; video_block: one "
                          "1024-query causal block against the 432000-token int2 cache; long_decode: "
@@ -838,7 +972,9 @@ def main():
                          "FETCH_SIZE / WRITE_SIZE counters); decode_paths: the decode call by "
                          "restore-to-HBM + dense attention against the fused kernel; paged_decode: "
                          "decode over paged caches (block table, ragged per-sequence lengths); paged_block: "
-                         "the video block over a paged cache, beside the uniform cache")
+                         "the video block over a paged cache, beside the uniform cache; hbm_read: the "
+                         "read-only stream probe swept over workgroups and loads in flight; mfma_peak: "
+                         "the matrix-core probe loop per instruction kind")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the library has no multi-GPU path; run with --gpus 1",
@@ -860,6 +996,10 @@ def main():
     kvq.load()
     if args.workload == "hbm_copy":
         res = run_hbm_copy(args, log)
+    elif args.workload == "hbm_read":
+        res = run_hbm_read(args, log)
+    elif args.workload == "mfma_peak":
+        res = run_mfma_peak(args, log)
     elif args.workload == "video_block":
         res = run_video_block(args, log)
     elif args.workload == "long_decode":

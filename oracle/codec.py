@@ -65,7 +65,7 @@ def scale_from_absmax(absmax, qmax: int, eps: float, storage: str = "fp32") -> n
 
 def _check4(x, what):
     if np.ndim(x) != 4:
-        raise ValueError(f"{what} must have shape [batch, heads, tokens, head_dim].")
+        raise ValueError(f"{what}: expected a 4-D [batch, heads, tokens, head_dim] array, got {np.ndim(x)}-D")
 
 
 def quantize_key_per_channel(key, qmax: int = 7, eps: float = 1e-8, storage: str = "fp32"):

@@ -74,6 +74,11 @@ def load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
                            "or python -m quantized_kv_cache_kvq_amd.build")
+    # torch carries its own copy of the HIP runtime under the same soname:
+    # loading torch first makes the library bind to that one copy (a library
+    # loaded first would pull in a second runtime, whose launches fail on
+    # torch's memory and streams).
+    import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
     P = ctypes.POINTER
     vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t

@@ -4,7 +4,9 @@
 
 Each translation unit under csrc/ compiles to an object in _build/ (in
 parallel), then the objects are linked into quantized_kv_cache_kvq_amd/libkvq.so.
-Packed FP32 vector instructions are disabled for the device code.
+The measurement kernels under probe/ (HBM stream read, matrix-core loop) are
+linked apart into quantized_kv_cache_kvq_amd/libkvq_probe.so.  Packed FP32
+vector instructions are disabled for the device code.
 """
 from __future__ import annotations
 
@@ -18,9 +20,11 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
+PROBE = os.path.join(PKG, "probe")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build", "libkvq")
 LIB = os.path.join(PKG, "libkvq.so")
+PROBE_LIB = os.path.join(PKG, "libkvq_probe.so")
 ARCH = "gfx950"
 
 
@@ -57,19 +61,25 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str):
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"link failed:\n{r.stderr[-6000:]}")
-    os.replace(tmp, LIB)
+        raise RuntimeError(f"link failed for {lib}:\n{r.stderr[-6000:]}")
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    probes = sorted(glob.glob(os.path.join(PROBE, "*.hip")))
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs) + len(probes))) as ex:
+        objs = list(ex.map(_compile, srcs + probes))
+    _link(objs[:len(srcs)], LIB)
+    _link(objs[len(srcs):], PROBE_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE_LIB}")
     return LIB
 
 
