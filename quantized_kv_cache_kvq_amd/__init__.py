@@ -419,8 +419,10 @@ class PagedKVCache:
         shape = (cfg.batch, cfg.kv_heads, k_new.shape[2] if k_new.dim() == 4 else None, cfg.head_dim)
         _need(k_new, shape, self._kvdt, "paged append keys")
         _need(v_new, shape, self._kvdt, "paged append values")
-        if n_new and max(n_new) > k_new.shape[2]:
-            raise KVQError(KVQ_EINVAL, f"paged append: a count exceeds the {k_new.shape[2]} rows given")
+        if not n_new or max(n_new) != k_new.shape[2]:
+            # the library reads sequence b's rows at a stride of max(n_new) rows
+            raise KVQError(KVQ_EINVAL, f"paged append: k_new / v_new must hold max(n_new) rows, "
+                                       f"got {k_new.shape[2]} rows for counts {n_new}")
         kvq_paged_append(self.cfg, self.states, self.c, k_new, v_new, list(n_new), stream)
 
     def workspace(self, q_heads: int, tq: int = 1, stream=None):
@@ -476,8 +478,10 @@ class PagedKVCache:
         shape = (cfg.batch, cfg.kv_heads, k_new.shape[2] if k_new.dim() == 4 else None, D)
         _need(k_new, shape, self._kvdt, "paged step keys")
         _need(v_new, shape, self._kvdt, "paged step values")
-        if n_new and max(n_new) > k_new.shape[2]:
-            raise KVQError(KVQ_EINVAL, f"paged step: a count exceeds the {k_new.shape[2]} rows given")
+        if not n_new or max(n_new) != k_new.shape[2]:
+            # the library reads sequence b's rows at a stride of max(n_new) rows
+            raise KVQError(KVQ_EINVAL, f"paged step: k_new / v_new must hold max(n_new) rows, "
+                                       f"got {k_new.shape[2]} rows for counts {n_new}")
         qshape = (cfg.batch, q.shape[1] if q.dim() == 3 else None, D)
         _need(q, qshape, self._kvdt, "paged step queries")
         _need(out, qshape, self._f32, "paged step output")

@@ -40,13 +40,14 @@ kvq_status validate_config(const kvq_config* cfg, Geom* g) {
 
 // Workspace layout (bytes), shared by the attention entry points:
 //   [0, 4 * units)            int32 arrival counters, one per (batch, KV head, row tile)
-//   aligned to 256            float partials: per (unit, split, row): m, l, acc[head_dim]
+//   aligned to 256            float partials: per (unit, split, row) head_dim + 4 floats
+//                             (acc[head_dim], m, l and padding; 16-byte rows)
 size_t workspace_bytes(const Geom& g, int q_heads, int tq) {
   const int64_t units = (int64_t)g.B * g.H * ((tq + 15) / 16 + 1);
   const int64_t counters = ((units * 4 + 255) / 256) * 256;
   const int64_t splits = tq <= 1 ? kMaxSplits : 8;
   const int64_t rows = (int64_t)g.B * q_heads * (tq < 1 ? 1 : tq);
-  return static_cast<size_t>(counters + rows * splits * (g.D + 2) * 4);
+  return static_cast<size_t>(counters + rows * splits * (g.D + 4) * 4);
 }
 
 size_t workspace_counter_bytes(const Geom& g, int tq) {

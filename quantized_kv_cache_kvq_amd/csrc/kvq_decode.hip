@@ -44,6 +44,8 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kTailChunk = 16;
+// Buffer resources: word 3 of a raw (untyped, stride 0) buffer.
+constexpr int kRsrcWord3 = 0x00020000;
 
 
 struct DecodeArgs {
@@ -61,12 +63,14 @@ struct DecodeArgs {
   const void* q;
   float qscale;          // sigma * log2(e)
   float* out;
-  float* part;           // [unit][split][gqa][D + 2]
+  float* part;           // [unit][split][gqa][D + 4]: acc[D], m, l, 2 pad (16-byte rows)
   int splits;
   int tiles_q, items;    // quantized tiles; work items = tiles_q + tail chunks
   int tq_div, tq_mod;    // tiles_q = splits * tq_div + tq_mod
   int ch_div, ch_mod;    // tail chunks, likewise
-  int force_part;        // write partials even with one split (the merge runs)
+  uint32_t* ctr;         // per-unit arrival counters (workspace), 0 between calls
+  int last_merge;        // 1: the last workgroup of a unit to arrive merges its splits;
+                         // 0: partials are written for merge_kernel (more than kLastMergeSplits splits)
   // Tokens appended by the same call (kvq_decode_step), folded in by the
   // merge: keys and values [unit][n_new][D] (bf16), and the window slot of
   // the first one; the merge of query head 0 copies them into the window.
@@ -78,6 +82,8 @@ struct DecodeArgs {
 };
 
 constexpr int kMaxStepNew = 16;   // appended tokens kvq_decode_step folds into the merge
+constexpr int kLastMergeSplits = 64;  // split counts merged inside the attention kernel
+constexpr int kMergeBatch = 16;   // partial loads in flight per output element in that merge
 constexpr int kMaxPagedSeqs = 64;
 
 // Paged caches: per-sequence lengths and the page of each tile.  A page
@@ -302,8 +308,8 @@ __global__ __launch_bounds__(D) void merge_kernel(DecodeArgs a, PD pd) {
   const int unit = blockIdx.x, h = blockIdx.y, c = threadIdx.x;
   const Geom& g = a.g;
   const int b = unit / g.H, kvh = unit % g.H;
-  const int stride = GQA * (D + 2);                  // floats between splits
-  const float* pu = a.part + (int64_t)unit * a.splits * stride + h * (D + 2);
+  const int stride = GQA * (D + 4);                  // floats between splits
+  const float* pu = a.part + (int64_t)unit * a.splits * stride + h * (D + 4);
   int S = a.splits;                                  // paged: the sequence's own split count
   int nn = a.n_new;                                  // appended tokens folded in (paged: this sequence's)
   int slot0 = a.new_slot0;
@@ -410,45 +416,248 @@ __global__ __launch_bounds__(D) void merge_kernel(DecodeArgs a, PD pd) {
   a.out[((int64_t)b * g.H * GQA + kvh * GQA + h) * D + c] = num / den;
 }
 
-// Fold the four waves of a workgroup and write a partial (or, with a single
-// split, the output).  red[w][c][h] holds wave w's accumulator relative to
-// its own maximum.
-template <int D, int GQA>
-__device__ __forceinline__ void fold_and_store(const DecodeArgs& a, int unit, int split,
-                                               float (*red)[D][GQA], float (*wml)[2][GQA],
-                                               const float* m, const float* l) {
+// Agent-scope accesses to the split partials: coherent across the XCDs
+// (sc1: written through to memory, read past the XCD's L2), with no
+// cache-wide writeback or invalidate (which an agent-scope fence implies on
+// gfx950: a whole-L2 writeback per workgroup).  The same cache policy the
+// compiler gives agent-scope relaxed atomic loads and stores, on 16-byte
+// buffer accesses.
+constexpr int kCoherent = 0x10;   // buffer cache policy: sc1
+typedef unsigned u4v_t __attribute__((ext_vector_type(4)));
+typedef unsigned u2v_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void store_agent4(__amdgpu_buffer_rsrc_t r, int off, float4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4v_t, v), r, off, 0, kCoherent);
+}
+__device__ __forceinline__ void store_agent2(__amdgpu_buffer_rsrc_t r, int off, float2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u2v_t, v), r, off, 0, kCoherent);
+}
+__device__ __forceinline__ float4 load_agent4(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCoherent));
+}
+__device__ __forceinline__ float2 load_agent2(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kCoherent));
+}
+// Wait until every memory operation this wave issued has been performed:
+// the partial stores above it are visible device-wide before the arrival
+// counter below it moves.
+__device__ __forceinline__ void wait_memory_done() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);      // vmcnt(0) expcnt(0) lgkmcnt(0)
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+__device__ __forceinline__ float4 f4_scale(float4 v, float s) { return make_float4(v.x * s, v.y * s, v.z * s, v.w * s); }
+__device__ __forceinline__ float4 f4_fma(float4 v, float s, float4 acc) {
+  return make_float4(fmaf(v.x, s, acc.x), fmaf(v.y, s, acc.y), fmaf(v.z, s, acc.z), fmaf(v.w, s, acc.w));
+}
+__device__ __forceinline__ float4 f4_add(float4 a, float4 b) { return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w); }
+
+// End of one workgroup's share of a unit (batch, KV head).  The four waves'
+// online-softmax states (m, l per head; red[w][c][h] = acc relative to the
+// wave's own maximum) are folded into the split's state.  Then:
+//   * one split and nothing appended: the workgroup writes the output;
+//   * more than kLastMergeSplits splits: it writes its partial for merge_kernel;
+//   * otherwise it publishes its partial (agent-scope stores, waited for) and
+//     takes an arrival ticket from the unit's counter (agent-scope increment
+//     that wraps back to 0 on the last arrival, leaving the counter ready for
+//     the next call).  The last workgroup to arrive merges every split's
+//     partial (flash-decoding merge, "KV Cache and autoregressive video
+//     generation", section 05), adds the nn tokens appended by the same call
+//     (decode step) as further softmax terms -- logit sigma log2(e) q . k_new
+//     from qf(h, c) = sigma log2(e) q[h][c] -- writes them into their window
+//     slots (slot0 + t, wrapped), and writes the output.
+// Thread t owns output channels c0 .. c0 + 3 of head h (group t % NT) and, in
+// the merge, every NSG-th split from t / NT; partial rows are D + 4 floats so
+// that every access is 16 bytes.  k_new / v_new rows of unit u start at row
+// u * nst.
+template <int D, int GQA, typename QF>
+__device__ __forceinline__ void finish_unit(const DecodeArgs& a, int unit, int split, int S, int nn, int nst,
+                                            int slot0, float (*red)[D][GQA], float (*wml)[2][GQA],
+                                            const float* m, const float* l, QF qf) {
+  constexpr int NT = GQA * D / 4;                            // 16-byte output groups of a unit
+  constexpr int NSG = kThreads / NT;                         // split groups of the merge
+  static_assert(NT <= kThreads && kThreads % NT == 0, "output groups tile the workgroup");
+  constexpr int RS = D + 4;                                  // floats per (split, head) partial row
+  constexpr int KPL = (D + kWave - 1) / kWave;               // key channels per lane (new-token logits)
   const Geom& g = a.g;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
-  const int b = unit / g.H, kvh = unit % g.H;
+  const int grp = tid % NT, sgi = tid / NT;
+  const int h = 4 * grp / D, c0 = 4 * grp % D;
+  __shared__ float sm[kLastMergeSplits][GQA], sl[kLastMergeSplits][GQA];
+  __shared__ float lg[kMaxStepNew][GQA], mx[GQA];
+  __shared__ float4 racc[NSG > 1 ? NSG - 1 : 1][NT];
+  __shared__ int last;
   if (lane == 0) {
 #pragma unroll
-    for (int h = 0; h < GQA; ++h) {
-      wml[wave][0][h] = m[h];
-      wml[wave][1][h] = l[h];
+    for (int hh = 0; hh < GQA; ++hh) {
+      wml[wave][0][hh] = m[hh];
+      wml[wave][1][hh] = l[hh];
     }
   }
   __syncthreads();
-  for (int i = tid; i < GQA * D; i += kThreads) {
-    const int h = i / D, c = i % D;
-    float M = -INFINITY;
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, wml[w][0][h]);
-    float s = 0.0f, L = 0.0f;
+  float4 fs = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  float fm = -INFINITY, fl = 0.0f;
+  if (sgi == 0) {
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) fm = fmaxf(fm, wml[w][0][h]);
+#pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      const float e = (wml[w][0][h] == -INFINITY) ? 0.0f : fast_exp2(wml[w][0][h] - M);
-      s += red[w][c][h] * e;
-      L += wml[w][1][h] * e;
+      const float e = (wml[w][0][h] == -INFINITY) ? 0.0f : fast_exp2(wml[w][0][h] - fm);
+      fs = f4_fma(make_float4(red[w][c0][h], red[w][c0 + 1][h], red[w][c0 + 2][h], red[w][c0 + 3][h]), e, fs);
+      fl += wml[w][1][h] * e;
     }
-    if (a.splits == 1 && !a.force_part) {
-      a.out[((int64_t)b * g.H * GQA + kvh * GQA + h) * D + c] = s / L;
-    } else {
-      float* part = a.part + ((int64_t)unit * a.splits + split) * GQA * (D + 2) + h * (D + 2);
-      part[c] = s;
-      if (c == 0) {
-        part[D] = M;
-        part[D + 1] = L;
+  }
+  float4* out = reinterpret_cast<float4*>(a.out + (int64_t)unit * GQA * D + h * D + c0);
+  if (S == 1 && nn == 0) {
+    if (sgi == 0) *out = f4_scale(fs, 1.0f / fl);
+    return;
+  }
+  const int sstride = GQA * RS;                              // floats between splits
+  float* pu = a.part + (int64_t)unit * a.splits * sstride;
+  if (!a.last_merge) {                                       // merge_kernel merges
+    if (sgi == 0) {
+      float* ps = pu + split * sstride + h * RS;
+      *reinterpret_cast<float4*>(ps + c0) = fs;
+      if (c0 == 0) *reinterpret_cast<float2*>(ps + D) = make_float2(fm, fl);
+    }
+    return;
+  }
+  // the unit's partials through one buffer resource (byte offsets)
+  const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(pu, (short)0, S * sstride * 4, kRsrcWord3);
+  if (S > 1) {
+    if (sgi == 0) {
+      store_agent4(rp, (split * sstride + h * RS + c0) * 4, fs);
+      if (c0 == 0) store_agent2(rp, (split * sstride + h * RS + D) * 4, make_float2(fm, fl));
+    }
+    wait_memory_done();
+    __syncthreads();
+    if (tid == 0)
+      last = __builtin_amdgcn_atomic_inc32(a.ctr + unit, (uint32_t)(S - 1), __ATOMIC_RELAXED, "agent") ==
+             (uint32_t)(S - 1);
+    __syncthreads();
+    if (!last) return;
+  }
+  // ---- the last workgroup of the unit: merge ----
+  // Every load of the merge goes out together: the first batch of partials,
+  // the split maxima and sums, and the appended tokens' keys and values.
+  float4 v[kMergeBatch];
+  auto load_batch = [&](int j0) {
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j) {
+      int sk = sgi + NSG * (j0 + j);
+      sk = sk < S ? sk : S - 1;                              // clamped: unconditional loads
+      v[j] = load_agent4(rp, (sk * sstride + h * RS + c0) * 4);
+    }
+  };
+  if (S > 1) {
+    load_batch(0);
+    for (int j = tid; j < S * GQA; j += kThreads) {
+      const float2 ml = load_agent2(rp, ((j / GQA) * sstride + (j % GQA) * RS + D) * 4);
+      sm[j / GQA][j % GQA] = ml.x;
+      sl[j / GQA][j % GQA] = ml.y;
+    }
+  } else {
+    v[0] = fs;
+    if (sgi == 0 && c0 == 0) {
+      sm[0][h] = fm;
+      sl[0][h] = fl;
+    }
+  }
+  const uint16_t* kn = a.k_new + (int64_t)unit * nst * D;
+  const uint16_t* vn = a.v_new + (int64_t)unit * nst * D;
+  uint16_t kr[kMaxStepNew][KPL];
+  uint2 vr[kMaxStepNew];                                     // channels c0 .. c0 + 3 (bf16)
+  if (nn > 0) {
+#pragma unroll
+    for (int t = 0; t < kMaxStepNew; ++t) {
+      const int tc = t < nn ? t : nn - 1;
+#pragma unroll
+      for (int j = 0; j < KPL; ++j) {
+        const int c = lane + j * kWave;
+        kr[t][j] = kn[tc * D + (c < D ? c : 0)];
+      }
+      vr[t] = *reinterpret_cast<const uint2*>(vn + tc * D + c0);
+    }
+    // logits of the appended tokens, one wave per head
+    for (int hh = wave; hh < GQA; hh += kWaves) {
+#pragma unroll
+      for (int t = 0; t < kMaxStepNew; ++t) {
+        if (t < nn) {
+          float x = 0.0f;
+#pragma unroll
+          for (int j = 0; j < KPL; ++j) {
+            const int c = lane + j * kWave;
+            if (c < D) x = fmaf(qf(hh, c), bf16_bits_to_f32(kr[t][j]), x);
+          }
+          x = wave_sum(x);
+          if (lane == 0) lg[t][hh] = x;
+        }
       }
     }
   }
+  __syncthreads();
+  if (tid < GQA) {
+    float M = -INFINITY;
+    for (int sk = 0; sk < S; ++sk) M = fmaxf(M, sm[sk][tid]);   // -inf only for empty splits
+    for (int t = 0; t < nn; ++t) M = fmaxf(M, lg[t][tid]);
+    mx[tid] = M;
+  }
+  __syncthreads();
+  for (int j = tid; j < S * GQA; j += kThreads) {
+    const int sk = j / GQA, hh = j % GQA;
+    const float e = sm[sk][hh] == -INFINITY ? 0.0f : fast_exp2(sm[sk][hh] - mx[hh]);   // empty split: 0
+    sm[sk][hh] = e;
+    sl[sk][hh] *= e;
+  }
+  __syncthreads();
+  float4 num = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  for (int j0 = 0; sgi + NSG * j0 < S; j0 += kMergeBatch) {
+    if (j0 > 0) load_batch(j0);
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j) {
+      const int sk = sgi + NSG * (j0 + j);
+      if (sk < S) num = f4_fma(v[j], sm[sk][h], num);
+    }
+  }
+  if (nn > 0 && wave == 0) {
+    // the appended keys into their window slots, from wave 0's registers
+    uint16_t* rk = a.ring_k + (int64_t)unit * g.ring * D;
+#pragma unroll
+    for (int t = 0; t < kMaxStepNew; ++t) {
+      if (t < nn) {
+        int slot = slot0 + t;
+        slot = slot >= g.ring ? slot - g.ring : slot;
+#pragma unroll
+        for (int j = 0; j < KPL; ++j) {
+          const int c = lane + j * kWave;
+          if (c < D) rk[slot * D + c] = kr[t][j];
+        }
+      }
+    }
+  }
+  if constexpr (NSG > 1) {
+    if (sgi > 0) racc[sgi - 1][grp] = num;
+    __syncthreads();
+  }
+  if (sgi != 0) return;
+#pragma unroll
+  for (int k = 0; k + 1 < NSG; ++k) num = f4_add(num, racc[k][grp]);
+  float den = 0.0f;
+  for (int sk = 0; sk < S; ++sk) den += sl[sk][h];
+#pragma unroll
+  for (int t = 0; t < kMaxStepNew; ++t) {
+    if (t < nn) {
+      const float e = fast_exp2(lg[t][h] - mx[h]);
+      num = f4_fma(make_float4(bf16_lo(vr[t].x), bf16_hi(vr[t].x), bf16_lo(vr[t].y), bf16_hi(vr[t].y)), e, num);
+      den += e;
+      if (h == 0) {                 // the appended values into their window slots
+        int slot = slot0 + t;
+        slot = slot >= g.ring ? slot - g.ring : slot;
+        *reinterpret_cast<uint2*>(a.ring_v + ((int64_t)unit * g.ring + slot) * D + c0) = vr[t];
+      }
+    }
+  }
+  *out = f4_scale(num, 1.0f / den);
 }
 
 template <int D, int GQA>
@@ -467,11 +676,14 @@ __device__ __forceinline__ void load_q(const DecodeArgs& a, int unit, float (*qs
   }
 }
 
-// Work of one wave: quantized tiles [t0, t1) and tail chunks [c0, c1).
-// Split s owns an equal share of the tiles and of the chunks (so the tail is
-// spread over the splits).  Its four waves share the concatenated list
-// (tiles, then chunks) in contiguous runs, so a wave meets each Key segment
-// once; a chunk counts as kChunkCost tiles when the runs are balanced.
+// Work of one wave: quantized tiles [t0, t1) and window chunks [c0, c1).
+// Split s owns an equal share of the tiles and of the chunks (so the window
+// is spread over the splits).  The split's chunks are dealt to its waves as
+// evenly as they go (one each while there are at most four), and the tiles
+// fill the waves around them, a chunk counting as kChunkCost tiles: a wave
+// then meets each Key segment once, and no wave has to read a second chunk
+// after computing its first (a dependent round trip at the end of the call)
+// unless the split holds more chunks than waves.
 struct WaveWork {
   int t0, t1, c0, c1;
 };
@@ -484,16 +696,23 @@ __device__ __forceinline__ WaveWork wave_work(const DecodeArgs& a, int split, in
   const int cs1 = cs0 + a.ch_div + (split < a.ch_mod ? 1 : 0);
   const int nt = ts1 - ts0, nc = cs1 - cs0;
   const int cost = nt + kChunkCost * nc;
-  const int lo = (cost * wave) / kWaves, hi = (cost * (wave + 1)) / kWaves;
-  // position p in [0, cost): tiles occupy [0, nt), chunk j occupies [nt + j c, nt + (j + 1) c)
-  auto tiles_before = [&](int p) { return p < nt ? p : nt; };
-  auto chunks_before = [&](int p) { return p <= nt ? 0 : (p - nt + kChunkCost - 1) / kChunkCost; };
-  WaveWork w;
-  w.t0 = ts0 + tiles_before(lo);
-  w.t1 = ts0 + tiles_before(hi);
-  w.c0 = cs0 + chunks_before(lo);
-  w.c1 = cs0 + chunks_before(hi);
-  return w;
+  // chunks before wave w, and tiles before it (clamped, non-decreasing in w)
+  auto chunks_before = [&](int w) { return (nc * w) / kWaves; };
+  auto tiles_before = [&](int w) {
+    int tb = 0;
+    for (int v = 1; v <= w; ++v) {
+      int x = (cost * v) / kWaves - kChunkCost * chunks_before(v);
+      x = x > nt ? nt : x;
+      tb = x > tb ? x : tb;
+    }
+    return tb;
+  };
+  WaveWork ww;
+  ww.t0 = ts0 + tiles_before(wave);
+  ww.t1 = ts0 + tiles_before(wave + 1);
+  ww.c0 = cs0 + chunks_before(wave);
+  ww.c1 = cs0 + chunks_before(wave + 1);
+  return ww;
 }
 
 // ---- vector-ALU kernel (every shape) ------------------------------------------------
@@ -510,6 +729,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a0, PagedDe
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   int unit = blockIdx.y;
   int split = blockIdx.x;
+  int S = a0.splits, nn = a0.n_new, slot0 = a0.new_slot0;
   // Paged caches: this sequence's lengths and work split (uniform caches:
   // the arguments as given).
   DecodeArgs pa = a0;
@@ -517,6 +737,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a0, PagedDe
     const PagedUnit pu = paged_unit(pd, a0.g.H, a0.g.B, blockIdx.x);
     unit = pu.unit;
     split = pu.split;
+    S = pu.ws;
+    nn = pd.n_new[unit / g.H];
+    slot0 = pd.new_slot0[unit / g.H];
     pa = paged_args(a0, pd, unit, pu.ws);
   }
   const DecodeArgs& a = pa;
@@ -541,7 +764,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a0, PagedDe
     for (int k = 0; k < TCPL; ++k) acc_tail[k][h] = 0.0f;
   }
 
-  const WaveWork ww = wave_work<1>(a, split, wave);
+  const WaveWork ww = wave_work<2>(a, split, wave);
   const uint8_t* kbase = a.k_codes + (int64_t)unit * g.code_stream;
   const uint8_t* vbase = a.v_codes + (int64_t)unit * g.code_stream;
   const uint16_t* ksbase = a.k_scale + (int64_t)unit * g.max_seg * D;
@@ -701,7 +924,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a0, PagedDe
 #pragma unroll
       for (int h = 0; h < GQA; ++h) red[wave][lane * TCPL + k][h] += acc_tail[k][h];
   }
-  fold_and_store<D, GQA>(a, unit, split, red, wml, m, l);
+  finish_unit<D, GQA>(a, unit, split, S, nn, a.n_new, slot0, red, wml, m, l,
+                      [&](int h, int c) { return qsT[c][h]; });
 }
 
 // ---- int8-MFMA kernel (int4 / int2 codes, head_dim 64 / 128, whole-group segments) ----
@@ -736,10 +960,6 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a0, PagedDe
 
 typedef int i4_t __attribute__((ext_vector_type(4)));
 
-// Buffer resources: word 3 of a raw (untyped, stride 0) buffer, and an
-// offset beyond every resource's size (such a load reads nothing).
-constexpr int kRsrcWord3 = 0x00020000;
-constexpr int kOutOfRange = (int)0x80000000u;
 typedef __bf16 bf8_t __attribute__((ext_vector_type(8)));
 typedef float f4_t __attribute__((ext_vector_type(4)));
 
@@ -774,6 +994,8 @@ struct Fields16<4> {
   }
   // dword j/4 = even or odd nibbles of word j/8; byte j%4
   __host__ __device__ static constexpr int field(int j) { return 8 * (j / 8) + 2 * (j % 4) + (j / 4) % 2; }
+  // operand slot of field f (the inverse of field)
+  __host__ __device__ static constexpr int slot(int f) { return 8 * (f / 8) + 4 * (f % 2) + (f % 8) / 2; }
 };
 
 template <>
@@ -786,7 +1008,16 @@ struct Fields16<2> {
   }
   // dword j/4 = field j/4 of every byte; byte j%4
   __host__ __device__ static constexpr int field(int j) { return 4 * (j % 4) + j / 4; }
+  __host__ __device__ static constexpr int slot(int f) { return 4 * (f % 4) + f / 4; }
 };
+
+template <int BITS>
+constexpr bool slots_invert_fields() {
+  for (int j = 0; j < 16; ++j)
+    if (Fields16<BITS>::slot(Fields16<BITS>::field(j)) != j) return false;
+  return true;
+}
+static_assert(slots_invert_fields<4>() && slots_invert_fields<2>(), "slot() inverts field()");
 
 // Low bytes of four registers -> one dword (byte k from bk).
 __device__ __forceinline__ uint32_t pack_bytes(uint32_t b0, uint32_t b1, uint32_t b2, uint32_t b3) {
@@ -808,6 +1039,17 @@ __device__ __forceinline__ float digits_value(const i4_t s) {
 
 // Two waves per SIMD (<= 256 registers); eight heads per KV head need the
 // register file of one wave per SIMD.
+//
+// Every wave works on its own from the first instruction to the workgroup
+// fold: it loads the query itself (one 16-byte load per lane for four heads
+// of 128 channels), and its run's first window chunk and first two tiles
+// are in flight before it waits for anything, so a run of up to two tiles
+// and a chunk (the Llama-3-8B shape at 4096 tokens) is one burst of loads.
+// A tile takes 18 load instructions (int4, head_dim 128), so the burst stays
+// within the 63 vector-memory instructions a wave can have outstanding and
+// every wait is exact.  Later tiles refill the two-tile ring as tiles are
+// computed.  The Value weights' fixed-point scale is set per tile from the
+// tile's own scales, so nothing has to be read ahead of the first tile.
 template <int D, int BITS, int GQA, typename PD = NoPaging>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(GQA > 4 ? 1 : 2)))
 void decode_i8_kernel(DecodeArgs a0, PD pd) {
@@ -822,29 +1064,36 @@ void decode_i8_kernel(DecodeArgs a0, PD pd) {
   constexpr int RPL = D / 64;             // Key-scale slots per lane in the operand build
   constexpr float kFixQ = 1047552.0f;     // 2^20 (1 - 2^-10): |round(a F)| <= 2^20
   constexpr float kFixP = 2097150.0f;     // P < 2^21: top digit <= 127
+  constexpr int NQ16 = GQA * D / 8;       // 16-byte pieces of one unit's bf16 queries
+  constexpr int QPL = (NQ16 + kWave - 1) / kWave;
   const Geom& g = a0.g;
   const int tid = threadIdx.x, lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int q4 = lane / 16, col = lane % 16;
   int unit = blockIdx.y;
   int split = blockIdx.x;
+  int S = a0.splits, nn = a0.n_new, slot0 = a0.new_slot0;
   DecodeArgs pa = a0;
   if constexpr (kPaged) {
     const PagedUnit pu = paged_unit(pd, a0.g.H, a0.g.B, blockIdx.x);
     unit = pu.unit;
     split = pu.split;
+    S = pu.ws;
+    nn = pd.n_new[unit / g.H];
+    slot0 = pd.new_slot0[unit / g.H];
     pa = paged_args(a0, pd, unit, pu.ws);
   }
   const DecodeArgs& a = pa;
 
-  // sigma log2e q as a bf16 high part and the bf16 rounding of the remainder
-  // (the window-chunk score operand), split once by the whole workgroup
-  __shared__ __attribute__((aligned(16))) uint16_t qsHL[2][GQA][D];
-  __shared__ __attribute__((aligned(16))) float qsP[GQA][D];     // same, channels in slot order
-  __shared__ __attribute__((aligned(16))) float rkP[kWaves][D];  // 1 / kscale, slot order
-  // Operand digits, one row per MFMA row; rows padded to 20 dwords so that
-  // the 16-byte operand reads (lane col reads row col) spread over all banks.
+  // Per wave: sigma log2(e) q in fp32 (channel order), its bf16 high part and
+  // the bf16 rounding of the remainder (the window-chunk score operand),
+  // 1 / kscale of the current segment (slot order), operand digits (rows
+  // padded to 20 dwords so that the 16-byte operand reads -- lane col reads
+  // row col -- spread over all banks) and window-chunk weights.
   constexpr int kRowPad = 20;
+  __shared__ __attribute__((aligned(16))) float qsC[kWaves][GQA][D];
+  __shared__ __attribute__((aligned(16))) uint16_t qsHL[kWaves][2][GQA][D];
+  __shared__ __attribute__((aligned(16))) float rkP[kWaves][D];
   __shared__ __attribute__((aligned(16))) uint32_t qD[kWaves][HG][MK][16][kRowPad];  // Key operand digits
   __shared__ __attribute__((aligned(16))) uint32_t pD[kWaves][HG][16][kRowPad];      // Value operand digits
   __shared__ float pw[kWaves][kTailChunk][GQA];
@@ -854,19 +1103,16 @@ void decode_i8_kernel(DecodeArgs a0, PD pd) {
   // Channel (or token) held in slot position p of a 64-wide group.
   auto chan = [](int p) { return (p & ~15) + F16::field(p & 15); };
 
-
   // A 16-token bf16 window chunk moves as many bytes as an int4 tile and,
-  // with its scores on the matrix cores and the query split done in the
-  // prologue, costs about as much.
-  const WaveWork ww = wave_work<1>(a, split, wave);
+  // with its scores on the matrix cores, costs about as much.
+  const WaveWork ww = wave_work<2>(a, split, wave);
   const int w_begin = ww.t0, q_end = ww.t1;
   const uint8_t* kbase = a.k_codes + (int64_t)unit * g.code_stream;
   const uint8_t* vbase = a.v_codes + (int64_t)unit * g.code_stream;
   const uint16_t* ksbase = a.k_scale + (int64_t)unit * g.max_seg * D;
   const uint16_t* vsbase = a.v_scale + (int64_t)unit * g.C;
 
-  // Per-lane constants: tokens T(gg, col) of the Key MFMAs, code byte offsets.
-  // Token of column col of Key MFMA gg (recomputed where used: no registers held).
+  // Token of column col of Key MFMA gg.
   auto tok = [&](int gg) { return 16 * (col / 4) + F16::field(4 * (col % 4) + gg); };
   // Byte of a Key word: chunk (r0 / 16) of token tok[gg], byte r0 % 16 in it,
   // r0 = 8 BITS mk + 2 BITS q4.
@@ -876,64 +1122,53 @@ void decode_i8_kernel(DecodeArgs a0, PD pd) {
   };
   const int voff = col * (8 * BITS) + 2 * BITS * q4;
 
-  // Online-softmax state: head 4 hg + q4 of this lane's row quad.
-  float m[HG], lsum[HG], inv[HG], mq[HG];
-  float acc_f[HG][NV];
-  auto init_state = [&]() {
+  // ---- the query: one wave's loads, issued first ----
+  uint4 qraw[QPL];
+  {
+    const uint4* qg = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + (int64_t)unit * GQA * D);
 #pragma unroll
-    for (int hg = 0; hg < HG; ++hg) {
-      m[hg] = -INFINITY;
-      lsum[hg] = 0.0f;
-      inv[hg] = 0.0f;
-#pragma unroll
-      for (int n = 0; n < NV; ++n) acc_f[hg][n] = 0.0f;
-      // max |q| of head 4 hg + q4 (bounds the fixed-point query with max 1/kscale)
-      const int h = 4 * hg + q4;
-      float mx = 0.0f;
-      if (h < GQA) {
-#pragma unroll
-        for (int k = 0; k < D / 16; ++k) mx = fmaxf(mx, fabsf(qsP[h][col * (D / 16) + k]));
-      }
-      mq[hg] = row16_max(mx);
+    for (int k = 0; k < QPL; ++k) {
+      const int i = lane + k * kWave;
+      qraw[k] = qg[i < NQ16 ? i : 0];
     }
-  };
+  }
 
+  // A tile's registers: Key and Value code words, the Key-scale row of its
+  // segment (channels RPL * lane .. + RPL - 1, one load) and the Value scales
+  // of the 8 (int4) or 16 (int2) consecutive tokens around the lane's four
+  // tokens tok[0..3] (one or two 16-byte loads), kept raw: widening them at
+  // load time would make the wave wait for the loads it has just issued.
+  constexpr int NVS = BITS == 4 ? 1 : 2;
   struct TileRegs {
     raw_t kw[4][MK];
     raw_t vw[NV];
-    // fp16 Value scales of tokens tok[0..3] and Key scales of slots
-    // lane * RPL + i, kept 16-bit: widening them at load time would make the
-    // wave wait for the loads it has just issued
-    uint16_t vs[4];
-    uint16_t ks[RPL];
+    uint4 vs[NVS];
+    uint32_t ks;
     bool new_seg;
   };
   static_assert(RPL <= 2, "two Key-scale slots per lane at most");
   // Every load of a tile or window chunk is issued unconditionally through a
-  // buffer resource; the loads of an item past the wave's run get an offset
-  // beyond the resource's size, which the hardware drops (no memory access,
-  // zero data).  The number of loads in flight is then the same on every
-  // path and the compiler waits for exactly the ones an item needs.  No
-  // loaded register is touched before its item is computed (packing two
-  // scales into one register at load time would make the wave wait for the
-  // loads it has just issued).
+  // buffer resource; the loads of an item past the wave's run get a
+  // zero-size resource, which the hardware drops (no memory access, zero
+  // data).  The number of loads in flight is then the same on every path and
+  // the compiler waits for exactly the ones an item needs.
   const __amdgpu_buffer_rsrc_t rK = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, (int)g.code_stream, kRsrcWord3);
   const __amdgpu_buffer_rsrc_t rV = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, (int)g.code_stream, kRsrcWord3);
   const __amdgpu_buffer_rsrc_t rKS = __builtin_amdgcn_make_buffer_rsrc((void*)ksbase, (short)0, g.max_seg * D * 2, kRsrcWord3);
   const __amdgpu_buffer_rsrc_t rVS = __builtin_amdgcn_make_buffer_rsrc((void*)vsbase, (short)0, g.C * 2, kRsrcWord3);
   const __amdgpu_buffer_rsrc_t rNull = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, 0, kRsrcWord3);
   // Paged caches: lane i holds the page of the run's tile w_begin + i (a run
-  // is at most 64 tiles: the launch keeps per_split <= 4 * 64), loaded before
-  // anything else; a tile's loads go through a resource over its page's part
-  // for this KV head: Key codes at 0, Value codes at 64 W, Value scales at
-  // 128 W, the segment's Key-scale row at 128 W + 128.
+  // is at most 64 tiles: the launch keeps per_split <= 4 * 64), loaded right
+  // after the query; a tile's loads go through a resource over its page's
+  // part for this KV head: Key codes at 0, Value codes at 64 W, Value scales
+  // at 128 W, the segment's Key-scale row at 128 W + 128.
   constexpr int kPgV = kTile * W, kPgVS = 2 * kTile * W, kPgKS = 2 * kTile * W + 2 * kTile;
   int tpages = 0;
   if constexpr (kPaged) {
     const int ti = w_begin + lane < pd.stride ? w_begin + lane : pd.stride - 1;
     tpages = pd.table[(int64_t)(unit / g.H) * pd.stride + ti];
   }
-  __builtin_amdgcn_sched_barrier(0);          // the page numbers go out first
+  __builtin_amdgcn_sched_barrier(0);          // the query (and page numbers) go out first
   auto page_rsrc = [&](int tile_, bool ok) -> __amdgpu_buffer_rsrc_t {
     if constexpr (kPaged) {
       int k = __builtin_amdgcn_readfirstlane(tile_ - w_begin);
@@ -947,17 +1182,16 @@ void decode_i8_kernel(DecodeArgs a0, PD pd) {
     }
   };
   // Per-lane byte offsets inside a tile (loop invariant); the tile's own
-  // offset travels in the scalar offset of each load, so a tile's loads need
-  // no per-tile vector arithmetic (and no temporaries that alias the
-  // destinations of loads still in flight).
-  int koffv[4], vsoffv[4], ksoffv[RPL];
+  // offset travels in the scalar offset of each load.
+  int koffv[4];
 #pragma unroll
-  for (int gg = 0; gg < 4; ++gg) {
-    koffv[gg] = koff(gg, 0);
-    vsoffv[gg] = tok(gg) * 2;
-  }
-#pragma unroll
-  for (int i = 0; i < RPL; ++i) ksoffv[i] = chan(lane * RPL + i) * 2;
+  for (int gg = 0; gg < 4; ++gg) koffv[gg] = koff(gg, 0);
+  // The lane's tokens tok[gg]: int4 16 (col / 4) + 8 (m / 2) + m % 2 + 2 gg,
+  // int2 16 (col / 4) + 4 gg + m (m = col % 4): Value scales loaded from the
+  // aligned run of 8 (int4) or 16 (int2) tokens that starts at vsoff / 2.
+  const int m4 = col % 4;
+  const int vsoff = BITS == 4 ? (16 * (col / 4) + 8 * (m4 / 2)) * 2 : 16 * (col / 4) * 2;
+  const int ksoff = RPL * lane * 2;
   constexpr int kMkBytes = ((8 * BITS) / 16) * 1024;   // koff(gg, mk) - koff(gg, 0) per mk
   auto ld_raw = [&](__amdgpu_buffer_rsrc_t rs, int voff_, int soff) -> raw_t {
     if constexpr (sizeof(raw_t) == 8)
@@ -966,8 +1200,9 @@ void decode_i8_kernel(DecodeArgs a0, PD pd) {
       return __builtin_bit_cast(raw_t, __builtin_amdgcn_raw_buffer_load_b32(rs, voff_, soff, 0));
   };
   // Tiles are loaded in order: the segment of the next one is tracked with a
-  // counter (no division per tile); the first load sets it.
-  int ld_seg = 0, ld_pos = 0;
+  // counter (no division per tile).
+  int ld_seg = w_begin / a.tiles_per_seg;
+  int ld_pos = w_begin - ld_seg * a.tiles_per_seg;
   auto load_tile = [&](int tile_, TileRegs& r) {
     // Loop counters are wave-uniform; taking them through readfirstlane first
     // keeps the whole offset computation in scalar registers.
@@ -975,8 +1210,6 @@ void decode_i8_kernel(DecodeArgs a0, PD pd) {
     const int seg = __builtin_amdgcn_readfirstlane(ld_seg);
     const bool ok = tile < q_end;              // past the run: a zero-size resource, nothing read
     r.new_seg = tile == w_begin || ld_pos == 0;
-    // scales first: the code words, issued last, are what a wait for the
-    // newest loads has to cover
     __amdgpu_buffer_rsrc_t rks, rvs, rk, rv;
     int kso, vso, to, vto;
     if constexpr (kPaged) {
@@ -995,10 +1228,11 @@ void decode_i8_kernel(DecodeArgs a0, PD pd) {
       to = ok ? tile * (kTile * W) : 0;
       vto = to;
     }
+    if constexpr (RPL == 2) r.ks = __builtin_amdgcn_raw_buffer_load_b32(rks, ksoff, kso, 0);
+    else r.ks = __builtin_amdgcn_raw_buffer_load_b16(rks, ksoff, kso, 0);
 #pragma unroll
-    for (int i = 0; i < RPL; ++i) r.ks[i] = __builtin_amdgcn_raw_buffer_load_b16(rks, ksoffv[i], kso, 0);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) r.vs[k] = __builtin_amdgcn_raw_buffer_load_b16(rvs, vsoffv[k], vso, 0);
+    for (int k = 0; k < NVS; ++k)
+      r.vs[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rvs, vsoff + 16 * k, vso, 0));
 #pragma unroll
     for (int gg = 0; gg < 4; ++gg)
 #pragma unroll
@@ -1010,184 +1244,6 @@ void decode_i8_kernel(DecodeArgs a0, PD pd) {
       ++ld_seg;
     }
   };
-
-  // Key operands of a segment: digit d of round(F a[head][c]) in row 4 h + d.
-  // Lane items: head 4 hg + q4, k-group (lane / 4) % 4, dword lane % 4, both halves mk.
-  i4_t qop[HG][MK];
-  auto build_key_operands = [&](const TileRegs& r) {
-    float rkmax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < RPL; ++i) {
-      const float rk = fast_rcp(fmaxf(half_bits_to_f32(r.ks[i]), g.eps));
-      rkP[wave][lane * RPL + i] = rk;
-      rkmax = fmaxf(rkmax, rk);
-    }
-    rkmax = wave_max(rkmax);
-    wave_lds_sync();
-    const int kgi = (lane / 4) % 4, qi = lane % 4;
-#pragma unroll
-    for (int hg = 0; hg < HG; ++hg) {
-      const int h = 4 * hg + q4;
-      // F only sets the fixed-point scale: the hardware reciprocal (about one
-      // ulp) keeps |round(a F)| below 2^20 thanks to the headroom in kFixQ,
-      // and inv undoes exactly the F used, up to one more ulp.
-      const float F = kFixQ * fast_rcp(fmaxf(mq[hg] * rkmax, 1e-30f));   // all-zero query: any finite F
-      inv[hg] = h < GQA ? fast_rcp(F * F16::kMul) : 0.0f;
-      if (h < GQA) {
-#pragma unroll
-        for (int mk = 0; mk < MK; ++mk) {
-          const int p0 = 64 * mk + 16 * kgi + 4 * qi;
-          const float4 qv = *reinterpret_cast<const float4*>(&qsP[h][p0]);
-          const float4 rv = *reinterpret_cast<const float4*>(&rkP[wave][p0]);
-          const uint32_t u[4] = {fixed_biased(qv.x * rv.x, F), fixed_biased(qv.y * rv.y, F),
-                                 fixed_biased(qv.z * rv.z, F), fixed_biased(qv.w * rv.w, F)};
-          uint32_t* dst = &qD[wave][hg][mk][4 * q4][4 * kgi + qi];
-          // balanced digits: (u & 127) - 64, ((u >> 7) & 127) - 64, (u >> 14) - 64
-          dst[0 * kRowPad] = pack_bytes((u[0] >> 14) - 64u, (u[1] >> 14) - 64u, (u[2] >> 14) - 64u,
-                                        (u[3] >> 14) - 64u);
-          dst[1 * kRowPad] = pack_bytes(((u[0] >> 7) & 127u) - 64u, ((u[1] >> 7) & 127u) - 64u,
-                                        ((u[2] >> 7) & 127u) - 64u, ((u[3] >> 7) & 127u) - 64u);
-          dst[2 * kRowPad] = pack_bytes((u[0] & 127u) - 64u, (u[1] & 127u) - 64u, (u[2] & 127u) - 64u,
-                                        (u[3] & 127u) - 64u);
-        }
-      }
-    }
-    wave_lds_sync();
-#pragma unroll
-    for (int hg = 0; hg < HG; ++hg)
-#pragma unroll
-      for (int mk = 0; mk < MK; ++mk) qop[hg][mk] = *reinterpret_cast<const i4_t*>(&qD[wave][hg][mk][col][4 * q4]);
-  };
-
-  float fv = 0.0f;        // Fv: P = fv * p / vscale
-  auto compute_tile = [&](const TileRegs& r) {
-    float x[HG][4];
-#pragma unroll
-    for (int gg = 0; gg < 4; ++gg) {
-      i4_t s[HG];
-#pragma unroll
-      for (int hg = 0; hg < HG; ++hg) s[hg] = i4_t{0, 0, 0, 0};
-#pragma unroll
-      for (int mk = 0; mk < MK; ++mk) {
-        const i4_t kb = F16::unpack(r.kw[gg][mk]);
-#pragma unroll
-        for (int hg = 0; hg < HG; ++hg) s[hg] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qop[hg][mk], kb, s[hg], 0, 0, 0);
-      }
-#pragma unroll
-      for (int hg = 0; hg < HG; ++hg) x[hg][gg] = digits_value(s[hg]) * inv[hg];
-    }
-    float alpha[HG];
-#pragma unroll
-    for (int hg = 0; hg < HG; ++hg) {
-      const float tm = row16_max(fmaxf(fmaxf(x[hg][0], x[hg][1]), fmaxf(x[hg][2], x[hg][3])));
-      const float mn = fmaxf(m[hg], tm);     // finite: every token of a tile is cached
-      alpha[hg] = fast_exp2(m[hg] - mn);     // exp2(-inf) = 0 on the first tile
-      m[hg] = mn;
-      lsum[hg] *= alpha[hg];
-    }
-    float vsrf[4];
-#pragma unroll
-    for (int gg = 0; gg < 4; ++gg)
-      vsrf[gg] = fv * fast_rcp(fmaxf(half_bits_to_f32(r.vs[gg]), g.eps));
-#pragma unroll
-    for (int hg = 0; hg < HG; ++hg) {
-      uint32_t P[4];
-#pragma unroll
-      for (int gg = 0; gg < 4; ++gg) {
-        const float p = fast_exp2(x[hg][gg] - m[hg]);
-        lsum[hg] += p;
-        P[gg] = (uint32_t)(p * vsrf[gg]);
-      }
-      uint32_t* dst = &pD[wave][hg][4 * q4][col];      // k-group col / 4, dword col % 4
-      dst[0 * kRowPad] = pack_bytes(P[0] >> 14, P[1] >> 14, P[2] >> 14, P[3] >> 14);
-      dst[1 * kRowPad] = pack_bytes((P[0] >> 7) & 127u, (P[1] >> 7) & 127u, (P[2] >> 7) & 127u, (P[3] >> 7) & 127u);
-      dst[2 * kRowPad] = pack_bytes(P[0] & 127u, P[1] & 127u, P[2] & 127u, P[3] & 127u);
-    }
-    wave_lds_sync();
-    i4_t pop[HG];
-#pragma unroll
-    for (int hg = 0; hg < HG; ++hg) pop[hg] = *reinterpret_cast<const i4_t*>(&pD[wave][hg][col][4 * q4]);
-    // The tile's int32 digit sums start from zero and are folded into the
-    // fp32 accumulator at once: nothing integer is carried between tiles.
-#pragma unroll
-    for (int n = 0; n < NV; ++n) {
-      const i4_t vb = F16::unpack(r.vw[n]);
-#pragma unroll
-      for (int hg = 0; hg < HG; ++hg) {
-        const i4_t d = __builtin_amdgcn_mfma_i32_16x16x64_i8(pop[hg], vb, i4_t{0, 0, 0, 0}, 0, 0, 0);
-        acc_f[hg][n] = fmaf(acc_f[hg][n], alpha[hg], digits_value(d));
-      }
-    }
-    wave_lds_sync();      // pD is rewritten by the next tile
-  };
-
-  // The query is read first, then the wave's first tile and its run's Value
-  // scales (which fix Fv): the tile index is clamped to an existing tile, so
-  // the loads are unconditional and writing the query to LDS waits for the
-  // query alone.  Later tiles are prefetched one ahead (a tile's loads are
-  // issued just before the previous tile is computed), so a wave starts
-  // computing as soon as its first tile lands instead of waiting behind a
-  // deep queue of its own loads.
-  constexpr int NQ = (GQA * D + kThreads - 1) / kThreads;
-  float qT[NQ], qP[NQ];
-  {
-    const int b = unit / g.H, kvh = unit % g.H;
-#pragma unroll
-    for (int k = 0; k < NQ; ++k) {
-      const int i = tid + k * kThreads;
-      const int ic = i < GQA * D ? i : 0;
-      const int h = ic / D, c = ic % D;
-      const int64_t row = ((int64_t)b * g.H * GQA + kvh * GQA + h) * D;
-      // bf16 only (the launch requires it): unconditional loads, so that the
-      // query's round trip overlaps the first tile's instead of preceding it
-      const uint16_t* qb = static_cast<const uint16_t*>(a.q);
-      qT[k] = bf16_bits_to_f32(qb[row + c]);
-      qP[k] = bf16_bits_to_f32(qb[row + chan(c)]);
-    }
-  }
-  // Every query load goes out before the tile's: waiting for the query then
-  // leaves the tile loads in flight.
-  __builtin_amdgcn_sched_barrier(0);
-  // Value scales of the run's first kRunScan tiles (for the P scale fv),
-  // also ahead of the tile loads so that their wait leaves those in flight.
-  constexpr int kRunScan = 8;
-  float vs_run[kRunScan];
-#pragma unroll
-  for (int k = 0; k < kRunScan; ++k) {
-    const int t = (w_begin + k) * kTile + lane;
-    float v;
-    if constexpr (kPaged) {     // pages hold whole tiles
-      v = half_bits_to_f32(__builtin_amdgcn_raw_buffer_load_b16(page_rsrc(w_begin + k, w_begin + k < q_end),
-                                                                lane * 2, kPgVS, 0));
-    } else {
-      v = half_bits_to_f32(vsbase[t < a.nq ? t : a.nq - 1]);
-    }
-    vs_run[k] = t < q_end * kTile ? v : INFINITY;
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  int tile = w_begin;
-  TileRegs bufA, bufB;
-  ld_seg = w_begin / a.tiles_per_seg;
-  ld_pos = w_begin - ld_seg * a.tiles_per_seg;
-  load_tile(w_begin, bufA);                   // nothing is read if the wave has no tiles
-#pragma unroll
-  for (int k = 0; k < NQ; ++k) {
-    const int i = tid + k * kThreads;
-    if (i < GQA * D) {
-      const float x = qT[k] * a.qscale;
-      const uint32_t hb = bf16_rne(x);
-      qsHL[0][i / D][i % D] = (uint16_t)hb;
-      qsHL[1][i / D][i % D] = (uint16_t)bf16_rne(x - bf16_bits_to_f32(hb));
-      qsP[i / D][i % D] = qP[k] * a.qscale;
-    }
-  }
-  {
-    uint4* z0 = reinterpret_cast<uint4*>(&qD[0][0][0][0][0]);
-    for (int i = tid; i < (int)(sizeof(qD) / 16); i += kThreads) z0[i] = uint4{0u, 0u, 0u, 0u};
-    uint4* z1 = reinterpret_cast<uint4*>(&pD[0][0][0][0]);
-    for (int i = tid; i < (int)(sizeof(pD) / 16); i += kThreads) z1[i] = uint4{0u, 0u, 0u, 0u};
-  }
-  __syncthreads();
   // Window chunks: this unit's ring through buffer resources (byte offsets
   // below ring * D * 2 < 2^29); a chunk past the wave's run reads nothing.
   const uint16_t* ring_k = static_cast<const uint16_t*>(a.k_tail) + (int64_t)unit * g.ring * D;
@@ -1214,60 +1270,212 @@ void decode_i8_kernel(DecodeArgs a0, PD pd) {
       else r.v[t] = __builtin_amdgcn_raw_buffer_load_b16(rv, vlane, row, 0);
     }
   };
-  ChunkRegs<D> crA, crB;
-  const bool has_chunks = ww.c0 < ww.c1;
-  chunk_load(ww.c0, crA);                     // computed after the tiles; nothing read without chunks
-  init_state();
 
-  if (tile < q_end) {
-    // Fv from the largest 1 / vscale of the run.
-    float vsr_max = 0.0f;
+  // The query lands first: sigma log2(e) q into this wave's LDS rows (fp32,
+  // and the bf16 high / low pair of the chunk scores).  Nothing else is in
+  // flight while it comes: issued ahead of the tile loads, the query lands
+  // only as the whole burst drains (measured: 8 us into the call instead of
+  // one round trip), and nothing can be computed before it.
 #pragma unroll
-    for (int k = 0; k < kRunScan; ++k) vsr_max = fmaxf(vsr_max, fast_rcp(fmaxf(vs_run[k], g.eps)));
-    for (int t0 = (w_begin + kRunScan) * kTile; t0 < q_end * kTile; t0 += 4 * kTile) {
-      float vs4[4];
+  for (int k = 0; k < QPL; ++k) {
+    const int i = lane + k * kWave;
+    if (i < NQ16) {
+      const uint32_t w4[4] = {qraw[k].x, qraw[k].y, qraw[k].z, qraw[k].w};
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {     // clamped index: four unconditional loads in flight together
-        const int t = t0 + k * kTile + lane;
-        float v;
-        if constexpr (kPaged) {
-          const int tl = t0 / kTile + k;
-          v = half_bits_to_f32(__builtin_amdgcn_raw_buffer_load_b16(page_rsrc(tl, tl < q_end), lane * 2, kPgVS, 0));
-        } else {
-          v = half_bits_to_f32(vsbase[t < a.nq ? t : a.nq - 1]);
+      for (int j = 0; j < 8; ++j) {
+        const int e = 8 * i + j, h = e / D, c = e % D;
+        const float x = bf16_bits_to_f32((w4[j / 2] >> (16 * (j % 2))) & 0xFFFFu) * a.qscale;
+        qsC[wave][h][c] = x;
+        const uint32_t hb = bf16_rne(x);
+        qsHL[wave][0][h][c] = (uint16_t)hb;
+        qsHL[wave][1][h][c] = (uint16_t)bf16_rne(x - bf16_bits_to_f32(hb));
+      }
+    }
+  }
+  wave_lds_sync();
+
+  __builtin_amdgcn_sched_barrier(0);        // the tile loads stay behind the query's wait
+
+  // The run's first window chunk, then its first two tiles: every load of a
+  // run of up to two tiles and a chunk (the Llama-3-8B shape at 4096
+  // tokens) goes out before the wave waits for anything else.  The chunk goes
+  // first so that the wait for a tile is the same on every pass of the loop
+  // below (the loads of the one tile after it in flight).
+  ChunkRegs<D> cr;
+  chunk_load(ww.c0, cr);
+  TileRegs buf0, buf1;
+  load_tile(w_begin, buf0);
+  load_tile(w_begin + 1, buf1);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // Online-softmax state: head 4 hg + q4 of this lane's row quad.
+  float m[HG], lsum[HG], inv[HG], mq[HG];
+  float acc_f[HG][NV];
+#pragma unroll
+  for (int hg = 0; hg < HG; ++hg) {
+    m[hg] = -INFINITY;
+    lsum[hg] = 0.0f;
+    inv[hg] = 0.0f;
+#pragma unroll
+    for (int n = 0; n < NV; ++n) acc_f[hg][n] = 0.0f;
+    // max |q| of head 4 hg + q4 (bounds the fixed-point query with max 1/kscale)
+    const int h = 4 * hg + q4;
+    float mx = 0.0f;
+    if (h < GQA) {
+#pragma unroll
+      for (int k = 0; k < D / 16; ++k) mx = fmaxf(mx, fabsf(qsC[wave][h][col * (D / 16) + k]));
+    }
+    mq[hg] = row16_max(mx);
+  }
+
+  // Key operands of a segment: digit d of round(F a[head][c]) in row 4 h + d.
+  // Lane items: head 4 hg + q4, k-group (lane / 4) % 4, dword lane % 4, both halves mk.
+  i4_t qop[HG][MK];
+  auto build_key_operands = [&](const TileRegs& r) {
+    float rkmax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < RPL; ++i) {
+      const float rk = fast_rcp(fmaxf(half_bits_to_f32((uint16_t)(r.ks >> (16 * i))), g.eps));
+      const int c = RPL * lane + i;
+      rkP[wave][(c & ~15) + F16::slot(c & 15)] = rk;
+      rkmax = fmaxf(rkmax, rk);
+    }
+    rkmax = wave_max(rkmax);
+    wave_lds_sync();
+    const int kgi = (lane / 4) % 4, qi = lane % 4;
+#pragma unroll
+    for (int hg = 0; hg < HG; ++hg) {
+      const int h = 4 * hg + q4;
+      // F only sets the fixed-point scale: the hardware reciprocal (about one
+      // ulp) keeps |round(a F)| below 2^20 thanks to the headroom in kFixQ,
+      // and inv undoes exactly the F used, up to one more ulp.
+      const float F = kFixQ * fast_rcp(fmaxf(mq[hg] * rkmax, 1e-30f));   // all-zero query: any finite F
+      inv[hg] = h < GQA ? fast_rcp(F * F16::kMul) : 0.0f;
+      if (h < GQA) {
+#pragma unroll
+        for (int mk = 0; mk < MK; ++mk) {
+          const int p0 = 64 * mk + 16 * kgi + 4 * qi;
+          const float4 rv = *reinterpret_cast<const float4*>(&rkP[wave][p0]);
+          const uint32_t u[4] = {fixed_biased(qsC[wave][h][chan(p0)] * rv.x, F),
+                                 fixed_biased(qsC[wave][h][chan(p0 + 1)] * rv.y, F),
+                                 fixed_biased(qsC[wave][h][chan(p0 + 2)] * rv.z, F),
+                                 fixed_biased(qsC[wave][h][chan(p0 + 3)] * rv.w, F)};
+          uint32_t* dst = &qD[wave][hg][mk][4 * q4][4 * kgi + qi];
+          // balanced digits: (u & 127) - 64, ((u >> 7) & 127) - 64, (u >> 14) - 64
+          dst[0 * kRowPad] = pack_bytes((u[0] >> 14) - 64u, (u[1] >> 14) - 64u, (u[2] >> 14) - 64u,
+                                        (u[3] >> 14) - 64u);
+          dst[1 * kRowPad] = pack_bytes(((u[0] >> 7) & 127u) - 64u, ((u[1] >> 7) & 127u) - 64u,
+                                        ((u[2] >> 7) & 127u) - 64u, ((u[3] >> 7) & 127u) - 64u);
+          dst[2 * kRowPad] = pack_bytes((u[0] & 127u) - 64u, (u[1] & 127u) - 64u, (u[2] & 127u) - 64u,
+                                        (u[3] & 127u) - 64u);
         }
-        vs4[k] = t < q_end * kTile ? v : INFINITY;
+      }
+    }
+    wave_lds_sync();
+#pragma unroll
+    for (int hg = 0; hg < HG; ++hg)
+#pragma unroll
+      for (int mk = 0; mk < MK; ++mk) qop[hg][mk] = *reinterpret_cast<const i4_t*>(&qD[wave][hg][mk][col][4 * q4]);
+  };
+
+  // One quantized tile.  Value weights: P = Fv p / vscale as a 21-bit
+  // integer, with Fv = kFixP / max(1 / vscale) over the tile's 64 tokens
+  // (every row of 16 lanes holds all of them), so p <= 1 keeps P < 2^21; the
+  // tile's digit sums are scaled back by 1 / Fv as they are folded into the
+  // fp32 accumulator (acc = acc alpha + sums / Fv): nothing integer is carried
+  // from tile to tile.
+  auto compute_tile = [&](const TileRegs& r) {
+    float x[HG][4];
+#pragma unroll
+    for (int gg = 0; gg < 4; ++gg) {
+      i4_t sk[HG];
+#pragma unroll
+      for (int hg = 0; hg < HG; ++hg) sk[hg] = i4_t{0, 0, 0, 0};
+#pragma unroll
+      for (int mk = 0; mk < MK; ++mk) {
+        const i4_t kb = F16::unpack(r.kw[gg][mk]);
+#pragma unroll
+        for (int hg = 0; hg < HG; ++hg) sk[hg] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qop[hg][mk], kb, sk[hg], 0, 0, 0);
       }
 #pragma unroll
-      for (int k = 0; k < 4; ++k) vsr_max = fmaxf(vsr_max, fast_rcp(fmaxf(vs4[k], g.eps)));
+      for (int hg = 0; hg < HG; ++hg) x[hg][gg] = digits_value(sk[hg]) * inv[hg];
     }
-    fv = kFixP / wave_max(vsr_max);
-  }
-  // Quantized tiles, the next one's loads in flight while one is computed.
-  // The refill goes out first (its registers then hold loads in flight and
-  // are not reused as scratch by the operand build) and a scheduling barrier
-  // keeps it ahead of the compute.  The run's last tile is computed in a
-  // copy of its own, with nothing to refill, so every refill is a real load
-  // and the number in flight is the same on every path into a compute.
-  auto step = [&](TileRegs& cur, TileRegs& refill) {
-    if (tile + 1 >= q_end) {
-      if (cur.new_seg) build_key_operands(cur);
-      compute_tile(cur);
-      return false;
+    float rv[4], rmax = 0.0f;
+#pragma unroll
+    for (int gg = 0; gg < 4; ++gg) {
+      uint32_t w;
+      if constexpr (BITS == 4) {
+        // token 2 gg + m % 2 of the run: dword gg, half m % 2
+        const uint32_t d[4] = {r.vs[0].x, r.vs[0].y, r.vs[0].z, r.vs[0].w};
+        w = d[gg] >> (16 * (m4 % 2));
+      } else {
+        // token 4 gg + m of the run: load gg / 2, dword 2 (gg % 2) + m / 2, half m % 2
+        const uint4 v = r.vs[gg / 2];
+        const uint32_t lo = gg % 2 ? v.z : v.x, hi = gg % 2 ? v.w : v.y;
+        w = (m4 / 2 ? hi : lo) >> (16 * (m4 % 2));
+      }
+      rv[gg] = fast_rcp(fmaxf(half_bits_to_f32((uint16_t)w), g.eps));
+      rmax = fmaxf(rmax, rv[gg]);
     }
-    load_tile(tile + 1, refill);
-    __builtin_amdgcn_sched_barrier(0);
-    if (cur.new_seg) build_key_operands(cur);
-    compute_tile(cur);
-    ++tile;
-    return true;
+    rmax = row16_max(rmax);
+    const float fv = kFixP * fast_rcp(rmax);
+    const float back = rmax * (1.0f / kFixP);              // 1 / Fv
+    float alpha[HG];
+#pragma unroll
+    for (int hg = 0; hg < HG; ++hg) {
+      const float tm = row16_max(fmaxf(fmaxf(x[hg][0], x[hg][1]), fmaxf(x[hg][2], x[hg][3])));
+      const float mn = fmaxf(m[hg], tm);     // finite: every token of a tile is cached
+      alpha[hg] = fast_exp2(m[hg] - mn);     // exp2(-inf) = 0 on the first tile
+      m[hg] = mn;
+      lsum[hg] *= alpha[hg];
+    }
+#pragma unroll
+    for (int gg = 0; gg < 4; ++gg) rv[gg] *= fv;
+#pragma unroll
+    for (int hg = 0; hg < HG; ++hg) {
+      uint32_t P[4];
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg) {
+        const float p = fast_exp2(x[hg][gg] - m[hg]);
+        lsum[hg] += p;
+        P[gg] = (uint32_t)(p * rv[gg]);
+      }
+      uint32_t* dst = &pD[wave][hg][4 * q4][col];      // k-group col / 4, dword col % 4
+      dst[0 * kRowPad] = pack_bytes(P[0] >> 14, P[1] >> 14, P[2] >> 14, P[3] >> 14);
+      dst[1 * kRowPad] = pack_bytes((P[0] >> 7) & 127u, (P[1] >> 7) & 127u, (P[2] >> 7) & 127u, (P[3] >> 7) & 127u);
+      dst[2 * kRowPad] = pack_bytes(P[0] & 127u, P[1] & 127u, P[2] & 127u, P[3] & 127u);
+    }
+    wave_lds_sync();
+    i4_t pop[HG];
+#pragma unroll
+    for (int hg = 0; hg < HG; ++hg) pop[hg] = *reinterpret_cast<const i4_t*>(&pD[wave][hg][col][4 * q4]);
+#pragma unroll
+    for (int n = 0; n < NV; ++n) {
+      const i4_t vb = F16::unpack(r.vw[n]);
+#pragma unroll
+      for (int hg = 0; hg < HG; ++hg) {
+        const i4_t d = __builtin_amdgcn_mfma_i32_16x16x64_i8(pop[hg], vb, i4_t{0, 0, 0, 0}, 0, 0, 0);
+        acc_f[hg][n] = fmaf(digits_value(d), back, acc_f[hg][n] * alpha[hg]);
+      }
+    }
+    wave_lds_sync();      // pD is rewritten by the next tile
   };
-  if (tile < q_end) {
-    while (step(bufA, bufB) && step(bufB, bufA)) {
-    }
+
+  // Quantized tiles through a ring of two: a tile is computed, then its
+  // registers take the loads of the tile two ahead (issued unconditionally:
+  // past the run they read nothing), so the next tile is in flight while one
+  // is computed.
+  for (int tile = w_begin; tile < q_end; tile += 2) {
+    if (buf0.new_seg) build_key_operands(buf0);
+    compute_tile(buf0);
+    load_tile(tile + 2, buf0);
+    if (tile + 1 >= q_end) break;
+    if (buf1.new_seg) build_key_operands(buf1);
+    compute_tile(buf1);
+    load_tile(tile + 3, buf1);
   }
 
-  // Tail chunks (bf16) after the quantized tiles.  Scores on the matrix
+  // Window chunks (bf16) after the quantized tiles.  Scores on the matrix
   // cores: A = the query in two bf16 rows per head (4 h: high part, 4 h + 1:
   // the rounding remainder, about 16 more bits), B = the chunk's Keys, so
   // lane (q4, col) receives head q4's score for token col -- the layout of
@@ -1278,7 +1486,7 @@ void decode_i8_kernel(DecodeArgs a0, PD pd) {
   for (int h = 0; h < GQA; ++h)
 #pragma unroll
     for (int k = 0; k < TCPL; ++k) acc_tail[k][h] = 0.0f;
-  if (has_chunks) {
+  if (ww.c0 < ww.c1) {
     bf8_t qa[HG][D / 32];
     {
       const int hq = col / 4, part = col % 4;
@@ -1288,24 +1496,24 @@ void decode_i8_kernel(DecodeArgs a0, PD pd) {
 #pragma unroll
         for (int mk = 0; mk < D / 32; ++mk) {
           uint4 w = make_uint4(0u, 0u, 0u, 0u);
-          if (h < GQA && part < 2) w = *reinterpret_cast<const uint4*>(&qsHL[part][h][32 * mk + 8 * q4]);
+          if (h < GQA && part < 2) w = *reinterpret_cast<const uint4*>(&qsHL[wave][part][h][32 * mk + 8 * q4]);
           qa[hg][mk] = __builtin_bit_cast(bf8_t, w);
         }
       }
     }
-    auto chunk_compute = [&](const ChunkRegs<D>& r) {
+    for (int chunk = ww.c0; chunk < ww.c1; ++chunk) {
       float al_u[GQA];
 #pragma unroll
       for (int hg = 0; hg < HG; ++hg) {
         f4_t sc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int mk = 0; mk < D / 32; ++mk)
-          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[hg][mk], __builtin_bit_cast(bf8_t, r.k[mk]), sc, 0, 0, 0);
-        const float x = col < r.nvalid ? sc[0] + sc[1] : -INFINITY;
-        const float mn = fmaxf(m[hg], row16_max(x));     // finite: a chunk has a valid token
+          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[hg][mk], __builtin_bit_cast(bf8_t, cr.k[mk]), sc, 0, 0, 0);
+        const float xs = col < cr.nvalid ? sc[0] + sc[1] : -INFINITY;
+        const float mn = fmaxf(m[hg], row16_max(xs));     // finite: a chunk has a valid token
         const float al = fast_exp2(m[hg] - mn);            // exp2(-inf) = 0 before the first token
         m[hg] = mn;
-        const float pr = fast_exp2(x - mn);                // 0 for padding tokens
+        const float pr = fast_exp2(xs - mn);               // 0 for padding tokens
         lsum[hg] = lsum[hg] * al + pr;
 #pragma unroll
         for (int n = 0; n < NV; ++n) acc_f[hg][n] *= al;
@@ -1318,8 +1526,8 @@ void decode_i8_kernel(DecodeArgs a0, PD pd) {
 #pragma unroll
       for (int t = 0; t < kTailChunk; ++t) {
         float v[TCPL];
-        v[0] = bf16_lo(r.v[t]);
-        if constexpr (TCPL == 2) v[1] = bf16_hi(r.v[t]);
+        v[0] = bf16_lo(cr.v[t]);
+        if constexpr (TCPL == 2) v[1] = bf16_hi(cr.v[t]);
 #pragma unroll
         for (int h = 0; h < GQA; ++h) {
           const float pt = pw[wave][t][h];
@@ -1329,13 +1537,7 @@ void decode_i8_kernel(DecodeArgs a0, PD pd) {
         }
       }
       wave_lds_sync();      // pw is rewritten by the next chunk
-    };
-    for (int chunk = ww.c0; chunk < ww.c1; chunk += 2) {
-      chunk_load(chunk + 1, crB);
-      chunk_compute(crA);
-      if (chunk + 1 >= ww.c1) break;
-      chunk_load(chunk + 2, crA);
-      chunk_compute(crB);
+      chunk_load(chunk + 1, cr);   // nothing is read past the run
     }
   }
 
@@ -1355,13 +1557,13 @@ void decode_i8_kernel(DecodeArgs a0, PD pd) {
   }
 
   // ---- wave result into red[wave][channel][head] ----
-  const float vscale_out = fv > 0.0f ? 1.0f / (fv * F16::kMul) : 0.0f;
+  constexpr float kOut = 1.0f / F16::kMul;
 #pragma unroll
   for (int hg = 0; hg < HG; ++hg) {
     const int h = 4 * hg + q4;
     if (h < GQA) {
 #pragma unroll
-      for (int n = 0; n < NV; ++n) red[wave][16 * n + col][h] = acc_f[hg][n] * vscale_out;
+      for (int n = 0; n < NV; ++n) red[wave][16 * n + col][h] = acc_f[hg][n] * kOut;
     }
   }
   wave_lds_sync();
@@ -1371,7 +1573,8 @@ void decode_i8_kernel(DecodeArgs a0, PD pd) {
 #pragma unroll
       for (int h = 0; h < GQA; ++h) red[wave][lane * TCPL + k][h] += acc_tail[k][h];
   }
-  fold_and_store<D, GQA>(a, unit, split, red, wml, mu, lu);
+  finish_unit<D, GQA>(a, unit, split, S, nn, a.n_new, slot0, red, wml, mu, lu,
+                      [&](int h, int c) { return qsC[0][h][c]; });
 }
 
 template <int D, int BITS, int GQA>
@@ -1402,24 +1605,18 @@ void launch(const DecodeArgs& a, const PagedDecode* pd, hipStream_t s) {
   } else {
     hipLaunchKernelGGL((decode_kernel<D, BITS, GQA>), grid, dim3(kThreads), 0, s, a, PagedDecode{});
   }
-  if (a.splits > 1 || a.force_part) {
+  if (!a.last_merge && (a.splits > 1 || a.n_new > 0)) {
+    // More splits than the in-kernel merge takes: a second kernel merges them,
+    // one workgroup per (batch, KV head, query head), 64 partials per round trip.
     const dim3 mgrid(a.g.B * a.g.H, GQA);
-    if (pd && a.n_new > 0) {
-      if (a.splits <= 8) hipLaunchKernelGGL((merge_kernel<D, GQA, 8, true, PagedDecode>), mgrid, dim3(D), 0, s, a, *pd);
-      else hipLaunchKernelGGL((merge_kernel<D, GQA, 32, true, PagedDecode>), mgrid, dim3(D), 0, s, a, *pd);
-    } else if (pd) {
-      if (a.splits <= 8) hipLaunchKernelGGL((merge_kernel<D, GQA, 8, false, PagedDecode>), mgrid, dim3(D), 0, s, a, *pd);
-      else if (a.splits <= 32) hipLaunchKernelGGL((merge_kernel<D, GQA, 32, false, PagedDecode>), mgrid, dim3(D), 0, s, a, *pd);
-      else hipLaunchKernelGGL((merge_kernel<D, GQA, 64, false, PagedDecode>), mgrid, dim3(D), 0, s, a, *pd);
-    } else if (a.n_new > 0) {
-      if (a.splits <= 8) hipLaunchKernelGGL((merge_kernel<D, GQA, 8, true>), mgrid, dim3(D), 0, s, a, NoPaging{});
-      else hipLaunchKernelGGL((merge_kernel<D, GQA, 32, true>), mgrid, dim3(D), 0, s, a, NoPaging{});
-    } else {
-      // one round trip for the partials of up to 8, 32 or 64 splits
-      if (a.splits <= 8) hipLaunchKernelGGL((merge_kernel<D, GQA, 8, false>), mgrid, dim3(D), 0, s, a, NoPaging{});
-      else if (a.splits <= 32) hipLaunchKernelGGL((merge_kernel<D, GQA, 32, false>), mgrid, dim3(D), 0, s, a, NoPaging{});
-      else hipLaunchKernelGGL((merge_kernel<D, GQA, 64, false>), mgrid, dim3(D), 0, s, a, NoPaging{});
-    }
+    if (pd && a.n_new > 0)
+      hipLaunchKernelGGL((merge_kernel<D, GQA, 64, true, PagedDecode>), mgrid, dim3(D), 0, s, a, *pd);
+    else if (pd)
+      hipLaunchKernelGGL((merge_kernel<D, GQA, 64, false, PagedDecode>), mgrid, dim3(D), 0, s, a, *pd);
+    else if (a.n_new > 0)
+      hipLaunchKernelGGL((merge_kernel<D, GQA, 64, true>), mgrid, dim3(D), 0, s, a, NoPaging{});
+    else
+      hipLaunchKernelGGL((merge_kernel<D, GQA, 64, false>), mgrid, dim3(D), 0, s, a, NoPaging{});
   }
 }
 
@@ -1451,9 +1648,12 @@ bool dispatch(const DecodeArgs& a, int gqa, hipStream_t s, const PagedDecode* pd
 }  // namespace
 
 int auto_splits(int units, int items) {
-  // Aim for about two workgroups per compute unit (256 CUs), at least four
-  // work items per workgroup, and never more splits than that allows.
-  int s = (2 * 256 + units - 1) / units;
+  // Aim for one workgroup per compute unit (256 CUs): a wave then has a run
+  // of several tiles, whose loads stream through the tile ring while earlier
+  // tiles are computed (at two workgroups per unit the Llama-3-8B call is a
+  // single burst of loads whose compute all comes after it: 16.2 us against
+  // 14.9 us).  At least four work items per workgroup.
+  int s = (256 + units - 1) / units;
   const int max_by_items = items / 4 > 0 ? items / 4 : 1;
   if (s > max_by_items) s = max_by_items;
   if (s > kMaxSplits) s = kMaxSplits;
@@ -1510,6 +1710,7 @@ DecodeArgs decode_args(const Geom& g, const kvq_state* st, const kvq_cache* cach
   a.q = q;
   a.qscale = softmax_scale * 1.4426950408889634f;
   a.out = out;
+  a.ctr = static_cast<uint32_t*>(workspace);
   a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + workspace_counter_bytes(g, 1));
   a.tiles_q = (a.nq + kTile - 1) / kTile;
   a.items = a.tiles_q + (a.nt + kTailChunk - 1) / kTailChunk;
@@ -1519,7 +1720,7 @@ DecodeArgs decode_args(const Geom& g, const kvq_state* st, const kvq_cache* cach
   a.tq_mod = a.tiles_q % a.splits;
   a.ch_div = (a.items - a.tiles_q) / a.splits;
   a.ch_mod = (a.items - a.tiles_q) % a.splits;
-  a.force_part = 0;
+  a.last_merge = a.splits <= kLastMergeSplits;
   a.k_new = nullptr;
   a.v_new = nullptr;
   a.ring_k = nullptr;
@@ -1578,7 +1779,6 @@ extern "C" kvq_status kvq_decode_step(const kvq_config* cfg, kvq_state* st, cons
                            workspace_size, stream);
   }
   DecodeArgs a = decode_args(g, st, cache, q, softmax_scale, num_splits, out, workspace);
-  a.force_part = 1;
   a.k_new = static_cast<const uint16_t*>(k_new);
   a.v_new = static_cast<const uint16_t*>(v_new);
   a.ring_k = static_cast<uint16_t*>(cache->k_tail);
@@ -1667,6 +1867,7 @@ kvq_status paged_decode_setup(const Geom& g, const kvq_state* st, const kvq_page
   if ((max_items + per_split - 1) / per_split > kMaxSplits) per_split = (max_items + kMaxSplits - 1) / kMaxSplits;
   pd.per_split = per_split;
   a.splits = (max_items + per_split - 1) / per_split;
+  a.last_merge = a.splits <= kLastMergeSplits;
   int wg = 0;
   for (int b = 0; b < kMaxPagedSeqs; ++b) {
     if (b < g.B) {
@@ -1740,7 +1941,6 @@ extern "C" kvq_status kvq_paged_decode_step(const kvq_config* cfg, kvq_state* st
   s = paged_decode_setup(g, st, cache, q, q_heads, softmax_scale, num_splits, out, workspace, workspace_size, &a,
                          &pd, &gqa);
   if (s != KVQ_OK) return s;
-  a.force_part = 1;
   a.k_new = static_cast<const uint16_t*>(k_new);
   a.v_new = static_cast<const uint16_t*>(v_new);
   a.ring_k = static_cast<uint16_t*>(cache->k_tail);

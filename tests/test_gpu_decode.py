@@ -69,7 +69,9 @@ def test_decode_split_invariance(splits):
     note(f"decode splits={splits}")
     got, _ = p.decode(q, num_splits=splits, ws=ws)
     assert max_abs(got, ref) <= TOL
-    # the workspace counters are left cleared: a second call on it is still right
+    # the arrival counters are left cleared: a second call on it is still right
+    torch.cuda.synchronize()
+    assert not ws[:64].any()
     got2, _ = p.decode(q, num_splits=splits, ws=ws)
     assert max_abs(got2, ref) <= TOL
 
@@ -194,3 +196,27 @@ def test_decode_graph_replay_matches_eager():
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, eager), r
+
+
+@needs_gpu
+@pytest.mark.parametrize("splits", [0, 8, 33, 64])
+def test_decode_many_calls_one_workspace(splits):
+    """96 calls queued back to back on one workspace, alternating over two
+    caches and four queries: every output is right, so no workgroup ever
+    merges a stale or missing partial, and the arrival counters end at 0."""
+    w = ks.small(ks.LLAMA3_DECODE, batch=2, kv_heads=4, q_heads=16)
+    pairs = [build(w, n, seed=seed)[0] for n, seed in ((1900, 3), (2600, 4))]
+    s = ks.Stream(w, seed=5)
+    qs = [ks.decode_query(s) for _ in range(4)]
+    refs = [[p.decode_ref(q) for q in qs] for p in pairs]
+    ws = pairs[0].cache.workspace(w.q_heads)
+    outs = []
+    note(f"decode 96 calls splits={splits}")
+    for i in range(96):
+        out = torch.empty(w.batch, w.q_heads, w.head_dim, device="cuda")
+        pairs[i % 2].cache.decode_attn(qs[(i // 2) % 4].cuda(), out, ws, num_splits=splits)
+        outs.append(out)
+    torch.cuda.synchronize()
+    for i, out in enumerate(outs):
+        assert max_abs(out.cpu().numpy(), refs[i % 2][(i // 2) % 4]) <= TOL, i
+    assert not ws[:64].any()

@@ -167,6 +167,9 @@ def test_paged_rejects_bad_calls():
         p.cache.append(k.float().cuda(), v.float().cuda(), [300, 10])
     with pytest.raises(kvq.KVQError):          # a count beyond the rows given
         p.cache.append(k.cuda(), v.cuda(), [301, 10])
+    with pytest.raises(kvq.KVQError):          # more rows than max(n_new): the row stride would be wrong
+        p.cache.append(k.cuda(), v.cuda(), [200, 10])
+    assert all(p.cache.states[b].total == 0 for b in range(2))
     p.append(k, v, [300, 10])
     q = ks.decode_query(s).cuda()
     out = torch.empty(2, 8, w.head_dim, device="cuda")
@@ -282,6 +285,9 @@ def test_paged_decode_step_errors_leave_states_unchanged():
     big_k, big_v = ks.kv_pair(s, 600)
     with pytest.raises(kvq.KVQError):          # capacity: sequence 0 would quantize 640 tokens into 8 pages of 64
         p.cache.decode_step(big_k.cuda(), big_v.cuda(), [600, 1], q, out, ws)
+    stage_k, stage_v = ks.kv_pair(s, 16)
+    with pytest.raises(kvq.KVQError):          # a 16-row staging buffer for one token each
+        p.cache.decode_step(stage_k.cuda(), stage_v.cuda(), [1, 1], q, out, ws)
     assert [(x.quantized, x.tail, x.total) for x in p.cache.states] == before
     p.check()
 
