@@ -113,3 +113,70 @@ def test_zero_inputs_give_saturated_scales_and_zero_codes():
     torch.cuda.synchronize()
     assert torch.all(p.cache.k_scale[:, :, :p.cache.state.segments] == 65504)
     assert not p.cache.k_codes.any() and not p.cache.v_codes.any()
+
+
+def _tie_rows(qmax, n_pairs, seed):
+    """(x, s, a) triples: x's float32 product with the fp16 scale s lands on a
+    half-integer that its exact product misses, and a range a whose stored
+    fp16 scale is s (so a row or column [a, x] quantizes x with s)."""
+    from fractions import Fraction
+
+    from exact import f32_tie_pairs, fr, nearest_f32
+    out = []
+    for x_t, sc in f32_tie_pairs(4 * n_pairs, qmax, seed=seed, scale_range=(2.0, 60.0)):
+        a = nearest_f32(Fraction(qmax) / fr(sc))
+        if np.float16(np.float32(qmax) / a) == sc and abs(x_t) <= a:
+            out.append((x_t, sc, a))
+        if len(out) == n_pairs:
+            return out
+    raise AssertionError("not enough tie pairs")
+
+
+@needs_gpu
+@pytest.mark.parametrize("bits,qmax,group", [(8, 7, 0), (4, 7, 64), (8, 127, 64)])
+def test_fp32_product_ties_bit_exact(bits, qmax, group):
+    """fp32 Keys and Values built so that the float32 product x * s of many
+    elements lands exactly on a half-integer while the exact product does
+    not, plus the round-half-even vector [7, 2.5, -2.5, 0.5, 1.5, -0.5, 3.5]
+    (scale 1) along both axes: the codes and scales the library writes equal
+    the oracle's bit for bit, and the tie elements' codes are the half-even
+    rounding of the float32 product (computed here by exact arithmetic)."""
+    from exact import fr, nearest_f32, round_half_even
+    D, H, n = (16 if bits == 8 else 32), 2, 64
+    w = ks.small(ks.TINY, batch=1, kv_heads=H, q_heads=H, head_dim=D, code_bits=bits, qmax=qmax,
+                 residual=8, group=group, kv_dtype="f32")
+    k = np.zeros((1, H, n + w.residual, D), np.float32)
+    v = np.zeros_like(k)
+    trip = _tie_rows(qmax, H * D + H * n, seed=bits * 1000 + qmax)
+    expect_k, expect_v = {}, {}
+    it = iter(trip)
+    for h in range(H):                       # Keys: channel c holds [a, x] at tokens 2c, 2c + 1
+        for c in range(D - 1):
+            x_t, sc, a = next(it)
+            k[0, h, 2 * c, c], k[0, h, 2 * c + 1, c] = a, x_t
+            expect_k[(h, 2 * c + 1, c)] = round_half_even(fr(nearest_f32(fr(x_t) * fr(sc))))
+        if qmax >= 7:                        # the tie vector down the last channel
+            k[0, h, 40:47, D - 1] = [7, 2.5, -2.5, 0.5, 1.5, -0.5, 3.5]
+    for h in range(H):                       # Values: token t holds [a, x, 0, ...]
+        for t in range(n):
+            x_t, sc, a = next(it)
+            v[0, h, t, 0], v[0, h, t, 1] = a, x_t
+            expect_v[(h, t, 1)] = round_half_even(fr(nearest_f32(fr(x_t) * fr(sc))))
+        if qmax >= 7:
+            v[0, h, n - 1, :7] = [7, 2.5, -2.5, 0.5, 1.5, -0.5, 3.5]
+            v[0, h, n - 1, 7:] = 0.0
+            expect_v.pop((h, n - 1, 1), None)
+    p = Pair(w, 256)
+    note(f"fp32 ties bits={bits} qmax={qmax} group={group}")
+    p.append(torch.from_numpy(k), torch.from_numpy(v))
+    p.check_state()
+    p.check_buffers()                         # device bytes == oracle images
+    from oracle.cache import stacked_codes
+    kc, vc = stacked_codes(p.ost, "key")[0], stacked_codes(p.ost, "value")[0]
+    for (h, t, c), want in expect_k.items():
+        assert int(kc[h, t, c]) == max(-qmax, min(qmax, want)), ("key", h, t, c)
+    for (h, t, c), want in expect_v.items():
+        assert int(vc[h, t, c]) == max(-qmax, min(qmax, want)), ("value", h, t, c)
+    if qmax == 7:
+        assert kc[0, 40:47, D - 1].tolist() == [7, 2, -2, 0, 2, 0, 4]
+        assert vc[0, n - 1, :7].tolist() == [7, 2, -2, 0, 2, 0, 4]
