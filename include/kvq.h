@@ -193,6 +193,22 @@ kvq_status kvq_decode_attn(const kvq_config* cfg, const kvq_state* st, const kvq
                            int32_t num_splits, float* out, void* workspace,
                            size_t workspace_bytes, void* stream);
 
+/* kvq_decode_attn for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, computation and errors as kvq_decode_attn, without the
+ * workspace: the split partials and arrival counters live in a device array
+ * of 8 MiB inside the library, one per GPU, held until the process ends
+ * (its address is looked up on the first call on each device).  Calls whose
+ * partials need more than that -- batch * q_heads * splits * (head_dim + 4)
+ * floats plus the counters -- return KVQ_EWORKSPACE.  The counters start at
+ * zero and every call leaves them at zero.  All calls on one GPU share the
+ * array: calls that overlap on one GPU (different streams, or threads) race
+ * and must be ordered by the caller.  Nothing is allocated or freed.
+ * Errors: KVQ_EINVAL, KVQ_EWORKSPACE, KVQ_EDEVICE. */
+kvq_status kvq_decode_attn_noalloc(const kvq_config* cfg, const kvq_state* st, const kvq_cache* cache,
+                                   const void* q, int32_t q_heads, float softmax_scale,
+                                   int32_t num_splits, float* out, void* stream);
+
 /* One decode step: append n_new tokens, then attend with q over the whole
  * cache including them -- the per-step order encode, append, attend of
  * "KV Cache quantization and compression", section 02.  The result is that

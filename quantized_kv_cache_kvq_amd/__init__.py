@@ -25,7 +25,8 @@ KVQ_BF16, KVQ_F32 = 0, 1
 EXPORTED = ("kvq_buffer_sizes", "kvq_plan_append", "kvq_append", "kvq_workspace_size",
             "kvq_workspace_init", "kvq_decode_attn", "kvq_decode_step", "kvq_block_attn",
             "kvq_restore", "kvq_paged_page_bytes", "kvq_paged_append", "kvq_paged_decode_attn",
-            "kvq_paged_decode_step", "kvq_paged_block_attn", "kvq_paged_restore", "kvq_status_str")
+            "kvq_paged_decode_step", "kvq_paged_block_attn", "kvq_paged_restore", "kvq_status_str",
+            "kvq_decode_attn_noalloc")
 
 
 class kvq_config(ctypes.Structure):
@@ -99,6 +100,7 @@ def load() -> ctypes.CDLL:
                                   i32, vp, vp, sz, vp],
         "kvq_workspace_init": [vp, sz, vp],
         "kvq_decode_attn": [P(kvq_config), P(kvq_state), P(kvq_cache), vp, i32, f32, i32, vp, vp, sz, vp],
+        "kvq_decode_attn_noalloc": [P(kvq_config), P(kvq_state), P(kvq_cache), vp, i32, f32, i32, vp, vp],
         "kvq_decode_step": [P(kvq_config), P(kvq_state), P(kvq_cache), vp, vp, i64, vp, i32, f32, i32,
                             vp, vp, sz, vp],
         "kvq_block_attn": [P(kvq_config), P(kvq_state), P(kvq_cache), vp, vp, vp, i32, i32, i32, f32,
@@ -248,6 +250,12 @@ def kvq_decode_attn(cfg, st, cache, q, q_heads, softmax_scale, num_splits, out, 
     _check(load().kvq_decode_attn(ctypes.byref(cfg), ctypes.byref(st), ctypes.byref(cache), _ptr(q),
                                   q_heads, softmax_scale, num_splits, _ptr(out), _ptr(ws),
                                   ws.numel() * ws.element_size(), _stream(stream)), "kvq_decode_attn")
+
+
+def kvq_decode_attn_noalloc(cfg, st, cache, q, q_heads, softmax_scale, num_splits, out, stream=None):
+    _check(load().kvq_decode_attn_noalloc(ctypes.byref(cfg), ctypes.byref(st), ctypes.byref(cache), _ptr(q),
+                                          q_heads, softmax_scale, num_splits, _ptr(out), _stream(stream)),
+           "kvq_decode_attn_noalloc")
 
 
 def kvq_decode_step(cfg, st, cache, k_new, v_new, n_new, q, q_heads, softmax_scale, num_splits, out, ws,

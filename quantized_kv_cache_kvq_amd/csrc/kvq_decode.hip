@@ -32,6 +32,8 @@
 //     ALUs.
 // A second, small kernel merges the split partials.
 // Hot-loop indexing is 32-bit; ring slots wrap with one subtraction.
+#include <mutex>
+
 #include "kvq_internal.h"
 
 namespace kvq {
@@ -1711,7 +1713,8 @@ DecodeArgs decode_args(const Geom& g, const kvq_state* st, const kvq_cache* cach
   a.qscale = softmax_scale * 1.4426950408889634f;
   a.out = out;
   a.ctr = static_cast<uint32_t*>(workspace);
-  a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + workspace_counter_bytes(g, 1));
+  a.part = workspace ? reinterpret_cast<float*>(static_cast<char*>(workspace) + workspace_counter_bytes(g, 1))
+                     : nullptr;
   a.tiles_q = (a.nq + kTile - 1) / kTile;
   a.items = a.tiles_q + (a.nt + kTailChunk - 1) / kTailChunk;
   const int units = g.B * g.H;
@@ -1744,6 +1747,64 @@ extern "C" kvq_status kvq_decode_attn(const kvq_config* cfg, const kvq_state* st
   s = check_decode(g, st, cache, q, q_heads, softmax_scale, num_splits, out, workspace, workspace_size, &gqa);
   if (s != KVQ_OK) return s;
   const DecodeArgs a = decode_args(g, st, cache, q, softmax_scale, num_splits, out, workspace);
+  clear_stale_hip_error();
+  if (!dispatch(a, gqa, static_cast<hipStream_t>(stream))) return KVQ_EINVAL;
+  return hipGetLastError() == hipSuccess ? KVQ_OK : KVQ_EDEVICE;
+}
+
+// ---- decode attention without a caller workspace ---------------------------
+// For callers that cannot allocate (code under HIP graph capture, serving
+// loops, harnesses that forbid hipMalloc): the split partials and arrival
+// counters live in one file-scope device array of kScratchBytes per GPU,
+// held until the process ends.  In host code the array's name only stands in
+// for the symbol: its device address comes from hipGetSymbolAddress, taken
+// once per device (with that device current) on the first call there.
+namespace kvq {
+namespace {
+constexpr size_t kScratchBytes = size_t(8) << 20;
+constexpr int kMaxScratchDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxScratchDevices] = {};
+
+// The scratch array's device address on the current device.
+kvq_status scratch_on_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) return KVQ_EDEVICE;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return KVQ_EDEVICE;
+    scratch_ptr[dev] = p;
+  }
+  *out = scratch_ptr[dev];
+  return KVQ_OK;
+}
+}  // namespace
+}  // namespace kvq
+
+extern "C" kvq_status kvq_decode_attn_noalloc(const kvq_config* cfg, const kvq_state* st, const kvq_cache* cache,
+                                              const void* q, int32_t q_heads, float softmax_scale,
+                                              int32_t num_splits, float* out, void* stream) {
+  Geom g;
+  kvq_status s = validate_config(cfg, &g);
+  if (s != KVQ_OK) return s;
+  int gqa = 0;
+  // every check of kvq_decode_attn except the caller's workspace (a dummy,
+  // large enough, stands in for it until the real size is known)
+  const void* dummy = cfg;
+  s = check_decode(g, st, cache, q, q_heads, softmax_scale, num_splits, out, dummy, SIZE_MAX, &gqa);
+  if (s != KVQ_OK) return s;
+  DecodeArgs a = decode_args(g, st, cache, q, softmax_scale, num_splits, out, nullptr);
+  // counters, then the partials of this call's split count
+  const size_t need = workspace_counter_bytes(g, 1) +
+                      (size_t)g.B * q_heads * a.splits * (g.D + 4) * sizeof(float);
+  if (need > kScratchBytes) return KVQ_EWORKSPACE;
+  void* ws = nullptr;
+  s = scratch_on_current_device(&ws);
+  if (s != KVQ_OK) return s;
+  a.ctr = static_cast<uint32_t*>(ws);
+  a.part = reinterpret_cast<float*>(static_cast<char*>(ws) + workspace_counter_bytes(g, 1));
   clear_stale_hip_error();
   if (!dispatch(a, gqa, static_cast<hipStream_t>(stream))) return KVQ_EINVAL;
   return hipGetLastError() == hipSuccess ? KVQ_OK : KVQ_EDEVICE;
