@@ -41,20 +41,19 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 
-# HBM bytes per decode call (decode_i8_kernel + merge_kernel), from separate
-# rocprofv3 --pmc passes of FETCH_SIZE and WRITE_SIZE over the same commands
-# bench.py runs, each scaled by what the counter reads for the hbm_copy
-# workload's known 256 MiB read + 256 MiB write (FETCH_SIZE x 2,
-# WRITE_SIZE x 1).  They describe the kernels in
-# profiles/decode_i8_*.md (paged: profiles/paged_decode_*.md) and are to be
-# reset to None when those change.
-DECODE_CALL_TRAFFIC = 41_405_030     # 4096-token Llama-3-8B shape (algorithmic 38.04 MB)
-LONG_CALL_TRAFFIC = 143_130_419      # one 131072-token layer (algorithmic 138.8 MB)
-# Same measurement for the other workloads: 128 appends (16 flushes + 128
-# window copies) and one block-attention call (block_kernel + block_merge_kernel).
-APPEND_RUN_TRAFFIC = {4: 444219392, 8: 478773248}
+# HBM bytes per call from separate rocprofv3 --pmc passes of FETCH_SIZE and
+# WRITE_SIZE over the same commands bench.py runs, each scaled by what the
+# counter reads for the hbm_copy workload's known 256 MiB read + 256 MiB
+# write (FETCH_SIZE x 2, WRITE_SIZE x 1).  Each describes the kernels named
+# in profiles/ and is None while those kernels have changed since the
+# counters were taken.
+DECODE_CALL_TRAFFIC = 39_771_465     # decode_i8_kernel, 4096-token Llama-3-8B shape (algorithmic 37.78 MB)
+LONG_CALL_TRAFFIC = None             # one 131072-token layer (algorithmic 138.8 MB)
+# 128 appends (16 flushes + 128 window copies) and one block-attention call
+# (block_kernel + block_merge_kernel).
+APPEND_RUN_TRAFFIC = {4: None, 8: None}
 BLOCK_CALL_TRAFFIC = 2_009_669_018    # the cache is streamed once per query-row tile
-PAGED_CALL_TRAFFIC = 44_977_562       # paged decode, ragged lengths (algorithmic 41.42 MB)
+PAGED_CALL_TRAFFIC = None             # paged decode, ragged lengths (algorithmic 41.42 MB)
 PAGED_BLOCK_CALL_TRAFFIC = 2_067_186_586   # the video block over a paged cache
 
 
@@ -212,7 +211,7 @@ def run_decode(args, log):
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": DECODE_CALL_TRAFFIC,
-                     "kernel": "kvq_decode_attn = decode_i8_kernel<128,4,4> + merge_kernel<128,4,8>"},
+                     "kernel": "kvq_decode_attn = decode_i8_kernel<128,4,4> (splits merged in-kernel)"},
     }
     return res, (cfg, w)
 
@@ -443,7 +442,7 @@ def run_paged_decode(args, log):
         "ragged_step_us_two_calls": round(results["step"][1], 3),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": PAGED_CALL_TRAFFIC,
-                     "kernel": "kvq_paged_decode_attn = decode_i8_kernel<128,4,4,paged> + merge_kernel<128,4,32,paged>"},
+                     "kernel": "kvq_paged_decode_attn = decode_i8_kernel<128,4,4,paged> (splits merged in-kernel)"},
     }
 
 
@@ -632,7 +631,7 @@ def run_long_decode(args, log):
         "bytes_per_step": int(nbytes),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": LONG_CALL_TRAFFIC,
-                     "kernel": "kvq_decode_attn = decode_i8_kernel<128,4,4> + merge_kernel<128,4,64>"},
+                     "kernel": "kvq_decode_attn = decode_i8_kernel<128,4,4> (splits merged in-kernel)"},
     }
 
 
@@ -745,15 +744,21 @@ def run_append(args, log, bits: int):
     }
 
 
-def cpu_baseline_decode(budget_s: float, log):
-    """Time the CPU oracle's decode attention on a bounded sample of units."""
-    import numpy as np
-    from threadpoolctl import threadpool_limits
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
 
+
+def _oracle_decode_case():
+    """The oracle's state and query for the Llama-3-8B int4 decode workload."""
     import kvq_synth as ks
-    from oracle import attention as oatt
     from oracle.cache import KVQuantizationStrategies
-    from quantized_kv_cache_kvq_amd import make_config
 
     w = ks.LLAMA3_DECODE
     s = ks.Stream(w, seed=0)
@@ -761,31 +766,68 @@ def cpu_baseline_decode(budget_s: float, log):
     o = KVQuantizationStrategies(qmax=w.qmax, scale_storage="fp16", group=w.group)
     st = o.append_and_partition(None, k.float().numpy(), v.float().numpy(), w.residual)
     q = ks.decode_query(s).float().numpy()
+    return w, st, q
+
+
+def _oracle_units_worker(units, budget_s):
+    """One process's share of the decode call: the oracle over its (batch,
+    KV head) units, repeated for about budget_s seconds, one thread."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import attention as oatt
+    w, st, q = _oracle_decode_case()
     sigma = 1.0 / math.sqrt(w.head_dim)
+    with threadpool_limits(limits=1):
+        oatt.decode_attention(st, q, sigma, units=units)      # warm
+        reps, t = 0, time.perf_counter()
+        while True:
+            oatt.decode_attention(st, q, sigma, units=units)
+            reps += 1
+            if time.perf_counter() - t >= budget_s:
+                break
+    return reps, time.perf_counter() - t
+
+
+def cpu_baseline_decode(budget_s: float, log):
+    """The CPU oracle's decode attention on the Llama-3-8B int4 workload:
+    whole calls (all 64 (batch, KV head) units) on one thread, then the same
+    units split over one process per host core (the per-process call time is
+    the slowest share's).  Runs before the GPU is touched."""
+    import concurrent.futures
+    import multiprocessing
+
+    from quantized_kv_cache_kvq_amd import make_config
+
+    w, st, q = _oracle_decode_case()
     cfg = make_config(batch=1, kv_heads=1, head_dim=w.head_dim, capacity=w.prefill,
                       code_bits=w.code_bits, qmax=w.qmax, residual=w.residual, group=w.group)
     nq, nt = st["quantized_tokens"], st["key_residual"].shape[-2]
     unit_bytes = decode_bytes(cfg, nq, nt, w.q_heads // w.kv_heads)
     units = [(b, h) for b in range(w.batch) for h in range(w.kv_heads)]
-    # Whole decode calls (all 64 units) repeated until the budget is spent.
-    with threadpool_limits(limits=1):
-        calls = 0
-        t = time.perf_counter()
-        while True:
-            oatt.decode_attention(st, q, sigma)
-            calls += 1
-            dt = time.perf_counter() - t
-            if dt >= budget_s:
-                break
-    n = calls * len(units)
-    log(f"cpu oracle: {calls} decode calls in {dt:.2f}s")
-    return {"value": round(n * unit_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle",
-            "sample": f"{calls} full fp64 decode-attention calls (restore + softmax over all "
-                      f"{len(units)} (batch, KV head) units) of the Llama-3-8B int4 workload "
-                      f"at {w.prefill} tokens, one thread, {dt:.1f} s; "
-                      f"{dt / calls * 1e3:.1f} ms per call",
-            "cpu": platform.processor() or platform.machine()}
+    call_bytes = len(units) * unit_bytes
+    reps1, dt1 = _oracle_units_worker(units, budget_s / 2)
+    one = call_bytes * reps1 / dt1 / 1e9
+    try:
+        ncpu = len(os.sched_getaffinity(0))
+    except AttributeError:
+        ncpu = os.cpu_count() or 1
+    n = max(1, min(16, ncpu, len(units)))
+    shares = [units[i::n] for i in range(n)]
+    ctx = multiprocessing.get_context("spawn")
+    with concurrent.futures.ProcessPoolExecutor(max_workers=n, mp_context=ctx) as ex:
+        res = list(ex.map(_oracle_units_worker, shares, [budget_s / 2] * n))
+    per_call = max(dt / reps for reps, dt in res)      # the slowest share sets the call
+    alln = call_bytes / per_call / 1e9
+    log(f"cpu oracle: {dt1 / reps1 * 1e3:.1f} ms per call on 1 thread, {per_call * 1e3:.1f} ms on {n} processes")
+    return {"value": round(alln, 4), "unit": "GB/s", "cores": n, "kind": "oracle",
+            "sample": f"full fp64 decode-attention calls (restore + softmax over all {len(units)} "
+                      f"(batch, KV head) units) of the Llama-3-8B int4 workload at {w.prefill} tokens: "
+                      f"{per_call * 1e3:.1f} ms per call with the units split over {n} single-thread "
+                      f"processes (the slowest share's time, {budget_s / 2:.0f} s each), "
+                      f"{dt1 / reps1 * 1e3:.1f} ms per call on one thread ({reps1} calls)",
+            "value_1thread": round(one, 4), "ms_per_call": round(per_call * 1e3, 2),
+            "ms_per_call_1thread": round(dt1 / reps1 * 1e3, 2),
+            "cpu": _cpu_model(), "nproc": os.cpu_count()}
 
 
 def run_hbm_copy(args, log):
@@ -985,6 +1027,9 @@ def main():
         if not args.quiet:
             print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
+    cpu = None
+    if args.workload == "llama3_decode" and not args.no_cpu_baseline:
+        cpu = cpu_baseline_decode(args.cpu_budget, log)      # before anything touches the GPU
     import torch
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -1014,8 +1059,8 @@ def main():
         res = run_append(args, log, 8 if args.workload == "append_int8" else 4)
     else:
         res, _ = run_decode(args, log)
-        if not args.no_cpu_baseline:
-            res["cpu_baseline"] = cpu_baseline_decode(args.cpu_budget, log)
+        if cpu is not None:
+            res["cpu_baseline"] = cpu
     print(json.dumps(res), flush=True)
 
 

@@ -18,6 +18,8 @@
 //   2. tail_kernel   -- copies the new tokens that stay in the window into
 //      their ring slots.  It runs after the flush because a ring slot being
 //      refilled may hold a token the flush is still reading.
+#include <type_traits>
+
 #include "kvq_internal.h"
 
 namespace kvq {
@@ -54,6 +56,19 @@ struct FlushArgs {
   int head_bytes;          // 128 W + 128 + 2 D
   int seq;                 // sequence index (window and input rows: seq * H + head)
 };
+
+constexpr int kMaxPagedSeqs = 64;
+
+// Paged appends flush every sequence in one launch (grid.z = sequence):
+// each sequence's accounting before the append and its segment count.
+struct PagedFlushSeqs {
+  int nq_old[kMaxPagedSeqs];
+  int nt_old[kMaxPagedSeqs];
+  int seg_base[kMaxPagedSeqs];
+  int nseg[kMaxPagedSeqs];       // segments this sequence flushes (0: its workgroups exit)
+  int table_stride;              // block-table row length
+};
+struct NoPagedSeqs {};
 
 // Base of KV head h's part of the page holding tile `tile` (paged caches);
 // out-of-range page numbers are clamped into the pool.
@@ -263,12 +278,25 @@ __device__ __forceinline__ void flush_values(const FlushArgs& a, int bh, int vw,
   }
 }
 
-// kPaged: codes and scales go to the sequence's pages (a.pool, a.table).
+// kPaged: codes and scales go to the sequence's pages (a.pool, a.table);
+// grid.z runs over the sequences, whose accounting comes from ps.
 template <int BITS, bool kPaged>
-__global__ __launch_bounds__(kFlushThreads) void flush_kernel(FlushArgs a) {
-  const int bh = kPaged ? a.seq * a.g.H + (int)blockIdx.y : (int)blockIdx.y;
+__global__ __launch_bounds__(kFlushThreads) void flush_kernel(FlushArgs a0,
+                                                              typename std::conditional<kPaged, PagedFlushSeqs, NoPagedSeqs>::type ps) {
+  FlushArgs a = a0;
   const int per_seg = 1 + a.v_wgs;
   const int64_t sl = blockIdx.x / per_seg;
+  if constexpr (kPaged) {
+    const int b = blockIdx.z;
+    if (sl >= ps.nseg[b]) return;                // this sequence flushes fewer segments
+    a.seq = b;
+    a.nq_old = ps.nq_old[b];
+    a.nt_old = ps.nt_old[b];
+    a.nq_slot_old = ps.nq_old[b] % a.g.ring;
+    a.seg_base = ps.seg_base[b];
+    a.table = a0.table + (int64_t)b * ps.table_stride;
+  }
+  const int bh = kPaged ? a.seq * a.g.H + (int)blockIdx.y : (int)blockIdx.y;
   const int role = blockIdx.x % per_seg;
   const int64_t seg = a.seg_base + sl;
   const int64_t p0 = a.nq_old + sl * a.seg_len;
@@ -313,9 +341,11 @@ __global__ __launch_bounds__(256) void tail_kernel(TailArgs a) {
   *dst = *src;
 }
 
-// Segment geometry of a flush of `flush` tokens after nq_old, and the launch
-// (grid.y: the (batch, head) units, or a paged sequence's heads).
-void launch_flush(const Geom& g, FlushArgs& a, int64_t flush, unsigned grid_y, hipStream_t hs) {
+// Segment geometry of a flush of `flush` tokens after nq_old (paged: the
+// most any sequence flushes), and the launch (grid.y: the (batch, head)
+// units, or the heads of every paged sequence, grid.z: the sequences).
+void launch_flush(const Geom& g, FlushArgs& a, int64_t flush, unsigned grid_y, hipStream_t hs,
+                  const PagedFlushSeqs* ps = nullptr) {
   a.seg_len = g.G == 0 ? flush : g.G;
   a.pieces = g.D * (g.dtype == KVQ_BF16 ? 2 : 4) / 16;
   const int per_tile = (kTile / (32 / g.bits)) * a.pieces;   // Value units of one tile
@@ -325,25 +355,23 @@ void launch_flush(const Geom& g, FlushArgs& a, int64_t flush, unsigned grid_y, h
   const int64_t seg_tiles = (p1 + kTile - 1) / kTile - p0 / kTile;
   a.v_wgs = static_cast<int>((seg_tiles + a.v_tiles_per_wg - 1) / a.v_tiles_per_wg);
   const int64_t nseg = flush / a.seg_len;
-  dim3 grid(static_cast<unsigned>(nseg * (1 + a.v_wgs)), grid_y);
-  const bool paged = a.pool != nullptr;
+  dim3 grid(static_cast<unsigned>(nseg * (1 + a.v_wgs)), grid_y, ps ? static_cast<unsigned>(g.B) : 1u);
+  const NoPagedSeqs np{};
   switch (g.bits) {
     case 8:
-      if (paged) hipLaunchKernelGGL((flush_kernel<8, true>), grid, dim3(kFlushThreads), 0, hs, a);
-      else hipLaunchKernelGGL((flush_kernel<8, false>), grid, dim3(kFlushThreads), 0, hs, a);
+      if (ps) hipLaunchKernelGGL((flush_kernel<8, true>), grid, dim3(kFlushThreads), 0, hs, a, *ps);
+      else hipLaunchKernelGGL((flush_kernel<8, false>), grid, dim3(kFlushThreads), 0, hs, a, np);
       break;
     case 4:
-      if (paged) hipLaunchKernelGGL((flush_kernel<4, true>), grid, dim3(kFlushThreads), 0, hs, a);
-      else hipLaunchKernelGGL((flush_kernel<4, false>), grid, dim3(kFlushThreads), 0, hs, a);
+      if (ps) hipLaunchKernelGGL((flush_kernel<4, true>), grid, dim3(kFlushThreads), 0, hs, a, *ps);
+      else hipLaunchKernelGGL((flush_kernel<4, false>), grid, dim3(kFlushThreads), 0, hs, a, np);
       break;
     default:
-      if (paged) hipLaunchKernelGGL((flush_kernel<2, true>), grid, dim3(kFlushThreads), 0, hs, a);
-      else hipLaunchKernelGGL((flush_kernel<2, false>), grid, dim3(kFlushThreads), 0, hs, a);
+      if (ps) hipLaunchKernelGGL((flush_kernel<2, true>), grid, dim3(kFlushThreads), 0, hs, a, *ps);
+      else hipLaunchKernelGGL((flush_kernel<2, false>), grid, dim3(kFlushThreads), 0, hs, a, np);
       break;
   }
 }
-
-constexpr int kMaxPagedSeqs = 64;
 
 struct PagedTailArgs {
   const uint8_t* k_new;
@@ -523,10 +551,21 @@ extern "C" kvq_status kvq_paged_append(const kvq_config* cfg, kvq_state* st, con
   if (!k_new || !v_new) return KVQ_EINVAL;
   hipStream_t hs = static_cast<hipStream_t>(stream);
   clear_stale_hip_error();
-  // each sequence flushes its own overflow into its own pages
-  for (int b = 0; b < g.B; ++b) {
-    const int64_t flush = next[b].flushed_last;
-    if (flush == 0) continue;
+  // every sequence flushes its own overflow into its own pages: one launch,
+  // grid.z over the sequences
+  PagedFlushSeqs ps;
+  int64_t max_flush = 0;
+  for (int b = 0; b < kMaxPagedSeqs; ++b) {
+    ps.nq_old[b] = ps.nt_old[b] = ps.seg_base[b] = ps.nseg[b] = 0;
+    if (b >= g.B) continue;
+    ps.nq_old[b] = static_cast<int>(st[b].quantized);
+    ps.nt_old[b] = static_cast<int>(st[b].tail);
+    ps.seg_base[b] = static_cast<int>(st[b].segments);
+    ps.nseg[b] = static_cast<int>(next[b].flushed_last / g.G);
+    max_flush = next[b].flushed_last > max_flush ? next[b].flushed_last : max_flush;
+  }
+  ps.table_stride = cache->table_stride;
+  if (max_flush > 0) {
     FlushArgs a;
     a.g = g;
     a.k_new = k_new;
@@ -539,17 +578,16 @@ extern "C" kvq_status kvq_paged_append(const kvq_config* cfg, kvq_state* st, con
     a.k_scale = nullptr;
     a.v_scale = nullptr;
     a.seg_index = nullptr;
-    a.nq_old = st[b].quantized;
-    a.nt_old = st[b].tail;
-    a.nq_slot_old = static_cast<int>(st[b].quantized % g.ring);
-    a.seg_base = st[b].segments;
+    a.nq_old = a.nt_old = 0;           // per sequence, from ps
+    a.nq_slot_old = 0;
+    a.seg_base = 0;
     a.pool = static_cast<uint8_t*>(cache->pool);
-    a.table = cache->block_table + (int64_t)b * cache->table_stride;
+    a.table = cache->block_table;      // row b: table + b * table_stride
     a.n_pages = cache->n_pages;
     a.page_bytes = page_bytes;
     a.head_bytes = 2 * kTile * g.W + 2 * kTile + 2 * g.D;
-    a.seq = b;
-    launch_flush(g, a, flush, static_cast<unsigned>(g.H), hs);
+    a.seq = 0;
+    launch_flush(g, a, max_flush, static_cast<unsigned>(g.H), hs, &ps);
   }
   // then the tokens that stay in each window
   PagedTailArgs t;

@@ -380,6 +380,30 @@ def test_paged_maximum_batch_of_64_sequences():
 
 
 @needs_gpu
+def test_paged_append_all_64_sequences_flush_in_one_call():
+    """One kvq_paged_append in which every one of 64 sequences flushes (one
+    or two 128-token groups, from different starting tails): all of them go
+    through a single flush launch, and every page, window and counter
+    matches the oracle run on that sequence alone."""
+    w = ks.small(ks.LLAMA3_DECODE, batch=64, kv_heads=2, q_heads=4, head_dim=64)
+    p = PagedPair(w, stride=10, seed=640)
+    s = ks.Stream(w)
+    first = [100 + b for b in range(64)]                  # 100 .. 163 tokens: no flush yet
+    k, v = ks.kv_pair(s, max(first))
+    p.append(k, v, first)
+    assert all(p.cache.states[b].quantized == 0 for b in range(64))
+    second = [160 + (b % 5) * 40 for b in range(64)]     # every tail passes residual + group
+    nxt = [kvq.kvq_plan_append(p.cfg, p.cache.states[b], second[b]) for b in range(64)]
+    assert all(x.flushed_last > 0 for x in nxt) and {x.flushed_last for x in nxt} == {128, 256}
+    k, v = ks.kv_pair(s, max(second))
+    note("paged append: 64 sequences flushing together")
+    p.append(k, v, second)
+    p.check()
+    q = ks.decode_query(s)
+    assert max_abs(p.decode(q), p.decode_ref(q)) <= TOL
+
+
+@needs_gpu
 def test_paged_decode_step_fp32_takes_the_two_calls():
     """fp32 windows: every step runs kvq_paged_append then kvq_paged_decode_attn
     inside the one call; outputs and states still match the oracle."""
