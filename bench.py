@@ -48,12 +48,12 @@ HBM_PEAK_GBS = 8000.0
 # in profiles/ and is None while those kernels have changed since the
 # counters were taken.
 DECODE_CALL_TRAFFIC = 39_771_465     # decode_i8_kernel, 4096-token Llama-3-8B shape (algorithmic 37.78 MB)
-LONG_CALL_TRAFFIC = None             # one 131072-token layer (algorithmic 138.8 MB)
+LONG_CALL_TRAFFIC = 140_361_300      # one 131072-token layer (algorithmic 138.8 MB)
 # 128 appends (16 flushes + 128 window copies) and one block-attention call
 # (block_kernel + block_merge_kernel).
-APPEND_RUN_TRAFFIC = {4: None, 8: None}
+APPEND_RUN_TRAFFIC = {4: 444_227_127, 8: 478_851_968}
 BLOCK_CALL_TRAFFIC = 2_009_669_018    # the cache is streamed once per query-row tile
-PAGED_CALL_TRAFFIC = None             # paged decode, ragged lengths (algorithmic 41.42 MB)
+PAGED_CALL_TRAFFIC = 44_925_590      # paged decode, ragged lengths (algorithmic 41.42 MB)
 PAGED_BLOCK_CALL_TRAFFIC = 2_067_186_586   # the video block over a paged cache
 
 

@@ -32,9 +32,15 @@ __global__ __launch_bounds__(kThreads) void stream_read_kernel(const uint4* __re
 #pragma unroll
     for (int k = 0; k < DEPTH; ++k) acc ^= v[k].x ^ v[k].y ^ v[k].z ^ v[k].w;
   }
-  for (int64_t i = full_end + threadIdx.x; i < end; i += kThreads) {   // ragged last round
-    const uint4 v = p[i];
-    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  if (full_end < end) {                         // the ragged last round, DEPTH loads in flight
+    uint4 v[DEPTH];
+#pragma unroll
+    for (int k = 0; k < DEPTH; ++k) {
+      const int64_t i = full_end + threadIdx.x + (int64_t)k * kThreads;
+      v[k] = i < end ? p[i] : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int k = 0; k < DEPTH; ++k) acc ^= v[k].x ^ v[k].y ^ v[k].z ^ v[k].w;
   }
   __shared__ uint32_t red;
   if (threadIdx.x == 0) red = 0u;
