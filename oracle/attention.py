@@ -9,7 +9,9 @@ h reads KV head floor(h / g) (section 04, ``attn_full`` / ``attn_step``).
 
 The cache supplies, per (batch, KV head), the restored quantized prefix
 (codes / max(scale, eps), "KV Cache Quantization Strategies" Step 4
-``restore``) followed by the high-precision tail; for decode the newest
+``restore``, with the scale of the token's segment and channel for KIVI Keys
+or of the token's run of channels in same-axis mode) followed by the
+high-precision tail; for decode the newest
 token has already been appended, so it is visible ("KV Cache quantization
 and compression", section 02 pseudo-code: append, then attention).
 
@@ -37,7 +39,7 @@ from __future__ import annotations
 import numpy as np
 
 from .cache import key_scales, segment_of_tokens, stacked_codes, value_scales
-from .codec import restore
+from .codec import restore, restore_grouped_per_token
 
 
 def attention_rows(q_rows, K, V, sigma: float, visible=None, mask=None) -> np.ndarray:
@@ -67,6 +69,7 @@ class _Joined:
         self.k_scales = key_scales(state)
         self.v_scales = value_scales(state)
         self.seg = segment_of_tokens(state)
+        self.axis_group = state.get("axis_group", 0)
 
 
 def restored_cache(state, b: int, h: int, eps: float = 1e-8, joined=None):
@@ -74,10 +77,16 @@ def restored_cache(state, b: int, h: int, eps: float = 1e-8, joined=None):
     j = joined if joined is not None else _Joined(state)
     k_codes = j.k_codes[b, h]                            # [Nq, D]
     v_codes = j.v_codes[b, h]
-    k_scale = j.k_scales[b, h][j.seg]                    # [Nq, D]: the token's segment row
-    v_scale = j.v_scales[b, h][:, None]                  # [Nq, 1]
-    k_hat = restore(k_codes, k_scale, eps, np.float64)
-    v_hat = restore(v_codes, v_scale, eps, np.float64)
+    if j.axis_group:                                     # same-axis: [Nq, runs] scales for both
+        k_hat = restore_grouped_per_token(k_codes[None, None], j.k_scales[b, h][None, None, :, :, None],
+                                          eps, np.float64)[0, 0]
+        v_hat = restore_grouped_per_token(v_codes[None, None], j.v_scales[b, h][None, None, :, :, None],
+                                          eps, np.float64)[0, 0]
+    else:
+        k_scale = j.k_scales[b, h][j.seg]                # [Nq, D]: the token's segment row
+        v_scale = j.v_scales[b, h][:, None]              # [Nq, 1]
+        k_hat = restore(k_codes, k_scale, eps, np.float64)
+        v_hat = restore(v_codes, v_scale, eps, np.float64)
     k_tail = np.asarray(state["key_residual"][b, h], np.float64)
     v_tail = np.asarray(state["value_residual"][b, h], np.float64)
     return np.concatenate((k_hat, k_tail)), np.concatenate((v_hat, v_tail))
