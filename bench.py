@@ -308,6 +308,152 @@ def run_decode_paths(args, log):
     }
 
 
+def same_axis_decode_bytes(cfg, nq: int, nt: int, q_heads: int) -> int:
+    """Algorithmic bytes of a decode call over a same-axis cache: codes, one
+    fp16 Key and one fp16 Value scale per token and run of 64 channels, tail, q."""
+    B, H, D = cfg.batch, cfg.kv_heads, cfg.head_dim
+    W = D * cfg.code_bits // 8
+    es = 2 if cfg.kv_dtype == 0 else 4
+    per_unit = 2 * nq * W + 2 * nq * (D // 64) * 2 + 2 * nt * D * es
+    return B * H * per_unit + B * q_heads * D * es
+
+
+def _graph_call_us(calls, replays, stream):
+    """Average time of one call of `calls` (one per cache), captured once into a
+    HIP graph and replayed back to back between one HIP event pair."""
+    import torch
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(stream)
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(graph, stream=cap):
+            for fn in calls:
+                fn(cap)
+    stream.wait_stream(cap)
+    for _ in range(2):
+        graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(replays):
+        graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (replays * len(calls))
+
+
+def run_axis_ab(args, log):
+    """KIVI (Keys per channel over a segment, Values per token) against
+    same-axis scales (Keys and Values per token, one scale per run of 64
+    channels) -- "KV Cache Quantization Strategies", Step 2 table and
+    section 5.1.
+
+    1. The decode call at the Llama-3-8B int4 shape (4096 tokens, 16 caches
+       rotated, graph replays): KIVI on the matrix-core kernel, KIVI on the
+       vector-ALU kernel, same-axis on the vector-ALU kernel; time and
+       algorithmic bytes per call, and each scheme's 4096-token prefill flush.
+    2. The error at the video cache's shape (432000 tokens, int2, 8 KV heads):
+       single-query decode attention over each quantized cache against exact
+       fp32 attention over the unquantized bf16 K/V, for 8 seeded queries.
+    """
+    import torch
+
+    import kvq_synth as ks
+    import quantized_kv_cache_kvq_amd as kvq
+
+    w = ks.LLAMA3_DECODE
+    stream = torch.cuda.current_stream()
+    out = torch.empty(w.batch, w.q_heads, w.head_dim, device="cuda")
+    variants = (("kivi_mfma", kvq.KVQ_KIVI, kvq.KVQ_KERNEL_AUTO),
+                ("kivi_valu", kvq.KVQ_KIVI, kvq.KVQ_KERNEL_VALU),
+                ("same_axis_valu", kvq.KVQ_SAME_AXIS, kvq.KVQ_KERNEL_VALU))
+    decode = {}
+    for name, scheme, kernel in variants:
+        cfg = kvq.make_config(batch=w.batch, kv_heads=w.kv_heads, head_dim=w.head_dim, capacity=w.prefill + 64,
+                              code_bits=w.code_bits, qmax=w.qmax, residual=w.residual, group=w.group,
+                              scheme=scheme, decode_kernel=kernel)
+        caches, qs, flush_ms = [], [], []
+        for i in range(args.caches):
+            k, v = ks.device_kv_pair(w, w.prefill, seed=i)
+            c = kvq.KVCache(cfg, zero=False)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            c.append(k, v)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            flush_ms.append(e0.elapsed_time(e1))
+            del k, v
+            caches.append(c)
+            qs.append(ks.device_queries(w, seed=i))
+        ws = caches[0].workspace(w.q_heads)
+        us = _graph_call_us([(lambda st, c=c, q=q: c.decode_attn(q, out, ws, stream=st)) for c, q in zip(caches, qs)],
+                            max(4, args.steps // args.caches), stream)
+        st = caches[0].state
+        nbytes = (same_axis_decode_bytes if scheme == kvq.KVQ_SAME_AXIS else decode_bytes)(cfg, st.quantized, st.tail,
+                                                                                          w.q_heads)
+        flush_ms.sort()
+        decode[name] = {"us_per_call": round(us, 3), "bytes_per_call": int(nbytes),
+                        "gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
+                        "prefill_append_us": round(flush_ms[len(flush_ms) // 2] * 1e3, 1)}
+        log(f"{name}: {us:.2f} us per decode call, {nbytes / 1e6:.2f} MB, prefill append "
+            f"{flush_ms[len(flush_ms) // 2] * 1e3:.1f} us")
+        del caches, qs
+        torch.cuda.empty_cache()
+
+    # attention error at the video cache's shape
+    wv = ks.VIDEO_BLOCK
+    k, v = ks.device_kv_pair(wv, wv.prefill, seed=0)
+    sigma = 1.0 / math.sqrt(wv.head_dim)
+    g = wv.q_heads // wv.kv_heads
+    queries = [ks.device_queries(wv, seed=100 + i) for i in range(8)]
+    exact = []
+    for q in queries:
+        o = torch.empty(wv.batch, wv.q_heads, wv.head_dim, device="cuda")
+        for h in range(wv.kv_heads):
+            K = k[0, h].float()
+            p = torch.softmax((q[0, h * g:(h + 1) * g].float() @ K.T) * sigma, dim=-1)
+            o[0, h * g:(h + 1) * g] = p @ v[0, h].float()
+        exact.append(o)
+    errors = {}
+    vout = torch.empty(wv.batch, wv.q_heads, wv.head_dim, device="cuda")
+    for name, scheme in (("kivi", kvq.KVQ_KIVI), ("same_axis", kvq.KVQ_SAME_AXIS)):
+        cfg = kvq.make_config(batch=wv.batch, kv_heads=wv.kv_heads, head_dim=wv.head_dim, capacity=wv.prefill + 128,
+                              code_bits=wv.code_bits, qmax=wv.qmax, residual=wv.residual, group=wv.group,
+                              scheme=scheme)
+        c = kvq.KVCache(cfg, zero=False)
+        c.append(k, v)
+        ws = c.workspace(wv.q_heads)
+        mx, sq, n = 0.0, 0.0, 0
+        for q, ref in zip(queries, exact):
+            c.decode_attn(q, vout, ws)
+            d = (vout - ref).double()
+            mx = max(mx, float(d.abs().max()))
+            sq += float((d * d).sum())
+            n += d.numel()
+        ref_rms = math.sqrt(sum(float((r.double() ** 2).sum()) for r in exact) / n)
+        errors[name] = {"attn_max_abs": round(mx, 5), "attn_rms": round(math.sqrt(sq / n), 6),
+                        "exact_output_rms": round(ref_rms, 6)}
+        log(f"int2 video shape, {name}: attention max-abs {mx:.4f}, RMS {math.sqrt(sq / n):.5f} "
+            f"(exact output RMS {ref_rms:.5f})")
+        del c, ws
+        torch.cuda.empty_cache()
+    kivi, sa = decode["kivi_mfma"], decode["same_axis_valu"]
+    return {
+        "metric": "decode call time, KIVI vs same-axis scales, Llama-3-8B shape int4",
+        "value": sa["us_per_call"], "unit": "us", "n_gpus": 1, "steps": max(4, args.steps // args.caches) * args.caches,
+        "warmup": 2, "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": "i8 MFMA or f32 VALU", "data": "synthetic (seeded, drawn on the device)",
+        "config": {"workload": "llama3_8b_decode_b8_ctx4096_int4_axis_ab", "batch": w.batch, "q_heads": w.q_heads,
+                   "kv_heads": w.kv_heads, "head_dim": w.head_dim, "context": w.prefill, "codes": "int4",
+                   "same_axis_run": 64, "caches_rotated": args.caches, "parallelism": "single-gpu",
+                   "error_workload": wv.name, "error_queries": len(queries)},
+        "decode": decode,
+        "int2_video_shape_error": errors,
+        "same_axis_over_kivi_bytes": round(sa["bytes_per_call"] / kivi["bytes_per_call"], 4),
+    }
+
+
 def paged_decode_bytes(cfg, states, q_heads: int) -> int:
     """Algorithmic bytes of one paged decode call: each sequence's codes,
     scales and window at its own length, plus the queries."""
@@ -1004,7 +1150,7 @@ def main():
                     help="video_block: frame length of the block mask (1 = token-causal)")
     ap.add_argument("--workload", choices=["llama3_decode", "video_block", "long_decode", "append_int8",
                                            "append_int4", "hbm_copy", "decode_paths", "paged_decode", "paged_block",
-                                           "hbm_read", "mfma_peak"],
+                                           "hbm_read", "mfma_peak", "axis_ab"],
                     default="llama3_decode",
                     help="llama3_decode (default): the append + decode step; video_block: one "
                          "1024-query causal block against the 432000-token int2 cache; long_decode: "
@@ -1016,7 +1162,9 @@ def main():
                          "decode over paged caches (block table, ragged per-sequence lengths); paged_block: "
                          "the video block over a paged cache, beside the uniform cache; hbm_read: the "
                          "read-only stream probe swept over workgroups and loads in flight; mfma_peak: "
-                         "the matrix-core probe loop per instruction kind")
+                         "the matrix-core probe loop per instruction kind; axis_ab: KIVI against "
+                         "same-axis scales (decode time and bytes at the Llama-3-8B shape, and the int2 "
+                         "attention error at the video cache's shape)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the library has no multi-GPU path; run with --gpus 1",
@@ -1055,6 +1203,8 @@ def main():
         res = run_paged_decode(args, log)
     elif args.workload == "paged_block":
         res = run_paged_block(args, log)
+    elif args.workload == "axis_ab":
+        res = run_axis_ab(args, log)
     elif args.workload.startswith("append_"):
         res = run_append(args, log, 8 if args.workload == "append_int8" else 4)
     else:

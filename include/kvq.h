@@ -38,6 +38,9 @@
  *   k_scale : fp16 [batch, kv_heads, max_segments, head_dim], one row per
  *             segment.  With group G > 0 segment s holds tokens [sG, (s+1)G).
  *   v_scale : fp16 [batch, kv_heads, C], one per quantized token.
+ *   Same-axis caches (scheme KVQ_SAME_AXIS) keep one scale per run of 64
+ *   channels of every quantized token, for Keys and Values alike:
+ *   k_scale and v_scale are fp16 [batch, kv_heads, C, head_dim / 64].
  *   k_tail, v_tail : kv_dtype [batch, kv_heads, ring, head_dim]; the tail
  *             token at absolute position p sits in slot p % ring, with
  *             ring = residual + group (group > 0) or residual (group == 0).
@@ -67,6 +70,29 @@ typedef enum kvq_dtype {
   KVQ_F32 = 1    /* float32 K/V/Q (the exercise's teaching case)          */
 } kvq_dtype;
 
+/* Which axes the scales run along ("KV Cache Quantization Strategies",
+ * Step 2 table).  KVQ_KIVI is the method: Keys per channel over a segment,
+ * Values per token.  KVQ_SAME_AXIS is the table's fixed local group in the
+ * setting of that page's section 5.1: Keys and Values both per token, one
+ * scale per run of 64 consecutive channels; it exists to compare the two
+ * and is supported by kvq_append, kvq_decode_attn(_noalloc) and
+ * kvq_decode_step on uniform caches with head_dim 64 or 128 and group > 0
+ * (every other entry point returns KVQ_EINVAL for it). */
+typedef enum kvq_scheme {
+  KVQ_KIVI = 0,
+  KVQ_SAME_AXIS = 1
+} kvq_scheme;
+
+/* Decode kernel choice.  KVQ_KERNEL_AUTO runs the int8 matrix-core kernel
+ * for the shapes it covers (bf16, int4 / int2 codes, head_dim 64 / 128,
+ * group > 0, KIVI) and the vector-ALU kernel otherwise; KVQ_KERNEL_VALU runs
+ * the vector-ALU kernel for every shape (same results within the attention
+ * tolerance; for comparing the two). */
+typedef enum kvq_decode_kernel {
+  KVQ_KERNEL_AUTO = 0,
+  KVQ_KERNEL_VALU = 1
+} kvq_decode_kernel;
+
 /* Static description of one cache (one layer).  Source: the exercise's
  * class constructor (qmax, eps) and ``append_and_partition``'s
  * residual_length; ``group`` and ``code_bits`` are the library's storage
@@ -84,6 +110,8 @@ typedef struct kvq_config {
   int32_t max_segments; /* rows of k_scale; >= capacity / group when group > 0    */
   int32_t kv_dtype;     /* kvq_dtype of appended K/V, of the tail and of queries  */
   float eps;            /* range floor, 1e-8 in the exercise                      */
+  int32_t scheme;       /* kvq_scheme (0 = KIVI)                                  */
+  int32_t decode_kernel;/* kvq_decode_kernel (0 = automatic)                      */
 } kvq_config;
 
 /* Host-side token accounting, owned by the caller and updated by kvq_append
@@ -133,7 +161,8 @@ kvq_status kvq_plan_append(const kvq_config* cfg, const kvq_state* st, int64_t n
  * compression", section 02).
  *   k_new, v_new : device, kv_dtype [batch, kv_heads, n_new, head_dim].
  * Tokens that overflow the residual window are quantized in place into the
- * next segment(s) (Keys per channel, Values per token) straight from the old
+ * next segment(s) (Keys per channel, Values per token; same-axis caches: both
+ * per token in runs of 64 channels) straight from the old
  * tail and from k_new / v_new, with no concatenation; the tokens that remain
  * in the window are copied into the tail ring.  Earlier segments, their
  * scales and the surviving tail slots are never written.  n_new == 0 is a

@@ -21,6 +21,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvq.so")
 
 KVQ_OK, KVQ_EINVAL, KVQ_ECAPACITY, KVQ_EWORKSPACE, KVQ_EDEVICE = range(5)
 KVQ_BF16, KVQ_F32 = 0, 1
+KVQ_KIVI, KVQ_SAME_AXIS = 0, 1            # kvq_scheme
+KVQ_KERNEL_AUTO, KVQ_KERNEL_VALU = 0, 1   # kvq_decode_kernel
 
 EXPORTED = ("kvq_buffer_sizes", "kvq_plan_append", "kvq_append", "kvq_workspace_size",
             "kvq_workspace_init", "kvq_decode_attn", "kvq_decode_step", "kvq_block_attn",
@@ -32,7 +34,8 @@ EXPORTED = ("kvq_buffer_sizes", "kvq_plan_append", "kvq_append", "kvq_workspace_
 class kvq_config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "batch", "kv_heads", "head_dim", "capacity", "code_bits", "qmax", "residual", "group",
-        "max_segments", "kv_dtype")] + [("eps", ctypes.c_float)]
+        "max_segments", "kv_dtype")] + [("eps", ctypes.c_float), ("scheme", ctypes.c_int32),
+                                        ("decode_kernel", ctypes.c_int32)]
 
 
 class kvq_state(ctypes.Structure):
@@ -153,12 +156,16 @@ def _stream(stream) -> Optional[int]:
 
 
 def make_config(batch, kv_heads, head_dim, capacity, code_bits, qmax, residual, group,
-                max_segments=None, kv_dtype=KVQ_BF16, eps=1e-8) -> kvq_config:
+                max_segments=None, kv_dtype=KVQ_BF16, eps=1e-8, scheme=None,
+                decode_kernel=None) -> kvq_config:
+    """scheme: KVQ_KIVI (default) or KVQ_SAME_AXIS; decode_kernel:
+    KVQ_KERNEL_AUTO (default) or KVQ_KERNEL_VALU."""
     capacity = int(math.ceil(capacity / 64) * 64)
     if max_segments is None:
         max_segments = capacity // group if group else max(capacity, 1)
     return kvq_config(batch, kv_heads, head_dim, capacity, code_bits, qmax, residual, group,
-                      max(max_segments, 1), kv_dtype, eps)
+                      max(max_segments, 1), kv_dtype, eps, KVQ_KIVI if scheme is None else scheme,
+                      KVQ_KERNEL_AUTO if decode_kernel is None else decode_kernel)
 
 
 # ---- the C entry points, one to one ----------------------------------------------
@@ -315,8 +322,12 @@ class KVCache:
         u8 = torch.uint8
         self.k_codes = alloc(B, H, self.sizes.k_codes // (B * H), dtype=u8, device=device)
         self.v_codes = alloc(B, H, self.sizes.v_codes // (B * H), dtype=u8, device=device)
-        self.k_scale = alloc(B, H, cfg.max_segments, D, dtype=torch.float16, device=device)
-        self.v_scale = alloc(B, H, cfg.capacity, dtype=torch.float16, device=device)
+        if cfg.scheme == KVQ_SAME_AXIS:     # one scale per token and run of 64 channels, K and V
+            self.k_scale = alloc(B, H, cfg.capacity, D // 64, dtype=torch.float16, device=device)
+            self.v_scale = alloc(B, H, cfg.capacity, D // 64, dtype=torch.float16, device=device)
+        else:
+            self.k_scale = alloc(B, H, cfg.max_segments, D, dtype=torch.float16, device=device)
+            self.v_scale = alloc(B, H, cfg.capacity, dtype=torch.float16, device=device)
         tdt = torch.bfloat16 if cfg.kv_dtype == KVQ_BF16 else torch.float32
         self._kvdt, self._f32, self._i32 = (tdt,), (torch.float32,), (torch.int32,)
         self.k_tail = alloc(B, H, self.sizes.ring, D, dtype=tdt, device=device)

@@ -21,6 +21,9 @@ kvq_status validate_config(const kvq_config* cfg, Geom* g) {
   // Keep every index of the device code inside int64 and launch limits.
   if ((int64_t)c.batch * c.kv_heads > 65535) return KVQ_EINVAL;
   if ((int64_t)c.residual + c.group > (1 << 20)) return KVQ_EINVAL;
+  if (c.scheme != KVQ_KIVI && c.scheme != KVQ_SAME_AXIS) return KVQ_EINVAL;
+  if (c.scheme == KVQ_SAME_AXIS && (c.head_dim % kRunChannels != 0 || c.group == 0)) return KVQ_EINVAL;
+  if (c.decode_kernel != KVQ_KERNEL_AUTO && c.decode_kernel != KVQ_KERNEL_VALU) return KVQ_EINVAL;
   g->B = c.batch;
   g->H = c.kv_heads;
   g->D = c.head_dim;
@@ -35,6 +38,9 @@ kvq_status validate_config(const kvq_config* cfg, Geom* g) {
   g->W = c.head_dim * c.code_bits / 8;
   g->ring = c.group > 0 ? c.residual + c.group : c.residual;
   g->code_stream = (int64_t)c.capacity * g->W;
+  g->scheme = c.scheme;
+  g->runs = c.scheme == KVQ_SAME_AXIS ? c.head_dim / kRunChannels : 0;
+  g->kernel = c.decode_kernel;
   return KVQ_OK;
 }
 
@@ -75,8 +81,13 @@ extern "C" kvq_status kvq_buffer_sizes(const kvq_config* cfg, kvq_sizes* out) {
   const size_t es = g.dtype == KVQ_BF16 ? 2 : 4;
   out->k_codes = streams * static_cast<size_t>(g.code_stream);
   out->v_codes = out->k_codes;
-  out->k_scale = streams * static_cast<size_t>(g.max_seg) * g.D * 2;
-  out->v_scale = streams * static_cast<size_t>(g.C) * 2;
+  if (g.scheme == KVQ_SAME_AXIS) {     // one scale per run of channels per token, K and V alike
+    out->k_scale = streams * static_cast<size_t>(g.C) * g.runs * 2;
+    out->v_scale = out->k_scale;
+  } else {
+    out->k_scale = streams * static_cast<size_t>(g.max_seg) * g.D * 2;
+    out->v_scale = streams * static_cast<size_t>(g.C) * 2;
+  }
   out->k_tail = streams * static_cast<size_t>(g.ring) * g.D * es;
   out->v_tail = out->k_tail;
   out->seg_index = g.G == 0 ? static_cast<size_t>(g.C) * 4 : 0;

@@ -278,13 +278,101 @@ __device__ __forceinline__ void flush_values(const FlushArgs& a, int bh, int vw,
   }
 }
 
+// Same-axis caches: the Keys (kKey) or the Values of one group of 64-token
+// tiles, both quantized per token with one scale per run of kRunChannels
+// channels ("KV Cache Quantization Strategies", Step 2 table, fixed local
+// group).  Units as in flush_values: (tile, token group wj, piece q) reads
+// piece q of 32/BITS consecutive tokens.  A run's pieces sit in aligned
+// groups of consecutive lanes, which reduce its absmax; the run's first
+// piece stores the scale.  Values are packed as in flush_values, Keys into
+// their tokens' 16-byte chunks as in flush_keys.  Segments are whole tiles
+// (group > 0), so no packed word is shared with the previous segment.
+template <int BITS, bool kKey>
+__device__ __forceinline__ void flush_runs(const FlushArgs& a, int bh, int vw, int64_t p0, int64_t p1) {
+  constexpr uint32_t kMask = (1u << BITS) - 1u;
+  constexpr int kTok = 32 / BITS;                // tokens per packed Value word
+  constexpr int kGroups = kTile / kTok;
+  const Geom& g = a.g;
+  const bool bf16 = g.dtype == KVQ_BF16;
+  const int epp = bf16 ? 8 : 4;
+  const int P = a.pieces;
+  const int rp = kRunChannels / epp;             // pieces per run: 8 (bf16) or 16 (fp32) lanes
+  const int per_tile = kGroups * P;
+  const int units = a.v_tiles_per_wg * per_tile; // a multiple of the block size
+  uint8_t* codes = (kKey ? a.k_codes : a.v_codes) + (int64_t)bh * g.code_stream;
+  uint16_t* scales = (kKey ? a.k_scale : a.v_scale) + (int64_t)bh * g.C * g.runs;
+  for (int u = threadIdx.x; u < units; u += kFlushThreads) {
+    const int q = u % P, wj = (u / P) % kGroups, tw = u / per_tile;
+    const int64_t t0 = (p0 / kTile + (int64_t)vw * a.v_tiles_per_wg + tw) * kTile;
+    const int64_t wt = t0 + wj * kTok;           // first token of the unit
+    uint4 x[kTok];
+#pragma unroll
+    for (int i = 0; i < kTok; ++i) {
+      int64_t p = wt + i;
+      p = p < p0 ? p0 : (p < p1 ? p : p1 - 1);    // clamped: the loads stay unconditional
+      x[i] = *reinterpret_cast<const uint4*>(flush_row(a, kKey, bh, p) + q * 16);
+    }
+    float s[kTok];
+#pragma unroll
+    for (int i = 0; i < kTok; ++i) {
+      float m = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (e < epp) m = fmaxf(m, fabsf(piece_elem(x[i], e, bf16)));
+      m = lane_group_max(m, rp);
+      const uint16_t h = f32_to_half_bits(scale_of(m, g.qmax, g.eps));
+      s[i] = half_bits_to_f32(h);
+      const int64_t t = wt + i;
+      if (q % rp == 0 && t >= p0 && t < p1) scales[t * g.runs + q / rp] = h;
+    }
+    if (wt + kTok <= p0 || wt >= p1) continue;   // no token of this unit is flushed here
+    if constexpr (kKey) {
+      const int cpc = 128 / BITS;                // channels per 16-byte chunk
+      const int j = (q * epp) / cpc;
+      const int byte_in_chunk = ((q * epp - j * cpc) * BITS) / 8;
+      const int bytes = epp * BITS / 8;          // 1, 2, 4 or 8
+#pragma unroll
+      for (int i = 0; i < kTok; ++i) {
+        const int64_t t = wt + i;
+        if (t < p0 || t >= p1) continue;
+        uint64_t bits = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (e < epp) bits |= static_cast<uint64_t>(code_field(piece_elem(x[i], e, bf16), s[i], g.qmax, kMask)) << (e * BITS);
+        uint8_t* dst = codes + (t / kTile) * kTile * g.W + j * 1024 + (t % kTile) * 16 + byte_in_chunk;
+        if (bytes == 8) *reinterpret_cast<uint2*>(dst) = make_uint2(static_cast<uint32_t>(bits), static_cast<uint32_t>(bits >> 32));
+        else if (bytes == 4) *reinterpret_cast<uint32_t*>(dst) = static_cast<uint32_t>(bits);
+        else if (bytes == 2) *reinterpret_cast<uint16_t*>(dst) = static_cast<uint16_t>(bits);
+        else *dst = static_cast<uint8_t>(bits);
+      }
+    } else {
+      uint32_t* dst = reinterpret_cast<uint32_t*>(codes + (t0 / kTile) * kTile * g.W) + wj;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if (e >= epp) continue;
+        const int c = q * epp + e;
+        uint32_t word = 0;
+#pragma unroll
+        for (int i = 0; i < kTok; ++i) {
+          const int64_t t = wt + i;
+          if (t >= p0 && t < p1) word |= code_field(piece_elem(x[i], e, bf16), s[i], g.qmax, kMask) << (i * BITS);
+        }
+        dst[c * 2 * BITS] = word;                // channel c: 8*BITS bytes (2*BITS words) per tile
+      }
+    }
+  }
+}
+
 // kPaged: codes and scales go to the sequence's pages (a.pool, a.table);
 // grid.z runs over the sequences, whose accounting comes from ps.
-template <int BITS, bool kPaged>
+// kSameAxis (uniform caches only): per segment, v_wgs workgroups quantize
+// the Keys and v_wgs the Values, both per token in runs of channels.
+template <int BITS, bool kPaged, bool kSameAxis = false>
 __global__ __launch_bounds__(kFlushThreads) void flush_kernel(FlushArgs a0,
                                                               typename std::conditional<kPaged, PagedFlushSeqs, NoPagedSeqs>::type ps) {
+  static_assert(!(kPaged && kSameAxis), "paged caches use the KIVI axes");
   FlushArgs a = a0;
-  const int per_seg = 1 + a.v_wgs;
+  const int per_seg = kSameAxis ? 2 * a.v_wgs : 1 + a.v_wgs;
   const int64_t sl = blockIdx.x / per_seg;
   if constexpr (kPaged) {
     const int b = blockIdx.z;
@@ -301,6 +389,11 @@ __global__ __launch_bounds__(kFlushThreads) void flush_kernel(FlushArgs a0,
   const int64_t seg = a.seg_base + sl;
   const int64_t p0 = a.nq_old + sl * a.seg_len;
   const int64_t p1 = p0 + a.seg_len;
+  if constexpr (kSameAxis) {
+    if (role < a.v_wgs) flush_runs<BITS, true>(a, bh, role, p0, p1);
+    else flush_runs<BITS, false>(a, bh, role - a.v_wgs, p0, p1);
+    return;
+  }
   __shared__ float red[kFlushThreads / kWave][128];
   __shared__ float sc[128];
   if (role == 0) {
@@ -355,8 +448,18 @@ void launch_flush(const Geom& g, FlushArgs& a, int64_t flush, unsigned grid_y, h
   const int64_t seg_tiles = (p1 + kTile - 1) / kTile - p0 / kTile;
   a.v_wgs = static_cast<int>((seg_tiles + a.v_tiles_per_wg - 1) / a.v_tiles_per_wg);
   const int64_t nseg = flush / a.seg_len;
-  dim3 grid(static_cast<unsigned>(nseg * (1 + a.v_wgs)), grid_y, ps ? static_cast<unsigned>(g.B) : 1u);
+  const bool same_axis = g.scheme == KVQ_SAME_AXIS;   // uniform caches only (checked by the entry points)
+  dim3 grid(static_cast<unsigned>(nseg * (same_axis ? 2 * a.v_wgs : 1 + a.v_wgs)), grid_y,
+            ps ? static_cast<unsigned>(g.B) : 1u);
   const NoPagedSeqs np{};
+  if (same_axis) {
+    switch (g.bits) {
+      case 8: hipLaunchKernelGGL((flush_kernel<8, false, true>), grid, dim3(kFlushThreads), 0, hs, a, np); break;
+      case 4: hipLaunchKernelGGL((flush_kernel<4, false, true>), grid, dim3(kFlushThreads), 0, hs, a, np); break;
+      default: hipLaunchKernelGGL((flush_kernel<2, false, true>), grid, dim3(kFlushThreads), 0, hs, a, np); break;
+    }
+    return;
+  }
   switch (g.bits) {
     case 8:
       if (ps) hipLaunchKernelGGL((flush_kernel<8, true>), grid, dim3(kFlushThreads), 0, hs, a, *ps);
@@ -518,7 +621,7 @@ extern "C" kvq_status kvq_append(const kvq_config* cfg, kvq_state* st, const kvq
 
 extern "C" kvq_status kvq_paged_page_bytes(const kvq_config* cfg, size_t* bytes) {
   Geom g;
-  kvq_status s = validate_config(cfg, &g);
+  kvq_status s = validate_kivi_config(cfg, &g);
   if (s != KVQ_OK) return s;
   if (!bytes) return KVQ_EINVAL;
   *bytes = static_cast<size_t>(g.H) * (2 * kTile * g.W + 2 * kTile + 2 * g.D);
@@ -529,7 +632,7 @@ extern "C" kvq_status kvq_paged_append(const kvq_config* cfg, kvq_state* st, con
                                        const void* k_new, const void* v_new, const int64_t* n_new,
                                        void* stream) {
   Geom g;
-  kvq_status s = validate_config(cfg, &g);
+  kvq_status s = validate_kivi_config(cfg, &g);
   if (s != KVQ_OK) return s;
   if (!st || !cache || !n_new) return KVQ_EINVAL;
   if (g.G <= 0 || g.B > kMaxPagedSeqs) return KVQ_EINVAL;

@@ -621,7 +621,7 @@ extern "C" kvq_status kvq_block_attn(const kvq_config* cfg, const kvq_state* st,
                                      int32_t num_splits, float* out, void* workspace,
                                      size_t workspace_size, void* stream) {
   Geom g;
-  kvq_status s = validate_config(cfg, &g);
+  kvq_status s = validate_kivi_config(cfg, &g);
   if (s != KVQ_OK) return s;
   if (!st || !cache || !q || !k_blk || !v_blk || !out) return KVQ_EINVAL;
   if (g.dtype != KVQ_BF16 || (g.D != 64 && g.D != 128)) return KVQ_EINVAL;
@@ -685,7 +685,7 @@ extern "C" kvq_status kvq_paged_block_attn(const kvq_config* cfg, const kvq_stat
                                            float softmax_scale, int32_t num_splits, float* out, void* workspace,
                                            size_t workspace_size, void* stream) {
   Geom g;
-  kvq_status s = validate_config(cfg, &g);
+  kvq_status s = validate_kivi_config(cfg, &g);
   if (s != KVQ_OK) return s;
   if (!st || !cache || !q || !k_blk || !v_blk || !out) return KVQ_EINVAL;
   if (g.dtype != KVQ_BF16 || (g.D != 64 && g.D != 128)) return KVQ_EINVAL;

@@ -719,12 +719,19 @@ __device__ __forceinline__ WaveWork wave_work(const DecodeArgs& a, int split, in
 
 // ---- vector-ALU kernel (every shape) ------------------------------------------------
 
-template <int D, int BITS, int GQA, bool kPaged = false>
+// kSameAxis (uniform caches): Keys and Values carry one scale per token and
+// run of kRunChannels channels.  A logit is then sum over runs r of
+// (sum_{c in r} q[c] code[c]) / kscale[t][r], and a Value weight depends on
+// the channel's run: p / vscale[t][r].
+template <int D, int BITS, int GQA, bool kPaged = false, bool kSameAxis = false>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a0, PagedDecode pd) {
+  static_assert(!(kPaged && kSameAxis), "paged caches use the KIVI axes");
+  static_assert(!kSameAxis || D % kRunChannels == 0, "same-axis runs divide head_dim");
   constexpr int W = D * BITS / 8;        // bytes per token row
   constexpr int NSLOT = W / 16;          // 16-byte units per lane per tile
   constexpr int TPU = 128 / BITS;        // tokens per Value unit
   constexpr int FPW = 32 / BITS;         // fields per 32-bit word
+  constexpr int NR = kSameAxis ? D / kRunChannels : 1;   // scales per token (same-axis)
   constexpr int TCPL = TailMap<D>::TCPL;
   const Geom& g = a0.g;
   const int tid = threadIdx.x, lane = tid % kWave;
@@ -748,7 +755,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a0, PagedDe
 
   __shared__ float qsT[D][GQA];
   __shared__ float aq[kWaves][D][GQA];
-  __shared__ float pw[kWaves][kTile][GQA];
+  __shared__ float pw[kWaves][kTile * NR][GQA];   // same-axis: row NR t + r
   __shared__ float red[kWaves][D][GQA];
   __shared__ float wml[kWaves][2][GQA];
 
@@ -808,12 +815,42 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a0, PagedDe
     for (int j = 0; j < NSLOT; ++j) kc[j] = *reinterpret_cast<const uint4*>(kt + j * 1024 + lane * 16);
 #pragma unroll
     for (int k = 0; k < NSLOT; ++k) vc[k] = *reinterpret_cast<const uint4*>(vt + (k * kWave + lane) * 16);
-    const float vs = valid ? half_bits_to_f32(vs_tile[lane]) : 1.0f;
+    const float vs = (valid && !kSameAxis) ? half_bits_to_f32(vs_tile[lane]) : 1.0f;
     float logit[GQA];
 #pragma unroll
     for (int h = 0; h < GQA; ++h) logit[h] = 0.0f;
+    float rvs[NR];            // same-axis: 1 / vscale of the token's runs
 
-    if (g.G > 0) {
+    if constexpr (kSameAxis) {
+      // this token's run scales (NR consecutive fp16 per token)
+      const int64_t srow = ((int64_t)unit * g.C + (valid ? t : 0)) * NR;
+      float rks[NR], part[NR][GQA];
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        rks[r] = valid ? fast_rcp(fmaxf(half_bits_to_f32(a.k_scale[srow + r]), g.eps)) : 0.0f;
+        rvs[r] = valid ? fast_rcp(fmaxf(half_bits_to_f32(a.v_scale[srow + r]), g.eps)) : 0.0f;
+#pragma unroll
+        for (int h = 0; h < GQA; ++h) part[r][h] = 0.0f;
+      }
+#pragma unroll
+      for (int j = 0; j < NSLOT; ++j) {
+        const uint32_t wd[4] = {kc[j].x, kc[j].y, kc[j].z, kc[j].w};
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+#pragma unroll
+          for (int f = 0; f < FPW; ++f) {
+            const int c = (j * 16 + w * 4) * (8 / BITS) + f;
+            const float code = static_cast<float>(sext_field<BITS>(wd[w], f * BITS));
+#pragma unroll
+            for (int h = 0; h < GQA; ++h) part[c / kRunChannels][h] = fmaf(qsT[c][h], code, part[c / kRunChannels][h]);
+          }
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < NR; ++r)
+#pragma unroll
+        for (int h = 0; h < GQA; ++h) logit[h] = fmaf(part[r][h], rks[r], logit[h]);
+    } else if (g.G > 0) {
       const int seg = tile / a.tiles_per_seg;
       if (seg != cur_seg) {
         cur_seg = seg;
@@ -873,7 +910,12 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a0, PagedDe
       for (int k = 0; k < NSLOT; ++k) acc[k][h] *= alpha[h];
 #pragma unroll
       for (int k = 0; k < TCPL; ++k) acc_tail[k][h] *= alpha[h];
-      pw[wave][lane][h] = p * vinv;
+      if constexpr (kSameAxis) {
+#pragma unroll
+        for (int r = 0; r < NR; ++r) pw[wave][lane * NR + r][h] = p * rvs[r];
+      } else {
+        pw[wave][lane][h] = p * vinv;
+      }
     }
     wave_lds_sync();
 
@@ -882,15 +924,19 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a0, PagedDe
     const int t0 = ((lane * 16) % (8 * BITS)) * 8 / BITS;
 #pragma unroll
     for (int f = 0; f < TPU; ++f) {
-      float pf[GQA];
+      float pf[NR][GQA];
 #pragma unroll
-      for (int h = 0; h < GQA; ++h) pf[h] = pw[wave][t0 + f][h];
+      for (int r = 0; r < NR; ++r)
+#pragma unroll
+        for (int h = 0; h < GQA; ++h) pf[r][h] = pw[wave][(t0 + f) * NR + r][h];
 #pragma unroll
       for (int k = 0; k < NSLOT; ++k) {
+        // slot k holds channel (64 k + lane) * 2 / BITS: run 2 k / BITS (same-axis)
+        const int r = kSameAxis ? (2 * k) / BITS : 0;
         const uint32_t wd[4] = {vc[k].x, vc[k].y, vc[k].z, vc[k].w};
         const float code = static_cast<float>(sext_field<BITS>(wd[f / FPW], (f % FPW) * BITS));
 #pragma unroll
-        for (int h = 0; h < GQA; ++h) acc[k][h] = fmaf(pf[h], code, acc[k][h]);
+        for (int h = 0; h < GQA; ++h) acc[k][h] = fmaf(pf[r][h], code, acc[k][h]);
       }
     }
   }
@@ -1589,18 +1635,21 @@ void launch(const DecodeArgs& a, const PagedDecode* pd, hipStream_t s) {
     // chunks), a wave at most a quarter of that, rounded up.
     bool i8 = false;
     if constexpr ((BITS == 4 || BITS == 2) && D >= 64)
-      i8 = a.g.dtype == KVQ_BF16 && pd->per_split + 2 <= kWaves * kWave;
+      i8 = a.g.dtype == KVQ_BF16 && a.g.kernel == KVQ_KERNEL_AUTO && pd->per_split + 2 <= kWaves * kWave;
     if (i8) {
       if constexpr ((BITS == 4 || BITS == 2) && D >= 64)
         hipLaunchKernelGGL((decode_i8_kernel<D, BITS, GQA, PagedDecode>), grid, dim3(kThreads), 0, s, a, *pd);
     } else {
       hipLaunchKernelGGL((decode_kernel<D, BITS, GQA, true>), grid, dim3(kThreads), 0, s, a, *pd);
     }
+  } else if (a.g.scheme == KVQ_SAME_AXIS) {
+    if constexpr (D % kRunChannels == 0)
+      hipLaunchKernelGGL((decode_kernel<D, BITS, GQA, false, true>), grid, dim3(kThreads), 0, s, a, PagedDecode{});
   } else if constexpr ((BITS == 4 || BITS == 2) && D >= 64) {
     // The matrix-core kernel addresses a unit's streams with 32-bit buffer offsets.
     const bool offsets32 = a.g.code_stream < (int64_t(1) << 31) &&
                            (int64_t)a.g.max_seg * a.g.D * 2 < (int64_t(1) << 31);
-    if (a.g.G > 0 && a.g.dtype == KVQ_BF16 && a.tiles_q > 0 && offsets32)
+    if (a.g.G > 0 && a.g.dtype == KVQ_BF16 && a.g.kernel == KVQ_KERNEL_AUTO && a.tiles_q > 0 && offsets32)
       hipLaunchKernelGGL((decode_i8_kernel<D, BITS, GQA>), grid, dim3(kThreads), 0, s, a, NoPaging{});
     else
       hipLaunchKernelGGL((decode_kernel<D, BITS, GQA>), grid, dim3(kThreads), 0, s, a, PagedDecode{});
@@ -1948,7 +1997,7 @@ extern "C" kvq_status kvq_paged_decode_attn(const kvq_config* cfg, const kvq_sta
                                             float softmax_scale, int32_t num_splits, float* out,
                                             void* workspace, size_t workspace_size, void* stream) {
   Geom g;
-  kvq_status s = validate_config(cfg, &g);
+  kvq_status s = validate_kivi_config(cfg, &g);
   if (s != KVQ_OK) return s;
   DecodeArgs a;
   PagedDecode pd;
@@ -1967,7 +2016,7 @@ extern "C" kvq_status kvq_paged_decode_step(const kvq_config* cfg, kvq_state* st
                                             int32_t num_splits, float* out, void* workspace,
                                             size_t workspace_size, void* stream) {
   Geom g;
-  kvq_status s = validate_config(cfg, &g);
+  kvq_status s = validate_kivi_config(cfg, &g);
   if (s != KVQ_OK) return s;
   if (!st || !cache || !n_new) return KVQ_EINVAL;
   if (g.G <= 0 || g.B > kMaxPagedSeqs) return KVQ_EINVAL;

@@ -12,6 +12,7 @@ constexpr int kTile = 64;         // tokens per packed tile
 constexpr int kWave = 64;         // gfx950 wavefront width
 constexpr int kMaxSplits = 256;   // sequence splits per (batch, KV head) in decode
 constexpr int kMaxGqa = 8;        // query heads per KV head supported by the kernels
+constexpr int kRunChannels = 64;  // channels per scale in same-axis caches
 
 // Launch geometry derived once from a validated kvq_config.
 struct Geom {
@@ -20,6 +21,9 @@ struct Geom {
   int W;              // packed bytes per token row
   int ring;           // tail ring slots
   int64_t code_stream;  // bytes of one (b, h) code stream = C * W
+  int scheme;         // kvq_scheme
+  int runs;           // same-axis: scales per token (head_dim / kRunChannels); KIVI: 0
+  int kernel;         // kvq_decode_kernel
 };
 
 // ---- scalar conversions (device) -------------------------------------------------
@@ -117,5 +121,12 @@ __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcp
 inline void clear_stale_hip_error() { (void)hipGetLastError(); }
 
 kvq_status validate_config(const kvq_config* cfg, Geom* g);
+
+// Entry points built for the KIVI axes only (block attention, restore, paged
+// caches): a same-axis configuration is an invalid argument there.
+inline kvq_status validate_kivi_config(const kvq_config* cfg, Geom* g) {
+  const kvq_status s = validate_config(cfg, g);
+  return s != KVQ_OK ? s : (g->scheme == KVQ_KIVI ? KVQ_OK : KVQ_EINVAL);
+}
 
 }  // namespace kvq

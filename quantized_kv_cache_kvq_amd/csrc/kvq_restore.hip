@@ -191,7 +191,7 @@ using namespace kvq;
 extern "C" kvq_status kvq_restore(const kvq_config* cfg, const kvq_state* st, const kvq_cache* cache,
                                   void* k_out, void* v_out, int32_t out_dtype, int64_t ld, void* stream) {
   Geom g;
-  kvq_status s = validate_config(cfg, &g);
+  kvq_status s = validate_kivi_config(cfg, &g);
   if (s != KVQ_OK) return s;
   if (!st || !cache) return KVQ_EINVAL;
   if (st->quantized < 0 || st->tail < 0 || st->total != st->quantized + st->tail || st->quantized > g.C)
@@ -224,7 +224,7 @@ extern "C" kvq_status kvq_restore(const kvq_config* cfg, const kvq_state* st, co
 extern "C" kvq_status kvq_paged_restore(const kvq_config* cfg, const kvq_state* st, const kvq_paged_cache* cache,
                                         void* k_out, void* v_out, int32_t out_dtype, int64_t ld, void* stream) {
   Geom g;
-  kvq_status s = validate_config(cfg, &g);
+  kvq_status s = validate_kivi_config(cfg, &g);
   if (s != KVQ_OK) return s;
   if (!st || !cache) return KVQ_EINVAL;
   if (g.G <= 0 || g.B > kMaxRestoreSeqs) return KVQ_EINVAL;

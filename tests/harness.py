@@ -26,12 +26,14 @@ def note(msg: str):
     sys.stdout.flush()
 
 
-def config_for(w: kvq_synth.Workload, capacity_tokens: int) -> kvq.kvq_config:
+def config_for(w: kvq_synth.Workload, capacity_tokens: int, scheme=kvq.KVQ_KIVI,
+               decode_kernel=kvq.KVQ_KERNEL_AUTO) -> kvq.kvq_config:
     return kvq.make_config(
         batch=w.batch, kv_heads=w.kv_heads, head_dim=w.head_dim, capacity=capacity_tokens,
         code_bits=w.code_bits, qmax=w.qmax, residual=w.residual, group=w.group,
         max_segments=None if w.group else max(capacity_tokens, 1),
-        kv_dtype=kvq.KVQ_BF16 if w.kv_dtype == "bf16" else kvq.KVQ_F32)
+        kv_dtype=kvq.KVQ_BF16 if w.kv_dtype == "bf16" else kvq.KVQ_F32,
+        scheme=scheme, decode_kernel=decode_kernel)
 
 
 def f32(t: torch.Tensor) -> np.ndarray:
@@ -41,12 +43,14 @@ def f32(t: torch.Tensor) -> np.ndarray:
 class Pair:
     """A device cache and the oracle state, advanced together."""
 
-    def __init__(self, w: kvq_synth.Workload, capacity_tokens: int):
+    def __init__(self, w: kvq_synth.Workload, capacity_tokens: int, scheme=kvq.KVQ_KIVI,
+                 decode_kernel=kvq.KVQ_KERNEL_AUTO):
         self.w = w
-        self.cfg = config_for(w, capacity_tokens)
+        self.cfg = config_for(w, capacity_tokens, scheme, decode_kernel)
         self.cache = kvq.KVCache(self.cfg)
         self.oracle = KVQuantizationStrategies(qmax=w.qmax, eps=1e-8, scale_storage="fp16",
-                                               group=w.group)
+                                               group=w.group,
+                                               axis_group=64 if scheme == kvq.KVQ_SAME_AXIS else 0)
         self.ost = None
 
     def append(self, k: torch.Tensor, v: torch.Tensor):
@@ -73,7 +77,8 @@ class Pair:
         got_v = c.v_codes.cpu().numpy()
         assert np.array_equal(got_k, exp_k), _first_diff(got_k, exp_k)
         assert np.array_equal(got_v, exp_v), _first_diff(got_v, exp_v)
-        nseg = c.state.segments
+        # KIVI: one Key-scale row per segment; same-axis: per token and run
+        nseg = nq if self.cfg.scheme == kvq.KVQ_SAME_AXIS else c.state.segments
         got_ks = c.k_scale[:, :, :nseg].cpu().numpy().view(np.uint16)
         exp_ks = key_scales(o).astype(np.float16).view(np.uint16)
         assert np.array_equal(got_ks, exp_ks), _first_diff(got_ks, exp_ks)

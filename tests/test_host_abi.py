@@ -56,10 +56,21 @@ def test_buffer_sizes_follow_the_layout():
     assert s0.ring == 8 and s0.seg_index == 128 * 4 and s0.k_tail == 2 * 2 * 8 * 16 * 4
 
 
+def test_same_axis_buffer_sizes():
+    """Same-axis caches: one fp16 scale per token and run of 64 channels, for
+    Keys and Values alike; codes and windows as in KIVI caches."""
+    s = kvq.kvq_buffer_sizes(cfg(scheme=kvq.KVQ_SAME_AXIS))
+    assert s.k_scale == s.v_scale == 2 * 2 * 1024 * 2 * 2
+    assert s.k_codes == 2 * 2 * 1024 * 64 and s.ring == 256
+    s64 = kvq.kvq_buffer_sizes(cfg(scheme=kvq.KVQ_SAME_AXIS, head_dim=64))
+    assert s64.k_scale == s64.v_scale == 2 * 2 * 1024 * 2
+
+
 @pytest.mark.parametrize("bad", [
     dict(head_dim=48), dict(head_dim=16, code_bits=4), dict(code_bits=3), dict(qmax=8),
     dict(qmax=0), dict(residual=0), dict(group=100), dict(capacity=100),
-    dict(kv_dtype=7), dict(eps=0.0), dict(max_segments=2),
+    dict(kv_dtype=7), dict(eps=0.0), dict(max_segments=2), dict(scheme=2), dict(decode_kernel=2),
+    dict(scheme=kvq.KVQ_SAME_AXIS, head_dim=32), dict(scheme=kvq.KVQ_SAME_AXIS, group=0),
 ])
 def test_invalid_configs_are_rejected(bad):
     c = cfg(**{k: v for k, v in bad.items() if k not in ("capacity", "max_segments")})
@@ -214,3 +225,24 @@ def test_paged_entry_points_validate_before_device_work():
                                     out, fake, ws_bytes, None) == kvq.KVQ_EINVAL
     assert lib.kvq_paged_block_attn(ctypes.byref(c), one, ctypes.byref(pc), fake, fake, fake, 64, 8, 1, 0.1, 0,
                                     out, fake, ws_bytes, None) == kvq.KVQ_EWORKSPACE
+
+
+def test_same_axis_is_rejected_where_only_kivi_is_built():
+    """Block attention, restore and the paged entry points take KIVI caches
+    only: a same-axis configuration is refused before any pointer is used."""
+    c = cfg(scheme=kvq.KVQ_SAME_AXIS)
+    lib = kvq.load()
+    st_ = kvq.kvq_state()
+    cache = kvq.kvq_cache()
+    paged = kvq.kvq_paged_cache()
+    size = ctypes.c_size_t()
+    assert lib.kvq_paged_page_bytes(ctypes.byref(c), ctypes.byref(size)) == kvq.KVQ_EINVAL
+    assert lib.kvq_restore(ctypes.byref(c), ctypes.byref(st_), ctypes.byref(cache), None, None, 0, 0,
+                           None) == kvq.KVQ_EINVAL
+    assert lib.kvq_block_attn(ctypes.byref(c), ctypes.byref(st_), ctypes.byref(cache), None, None, None,
+                              1, 8, 1, ctypes.c_float(0.1), 0, None, None, 0, None) == kvq.KVQ_EINVAL
+    states = (kvq.kvq_state * 2)()
+    assert lib.kvq_paged_decode_attn(ctypes.byref(c), states, ctypes.byref(paged), None, 8,
+                                     ctypes.c_float(0.1), 0, None, None, 0, None) == kvq.KVQ_EINVAL
+    # the KIVI page size is defined
+    assert lib.kvq_paged_page_bytes(ctypes.byref(cfg()), ctypes.byref(size)) == kvq.KVQ_OK
