@@ -1509,6 +1509,81 @@ void decode_i8_kernel(DecodeArgs a0, PD pd) {
     wave_lds_sync();      // pD is rewritten by the next tile
   };
 
+  // Window chunks (bf16).  Scores on the matrix cores: A = the query in two
+  // bf16 rows per head (4 h: high part, 4 h + 1: the rounding remainder,
+  // about 16 more bits), B = the chunk's Keys, so lane (q4, col) receives
+  // head q4's score for token col -- the layout of the tile scores.
+  // Weighted Values on the vector ALUs, each lane owning TCPL channels of
+  // every head.  The chunks keep a softmax state of their own (mC, lC,
+  // acc_tail), merged with the tiles' once at the end, so that the first
+  // chunk can be computed before the tiles.
+  float acc_tail[TCPL][GQA], mC[HG], lC[HG];
+#pragma unroll
+  for (int h = 0; h < GQA; ++h)
+#pragma unroll
+    for (int k = 0; k < TCPL; ++k) acc_tail[k][h] = 0.0f;
+#pragma unroll
+  for (int hg = 0; hg < HG; ++hg) {
+    mC[hg] = -INFINITY;
+    lC[hg] = 0.0f;
+  }
+  auto load_qa = [&](bf8_t (&qa)[HG][D / 32]) {
+    const int hq = col / 4, part = col % 4;
+#pragma unroll
+    for (int hg = 0; hg < HG; ++hg) {
+      const int h = 4 * hg + hq;
+#pragma unroll
+      for (int mk = 0; mk < D / 32; ++mk) {
+        uint4 w = make_uint4(0u, 0u, 0u, 0u);
+        if (h < GQA && part < 2) w = *reinterpret_cast<const uint4*>(&qsHL[wave][part][h][32 * mk + 8 * q4]);
+        qa[hg][mk] = __builtin_bit_cast(bf8_t, w);
+      }
+    }
+  };
+  auto compute_chunk = [&](const bf8_t (&qa)[HG][D / 32]) {
+    float al_u[GQA];
+#pragma unroll
+    for (int hg = 0; hg < HG; ++hg) {
+      f4_t sc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int mk = 0; mk < D / 32; ++mk)
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[hg][mk], __builtin_bit_cast(bf8_t, cr.k[mk]), sc, 0, 0, 0);
+      const float xs = col < cr.nvalid ? sc[0] + sc[1] : -INFINITY;
+      const float mn = fmaxf(mC[hg], row16_max(xs));    // finite: a chunk has a valid token
+      const float al = fast_exp2(mC[hg] - mn);           // exp2(-inf) = 0 before the first token
+      mC[hg] = mn;
+      const float pr = fast_exp2(xs - mn);               // 0 for padding tokens
+      lC[hg] = lC[hg] * al + pr;
+      if (4 * hg + q4 < GQA) pw[wave][col][4 * hg + q4] = pr;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (4 * hg + i < GQA) al_u[4 * hg + i] = lane_value(al, 16 * i);
+    }
+    wave_lds_sync();
+#pragma unroll
+    for (int t = 0; t < kTailChunk; ++t) {
+      float v[TCPL];
+      v[0] = bf16_lo(cr.v[t]);
+      if constexpr (TCPL == 2) v[1] = bf16_hi(cr.v[t]);
+#pragma unroll
+      for (int h = 0; h < GQA; ++h) {
+        const float pt = pw[wave][t][h];
+#pragma unroll
+        for (int k = 0; k < TCPL; ++k)
+          acc_tail[k][h] = fmaf(pt, v[k], t == 0 ? acc_tail[k][h] * al_u[h] : acc_tail[k][h]);
+      }
+    }
+    wave_lds_sync();      // pw is rewritten by the next chunk
+  };
+
+  // The run's first window chunk comes before its tiles: its loads went out
+  // first, so it is computed while the tiles' data is still on the way.
+  if (ww.c0 < ww.c1) {
+    bf8_t qa[HG][D / 32];
+    load_qa(qa);
+    compute_chunk(qa);
+  }
+
   // Quantized tiles through a ring of two: a tile is computed, then its
   // registers take the loads of the tile two ahead (issued unconditionally:
   // past the run they read nothing), so the next tile is in flight while one
@@ -1523,70 +1598,41 @@ void decode_i8_kernel(DecodeArgs a0, PD pd) {
     load_tile(tile + 3, buf1);
   }
 
-  // Window chunks (bf16) after the quantized tiles.  Scores on the matrix
-  // cores: A = the query in two bf16 rows per head (4 h: high part, 4 h + 1:
-  // the rounding remainder, about 16 more bits), B = the chunk's Keys, so
-  // lane (q4, col) receives head q4's score for token col -- the layout of
-  // the tile scores, and the same online-softmax state.  Weighted Values on
-  // the vector ALUs, each lane owning TCPL channels of every head.
-  float acc_tail[TCPL][GQA];
-#pragma unroll
-  for (int h = 0; h < GQA; ++h)
-#pragma unroll
-    for (int k = 0; k < TCPL; ++k) acc_tail[k][h] = 0.0f;
-  if (ww.c0 < ww.c1) {
+  // Further window chunks of the run (a run holds more than one only when a
+  // split has more chunks than waves), after the tiles.
+  if (ww.c0 + 1 < ww.c1) {
     bf8_t qa[HG][D / 32];
-    {
-      const int hq = col / 4, part = col % 4;
+    load_qa(qa);
+    for (int chunk = ww.c0 + 1; chunk < ww.c1; ++chunk) {
+      chunk_load(chunk, cr);
+      compute_chunk(qa);
+    }
+  }
+  // Merge the chunks' softmax state into the tiles': both scaled to the
+  // common maximum (a wave with neither tiles nor chunks keeps -inf and 0).
+  {
+    float aC[HG];
 #pragma unroll
-      for (int hg = 0; hg < HG; ++hg) {
-        const int h = 4 * hg + hq;
+    for (int hg = 0; hg < HG; ++hg) {
+      const float mx = fmaxf(m[hg], mC[hg]);
+      const float aT = mx == -INFINITY ? 0.0f : fast_exp2(m[hg] - mx);
+      aC[hg] = mx == -INFINITY ? 0.0f : fast_exp2(mC[hg] - mx);
+      m[hg] = mx;
+      lsum[hg] = lsum[hg] * aT + lC[hg] * aC[hg];
 #pragma unroll
-        for (int mk = 0; mk < D / 32; ++mk) {
-          uint4 w = make_uint4(0u, 0u, 0u, 0u);
-          if (h < GQA && part < 2) w = *reinterpret_cast<const uint4*>(&qsHL[wave][part][h][32 * mk + 8 * q4]);
-          qa[hg][mk] = __builtin_bit_cast(bf8_t, w);
+      for (int n = 0; n < NV; ++n) acc_f[hg][n] *= aT;
+    }
+#pragma unroll
+    for (int hg = 0; hg < HG; ++hg)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int h = 4 * hg + i;
+        if (h < GQA) {
+          const float a = lane_value(aC[hg], 16 * i);
+#pragma unroll
+          for (int k = 0; k < TCPL; ++k) acc_tail[k][h] *= a;
         }
       }
-    }
-    for (int chunk = ww.c0; chunk < ww.c1; ++chunk) {
-      float al_u[GQA];
-#pragma unroll
-      for (int hg = 0; hg < HG; ++hg) {
-        f4_t sc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int mk = 0; mk < D / 32; ++mk)
-          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[hg][mk], __builtin_bit_cast(bf8_t, cr.k[mk]), sc, 0, 0, 0);
-        const float xs = col < cr.nvalid ? sc[0] + sc[1] : -INFINITY;
-        const float mn = fmaxf(m[hg], row16_max(xs));     // finite: a chunk has a valid token
-        const float al = fast_exp2(m[hg] - mn);            // exp2(-inf) = 0 before the first token
-        m[hg] = mn;
-        const float pr = fast_exp2(xs - mn);               // 0 for padding tokens
-        lsum[hg] = lsum[hg] * al + pr;
-#pragma unroll
-        for (int n = 0; n < NV; ++n) acc_f[hg][n] *= al;
-        if (4 * hg + q4 < GQA) pw[wave][col][4 * hg + q4] = pr;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (4 * hg + i < GQA) al_u[4 * hg + i] = lane_value(al, 16 * i);
-      }
-      wave_lds_sync();
-#pragma unroll
-      for (int t = 0; t < kTailChunk; ++t) {
-        float v[TCPL];
-        v[0] = bf16_lo(cr.v[t]);
-        if constexpr (TCPL == 2) v[1] = bf16_hi(cr.v[t]);
-#pragma unroll
-        for (int h = 0; h < GQA; ++h) {
-          const float pt = pw[wave][t][h];
-#pragma unroll
-          for (int k = 0; k < TCPL; ++k)
-            acc_tail[k][h] = fmaf(pt, v[k], t == 0 ? acc_tail[k][h] * al_u[h] : acc_tail[k][h]);
-        }
-      }
-      wave_lds_sync();      // pw is rewritten by the next chunk
-      chunk_load(chunk + 1, cr);   // nothing is read past the run
-    }
   }
 
   // Per-head state as wave-uniform values (head 4 hg + i lives in lanes 16 i..).
@@ -1954,15 +2000,18 @@ kvq_status paged_decode_setup(const Geom& g, const kvq_state* st, const kvq_page
   a = decode_args(g, &st[0], &dense, q, softmax_scale, num_splits, out, workspace);
   // Splits sized by work: every split of every sequence gets about per_split
   // items (window chunks count as tiles), so a long sequence takes more
-  // splits instead of setting the time for the batch.  Auto: about two
-  // workgroups per compute unit, at least four items each.
+  // splits instead of setting the time for the batch.  Auto: about one
+  // workgroup per compute unit (as for uniform caches), at least four items
+  // each.
   int per_split;
   if (num_splits > 0) {
     per_split = (max_items + num_splits - 1) / num_splits;
   } else {
     // Each sequence rounds its split count up: grow per_split until the
-    // workgroups with work fit in one round of two per compute unit.
-    const int64_t target = (sum_items + 2 * 256 - 1) / (2 * 256);
+    // workgroups with work fit in one per compute unit (256).  Measured on
+    // the ragged Llama-3-8B batch: 17.9 us per call against 19.3 us at two
+    // per compute unit.
+    const int64_t target = (sum_items + 256 - 1) / 256;
     per_split = static_cast<int>(target < 4 ? 4 : target);
     for (;;) {
       int64_t wgs = 0;
@@ -1970,7 +2019,7 @@ kvq_status paged_decode_setup(const Geom& g, const kvq_state* st, const kvq_page
         const int items = static_cast<int>((st[b].quantized + kTile - 1) / kTile + (st[b].tail + kTailChunk - 1) / kTailChunk);
         wgs += (int64_t)g.H * ((items + per_split - 1) / per_split);
       }
-      if (wgs <= 2 * 256 || per_split >= max_items) break;
+      if (wgs <= 256 || per_split >= max_items) break;
       ++per_split;
     }
   }
