@@ -96,7 +96,7 @@ def run_decode(args, log):
 
     w = ks.LLAMA3_DECODE
     steps, warmup = args.steps, args.warmup
-    capacity = w.prefill + (2 * steps + warmup) // args.caches + 256
+    capacity = w.prefill + (3 * steps + warmup) // args.caches + 128 + 256
     cfg, caches = build_caches(w, args.caches, capacity, log)
     pool = 32
     s = ks.Stream(w, seed=10_000)
@@ -149,6 +149,23 @@ def run_decode(args, log):
     torch.cuda.synchronize()
     two_call_ms = start.elapsed_time(end) / steps
 
+    # Steps through a flush, as in a real decode loop with G = 128: 128 more
+    # steps per cache, round robin over the caches (each cache's window,
+    # 128..255 tokens, reaches 256 exactly once and flushes 128 tokens).
+    flush_rounds = 128
+    f_bytes, f0 = 0, sum(c.state.segments for c in caches)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for r in range(flush_rounds):
+        for j in range(len(caches)):
+            c = step(r * len(caches) + j)
+            f_bytes += decode_bytes(cfg, c.state.quantized, c.state.tail, w.q_heads)
+    end.record(stream)
+    torch.cuda.synchronize()
+    flush_steps = flush_rounds * len(caches)
+    flushes = sum(c.state.segments for c in caches) - f0
+    flush_ms = start.elapsed_time(end) / flush_steps
+
     # The decode call alone, eager: the same caches, back-to-back calls on the
     # launch stream, one HIP event pair around all of them (the host-side
     # launch cost of each call is included when it exceeds the GPU time).
@@ -187,6 +204,7 @@ def run_decode(args, log):
     torch.cuda.synchronize()
     dec_ms = d0.elapsed_time(d1) / (replays * len(caches))
     achieved = g_bytes / len(caches) / (dec_ms * 1e-3) / 1e9
+    log(f"{flush_steps} steps with {flushes} flushes: {flush_ms*1e3:.2f} us per step")
     log(f"wall {wall:.3f}s for {steps} steps; {ms_step*1e3:.2f} us per step "
         f"({two_call_ms*1e3:.2f} us as append + decode_attn); decode call "
         f"{dec_ms*1e3:.2f} us (graph replay), {eager_ms*1e3:.2f} us (eager back to back)")
@@ -198,6 +216,9 @@ def run_decode(args, log):
         "ms_per_step": round(ms_step, 5),
         "us_per_step": round(ms_step * 1e3, 3),
         "us_per_step_two_calls": round(two_call_ms * 1e3, 3),
+        "us_per_step_with_flushes": round(flush_ms * 1e3, 3),
+        "steps_with_flushes": {"steps": flush_steps, "flushes": int(flushes),
+                               "gbs": round(f_bytes / flush_steps / (flush_ms * 1e-3) / 1e9, 2)},
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "i8 MFMA (i32 acc) + f32 softmax", "data": "synthetic",
@@ -1060,6 +1081,20 @@ def run_hbm_read(args, log):
             log(f"hbm read {dec} B, {wgs} workgroups, depth {depth}: {us:.2f} us, {dec / us / 1e3:.0f} GB/s")
     del bufs
     torch.cuda.empty_cache()
+    # The input of one 128-token flush of the append workload (16 x 8 heads,
+    # K and V, bf16): 8,388,608 bytes, 40 buffers rotated (335 MB).
+    fl = ks.APPEND_INT4
+    fbytes = fl.batch * fl.kv_heads * fl.group * fl.head_dim * 2 * 2
+    fbufs = [torch.ones(fbytes // 4, dtype=torch.int32, device="cuda") for _ in range(40)]
+    flush = {}
+    for wgs in (256, 512, 1024, 2048):
+        for depth in (2, 4, 8, 16):
+            us = _graph_us([(lambda st, b=b: probes.stream_read(b, wgs, depth, sink, st)) for b in fbufs], reps)
+            flush[f"{wgs}x{depth}"] = round(us, 3)
+            log(f"hbm read {fbytes} B, {wgs} workgroups, depth {depth}: {us:.2f} us, {fbytes / us / 1e3:.0f} GB/s")
+    del fbufs
+    torch.cuda.empty_cache()
+    best_flush = min(flush.items(), key=lambda kv: kv[1])
     big_bytes = 1 << 30
     big = torch.ones(big_bytes // 4, dtype=torch.int32, device="cuda")
     large = {}
@@ -1088,7 +1123,9 @@ def run_hbm_read(args, log):
         "small_512wg_us": at512[0], "small_512wg_shape": at512[1],
         "small_512wg_gbs": round(dec / at512[0] / 1e3, 2),
         "large_best_shape": best_large[0],
-        "small_us_by_shape": small, "large_us_by_shape": large, "empty_kernel_us": empty,
+        "flush_input_bytes": fbytes, "flush_input_best_us": best_flush[1], "flush_input_best_shape": best_flush[0],
+        "small_us_by_shape": small, "large_us_by_shape": large, "flush_input_us_by_shape": flush,
+        "empty_kernel_us": empty,
         "roofline": {"bound": "hbm", "achieved": round(big_bytes / best_large[1] / 1e3, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(big_bytes / best_large[1] / 1e3 / HBM_PEAK_GBS, 4),
                      "traffic": None, "kernel": "stream_read_kernel"},
