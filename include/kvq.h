@@ -207,8 +207,10 @@ kvq_status kvq_workspace_init(void* workspace, size_t bytes, void* stream);
  * quantized prefix are restored inside the kernel (read path "decode inside
  * the kernel", "KV Cache quantization and compression", section 06); the
  * tail is read as stored.  The sequence axis is split across workgroups and
- * the partial softmax states are merged by a second, small kernel
- * (flash-decoding split, the former page, section 05).
+ * the partial softmax states are merged (flash-decoding split, the former
+ * page, section 05) by the last workgroup of each (batch, KV head) to
+ * finish, in the same kernel; with more than 64 splits by a second, small
+ * kernel.
  *   q   : device, kv_dtype [batch, q_heads, head_dim]
  *   out : device, float32 [batch, q_heads, head_dim]
  *   softmax_scale : sigma (1/sqrt(head_dim) for standard attention)
@@ -245,11 +247,12 @@ kvq_status kvq_decode_attn_noalloc(const kvq_config* cfg, const kvq_state* st, c
  * kvq_decode_attn(cfg, st, cache, q, ...): the same cache bytes and state,
  * and attention outputs equal within float rounding.  When the append
  * flushes nothing (1 <= n_new <= 16, kv_dtype bf16, a non-empty cache) the
- * step runs without the append's own kernels: attention runs over the cache
- * as it was, and the merge pass adds the new tokens as further softmax
- * terms and writes them into their window slots (cutting the per-step
- * kernel launches, "KV Cache and autoregressive video generation",
- * section 05).  Otherwise it runs kvq_append, then kvq_decode_attn.
+ * step is one kernel launch: attention runs over the cache as it was, and
+ * the workgroup that merges a (batch, KV head)'s splits adds the new tokens
+ * as further softmax terms and writes them into their window slots
+ * (cutting the per-step kernel launches, "KV Cache and autoregressive video
+ * generation", section 05).  Otherwise it runs kvq_append, then
+ * kvq_decode_attn.
  *   st           : host, advanced as kvq_plan_append says on KVQ_OK
  *   k_new, v_new : device, kv_dtype [batch, kv_heads, n_new, head_dim]
  *   q, out, softmax_scale, num_splits, workspace : as for kvq_decode_attn
