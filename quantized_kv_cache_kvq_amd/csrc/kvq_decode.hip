@@ -13,10 +13,15 @@
 // each).  Split s owns a contiguous run of items and hands each of its four
 // waves a contiguous sub-run (so a wave meets each Key segment once); every
 // wave keeps one online-softmax state per query head (m, l, acc) in the log2
-// domain.  The workgroup folds its waves into one partial; a second, small
-// kernel merges the partials of each (batch, KV head).  With a single split
-// the workgroup writes the output itself.  No device-scope fence is used: on
-// gfx950 one costs a whole-L2 writeback and invalidate per workgroup.
+// domain.  The workgroup folds its waves into one partial; the last
+// workgroup of each (batch, KV head) to finish merges the partials (see
+// finish_unit), or, above 64 splits, a second, small kernel does.  With a
+// single split the workgroup writes the output itself.  No device-scope
+// fence is used: on gfx950 one costs a whole-L2 writeback and invalidate
+// per workgroup.
+//
+// Same-axis caches (Keys and Values per token, one scale per run of 64
+// channels) run on decode_kernel<..., kSameAxis = true>.
 //
 // Scale folding: the per-channel Key scale of a segment is folded into the
 // query once per segment (aq = sigma * log2(e) * q / kscale), the per-token
@@ -28,9 +33,9 @@
 //     segments, bf16 window): both contractions of a quantized tile run on
 //     the integer matrix cores (v_mfma_i32_16x16x64_i8, see the comment
 //     above that kernel); window chunks score on v_mfma_f32_16x16x32_bf16.
-//   * decode_kernel (every other shape): the same work items on the vector
+//   * decode_kernel (every other shape, same-axis caches, or the vector-ALU
+//     kernel chosen in the configuration): the same work items on the vector
 //     ALUs.
-// A second, small kernel merges the split partials.
 // Hot-loop indexing is 32-bit; ring slots wrap with one subtraction.
 #include <mutex>
 
