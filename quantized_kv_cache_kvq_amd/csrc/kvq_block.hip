@@ -130,16 +130,21 @@ void block_kernel(BlockArgs a0, PB pb) {
   const int split = blockIdx.y;
   const int b = unit / g.H, kvh = unit % g.H;
   // Paged caches: this sequence's own lengths (uniform caches: as given).
-  BlockArgs pa = a0;
-  if constexpr (kPaged) {
-    pa.nq = pb.nq[b];
-    pa.nt = pb.nt[b];
-    pa.nq_slot = pa.nq % g.ring;
-    pa.cached = pa.nq + pa.nt;
-    pa.tiles_q = (pa.nq + kTile - 1) / kTile;
-    pa.tiles_t = (pa.nt + kTile - 1) / kTile;
-  }
-  const BlockArgs& a = pa;
+  // (kept in scalars rather than a modified copy of the arguments, which
+  // the compiler would leave in scratch memory)
+  const int s_nq = [&] {
+    if constexpr (kPaged) return pb.nq[b];
+    else return a0.nq;
+  }();
+  const int s_nt = [&] {
+    if constexpr (kPaged) return pb.nt[b];
+    else return a0.nt;
+  }();
+  const int s_nq_slot = kPaged ? s_nq % g.ring : a0.nq_slot;
+  const int s_cached = kPaged ? s_nq + s_nt : a0.cached;
+  const int s_tiles_q = kPaged ? (s_nq + kTile - 1) / kTile : a0.tiles_q;
+  const int s_tiles_t = kPaged ? (s_nt + kTile - 1) / kTile : a0.tiles_t;
+  const BlockArgs& a = a0;
   // Base of this KV head's part of the page of quantized tile `item`
   // (paged); page numbers outside the pool are clamped into it.
   auto page_head = [&](int item) -> const uint8_t* {
@@ -154,10 +159,12 @@ void block_kernel(BlockArgs a0, PB pb) {
   const int r0 = blockIdx.x * kRowsWG;
   const int Hq = g.H * a.gqa;
 
-  __shared__ __attribute__((aligned(16))) __bf16 Khi[kTile][KROW];
-  __shared__ __attribute__((aligned(16))) __bf16 Klo[kTile][KROW];
-  __shared__ __attribute__((aligned(16))) _Float16 Vs[D][VROW];
-  __shared__ __attribute__((aligned(16))) float vsr[kTile];
+  // Two tile buffers: tile j of the split's run lives in buffer j % 2, so a
+  // tile is restored while the one before it is computed.
+  __shared__ __attribute__((aligned(16))) __bf16 Khi[2][kTile][KROW];
+  __shared__ __attribute__((aligned(16))) __bf16 Klo[2][kTile][KROW];
+  __shared__ __attribute__((aligned(16))) _Float16 Vs[2][D][VROW];
+  __shared__ __attribute__((aligned(16))) float vsr[2][kTile];
   __shared__ __attribute__((aligned(16))) float2 rkL[2][D];  // 1 / kscale split into bf16 hi, lo (as fp32),
                                                              // by item parity (G > 0)
   __shared__ float xch[kBWaves][kRowsWave];   // per-row values exchanged inside a wave
@@ -168,7 +175,7 @@ void block_kernel(BlockArgs a0, PB pb) {
   // Last block token each of those rows sees: the end of its frame
   // floor((N + pos) / F), clipped to the block.
   auto own_limit = [&](int pos) {
-    return min(a.tq - 1, ((a.cached + pos) / a.frame + 1) * a.frame - 1 - a.cached);
+    return min(a.tq - 1, ((s_cached + pos) / a.frame + 1) * a.frame - 1 - s_cached);
   };
   int qlim[2];
 #pragma unroll
@@ -195,7 +202,7 @@ void block_kernel(BlockArgs a0, PB pb) {
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) acc[qb][cb] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-  const int items = a.tiles_q + a.tiles_t + a.tiles_b;
+  const int items = s_tiles_q + s_tiles_t + a.tiles_b;
   const int i0 = (int)(((int64_t)items * split) / a.splits);
   const int i1 = (int)(((int64_t)items * (split + 1)) / a.splits);
   const int64_t stream = (int64_t)unit * g.code_stream;
@@ -209,7 +216,7 @@ void block_kernel(BlockArgs a0, PB pb) {
     const float hi = (float)(__bf16)r;
     return float2{hi, (float)(__bf16)(r - hi)};
   };
-  if (g.G > 0 && i0 < i1 && i0 < a.tiles_q && tid < D) rkL[i0 & 1][tid] = seg_rk(i0);
+  if (g.G > 0 && i0 < i1 && i0 < s_tiles_q && tid < D) rkL[i0 & 1][tid] = seg_rk(i0);
   // Raw codes and the Value scale a thread restores from a quantized tile;
   // the next tile's are loaded while the current one is computed.
   struct QRaw {
@@ -219,7 +226,7 @@ void block_kernel(BlockArgs a0, PB pb) {
   };
   auto load_qraw = [&](int item, QRaw& r) {
     const int t0 = item * kTile;
-    const int count = min(kTile, a.nq - t0);
+    const int count = min(kTile, s_nq - t0);
     const int i = tid % kTile, grp = tid / kTile;
     const uint8_t* kt = kPaged ? page_head(item) : a.k_codes + stream + (int64_t)item * (kTile * g.W);
     const int rb = grp * CG * BITS / 8;
@@ -237,115 +244,142 @@ void block_kernel(BlockArgs a0, PB pb) {
                                    : a.v_scale + (int64_t)unit * g.C + t0;
     r.vs = tid < count ? vsrow[tid] : (uint16_t)0;
   };
+  // Tiles past the last block tile any row of the workgroup sees are skipped.
+  const int i_end = min(i1, s_tiles_q + s_tiles_t + lim_hi / kTile + 1);
   QRaw cur;
-  if (i0 < i1 && i0 < a.tiles_q) load_qraw(i0, cur);
-  __syncthreads();
-
-  for (int item = i0; item < i1; ++item) {
-    const int kind = item < a.tiles_q ? kQuant : (item < a.tiles_q + a.tiles_t ? kTail : kOwn);
-    const int tile = kind == kQuant ? item : (kind == kTail ? item - a.tiles_q : item - a.tiles_q - a.tiles_t);
+  // ---- restore tile `item` into LDS buffer bf (a quantized tile from cur) ----
+  auto restore = [&](int item, int bf) __attribute__((always_inline)) {
+    const int kind = item < s_tiles_q ? kQuant : (item < s_tiles_q + s_tiles_t ? kTail : kOwn);
+    const int tile = kind == kQuant ? item : (kind == kTail ? item - s_tiles_q : item - s_tiles_q - s_tiles_t);
     const int t0 = tile * kTile;
-    if (kind == kOwn && t0 > lim_hi) break;   // later block tiles are masked for every row here
-    const int count = kind == kQuant ? min(kTile, a.nq - t0)
-                                     : (kind == kTail ? min(kTile, a.nt - t0) : min(kTile, a.tq - t0));
-
-    // ---- fill: restore the tile into LDS ----
-    {
-      const int i = tid % kTile, grp = tid / kTile;     // K: token i, channels grp * CG ..
-      const bool tv = i < count;
-      if (kind == kQuant) {
-        const uint32_t* w = cur.w;
-        // one segment per flush (G == 0): each token reads its own Key-scale row
-        const uint16_t* ks = kscale_unit + (g.G > 0 ? 0 : (tv ? a.seg_index[t0 + i] : 0)) * D + grp * CG;
-        const float2* rks = &rkL[item & 1][grp * CG];
-#pragma unroll
-        for (int e = 0; e < CG; e += 8) {
-          __bf16 hi[8], lo[8];
-          if (g.G > 0) {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-              const int f = e + j;
-              const float code = (float)sext_field<BITS>(w[f * BITS / 32], (f * BITS) % 32);
-              const float2 rk = rks[e + j];     // 1 / kscale = rk.x + rk.y, both bf16 values
-              if constexpr (BITS == 2) {
-                // code in {-1, 0, 1}: code * rk.x and code * rk.y are exact bf16 values
-                hi[j] = (__bf16)(code * rk.x);
-                lo[j] = (__bf16)(code * rk.y);
-              } else {
-                const float x = fmaf(code, rk.x, code * rk.y);
+    const int count = kind == kQuant ? min(kTile, s_nq - t0)
+                                     : (kind == kTail ? min(kTile, s_nt - t0) : min(kTile, a.tq - t0));
+      // ---- fill: restore the tile into LDS ----
+      {
+        const int i = tid % kTile, grp = tid / kTile;     // K: token i, channels grp * CG ..
+        const bool tv = i < count;
+        if (kind == kQuant) {
+          const uint32_t* w = cur.w;
+          // one segment per flush (G == 0): each token reads its own Key-scale row
+          const uint16_t* ks = kscale_unit + (g.G > 0 ? 0 : (tv ? a.seg_index[t0 + i] : 0)) * D + grp * CG;
+          const float2* rks = &rkL[item & 1][grp * CG];
+  #pragma unroll
+          for (int e = 0; e < CG; e += 8) {
+            __bf16 hi[8], lo[8];
+            if (g.G > 0) {
+  #pragma unroll
+              for (int j = 0; j < 8; ++j) {
+                const int f = e + j;
+                const float code = (float)sext_field<BITS>(w[f * BITS / 32], (f * BITS) % 32);
+                const float2 rk = rks[e + j];     // 1 / kscale = rk.x + rk.y, both bf16 values
+                if constexpr (BITS == 2) {
+                  // code in {-1, 0, 1}: code * rk.x and code * rk.y are exact bf16 values
+                  hi[j] = (__bf16)(code * rk.x);
+                  lo[j] = (__bf16)(code * rk.y);
+                } else {
+                  const float x = fmaf(code, rk.x, code * rk.y);
+                  hi[j] = (__bf16)x;
+                  lo[j] = (__bf16)(x - (float)hi[j]);
+                }
+              }
+            } else {
+              const uint4 sw = *reinterpret_cast<const uint4*>(ks + e);
+              const uint32_t sv[4] = {sw.x, sw.y, sw.z, sw.w};
+  #pragma unroll
+              for (int j = 0; j < 8; ++j) {
+                const int f = e + j;
+                const float rk = fast_rcp(fmaxf(half_bits_to_f32((uint16_t)(sv[j / 2] >> (16 * (j % 2)))), g.eps));
+                const float x = (float)sext_field<BITS>(w[f * BITS / 32], (f * BITS) % 32) * rk;
                 hi[j] = (__bf16)x;
                 lo[j] = (__bf16)(x - (float)hi[j]);
               }
             }
-          } else {
-            const uint4 sw = *reinterpret_cast<const uint4*>(ks + e);
-            const uint32_t sv[4] = {sw.x, sw.y, sw.z, sw.w};
-#pragma unroll
+            *reinterpret_cast<uint4*>(&Khi[bf][i][grp * CG + e]) = __builtin_bit_cast(uint4, hi);
+            *reinterpret_cast<uint4*>(&Klo[bf][i][grp * CG + e]) = __builtin_bit_cast(uint4, lo);
+          }
+          // V: channel c, tokens vt0 .. vt0 + NTV - 1 (a run of the channel's row)
+          const int c = tid % D, vt0 = (tid / D) * NTV;
+          const uint32_t* vw = cur.vw;
+  #pragma unroll
+          for (int j0 = 0; j0 < NTV; j0 += 8) {
+            _Float16 v8[8];
+  #pragma unroll
             for (int j = 0; j < 8; ++j) {
-              const int f = e + j;
-              const float rk = fast_rcp(fmaxf(half_bits_to_f32((uint16_t)(sv[j / 2] >> (16 * (j % 2)))), g.eps));
-              const float x = (float)sext_field<BITS>(w[f * BITS / 32], (f * BITS) % 32) * rk;
-              hi[j] = (__bf16)x;
-              lo[j] = (__bf16)(x - (float)hi[j]);
+              const int f = j0 + j;
+              v8[j] = (_Float16)(float)sext_field<BITS>(vw[f * BITS / 32], (f * BITS) % 32);
+            }
+            const uint4 v8w = __builtin_bit_cast(uint4, v8);
+            *reinterpret_cast<uint2*>(&Vs[bf][c][vt0 + j0]) = uint2{v8w.x, v8w.y};
+            *reinterpret_cast<uint2*>(&Vs[bf][c][vt0 + j0 + 4]) = uint2{v8w.z, v8w.w};
+          }
+          if (tid < kTile) vsr[bf][tid] = tid < count ? fast_rcp(fmaxf(half_bits_to_f32(cur.vs), g.eps)) : 0.0f;
+        } else {
+          // bf16 rows: K copied as the hi part (lo = 0), V transposed into fp16
+          const uint16_t* krow;
+          const uint16_t* vrow;
+          if (kind == kTail) {
+            int slot = s_nq_slot + t0 + (tv ? i : 0);
+            slot = slot >= g.ring ? slot - g.ring : slot;
+            krow = a.k_tail + ((int64_t)unit * g.ring + slot) * D;
+            vrow = a.v_tail + ((int64_t)unit * g.ring + slot) * D;
+          } else {
+            const int j = t0 + (tv ? i : 0);
+            krow = a.k_blk + (((int64_t)b * a.tq + j) * g.H + kvh) * D;
+            vrow = a.v_blk + (((int64_t)b * a.tq + j) * g.H + kvh) * D;
+          }
+  #pragma unroll
+          for (int e = 0; e < CG; e += 8) {
+            const uint4 kw = tv ? *reinterpret_cast<const uint4*>(krow + grp * CG + e) : uint4{0u, 0u, 0u, 0u};
+            const uint4 vv = tv ? *reinterpret_cast<const uint4*>(vrow + grp * CG + e) : uint4{0u, 0u, 0u, 0u};
+            *reinterpret_cast<uint4*>(&Khi[bf][i][grp * CG + e]) = kw;
+            *reinterpret_cast<uint4*>(&Klo[bf][i][grp * CG + e]) = uint4{0u, 0u, 0u, 0u};
+            const uint32_t vs4[4] = {vv.x, vv.y, vv.z, vv.w};
+  #pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              const float v = __uint_as_float((vs4[j / 2] >> (16 * (j % 2))) << 16);
+              Vs[bf][grp * CG + e + j][i] = (_Float16)v;
             }
           }
-          *reinterpret_cast<uint4*>(&Khi[i][grp * CG + e]) = __builtin_bit_cast(uint4, hi);
-          *reinterpret_cast<uint4*>(&Klo[i][grp * CG + e]) = __builtin_bit_cast(uint4, lo);
+          if (tid < kTile) vsr[bf][tid] = tid < count ? 1.0f : 0.0f;
         }
-        // V: channel c, tokens vt0 .. vt0 + NTV - 1 (a run of the channel's row)
-        const int c = tid % D, vt0 = (tid / D) * NTV;
-        const uint32_t* vw = cur.vw;
-#pragma unroll
-        for (int j0 = 0; j0 < NTV; j0 += 8) {
-          _Float16 v8[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const int f = j0 + j;
-            v8[j] = (_Float16)(float)sext_field<BITS>(vw[f * BITS / 32], (f * BITS) % 32);
-          }
-          const uint4 v8w = __builtin_bit_cast(uint4, v8);
-          *reinterpret_cast<uint2*>(&Vs[c][vt0 + j0]) = uint2{v8w.x, v8w.y};
-          *reinterpret_cast<uint2*>(&Vs[c][vt0 + j0 + 4]) = uint2{v8w.z, v8w.w};
-        }
-        if (tid < kTile) vsr[tid] = tid < count ? fast_rcp(fmaxf(half_bits_to_f32(cur.vs), g.eps)) : 0.0f;
-      } else {
-        // bf16 rows: K copied as the hi part (lo = 0), V transposed into fp16
-        const uint16_t* krow;
-        const uint16_t* vrow;
-        if (kind == kTail) {
-          int slot = a.nq_slot + t0 + (tv ? i : 0);
-          slot = slot >= g.ring ? slot - g.ring : slot;
-          krow = a.k_tail + ((int64_t)unit * g.ring + slot) * D;
-          vrow = a.v_tail + ((int64_t)unit * g.ring + slot) * D;
-        } else {
-          const int j = t0 + (tv ? i : 0);
-          krow = a.k_blk + (((int64_t)b * a.tq + j) * g.H + kvh) * D;
-          vrow = a.v_blk + (((int64_t)b * a.tq + j) * g.H + kvh) * D;
-        }
-#pragma unroll
-        for (int e = 0; e < CG; e += 8) {
-          const uint4 kw = tv ? *reinterpret_cast<const uint4*>(krow + grp * CG + e) : uint4{0u, 0u, 0u, 0u};
-          const uint4 vv = tv ? *reinterpret_cast<const uint4*>(vrow + grp * CG + e) : uint4{0u, 0u, 0u, 0u};
-          *reinterpret_cast<uint4*>(&Khi[i][grp * CG + e]) = kw;
-          *reinterpret_cast<uint4*>(&Klo[i][grp * CG + e]) = uint4{0u, 0u, 0u, 0u};
-          const uint32_t vs4[4] = {vv.x, vv.y, vv.z, vv.w};
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const float v = __uint_as_float((vs4[j / 2] >> (16 * (j % 2))) << 16);
-            Vs[grp * CG + e + j][i] = (_Float16)v;
-          }
-        }
-        if (tid < kTile) vsr[tid] = tid < count ? 1.0f : 0.0f;
       }
+  };
+  // The raw codes and Key-scale reciprocals of quantized tile `item`; rk is
+  // written to rkL[item & 1] before the barrier that precedes its restore.
+  float2 rk_next = float2{0.0f, 0.0f};
+  auto fetch = [&](int item) __attribute__((always_inline)) {
+    if (item < i_end && item < s_tiles_q) {
+      if (g.G > 0 && tid < D) rk_next = seg_rk(item);
+      load_qraw(item, cur);
     }
-    __syncthreads();
-    // The next quantized tile's Key-scale reciprocals (read by its fill after
-    // the closing barrier); the load's latency hides behind this tile.
-    const bool next_q = item + 1 < i1 && item + 1 < a.tiles_q;
-    const bool next_rk = g.G > 0 && next_q && tid < D;
-    float2 rk_next = float2{0.0f, 0.0f};
-    if (next_rk) rk_next = seg_rk(item + 1);
-    if (next_q) load_qraw(item + 1, cur);    // cur's fill is done: its registers are free
+  };
+  if (i0 < i_end && i0 < s_tiles_q) load_qraw(i0, cur);
+  __syncthreads();                 // rkL of the first tile
+  if (i0 < i_end) restore(i0, 0);
+  fetch(i0 + 1);
+  if (g.G > 0 && i0 + 1 < i_end && i0 + 1 < s_tiles_q && tid < D) rkL[(i0 + 1) & 1][tid] = rk_next;
+  __syncthreads();                 // the first tile is restored
+
+  // Each step computes tile `item` from buffer b and restores tile item + 1
+  // into the other buffer, with one barrier per tile.  The two waves of a
+  // SIMD (wave w and w + half) take the phases in different orders --
+  // logits, softmax, P.V, restore against restore, logits, softmax, P.V --
+  // so that one of them is on the matrix cores while the other is on the
+  // vector ALUs; the logits and the P operands are never live during a
+  // restore.
+  const bool restore_first = wave >= kBWaves / 2;
+  for (int item = i0; item < i_end; ++item) {
+    const int b = (item - i0) & 1;
+    const int kind = item < s_tiles_q ? kQuant : (item < s_tiles_q + s_tiles_t ? kTail : kOwn);
+    const int tile = kind == kQuant ? item : (kind == kTail ? item - s_tiles_q : item - s_tiles_q - s_tiles_t);
+    const int t0 = tile * kTile;
+    const int count = kind == kQuant ? min(kTile, s_nq - t0)
+                                     : (kind == kTail ? min(kTile, s_nt - t0) : min(kTile, a.tq - t0));
+    auto restore_next = [&]() __attribute__((always_inline)) {
+      if (item + 1 < i_end) restore(item + 1, b ^ 1);
+      fetch(item + 2);             // cur's restore is done: its registers are free
+    };
+    if (restore_first) restore_next();
 
     // ---- logits S^T[token][query] (token block tb, query block qb) ----
     // The Key operands of k step ks + 1 are read from LDS while the MFMAs of
@@ -362,8 +396,8 @@ void block_kernel(BlockArgs a0, PB pb) {
       auto kread = [&](int ks, bf8_t (&h)[4], bf8_t (&l)[4]) {
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) {
-          h[tb] = *reinterpret_cast<const bf8_t*>(&Khi[tb * 16 + col][32 * ks + 8 * q4]);
-          if constexpr (kLo) l[tb] = *reinterpret_cast<const bf8_t*>(&Klo[tb * 16 + col][32 * ks + 8 * q4]);
+          h[tb] = *reinterpret_cast<const bf8_t*>(&Khi[b][tb * 16 + col][32 * ks + 8 * q4]);
+          if constexpr (kLo) l[tb] = *reinterpret_cast<const bf8_t*>(&Klo[b][tb * 16 + col][32 * ks + 8 * q4]);
         }
       };
       kread(0, kh[0], kl[0]);
@@ -400,7 +434,7 @@ void block_kernel(BlockArgs a0, PB pb) {
     float vr[4][4];       // 1 / vscale of the lane's tokens (shared by both query blocks)
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
-      const float4 v4 = *reinterpret_cast<const float4*>(&vsr[16 * tb + 4 * q4]);
+      const float4 v4 = *reinterpret_cast<const float4*>(&vsr[b][16 * tb + 4 * q4]);
       vr[tb][0] = v4.x; vr[tb][1] = v4.y; vr[tb][2] = v4.z; vr[tb][3] = v4.w;
     }
     const bool full = kind == kQuant && count == kTile;   // no masking needed
@@ -478,8 +512,8 @@ void block_kernel(BlockArgs a0, PB pb) {
 #pragma unroll
       for (int j = 0; j < kVB; ++j) {
         const int cb = cb0 + j;
-        const h4_t v0 = *reinterpret_cast<const h4_t*>(&Vs[16 * cb + col][32 * ks + 4 * q4]);
-        const h4_t v1 = *reinterpret_cast<const h4_t*>(&Vs[16 * cb + col][32 * ks + 16 + 4 * q4]);
+        const h4_t v0 = *reinterpret_cast<const h4_t*>(&Vs[b][16 * cb + col][32 * ks + 4 * q4]);
+        const h4_t v1 = *reinterpret_cast<const h4_t*>(&Vs[b][16 * cb + col][32 * ks + 16 + 4 * q4]);
         v[j] = h8_t{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
       }
     };
@@ -496,8 +530,10 @@ void block_kernel(BlockArgs a0, PB pb) {
           acc[qb][cb0 + j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[qb][ks], vop[bi & 1][j], acc[qb][cb0 + j], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (next_rk) rkL[(item + 1) & 1][tid] = rk_next;
-    __syncthreads();      // the next tile overwrites the LDS tile
+    if (!restore_first) restore_next();
+    // the Key-scale reciprocals of tile item + 2 into the slot tile item used
+    if (g.G > 0 && item + 2 < i_end && item + 2 < s_tiles_q && tid < D) rkL[item & 1][tid] = rk_next;
+    __syncthreads();      // tile item + 1 is restored; buffer b is free
   }
 
   // ---- write: rows 4 q4 + i of block qb, channel 16 cb + col ----
