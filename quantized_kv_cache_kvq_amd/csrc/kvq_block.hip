@@ -422,11 +422,6 @@ void block_kernel(BlockArgs a0, PB pb) {
     };
     if (kind == kQuant) logits(Par<1>{});
     else logits(Par<0>{});
-    // The softmax runs at raised wave priority: the SIMD's other wave is then
-    // more often in a matrix phase while this one does vector work (measured
-    // about 1% on the video block; raising it for the matrix phases instead,
-    // or for the restore, was slower).
-    __builtin_amdgcn_s_setprio(1);
 
     // ---- online softmax per query (lane's column col of block qb) ----
     // S[tb][qb][i]: token t0 + 16 tb + 4 q4 + i; the logit (log2 domain) is
@@ -499,7 +494,6 @@ void block_kernel(BlockArgs a0, PB pb) {
       wave_lds_sync();
     }
 
-    __builtin_amdgcn_s_setprio(0);
 
     // ---- acc[query][channel] += P' . V (k step outermost; the Value
     // operands of k step 1 are read while the MFMAs of k step 0 run) ----
