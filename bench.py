@@ -52,9 +52,9 @@ LONG_CALL_TRAFFIC = 140_361_300      # one 131072-token layer (algorithmic 138.8
 # 128 appends (16 flushes + 128 window copies) and one block-attention call
 # (block_kernel + block_merge_kernel).
 APPEND_RUN_TRAFFIC = {4: 444_227_127, 8: 478_851_968}
-BLOCK_CALL_TRAFFIC = 2_009_669_018    # the cache is streamed once per query-row tile
+BLOCK_CALL_TRAFFIC = 2_014_996_480    # the cache is streamed once per query-row tile
 PAGED_CALL_TRAFFIC = 44_925_590      # paged decode, ragged lengths (algorithmic 41.42 MB)
-PAGED_BLOCK_CALL_TRAFFIC = 2_067_186_586   # the video block over a paged cache
+PAGED_BLOCK_CALL_TRAFFIC = None            # the video block over a paged cache
 
 
 def decode_bytes(cfg, nq: int, nt: int, q_heads: int) -> int:
