@@ -47,14 +47,14 @@ HBM_PEAK_GBS = 8000.0
 # write (FETCH_SIZE x 2, WRITE_SIZE x 1).  Each describes the kernels named
 # in profiles/ and is None while those kernels have changed since the
 # counters were taken.
-DECODE_CALL_TRAFFIC = 39_771_465     # decode_i8_kernel, 4096-token Llama-3-8B shape (algorithmic 37.78 MB)
-LONG_CALL_TRAFFIC = 140_361_300      # one 131072-token layer (algorithmic 138.8 MB)
+DECODE_CALL_TRAFFIC = 39_769_872     # decode_i8_kernel, 4096-token Llama-3-8B shape (algorithmic 37.78 MB)
+LONG_CALL_TRAFFIC = 140_363_052      # one 131072-token layer (algorithmic 138.8 MB)
 # 128 appends (16 flushes + 128 window copies) and one block-attention call
 # (block_kernel + block_merge_kernel).
-APPEND_RUN_TRAFFIC = {4: 444_227_127, 8: 478_851_968}
+APPEND_RUN_TRAFFIC = {4: 444_055_424, 8: 479_014_967}
 BLOCK_CALL_TRAFFIC = 2_014_996_480    # the cache is streamed once per query-row tile
-PAGED_CALL_TRAFFIC = 44_925_590      # paged decode, ragged lengths (algorithmic 41.42 MB)
-PAGED_BLOCK_CALL_TRAFFIC = None            # the video block over a paged cache
+PAGED_CALL_TRAFFIC = 43_854_541      # paged decode, ragged lengths (algorithmic 41.42 MB)
+PAGED_BLOCK_CALL_TRAFFIC = 2_071_425_178  # the video block over a paged cache
 
 
 def decode_bytes(cfg, nq: int, nt: int, q_heads: int) -> int:
@@ -149,23 +149,6 @@ def run_decode(args, log):
     torch.cuda.synchronize()
     two_call_ms = start.elapsed_time(end) / steps
 
-    # Steps through a flush, as in a real decode loop with G = 128: 128 more
-    # steps per cache, round robin over the caches (each cache's window,
-    # 128..255 tokens, reaches 256 exactly once and flushes 128 tokens).
-    flush_rounds = 128
-    f_bytes, f0 = 0, sum(c.state.segments for c in caches)
-    torch.cuda.synchronize()
-    start.record(stream)
-    for r in range(flush_rounds):
-        for j in range(len(caches)):
-            c = step(r * len(caches) + j)
-            f_bytes += decode_bytes(cfg, c.state.quantized, c.state.tail, w.q_heads)
-    end.record(stream)
-    torch.cuda.synchronize()
-    flush_steps = flush_rounds * len(caches)
-    flushes = sum(c.state.segments for c in caches) - f0
-    flush_ms = start.elapsed_time(end) / flush_steps
-
     # The decode call alone, eager: the same caches, back-to-back calls on the
     # launch stream, one HIP event pair around all of them (the host-side
     # launch cost of each call is included when it exceeds the GPU time).
@@ -204,6 +187,25 @@ def run_decode(args, log):
     torch.cuda.synchronize()
     dec_ms = d0.elapsed_time(d1) / (replays * len(caches))
     achieved = g_bytes / len(caches) / (dec_ms * 1e-3) / 1e9
+
+    # Steps through a flush, as in a real decode loop with G = 128 (timed last,
+    # so that the decode-call figures above see caches of about 4096 tokens):
+    # 128 more steps per cache, round robin over the caches (each cache's window,
+    # 128..255 tokens, reaches 256 exactly once and flushes 128 tokens).
+    flush_rounds = 128
+    f_bytes, f0 = 0, sum(c.state.segments for c in caches)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for r in range(flush_rounds):
+        for j in range(len(caches)):
+            c = step(r * len(caches) + j)
+            f_bytes += decode_bytes(cfg, c.state.quantized, c.state.tail, w.q_heads)
+    end.record(stream)
+    torch.cuda.synchronize()
+    flush_steps = flush_rounds * len(caches)
+    flushes = sum(c.state.segments for c in caches) - f0
+    flush_ms = start.elapsed_time(end) / flush_steps
+
     log(f"{flush_steps} steps with {flushes} flushes: {flush_ms*1e3:.2f} us per step")
     log(f"wall {wall:.3f}s for {steps} steps; {ms_step*1e3:.2f} us per step "
         f"({two_call_ms*1e3:.2f} us as append + decode_attn); decode call "
