@@ -14,14 +14,19 @@
 // and a contiguous range of 64-token KV tiles: quantized tiles, then tail
 // tiles (bf16 ring), then own-block tiles (bf16, causal).  Its threads
 // restore each tile once into LDS, shared by its waves (32 rows each):
-//   Khi, Klo [token][channel]  bf16 hi + lo of code / kscale (tail and block
-//                              tokens: the stored value, lo = 0)
+//   Khi [token][channel]       bf16 hi of code / kscale (tail and block
+//                              tokens: the stored value)
+//   Klo8 [token][channel]      fp8 e4m3 low part (x - hi) times 2^ls, one power
+//                              of two per workgroup (quantized tiles only)
 //   V [channel][token]         fp16: the codes (exact), or the stored values
 //   vsr [token]                1 / vscale, 1 for tail and block tokens
-// Logits are computed transposed, S^T = Khat . Q^T, on
-// v_mfma_f32_16x16x32_bf16: queries are bf16 (exact) and Khat = hi + lo keeps
-// ~16 significant bits (one 16-bit rounding of an outlier channel's 1/kscale
-// alone moves logits by ~1e-3).  A lane then holds four consecutive tokens of
+// Logits are computed transposed, S^T = Khat . Q^T: the hi part on
+// v_mfma_f32_16x16x32_bf16 against the bf16 queries (exact), the low part on
+// v_mfma_scale_f32_16x16x128_f8f6f4 against the queries in fp8 (one power-of-two
+// scale per wave), the scale operands undoing both powers of two.  |lo| is at
+// most 2^-8 |Khat|, so the fp8 product adds about 2^-13 relative per term:
+// Khat keeps ~13 significant bits (one 16-bit rounding of an outlier
+// channel's 1/kscale alone moves logits by ~1e-3).  A lane then holds four consecutive tokens of
 // one query in each 16-token block -- exactly its operand of the P.V product
 // on v_mfma_f32_16x16x32_f16 once that MFMA's k slots of lane group kg are the
 // tokens 32 ks + 4 kg + j (j < 4) and 32 ks + 16 + 4 kg + (j - 4): no transpose
@@ -57,6 +62,7 @@ typedef __bf16 bf8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
 typedef float f4_t __attribute__((ext_vector_type(4)));
+typedef int f8x32_t __attribute__((ext_vector_type(8)));   // 32 fp8 e4m3 values
 
 struct BlockArgs {
   Geom g;
@@ -113,7 +119,8 @@ void block_kernel(BlockArgs a0, PB pb) {
   constexpr int kBWaves = BlockShape<D>::kWaves;
   constexpr int kRowsWG = BlockShape<D>::kRows;
   constexpr int CG = D / (kBT / kTile);    // channels per thread in the K fill
-  constexpr int KROW = D + 8;              // LDS row pitch (bf16) of Khi / Klo: no bank conflicts
+  constexpr int KROW = D + 8;              // LDS row pitch (bf16) of Khi: no bank conflicts
+  constexpr int K8ROW = D + 16;            // LDS row pitch (bytes) of Klo8
   constexpr int VROW = kTile + 4;          // LDS row pitch (fp16) of V: 34 banks, 16 rows of a
                                            // 64-bit operand read hit 32 distinct banks
   constexpr int KS = D / 32;               // k steps of the logit MFMAs
@@ -162,12 +169,15 @@ void block_kernel(BlockArgs a0, PB pb) {
   // Two tile buffers: tile j of the split's run lives in buffer j % 2, so a
   // tile is restored while the one before it is computed.
   __shared__ __attribute__((aligned(16))) __bf16 Khi[2][kTile][KROW];
-  __shared__ __attribute__((aligned(16))) __bf16 Klo[2][kTile][KROW];
+  // Klo8 byte 8 KS g + 8 ks + j holds channel 32 ks + 8 g + j: lane group g
+  // of the fp8 product reads its 8 KS bytes in one piece.
+  __shared__ __attribute__((aligned(16))) uint8_t Klo8[2][kTile][K8ROW];
   __shared__ __attribute__((aligned(16))) _Float16 Vs[2][D][VROW];
   __shared__ __attribute__((aligned(16))) float vsr[2][kTile];
   __shared__ __attribute__((aligned(16))) float2 rkL[2][D];  // 1 / kscale split into bf16 hi, lo (as fp32),
                                                              // by item parity (G > 0)
   __shared__ float xch[kBWaves][kRowsWave];   // per-row values exchanged inside a wave
+  __shared__ float kred[kBWaves];             // per-wave minima of the Key scales
 
   // ---- this wave's query rows: operand B of S^T = Khat . Q^T ----
   bf8_t qop[2][KS];
@@ -205,18 +215,103 @@ void block_kernel(BlockArgs a0, PB pb) {
   const int items = s_tiles_q + s_tiles_t + a.tiles_b;
   const int i0 = (int)(((int64_t)items * split) / a.splits);
   const int i1 = (int)(((int64_t)items * (split + 1)) / a.splits);
+  // Tiles past the last block tile any row of the workgroup sees are skipped.
+  const int i_end = min(i1, s_tiles_q + s_tiles_t + lim_hi / kTile + 1);
   const int64_t stream = (int64_t)unit * g.code_stream;
   const uint16_t* kscale_unit = a.k_scale + (int64_t)unit * g.max_seg * D;
+  auto ksrow_page = [&](int item) {
+    return reinterpret_cast<const uint16_t*>(page_head(item) + 2 * kTile * g.W + 2 * kTile);
+  };
+
+  // ---- power of two of the fp8 low parts ----
+  // |Khat| <= qmax / min kscale over the workgroup's quantized tiles, and
+  // |lo| <= 2^-8 |Khat|; with |Khat| < 2^e the low parts are stored times
+  // 2^ls, ls = 16 - e, so at most 2^8 in magnitude (fp8 e4m3 reaches 448).
+  float kmin = INFINITY;
+  {
+    constexpr int C8 = D / 8;
+    auto min8 = [](uint4 w) {
+      const uint32_t v[4] = {w.x, w.y, w.z, w.w};
+      float m = INFINITY;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) m = fminf(m, half_bits_to_f32((uint16_t)(v[j / 2] >> (16 * (j % 2)))));
+      return m;
+    };
+    const int qe = min(i_end, s_tiles_q);
+    if (i0 < qe) {
+      if constexpr (kPaged) {
+        const int n = (qe - i0) * C8;
+        for (int e = tid; e < n; e += kBT)
+          kmin = fminf(kmin, min8(*reinterpret_cast<const uint4*>(ksrow_page(i0 + e / C8) + 8 * (e % C8))));
+      } else {
+        const int s0 = g.G > 0 ? i0 * kTile / g.G : a.seg_index[i0 * kTile];
+        const int s1 = g.G > 0 ? (qe * kTile - 1) / g.G : a.seg_index[min(qe * kTile, s_nq) - 1];
+        const int n = (s1 - s0 + 1) * C8;
+        for (int e = tid; e < n; e += kBT)
+          kmin = fminf(kmin, min8(*reinterpret_cast<const uint4*>(kscale_unit + (int64_t)(s0 + e / C8) * D +
+                                                                  8 * (e % C8))));
+      }
+    }
+    kmin = -wave_max(-kmin);
+    if (lane == 0) kred[wave] = kmin;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kBWaves; ++w) kmin = fminf(kmin, kred[w]);
+  }
+  int ls = 0;
+  if (kmin < INFINITY) {
+    const float bound = (float)g.qmax / fmaxf(kmin, g.eps);
+    const int e = (int)((__float_as_uint(bound) >> 23) & 255) - 126;    // bound < 2^e
+    ls = min(max(16 - e, -100), 100);
+  }
+  const float lsf = __uint_as_float((uint32_t)(ls + 127) << 23);      // 2^ls
+  const float lsinv = __uint_as_float((uint32_t)(127 - ls) << 23);    // 2^-ls
+  const int lo_scale = 127 - ls;                                      // E8M0 2^-ls
+
+  // ---- the wave's queries in fp8 (operand B of the low product) ----
+  // times 2^-qe with max |q| * 2^-qe < 2^8; slot 8 ks + j of lane group q4 is
+  // channel 32 ks + 8 q4 + j, as in qop.
+  f8x32_t q8[2];
+  int q_scale;
+  {
+    float qa = 0.0f;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) qa = fmaxf(qa, fabsf((float)qop[qb][ks][j]));
+    qa = wave_max(qa);
+    const int qe = qa > 0.0f ? min(max((int)((__float_as_uint(qa) >> 23) & 255) - 126 - 8, -120), 120) : 0;
+    const float qsf = __uint_as_float((uint32_t)(127 - qe) << 23);
+    q_scale = 127 + qe;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          int w = 0;
+          if (ks < KS) {
+            const bf8_t& v = qop[qb][ks];
+            w = __builtin_amdgcn_cvt_pk_fp8_f32((float)v[4 * h] * qsf, (float)v[4 * h + 1] * qsf, 0, false);
+            w = __builtin_amdgcn_cvt_pk_fp8_f32((float)v[4 * h + 2] * qsf, (float)v[4 * h + 3] * qsf, w, true);
+          }
+          q8[qb][2 * ks + h] = w;
+        }
+    }
+  }
+
   // With whole-group segments every token of a tile shares one Key-scale row:
-  // its reciprocals are computed once per tile (one per thread) into rkL.
+  // its reciprocals are computed once per tile (one per thread) into rkL, the
+  // low part already times 2^ls.
   auto seg_rk = [&](int item) {
-    const uint16_t* ksrow = kPaged ? reinterpret_cast<const uint16_t*>(page_head(item) + 2 * kTile * g.W + 2 * kTile)
-                                   : kscale_unit + (item * kTile / g.G) * D;
+    const uint16_t* ksrow = kPaged ? ksrow_page(item) : kscale_unit + (item * kTile / g.G) * D;
     const float r = fast_rcp(fmaxf(half_bits_to_f32(ksrow[tid]), g.eps));
     const float hi = (float)(__bf16)r;
-    return float2{hi, (float)(__bf16)(r - hi)};
+    return float2{hi, (float)(__bf16)(r - hi) * lsf};
   };
-  if (g.G > 0 && i0 < i1 && i0 < s_tiles_q && tid < D) rkL[i0 & 1][tid] = seg_rk(i0);
+  if (g.G > 0 && i0 < i_end && i0 < s_tiles_q && tid < D) rkL[i0 & 1][tid] = seg_rk(i0);
   // Raw codes and the Value scale a thread restores from a quantized tile;
   // the next tile's are loaded while the current one is computed.
   struct QRaw {
@@ -244,8 +339,6 @@ void block_kernel(BlockArgs a0, PB pb) {
                                    : a.v_scale + (int64_t)unit * g.C + t0;
     r.vs = tid < count ? vsrow[tid] : (uint16_t)0;
   };
-  // Tiles past the last block tile any row of the workgroup sees are skipped.
-  const int i_end = min(i1, s_tiles_q + s_tiles_t + lim_hi / kTile + 1);
   QRaw cur;
   // ---- restore tile `item` into LDS buffer bf (a quantized tile from cur) ----
   auto restore = [&](int item, int bf) __attribute__((always_inline)) {
@@ -265,21 +358,22 @@ void block_kernel(BlockArgs a0, PB pb) {
           const float2* rks = &rkL[item & 1][grp * CG];
   #pragma unroll
           for (int e = 0; e < CG; e += 8) {
-            __bf16 hi[8], lo[8];
+            __bf16 hi[8];
+            float lo[8];          // low parts times 2^ls
             if (g.G > 0) {
   #pragma unroll
               for (int j = 0; j < 8; ++j) {
                 const int f = e + j;
                 const float code = (float)sext_field<BITS>(w[f * BITS / 32], (f * BITS) % 32);
-                const float2 rk = rks[e + j];     // 1 / kscale = rk.x + rk.y, both bf16 values
+                const float2 rk = rks[e + j];     // 1 / kscale = rk.x + rk.y 2^-ls (rk.x, rk.y 2^-ls bf16 values)
                 if constexpr (BITS == 2) {
-                  // code in {-1, 0, 1}: code * rk.x and code * rk.y are exact bf16 values
+                  // code in {-1, 0, 1}: code * rk.x and code * rk.y are exact
                   hi[j] = (__bf16)(code * rk.x);
-                  lo[j] = (__bf16)(code * rk.y);
+                  lo[j] = code * rk.y;
                 } else {
-                  const float x = fmaf(code, rk.x, code * rk.y);
+                  const float x = fmaf(code, rk.x, code * rk.y * lsinv);
                   hi[j] = (__bf16)x;
-                  lo[j] = (__bf16)(x - (float)hi[j]);
+                  lo[j] = (x - (float)hi[j]) * lsf;
                 }
               }
             } else {
@@ -291,11 +385,18 @@ void block_kernel(BlockArgs a0, PB pb) {
                 const float rk = fast_rcp(fmaxf(half_bits_to_f32((uint16_t)(sv[j / 2] >> (16 * (j % 2)))), g.eps));
                 const float x = (float)sext_field<BITS>(w[f * BITS / 32], (f * BITS) % 32) * rk;
                 hi[j] = (__bf16)x;
-                lo[j] = (__bf16)(x - (float)hi[j]);
+                lo[j] = (x - (float)hi[j]) * lsf;
               }
             }
             *reinterpret_cast<uint4*>(&Khi[bf][i][grp * CG + e]) = __builtin_bit_cast(uint4, hi);
-            *reinterpret_cast<uint4*>(&Klo[bf][i][grp * CG + e]) = __builtin_bit_cast(uint4, lo);
+            // channels c0 .. c0 + 7 (c0 = 32 ks + 8 g) at byte 8 KS g + 8 ks
+            const int c0 = grp * CG + e;
+            int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(lo[0], lo[1], 0, false);
+            w0 = __builtin_amdgcn_cvt_pk_fp8_f32(lo[2], lo[3], w0, true);
+            int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(lo[4], lo[5], 0, false);
+            w1 = __builtin_amdgcn_cvt_pk_fp8_f32(lo[6], lo[7], w1, true);
+            *reinterpret_cast<uint2*>(&Klo8[bf][i][8 * KS * ((c0 % 32) / 8) + 8 * (c0 / 32)]) =
+                uint2{(uint32_t)w0, (uint32_t)w1};
           }
           // V: channel c, tokens vt0 .. vt0 + NTV - 1 (a run of the channel's row)
           const int c = tid % D, vt0 = (tid / D) * NTV;
@@ -332,7 +433,6 @@ void block_kernel(BlockArgs a0, PB pb) {
             const uint4 kw = tv ? *reinterpret_cast<const uint4*>(krow + grp * CG + e) : uint4{0u, 0u, 0u, 0u};
             const uint4 vv = tv ? *reinterpret_cast<const uint4*>(vrow + grp * CG + e) : uint4{0u, 0u, 0u, 0u};
             *reinterpret_cast<uint4*>(&Khi[bf][i][grp * CG + e]) = kw;
-            *reinterpret_cast<uint4*>(&Klo[bf][i][grp * CG + e]) = uint4{0u, 0u, 0u, 0u};
             const uint32_t vs4[4] = {vv.x, vv.y, vv.z, vv.w};
   #pragma unroll
             for (int j = 0; j < 8; ++j) {
@@ -392,18 +492,27 @@ void block_kernel(BlockArgs a0, PB pb) {
       for (int qb = 0; qb < 2; ++qb) S[tb][qb] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
     auto logits = [&](auto with_lo) {
       constexpr bool kLo = decltype(with_lo)::value != 0;
-      bf8_t kh[2][4], kl[2][4];
-      auto kread = [&](int ks, bf8_t (&h)[4], bf8_t (&l)[4]) {
+      bf8_t kh[2][4];
+      f8x32_t kq[2];        // fp8 low operand of token block tb, one step ahead
+      auto kread = [&](int ks, bf8_t (&h)[4]) {
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
+        for (int tb = 0; tb < 4; ++tb)
           h[tb] = *reinterpret_cast<const bf8_t*>(&Khi[b][tb * 16 + col][32 * ks + 8 * q4]);
-          if constexpr (kLo) l[tb] = *reinterpret_cast<const bf8_t*>(&Klo[b][tb * 16 + col][32 * ks + 8 * q4]);
-        }
       };
-      kread(0, kh[0], kl[0]);
+      auto lread = [&](int tb, f8x32_t& k) {
+        const uint8_t* src = &Klo8[b][tb * 16 + col][8 * KS * q4];
+        const uint4 w0 = *reinterpret_cast<const uint4*>(src);
+        const uint4 w1 = KS == 4 ? *reinterpret_cast<const uint4*>(src + 16) : uint4{0u, 0u, 0u, 0u};
+        k = f8x32_t{(int)w0.x, (int)w0.y, (int)w0.z, (int)w0.w, (int)w1.x, (int)w1.y, (int)w1.z, (int)w1.w};
+      };
+      // k step ks also takes the low product of token block ks (KS = 4), or of
+      // token blocks 2 ks and 2 ks + 1 (KS = 2)
+      constexpr int kLoPerStep = 4 / KS;
+      kread(0, kh[0]);
+      if constexpr (kLo) lread(0, kq[0]);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        if (ks + 1 < KS) kread(ks + 1, kh[(ks + 1) & 1], kl[(ks + 1) & 1]);
+        if (ks + 1 < KS) kread(ks + 1, kh[(ks + 1) & 1]);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb)
@@ -412,10 +521,14 @@ void block_kernel(BlockArgs a0, PB pb) {
             S[tb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh[ks & 1][tb], qop[qb][ks], S[tb][qb], 0, 0, 0);
         if constexpr (kLo) {
 #pragma unroll
-          for (int tb = 0; tb < 4; ++tb)
+          for (int u = 0; u < kLoPerStep; ++u) {
+            const int tb = ks * kLoPerStep + u;
+            if (tb + 1 < 4) lread(tb + 1, kq[(tb + 1) & 1]);
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb)
-              S[tb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kl[ks & 1][tb], qop[qb][ks], S[tb][qb], 0, 0, 0);
+              S[tb][qb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kq[tb & 1], q8[qb], S[tb][qb], 0, 0, 0,
+                                                                           lo_scale, 0, q_scale);
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
       }
