@@ -52,9 +52,9 @@ LONG_CALL_TRAFFIC = 140_363_052      # one 131072-token layer (algorithmic 138.8
 # 128 appends (16 flushes + 128 window copies) and one block-attention call
 # (block_kernel + block_merge_kernel).
 APPEND_RUN_TRAFFIC = {4: 444_055_424, 8: 479_014_967}
-BLOCK_CALL_TRAFFIC = 2_014_996_480    # the cache is streamed once per query-row tile
+BLOCK_CALL_TRAFFIC = 2_067_551_539    # the cache is streamed once per query-row tile
 PAGED_CALL_TRAFFIC = 43_854_541      # paged decode, ragged lengths (algorithmic 41.42 MB)
-PAGED_BLOCK_CALL_TRAFFIC = 2_071_425_178  # the video block over a paged cache
+PAGED_BLOCK_CALL_TRAFFIC = 2_180_594_893  # the video block over a paged cache
 
 
 def decode_bytes(cfg, nq: int, nt: int, q_heads: int) -> int:
