@@ -477,10 +477,25 @@ __device__ __forceinline__ float4 f4_add(float4 a, float4 b) { return make_float
 // the merge, every NSG-th split from t / NT; partial rows are D + 4 floats so
 // that every access is 16 bytes.  k_new / v_new rows of unit u start at row
 // u * nst.
-template <int D, int GQA, typename QF>
+// A decode step's first appended token as the kernel prologue prepared it
+// (loaded with the query, its logits computed while the tiles stream):
+// logit of head wave + kWaves i, key channels lane + kWave j, and value
+// channels c0 .. c0 + 3 of the thread's output group.
+template <int D, int GQA>
+struct FirstNew {
+  static constexpr int kHeads = (GQA + kWaves - 1) / kWaves;
+  static constexpr int kKeys = (D + kWave - 1) / kWave;
+  float lg[kHeads];
+  uint16_t kr[kKeys];
+  uint2 vr;
+};
+struct NoFirstNew {};
+
+template <int D, int GQA, typename QF, typename FN = NoFirstNew>
 __device__ __forceinline__ void finish_unit(const DecodeArgs& a, int unit, int split, int S, int nn, int nst,
                                             int slot0, float (*red)[D][GQA], float (*wml)[2][GQA],
-                                            const float* m, const float* l, QF qf) {
+                                            const float* m, const float* l, QF qf, const FN& fn = FN{}) {
+  constexpr bool kFirst = !__is_same(FN, NoFirstNew);
   constexpr int NT = GQA * D / 4;                            // 16-byte output groups of a unit
   constexpr int NSG = kThreads / NT;                         // split groups of the merge
   static_assert(NT <= kThreads && kThreads % NT == 0, "output groups tile the workgroup");
@@ -575,29 +590,46 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs& a, int unit, int s
   uint16_t kr[kMaxStepNew][KPL];
   uint2 vr[kMaxStepNew];                                     // channels c0 .. c0 + 3 (bf16)
   if (nn > 0) {
+    // token 0 from the prologue when it prepared it; the others (and every
+    // token otherwise) loaded here, together
+    if constexpr (kFirst) {
 #pragma unroll
-    for (int t = 0; t < kMaxStepNew; ++t) {
-      const int tc = t < nn ? t : nn - 1;
+      for (int j = 0; j < KPL; ++j) kr[0][j] = fn.kr[j];
+      vr[0] = fn.vr;
+    }
+    if (!kFirst || nn > 1) {
 #pragma unroll
-      for (int j = 0; j < KPL; ++j) {
-        const int c = lane + j * kWave;
-        kr[t][j] = kn[tc * D + (c < D ? c : 0)];
+      for (int t = kFirst ? 1 : 0; t < kMaxStepNew; ++t) {
+        const int tc = t < nn ? t : nn - 1;
+#pragma unroll
+        for (int j = 0; j < KPL; ++j) {
+          const int c = lane + j * kWave;
+          kr[t][j] = kn[tc * D + (c < D ? c : 0)];
+        }
+        vr[t] = *reinterpret_cast<const uint2*>(vn + tc * D + c0);
       }
-      vr[t] = *reinterpret_cast<const uint2*>(vn + tc * D + c0);
     }
     // logits of the appended tokens, one wave per head
-    for (int hh = wave; hh < GQA; hh += kWaves) {
 #pragma unroll
-      for (int t = 0; t < kMaxStepNew; ++t) {
-        if (t < nn) {
-          float x = 0.0f;
+    for (int i = 0; i < (GQA + kWaves - 1) / kWaves; ++i) {
+      const int hh = wave + kWaves * i;
+      if (hh < GQA) {
 #pragma unroll
-          for (int j = 0; j < KPL; ++j) {
-            const int c = lane + j * kWave;
-            if (c < D) x = fmaf(qf(hh, c), bf16_bits_to_f32(kr[t][j]), x);
+        for (int t = 0; t < kMaxStepNew; ++t) {
+          if (t < nn) {
+            float x = 0.0f;
+            if (kFirst && t == 0) {
+              if constexpr (kFirst) x = fn.lg[i];
+            } else {
+#pragma unroll
+              for (int j = 0; j < KPL; ++j) {
+                const int c = lane + j * kWave;
+                if (c < D) x = fmaf(qf(hh, c), bf16_bits_to_f32(kr[t][j]), x);
+              }
+              x = wave_sum(x);
+            }
+            if (lane == 0) lg[t][hh] = x;
           }
-          x = wave_sum(x);
-          if (lane == 0) lg[t][hh] = x;
         }
       }
     }
@@ -1221,6 +1253,20 @@ void decode_i8_kernel(DecodeArgs a0, PD pd) {
     const int ti = w_begin + lane < pd.stride ? w_begin + lane : pd.stride - 1;
     tpages = pd.table[(int64_t)(unit / g.H) * pd.stride + ti];
   }
+  // Decode step: the first appended token's key (channels lane + kWave j)
+  // and value (this thread's output channels in the merge) go out with the
+  // query, so the last workgroup's merge does not wait for them.
+  FirstNew<D, GQA> fnew;
+  if (nn > 0) {
+    const uint16_t* kn = a.k_new + (int64_t)unit * a.n_new * D;
+    const uint16_t* vn = a.v_new + (int64_t)unit * a.n_new * D;
+#pragma unroll
+    for (int j = 0; j < FirstNew<D, GQA>::kKeys; ++j) {
+      const int c = lane + j * kWave;
+      fnew.kr[j] = kn[c < D ? c : 0];
+    }
+    fnew.vr = *reinterpret_cast<const uint2*>(vn + 4 * (tid % (GQA * D / 4)) % D);
+  }
   __builtin_amdgcn_sched_barrier(0);          // the query (and page numbers) go out first
   auto page_rsrc = [&](int tile_, bool ok) -> __amdgpu_buffer_rsrc_t {
     if constexpr (kPaged) {
@@ -1360,6 +1406,22 @@ void decode_i8_kernel(DecodeArgs a0, PD pd) {
   load_tile(w_begin, buf0);
   load_tile(w_begin + 1, buf1);
   __builtin_amdgcn_sched_barrier(0);
+  // ... and its logits (head wave + kWaves i) while the tiles are on the way
+  if (nn > 0) {
+#pragma unroll
+    for (int i = 0; i < FirstNew<D, GQA>::kHeads; ++i) {
+      const int hh = wave + kWaves * i;
+      float x = 0.0f;
+      if (hh < GQA) {
+#pragma unroll
+        for (int j = 0; j < FirstNew<D, GQA>::kKeys; ++j) {
+          const int c = lane + j * kWave;
+          if (c < D) x = fmaf(qsC[wave][hh][c], bf16_bits_to_f32(fnew.kr[j]), x);
+        }
+      }
+      fnew.lg[i] = wave_sum(x);
+    }
+  }
 
   // Online-softmax state: head 4 hg + q4 of this lane's row quad.
   float m[HG], lsum[HG], inv[HG], mq[HG];
@@ -1673,7 +1735,7 @@ void decode_i8_kernel(DecodeArgs a0, PD pd) {
       for (int h = 0; h < GQA; ++h) red[wave][lane * TCPL + k][h] += acc_tail[k][h];
   }
   finish_unit<D, GQA>(a, unit, split, S, nn, a.n_new, slot0, red, wml, mu, lu,
-                      [&](int h, int c) { return qsC[0][h][c]; });
+                      [&](int h, int c) { return qsC[0][h][c]; }, fnew);
 }
 
 template <int D, int BITS, int GQA>
