@@ -587,49 +587,50 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs& a, int unit, int s
   }
   const uint16_t* kn = a.k_new + (int64_t)unit * nst * D;
   const uint16_t* vn = a.v_new + (int64_t)unit * nst * D;
-  uint16_t kr[kMaxStepNew][KPL];
-  uint2 vr[kMaxStepNew];                                     // channels c0 .. c0 + 3 (bf16)
+  // Token 0 in registers (from the prologue when it prepared it); tokens
+  // 1 .. nn - 1 (a step of several tokens) are read again where they are
+  // used, in loops that do not run for a single token.
+  uint16_t kr0[KPL];
+  uint2 vr0 = make_uint2(0u, 0u);                            // channels c0 .. c0 + 3 (bf16)
   if (nn > 0) {
-    // token 0 from the prologue when it prepared it; the others (and every
-    // token otherwise) loaded here, together
     if constexpr (kFirst) {
 #pragma unroll
-      for (int j = 0; j < KPL; ++j) kr[0][j] = fn.kr[j];
-      vr[0] = fn.vr;
-    }
-    if (!kFirst || nn > 1) {
+      for (int j = 0; j < KPL; ++j) kr0[j] = fn.kr[j];
+      vr0 = fn.vr;
+    } else {
 #pragma unroll
-      for (int t = kFirst ? 1 : 0; t < kMaxStepNew; ++t) {
-        const int tc = t < nn ? t : nn - 1;
-#pragma unroll
-        for (int j = 0; j < KPL; ++j) {
-          const int c = lane + j * kWave;
-          kr[t][j] = kn[tc * D + (c < D ? c : 0)];
-        }
-        vr[t] = *reinterpret_cast<const uint2*>(vn + tc * D + c0);
+      for (int j = 0; j < KPL; ++j) {
+        const int c = lane + j * kWave;
+        kr0[j] = kn[c < D ? c : 0];
       }
+      vr0 = *reinterpret_cast<const uint2*>(vn + c0);
     }
     // logits of the appended tokens, one wave per head
 #pragma unroll
     for (int i = 0; i < (GQA + kWaves - 1) / kWaves; ++i) {
       const int hh = wave + kWaves * i;
       if (hh < GQA) {
+        float x0 = 0.0f;
+        if constexpr (kFirst) {
+          x0 = fn.lg[i];
+        } else {
 #pragma unroll
-        for (int t = 0; t < kMaxStepNew; ++t) {
-          if (t < nn) {
-            float x = 0.0f;
-            if (kFirst && t == 0) {
-              if constexpr (kFirst) x = fn.lg[i];
-            } else {
-#pragma unroll
-              for (int j = 0; j < KPL; ++j) {
-                const int c = lane + j * kWave;
-                if (c < D) x = fmaf(qf(hh, c), bf16_bits_to_f32(kr[t][j]), x);
-              }
-              x = wave_sum(x);
-            }
-            if (lane == 0) lg[t][hh] = x;
+          for (int j = 0; j < KPL; ++j) {
+            const int c = lane + j * kWave;
+            if (c < D) x0 = fmaf(qf(hh, c), bf16_bits_to_f32(kr0[j]), x0);
           }
+          x0 = wave_sum(x0);
+        }
+        if (lane == 0) lg[0][hh] = x0;
+        for (int t = 1; t < nn; ++t) {
+          float x = 0.0f;
+#pragma unroll
+          for (int j = 0; j < KPL; ++j) {
+            const int c = lane + j * kWave;
+            if (c < D) x = fmaf(qf(hh, c), bf16_bits_to_f32(kn[t * D + c]), x);
+          }
+          x = wave_sum(x);
+          if (lane == 0) lg[t][hh] = x;
         }
       }
     }
@@ -658,42 +659,50 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs& a, int unit, int s
       if (sk < S) num = f4_fma(v[j], sm[sk][h], num);
     }
   }
-  if (nn > 0 && wave == 0) {
-    // the appended keys into their window slots, from wave 0's registers
-    uint16_t* rk = a.ring_k + (int64_t)unit * g.ring * D;
+  // the appended keys into their window slots, from wave 0's registers --
+  // after the last barrier when all of wave 0 gets there (a barrier waits
+  // for the stores before it)
+  constexpr bool kKeysLate = NT >= kWave;
+  auto store_keys = [&]() {
+    if (nn > 0 && wave == 0) {
+      uint16_t* rk = a.ring_k + (int64_t)unit * g.ring * D;
 #pragma unroll
-    for (int t = 0; t < kMaxStepNew; ++t) {
-      if (t < nn) {
+      for (int j = 0; j < KPL; ++j) {
+        const int c = lane + j * kWave;
+        if (c < D) rk[slot0 * D + c] = kr0[j];
+      }
+      for (int t = 1; t < nn; ++t) {
         int slot = slot0 + t;
         slot = slot >= g.ring ? slot - g.ring : slot;
 #pragma unroll
         for (int j = 0; j < KPL; ++j) {
           const int c = lane + j * kWave;
-          if (c < D) rk[slot * D + c] = kr[t][j];
+          if (c < D) rk[slot * D + c] = kn[t * D + c];
         }
       }
     }
-  }
+  };
+  if constexpr (!kKeysLate) store_keys();
   if constexpr (NSG > 1) {
     if (sgi > 0) racc[sgi - 1][grp] = num;
     __syncthreads();
   }
   if (sgi != 0) return;
+  if constexpr (kKeysLate) store_keys();
 #pragma unroll
   for (int k = 0; k + 1 < NSG; ++k) num = f4_add(num, racc[k][grp]);
   float den = 0.0f;
   for (int sk = 0; sk < S; ++sk) den += sl[sk][h];
-#pragma unroll
-  for (int t = 0; t < kMaxStepNew; ++t) {
-    if (t < nn) {
-      const float e = fast_exp2(lg[t][h] - mx[h]);
-      num = f4_fma(make_float4(bf16_lo(vr[t].x), bf16_hi(vr[t].x), bf16_lo(vr[t].y), bf16_hi(vr[t].y)), e, num);
-      den += e;
-      if (h == 0) {                 // the appended values into their window slots
-        int slot = slot0 + t;
-        slot = slot >= g.ring ? slot - g.ring : slot;
-        *reinterpret_cast<uint2*>(a.ring_v + ((int64_t)unit * g.ring + slot) * D + c0) = vr[t];
-      }
+  // the appended tokens' terms, and their values into their window slots
+  for (int t = 0; t < nn; ++t) {
+    const uint2 vt = t == 0 ? vr0 : *reinterpret_cast<const uint2*>(vn + t * D + c0);
+    const float e = fast_exp2(lg[t][h] - mx[h]);
+    num = f4_fma(make_float4(bf16_lo(vt.x), bf16_hi(vt.x), bf16_lo(vt.y), bf16_hi(vt.y)), e, num);
+    den += e;
+    if (h == 0) {
+      int slot = slot0 + t;
+      slot = slot >= g.ring ? slot - g.ring : slot;
+      *reinterpret_cast<uint2*>(a.ring_v + ((int64_t)unit * g.ring + slot) * D + c0) = vt;
     }
   }
   *out = f4_scale(num, 1.0f / den);
