@@ -481,6 +481,14 @@ __device__ __forceinline__ float4 f4_add(float4 a, float4 b) { return make_float
 // (loaded with the query, its logits computed while the tiles stream):
 // logit of head wave + kWaves i, key channels lane + kWave j, and value
 // channels c0 .. c0 + 3 of the thread's output group.
+// First output channel of thread tid in the merge (groups of four channels,
+// head-major): the value channels a decode step's first appended token
+// contributes through that thread.
+template <int D, int GQA>
+__device__ __forceinline__ int merge_c0(int tid) {
+  return 4 * (tid % (GQA * D / 4)) % D;
+}
+
 template <int D, int GQA>
 struct FirstNew {
   static constexpr int kHeads = (GQA + kWaves - 1) / kWaves;
@@ -504,7 +512,7 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs& a, int unit, int s
   const Geom& g = a.g;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int grp = tid % NT, sgi = tid / NT;
-  const int h = 4 * grp / D, c0 = 4 * grp % D;
+  const int h = 4 * grp / D, c0 = merge_c0<D, GQA>(tid);
   __shared__ float sm[kLastMergeSplits][GQA], sl[kLastMergeSplits][GQA];
   __shared__ float lg[kMaxStepNew][GQA], mx[GQA];
   __shared__ float4 racc[NSG > 1 ? NSG - 1 : 1][NT];
@@ -1274,7 +1282,7 @@ void decode_i8_kernel(DecodeArgs a0, PD pd) {
       const int c = lane + j * kWave;
       fnew.kr[j] = kn[c < D ? c : 0];
     }
-    fnew.vr = *reinterpret_cast<const uint2*>(vn + 4 * (tid % (GQA * D / 4)) % D);
+    fnew.vr = *reinterpret_cast<const uint2*>(vn + merge_c0<D, GQA>(tid));
   }
   __builtin_amdgcn_sched_barrier(0);          // the query (and page numbers) go out first
   auto page_rsrc = [&](int tile_, bool ok) -> __amdgpu_buffer_rsrc_t {
