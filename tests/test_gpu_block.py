@@ -177,3 +177,26 @@ def test_block_video_full_size():
         err = max_abs(got[:, rows], ref[:, rows])
         note(f"block video full size frames={frame}: max-abs {err:.3e} over {rows.size} rows x {w.q_heads} heads")
         assert err <= TOL
+
+
+@needs_gpu
+def test_block_fp8_low_part_scales():
+    """The powers of two of the fp8 low product: one Key segment eight times
+    larger than the rest (so the smallest Key scale, and with it the
+    workgroup's power of two, comes from one segment of its run) and query
+    rows of very different size inside one wave (every other position a
+    64th of the others, which sets the wave's query power of two).  Same
+    oracle bound as every block test."""
+    w = ks.small(ks.VIDEO_BLOCK, batch=1, kv_heads=2, q_heads=8)
+    p = Pair(w, 1200)
+    s = ks.Stream(w, 77)
+    k, v = ks.kv_pair(s, 1100)
+    k[:, :, 256:384] *= 8                        # one 128-token segment (the third)
+    p.append(k, v)
+    q, kb, vb = ks.block_inputs(s, 96)
+    q[:, 1::2] /= 64                             # rows of one wave differ by 2^6
+    note("block fp8 low-part scales")
+    got = p.block(q, kb, vb, num_splits=3)
+    err = max_abs(got, p.block_ref(q, kb, vb))
+    note(f"block fp8 low-part scales: max-abs {err:.3e}")
+    assert err <= TOL
