@@ -1387,11 +1387,26 @@ void decode_i8_kernel(DecodeArgs a0, PD pd) {
     }
   };
 
-  // The query lands first: sigma log2(e) q into this wave's LDS rows (fp32,
-  // and the bf16 high / low pair of the chunk scores).  Nothing else is in
-  // flight while it comes: issued ahead of the tile loads, the query lands
-  // only as the whole burst drains (measured: 8 us into the call instead of
-  // one round trip), and nothing can be computed before it.
+  __builtin_amdgcn_sched_barrier(0);        // the tile loads stay behind the query's wait
+
+  // The run's first window chunk and first tile, before the query's wait;
+  // the second tile after it.  Every load of a run of up to two tiles and a
+  // chunk (the Llama-3-8B shape at 4096 tokens) goes out before the wave
+  // waits for tile data.  The chunk goes first so that the wait for a tile is
+  // the same on every pass of the loop below (the loads of the one tile after
+  // it in flight).
+  ChunkRegs<D> cr;
+  chunk_load(ww.c0, cr);
+  TileRegs buf0, buf1;
+  load_tile(w_begin, buf0);
+  __builtin_amdgcn_sched_barrier(0);
+  // The query lands: sigma log2(e) q into this wave's LDS rows (fp32, and
+  // the bf16 high / low pair of the chunk scores).  The run's first window
+  // chunk and first tile are already on the way (issued above, after the
+  // query, so the wait below is for the query alone): the query still lands
+  // early, and the memory system is busy from the start.  Issuing the second
+  // tile before this wait as well measured no better; with every load of the
+  // run ahead of it, the query landed only as the whole burst drained.
 #pragma unroll
   for (int k = 0; k < QPL; ++k) {
     const int i = lane + k * kWave;
@@ -1410,17 +1425,7 @@ void decode_i8_kernel(DecodeArgs a0, PD pd) {
   }
   wave_lds_sync();
 
-  __builtin_amdgcn_sched_barrier(0);        // the tile loads stay behind the query's wait
-
-  // The run's first window chunk, then its first two tiles: every load of a
-  // run of up to two tiles and a chunk (the Llama-3-8B shape at 4096
-  // tokens) goes out before the wave waits for anything else.  The chunk goes
-  // first so that the wait for a tile is the same on every pass of the loop
-  // below (the loads of the one tile after it in flight).
-  ChunkRegs<D> cr;
-  chunk_load(ww.c0, cr);
-  TileRegs buf0, buf1;
-  load_tile(w_begin, buf0);
+  __builtin_amdgcn_sched_barrier(0);
   load_tile(w_begin + 1, buf1);
   __builtin_amdgcn_sched_barrier(0);
   // ... and its logits (head wave + kWaves i) while the tiles are on the way
