@@ -460,7 +460,7 @@ __device__ __forceinline__ float4 f4_fma(float4 v, float s, float4 acc) {
 __device__ __forceinline__ float4 f4_add(float4 a, float4 b) { return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w); }
 
 // End of one workgroup's share of a unit (batch, KV head).  The four waves'
-// online-softmax states (m, l per head; red[w][c][h] = acc relative to the
+// online-softmax states (m, l per head; red[w][h][c] = acc relative to the
 // wave's own maximum) are folded into the split's state.  Then:
 //   * one split and nothing appended: the workgroup writes the output;
 //   * more than kLastMergeSplits splits: it writes its partial for merge_kernel;
@@ -484,6 +484,11 @@ __device__ __forceinline__ float4 f4_add(float4 a, float4 b) { return make_float
 // First output channel of thread tid in the merge (groups of four channels,
 // head-major): the value channels a decode step's first appended token
 // contributes through that thread.
+// Row pitch (floats) of a wave's per-head results in LDS: rows of successive
+// heads start 16 banks apart, so the sixteen-channel stores of four heads and
+// the merge's 16-byte reads of consecutive channels are free of bank conflicts.
+constexpr int red_pitch(int d) { return d + 16; }
+
 template <int D, int GQA>
 __device__ __forceinline__ int merge_c0(int tid) {
   return 4 * (tid % (GQA * D / 4)) % D;
@@ -501,7 +506,7 @@ struct NoFirstNew {};
 
 template <int D, int GQA, typename QF, typename FN = NoFirstNew>
 __device__ __forceinline__ void finish_unit(const DecodeArgs& a, int unit, int split, int S, int nn, int nst,
-                                            int slot0, float (*red)[D][GQA], float (*wml)[2][GQA],
+                                            int slot0, float (*red)[GQA][red_pitch(D)], float (*wml)[2][GQA],
                                             const float* m, const float* l, QF qf, const FN& fn = FN{}) {
   constexpr bool kFirst = !__is_same(FN, NoFirstNew);
   constexpr int NT = GQA * D / 4;                            // 16-byte output groups of a unit
@@ -533,7 +538,7 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs& a, int unit, int s
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
       const float e = (wml[w][0][h] == -INFINITY) ? 0.0f : fast_exp2(wml[w][0][h] - fm);
-      fs = f4_fma(make_float4(red[w][c0][h], red[w][c0 + 1][h], red[w][c0 + 2][h], red[w][c0 + 3][h]), e, fs);
+      fs = f4_fma(*reinterpret_cast<const float4*>(&red[w][h][c0]), e, fs);
       fl += wml[w][1][h] * e;
     }
   }
@@ -810,7 +815,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a0, PagedDe
   __shared__ float qsT[D][GQA];
   __shared__ float aq[kWaves][D][GQA];
   __shared__ float pw[kWaves][kTile * NR][GQA];   // same-axis: row NR t + r
-  __shared__ float red[kWaves][D][GQA];
+  __shared__ __attribute__((aligned(16))) float red[kWaves][GQA][red_pitch(D)];
   __shared__ float wml[kWaves][2][GQA];
 
   load_q<D, GQA>(a, unit, qsT);
@@ -1016,7 +1021,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a0, PagedDe
     if (u % (BITS / 2) == 0) {
       const int c = u * 2 / BITS;
 #pragma unroll
-      for (int h = 0; h < GQA; ++h) red[wave][c][h] = acc[k][h];
+      for (int h = 0; h < GQA; ++h) red[wave][h][c] = acc[k][h];
     }
   }
   wave_lds_sync();
@@ -1024,7 +1029,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a0, PagedDe
 #pragma unroll
     for (int k = 0; k < TCPL; ++k)
 #pragma unroll
-      for (int h = 0; h < GQA; ++h) red[wave][lane * TCPL + k][h] += acc_tail[k][h];
+      for (int h = 0; h < GQA; ++h) red[wave][h][lane * TCPL + k] += acc_tail[k][h];
   }
   finish_unit<D, GQA>(a, unit, split, S, nn, a.n_new, slot0, red, wml, m, l,
                       [&](int h, int c) { return qsT[c][h]; });
@@ -1199,7 +1204,7 @@ void decode_i8_kernel(DecodeArgs a0, PD pd) {
   __shared__ __attribute__((aligned(16))) uint32_t qD[kWaves][HG][MK][16][kRowPad];  // Key operand digits
   __shared__ __attribute__((aligned(16))) uint32_t pD[kWaves][HG][16][kRowPad];      // Value operand digits
   __shared__ float pw[kWaves][kTailChunk][GQA];
-  __shared__ float red[kWaves][D][GQA];
+  __shared__ __attribute__((aligned(16))) float red[kWaves][GQA][red_pitch(D)];
   __shared__ float wml[kWaves][2][GQA];
 
   // Channel (or token) held in slot position p of a 64-wide group.
@@ -1739,14 +1744,14 @@ void decode_i8_kernel(DecodeArgs a0, PD pd) {
     }
   }
 
-  // ---- wave result into red[wave][channel][head] ----
+  // ---- wave result into red[wave][head][channel] ----
   constexpr float kOut = 1.0f / F16::kMul;
 #pragma unroll
   for (int hg = 0; hg < HG; ++hg) {
     const int h = 4 * hg + q4;
     if (h < GQA) {
 #pragma unroll
-      for (int n = 0; n < NV; ++n) red[wave][16 * n + col][h] = acc_f[hg][n] * kOut;
+      for (int n = 0; n < NV; ++n) red[wave][h][16 * n + col] = acc_f[hg][n] * kOut;
     }
   }
   wave_lds_sync();
@@ -1754,7 +1759,7 @@ void decode_i8_kernel(DecodeArgs a0, PD pd) {
 #pragma unroll
     for (int k = 0; k < TCPL; ++k)
 #pragma unroll
-      for (int h = 0; h < GQA; ++h) red[wave][lane * TCPL + k][h] += acc_tail[k][h];
+      for (int h = 0; h < GQA; ++h) red[wave][h][lane * TCPL + k] += acc_tail[k][h];
   }
   finish_unit<D, GQA>(a, unit, split, S, nn, a.n_new, slot0, red, wml, mu, lu,
                       [&](int h, int c) { return qsC[0][h][c]; }, fnew);
