@@ -575,13 +575,14 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs& a, int unit, int s
   // ---- the last workgroup of the unit: merge ----
   // Every load of the merge goes out together: the first batch of partials,
   // the split maxima and sums, and the appended tokens' keys and values.
+  // Only the splits that exist are read (with few splits most of a batch's
+  // slots are empty).
   float4 v[kMergeBatch];
   auto load_batch = [&](int j0) {
 #pragma unroll
     for (int j = 0; j < kMergeBatch; ++j) {
-      int sk = sgi + NSG * (j0 + j);
-      sk = sk < S ? sk : S - 1;                              // clamped: unconditional loads
-      v[j] = load_agent4(rp, (sk * sstride + h * RS + c0) * 4);
+      const int sk = sgi + NSG * (j0 + j);
+      if (sk < S) v[j] = load_agent4(rp, (sk * sstride + h * RS + c0) * 4);
     }
   };
   if (S > 1) {
