@@ -575,9 +575,11 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs& a, int unit, int s
   // ---- the last workgroup of the unit: merge ----
   // Every load of the merge goes out together: the first batch of partials,
   // the split maxima and sums, and the appended tokens' keys and values.
-  // Only the splits that exist are read (with few splits most of a batch's
-  // slots are empty).
+  // Only the splits that exist are read; with at most two partials per
+  // thread a short path does it (the unrolled batch's skipped slots and its
+  // longer code cost about half a microsecond on this serial tail).
   float4 v[kMergeBatch];
+  const bool few = S <= 2 * NSG;
   auto load_batch = [&](int j0) {
 #pragma unroll
     for (int j = 0; j < kMergeBatch; ++j) {
@@ -586,7 +588,15 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs& a, int unit, int s
     }
   };
   if (S > 1) {
-    load_batch(0);
+    if (few) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int sk = sgi + NSG * j;
+        if (sk < S) v[j] = load_agent4(rp, (sk * sstride + h * RS + c0) * 4);
+      }
+    } else {
+      load_batch(0);
+    }
     for (int j = tid; j < S * GQA; j += kThreads) {
       const float2 ml = load_agent2(rp, ((j / GQA) * sstride + (j % GQA) * RS + D) * 4);
       sm[j / GQA][j % GQA] = ml.x;
@@ -665,12 +675,20 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs& a, int unit, int s
   }
   __syncthreads();
   float4 num = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-  for (int j0 = 0; sgi + NSG * j0 < S; j0 += kMergeBatch) {
-    if (j0 > 0) load_batch(j0);
+  if (few) {
 #pragma unroll
-    for (int j = 0; j < kMergeBatch; ++j) {
-      const int sk = sgi + NSG * (j0 + j);
+    for (int j = 0; j < 2; ++j) {
+      const int sk = sgi + NSG * j;
       if (sk < S) num = f4_fma(v[j], sm[sk][h], num);
+    }
+  } else {
+    for (int j0 = 0; sgi + NSG * j0 < S; j0 += kMergeBatch) {
+      if (j0 > 0) load_batch(j0);
+#pragma unroll
+      for (int j = 0; j < kMergeBatch; ++j) {
+        const int sk = sgi + NSG * (j0 + j);
+        if (sk < S) num = f4_fma(v[j], sm[sk][h], num);
+      }
     }
   }
   // the appended keys into their window slots, from wave 0's registers --
