@@ -88,7 +88,8 @@ struct DecodeArgs {
   int n_new, new_slot0;
 };
 
-constexpr int kMaxStepNew = 16;   // appended tokens kvq_decode_step folds into the merge
+constexpr int kMaxStepNew = 16;
+constexpr int kWaveMergeSplits = 4;    // split counts whose merge wave 0 does alone   // appended tokens kvq_decode_step folds into the merge
 constexpr int kLastMergeSplits = 64;  // split counts merged inside the attention kernel
 constexpr int kMergeBatch = 16;   // partial loads in flight per output element in that merge
 constexpr int kMaxPagedSeqs = 64;
@@ -504,6 +505,159 @@ struct FirstNew {
 };
 struct NoFirstNew {};
 
+// The end of a unit's share done by wave 0 alone (finish_unit decides when):
+// lane i folds the four waves' results of output groups i, i + 64, ... (a
+// group is four channels of one head), publishes them and takes the ticket
+// itself (its own stores waited for), and as the last arriver merges the
+// splits' partials, weighted by a butterfly over the lanes that hold the
+// splits' (m, l), and the appended token when there is one (folded in by an
+// online-softmax rescale).  Partial rows and the ticket are those of
+// finish_unit's workgroup-wide path.
+template <int D, int GQA, int GPL, bool kFirst, typename QF, typename FN>
+__device__ __forceinline__ void merge_in_wave(const DecodeArgs& a, int unit, int split, int S, int nn, int slot0,
+                                              float (*red)[GQA][red_pitch(D)], float (*wml)[2][GQA],
+                                              float (*sm)[GQA], float (*sl)[GQA], float (*lg)[GQA], QF qf,
+                                              const FN& fn) {
+  constexpr int NT = GQA * D / 4;
+  constexpr int RS = D + 4;
+  constexpr int KPL = (D + kWave - 1) / kWave;
+  constexpr int sstride = GQA * RS;
+  const int lane = threadIdx.x % kWave;
+  int hk[GPL], ck[GPL];
+  float4 num[GPL];
+  float den[GPL], mk[GPL];
+#pragma unroll
+  for (int k = 0; k < GPL; ++k) {
+    const int gk = (lane + kWave * k) % NT;                  // lanes past NT repeat a group, write nothing
+    hk[k] = 4 * gk / D;
+    ck[k] = 4 * gk % D;
+    float mm = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) mm = fmaxf(mm, wml[w][0][hk[k]]);
+    float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    float ll = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float e = (wml[w][0][hk[k]] == -INFINITY) ? 0.0f : fast_exp2(wml[w][0][hk[k]] - mm);
+      acc = f4_fma(*reinterpret_cast<const float4*>(&red[w][hk[k]][ck[k]]), e, acc);
+      ll += wml[w][1][hk[k]] * e;
+    }
+    num[k] = acc;
+    den[k] = ll;
+    mk[k] = mm;
+  }
+  auto owns = [&](int k) { return lane + kWave * k < NT; };
+  if (S > 1) {
+    float* pu = a.part + (int64_t)unit * a.splits * sstride;
+    const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(pu, (short)0, S * sstride * 4, kRsrcWord3);
+#pragma unroll
+    for (int k = 0; k < GPL; ++k) {
+      if (owns(k)) {
+        store_agent4(rp, (split * sstride + hk[k] * RS + ck[k]) * 4, num[k]);
+        if (ck[k] == 0) store_agent2(rp, (split * sstride + hk[k] * RS + D) * 4, make_float2(mk[k], den[k]));
+      }
+    }
+    wait_memory_done();
+    uint32_t t = 0;
+    if (lane == 0) t = __builtin_amdgcn_atomic_inc32(a.ctr + unit, (uint32_t)(S - 1), __ATOMIC_RELAXED, "agent");
+    t = __builtin_amdgcn_readfirstlane(t);
+    if (t != (uint32_t)(S - 1)) return;
+    // the last arriver: every other split's partials and every (m, l)
+    float4 v[GPL][kWaveMergeSplits];
+#pragma unroll
+    for (int sk = 0; sk < kWaveMergeSplits; ++sk) {
+      if (sk < S && sk != split) {
+#pragma unroll
+        for (int k = 0; k < GPL; ++k) v[k][sk] = load_agent4(rp, (sk * sstride + hk[k] * RS + ck[k]) * 4);
+      }
+    }
+    const float2 ml = lane < S * GQA ? load_agent2(rp, ((lane / GQA) * sstride + (lane % GQA) * RS + D) * 4)
+                                     : make_float2(-INFINITY, 0.0f);
+    // lane j holds split j / GQA, head j % GQA (GQA a power of two)
+    float M = ml.x;
+#pragma unroll
+    for (int msk = GQA; msk < kWave; msk *= 2) M = fmaxf(M, __shfl_xor(M, msk));
+    if (lane < S * GQA) {
+      const float e = ml.x == -INFINITY ? 0.0f : fast_exp2(ml.x - M);   // empty split: 0
+      sm[lane / GQA][lane % GQA] = e;
+      sl[lane / GQA][lane % GQA] = ml.y * e;
+    }
+    if (lane < GQA) lg[kMaxStepNew - 1][lane] = M;             // the heads' maxima (a spare row)
+    wave_lds_sync();
+#pragma unroll
+    for (int k = 0; k < GPL; ++k) {
+      float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      float ll = 0.0f;
+#pragma unroll
+      for (int sk = 0; sk < kWaveMergeSplits; ++sk) {
+        if (sk < S) {
+          acc = f4_fma(sk == split ? num[k] : v[k][sk], sm[sk][hk[k]], acc);
+          ll += sl[sk][hk[k]];
+        }
+      }
+      num[k] = acc;
+      den[k] = ll;
+      mk[k] = lg[kMaxStepNew - 1][hk[k]];
+    }
+  }
+  if (nn == 1) {
+    // the appended token: its key and value (channels c0 .. c0 + 3, the same
+    // for every group of a lane), its logits per head
+    const uint16_t* kn = a.k_new + (int64_t)unit * a.n_new * D;
+    const uint16_t* vn = a.v_new + (int64_t)unit * a.n_new * D;
+    uint16_t kr[KPL];
+    uint2 vr;
+    float lgh[GQA];
+    if constexpr (kFirst) {
+#pragma unroll
+      for (int j = 0; j < KPL; ++j) kr[j] = fn.kr[j];
+      vr = fn.vr;
+#pragma unroll
+      for (int hh = 0; hh < GQA; ++hh) lgh[hh] = lg[0][hh];
+    } else {
+#pragma unroll
+      for (int j = 0; j < KPL; ++j) {
+        const int c = lane + j * kWave;
+        kr[j] = kn[c < D ? c : 0];
+      }
+      vr = *reinterpret_cast<const uint2*>(vn + ck[0]);
+#pragma unroll
+      for (int hh = 0; hh < GQA; ++hh) {
+        float x = 0.0f;
+#pragma unroll
+        for (int j = 0; j < KPL; ++j) {
+          const int c = lane + j * kWave;
+          if (c < D) x = fmaf(qf(hh, c), bf16_bits_to_f32(kr[j]), x);
+        }
+        lgh[hh] = wave_sum(x);
+      }
+    }
+    const float4 vt = make_float4(bf16_lo(vr.x), bf16_hi(vr.x), bf16_lo(vr.y), bf16_hi(vr.y));
+#pragma unroll
+    for (int k = 0; k < GPL; ++k) {
+      float x = lgh[0];
+#pragma unroll
+      for (int hh = 1; hh < GQA; ++hh) x = hk[k] == hh ? lgh[hh] : x;
+      const float mt = fmaxf(mk[k], x);
+      const float sc = mk[k] == -INFINITY ? 0.0f : fast_exp2(mk[k] - mt);   // no cached term: 0
+      const float e = fast_exp2(x - mt);
+      num[k] = f4_fma(vt, e, f4_scale(num[k], sc));
+      den[k] = den[k] * sc + e;
+    }
+    // the token into its window slot
+    uint16_t* rk = a.ring_k + (int64_t)unit * a.g.ring * D;
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) {
+      const int c = lane + j * kWave;
+      if (c < D) rk[slot0 * D + c] = kr[j];
+    }
+    if (4 * lane < D) *reinterpret_cast<uint2*>(a.ring_v + ((int64_t)unit * a.g.ring + slot0) * D + 4 * lane) = vr;
+  }
+#pragma unroll
+  for (int k = 0; k < GPL; ++k)
+    if (owns(k)) *reinterpret_cast<float4*>(a.out + (int64_t)unit * GQA * D + hk[k] * D + ck[k]) = f4_scale(num[k], 1.0f / den[k]);
+}
+
 template <int D, int GQA, typename QF, typename FN = NoFirstNew>
 __device__ __forceinline__ void finish_unit(const DecodeArgs& a, int unit, int split, int S, int nn, int nst,
                                             int slot0, float (*red)[GQA][red_pitch(D)], float (*wml)[2][GQA],
@@ -529,7 +683,28 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs& a, int unit, int s
       wml[wave][1][hh] = l[hh];
     }
   }
+  // Few splits and at most one appended token: after the fold's barrier wave
+  // 0 does the rest alone (fold, publication, ticket, merge), with no further
+  // workgroup barrier.  The appended token's logits go through LDS first.
+  constexpr int GPL = (NT + kWave - 1) / kWave;              // output groups per lane of wave 0
+  const bool wave_merge = GPL <= 4 && nn <= 1 && ((S > 1 && S <= kWaveMergeSplits && a.last_merge) ||
+                                                 (S == 1 && nn == 1));
+  if constexpr (kFirst) {
+    if (wave_merge && nn == 1 && lane == 0) {
+#pragma unroll
+      for (int i = 0; i < FN::kHeads; ++i) {
+        const int hh = wave + kWaves * i;
+        if (hh < GQA) lg[0][hh] = fn.lg[i];
+      }
+    }
+  }
   __syncthreads();
+  if constexpr (GPL <= 4) {
+    if (wave_merge) {
+      if (wave == 0) merge_in_wave<D, GQA, GPL, kFirst>(a, unit, split, S, nn, slot0, red, wml, sm, sl, lg, qf, fn);
+      return;
+    }
+  }
   float4 fs = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   float fm = -INFINITY, fl = 0.0f;
   if (sgi == 0) {
@@ -580,6 +755,7 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs& a, int unit, int s
   // longer code cost about half a microsecond on this serial tail).
   float4 v[kMergeBatch];
   const bool few = S <= 2 * NSG;
+  const bool in_wave = S * GQA <= kWave;                    // every split's (m, l) in one wave
   auto load_batch = [&](int j0) {
 #pragma unroll
     for (int j = 0; j < kMergeBatch; ++j) {
@@ -597,18 +773,37 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs& a, int unit, int s
     } else {
       load_batch(0);
     }
-    for (int j = tid; j < S * GQA; j += kThreads) {
-      const float2 ml = load_agent2(rp, ((j / GQA) * sstride + (j % GQA) * RS + D) * 4);
-      sm[j / GQA][j % GQA] = ml.x;
-      sl[j / GQA][j % GQA] = ml.y;
+    if (in_wave) {
+      // Lane j of wave 0 holds split j / GQA's (m, l) for head j % GQA: the
+      // heads' maxima over the splits by a butterfly over the lanes of one
+      // head (GQA is a power of two), then each split's weight.
+      if (tid < kWave) {
+        const float2 ml = tid < S * GQA ? load_agent2(rp, ((tid / GQA) * sstride + (tid % GQA) * RS + D) * 4)
+                                        : make_float2(-INFINITY, 0.0f);
+        float M = ml.x;
+#pragma unroll
+        for (int msk = GQA; msk < kWave; msk *= 2) M = fmaxf(M, __shfl_xor(M, msk));
+        if (tid < S * GQA) {
+          const float e = ml.x == -INFINITY ? 0.0f : fast_exp2(ml.x - M);   // empty split: 0
+          sm[tid / GQA][tid % GQA] = e;
+          sl[tid / GQA][tid % GQA] = ml.y * e;
+        }
+        if (tid < GQA) mx[tid] = M;
+      }
+    } else {
+      for (int j = tid; j < S * GQA; j += kThreads) {
+        const float2 ml = load_agent2(rp, ((j / GQA) * sstride + (j % GQA) * RS + D) * 4);
+        sm[j / GQA][j % GQA] = ml.x;
+        sl[j / GQA][j % GQA] = ml.y;
+      }
     }
-  } else {
-    v[0] = fs;
-    if (sgi == 0 && c0 == 0) {
-      sm[0][h] = fm;
-      sl[0][h] = fl;
-    }
+  } else if (sgi == 0 && c0 == 0) {                          // one split: weight 1
+    const float e = fm == -INFINITY ? 0.0f : 1.0f;
+    sm[0][h] = e;
+    sl[0][h] = fl * e;
+    mx[h] = fm;
   }
+  if (S == 1) v[0] = fs;
   const uint16_t* kn = a.k_new + (int64_t)unit * nst * D;
   const uint16_t* vn = a.v_new + (int64_t)unit * nst * D;
   // Token 0 in registers (from the prologue when it prepared it); tokens
@@ -660,20 +855,22 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs& a, int unit, int s
     }
   }
   __syncthreads();
-  if (tid < GQA) {
-    float M = -INFINITY;
-    for (int sk = 0; sk < S; ++sk) M = fmaxf(M, sm[sk][tid]);   // -inf only for empty splits
-    for (int t = 0; t < nn; ++t) M = fmaxf(M, lg[t][tid]);
-    mx[tid] = M;
+  if (!in_wave && S > 1) {
+    // Many splits: the heads' maxima over the splits, then the weights.
+    if (tid < GQA) {
+      float M = -INFINITY;
+      for (int sk = 0; sk < S; ++sk) M = fmaxf(M, sm[sk][tid]);   // -inf only for empty splits
+      mx[tid] = M;
+    }
+    __syncthreads();
+    for (int j = tid; j < S * GQA; j += kThreads) {
+      const int sk = j / GQA, hh = j % GQA;
+      const float e = sm[sk][hh] == -INFINITY ? 0.0f : fast_exp2(sm[sk][hh] - mx[hh]);   // empty split: 0
+      sm[sk][hh] = e;
+      sl[sk][hh] *= e;
+    }
+    __syncthreads();
   }
-  __syncthreads();
-  for (int j = tid; j < S * GQA; j += kThreads) {
-    const int sk = j / GQA, hh = j % GQA;
-    const float e = sm[sk][hh] == -INFINITY ? 0.0f : fast_exp2(sm[sk][hh] - mx[hh]);   // empty split: 0
-    sm[sk][hh] = e;
-    sl[sk][hh] *= e;
-  }
-  __syncthreads();
   float4 num = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   if (few) {
 #pragma unroll
@@ -725,10 +922,19 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs& a, int unit, int s
   for (int k = 0; k + 1 < NSG; ++k) num = f4_add(num, racc[k][grp]);
   float den = 0.0f;
   for (int sk = 0; sk < S; ++sk) den += sl[sk][h];
-  // the appended tokens' terms, and their values into their window slots
+  // The appended tokens' terms (and their values into their window slots):
+  // the splits' sum, relative to their maximum, is rescaled to the maximum
+  // that includes the new logits (online softmax).
+  float mt = mx[h];
+  if (nn > 0) {
+    for (int t = 0; t < nn; ++t) mt = fmaxf(mt, lg[t][h]);
+    const float sc = mx[h] == -INFINITY ? 0.0f : fast_exp2(mx[h] - mt);   // no cached term: 0
+    num = f4_scale(num, sc);
+    den *= sc;
+  }
   for (int t = 0; t < nn; ++t) {
     const uint2 vt = t == 0 ? vr0 : *reinterpret_cast<const uint2*>(vn + t * D + c0);
-    const float e = fast_exp2(lg[t][h] - mx[h]);
+    const float e = fast_exp2(lg[t][h] - mt);
     num = f4_fma(make_float4(bf16_lo(vt.x), bf16_hi(vt.x), bf16_lo(vt.y), bf16_hi(vt.y)), e, num);
     den += e;
     if (h == 0) {
