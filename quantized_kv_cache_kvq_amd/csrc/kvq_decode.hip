@@ -89,7 +89,7 @@ struct DecodeArgs {
 };
 
 constexpr int kMaxStepNew = 16;
-constexpr int kWaveMergeSplits = 4;    // split counts whose merge wave 0 does alone   // appended tokens kvq_decode_step folds into the merge
+constexpr int kWaveMergeSplits = 8;    // split counts whose merge wave 0 does alone   // appended tokens kvq_decode_step folds into the merge
 constexpr int kLastMergeSplits = 64;  // split counts merged inside the attention kernel
 constexpr int kMergeBatch = 16;   // partial loads in flight per output element in that merge
 constexpr int kMaxPagedSeqs = 64;
@@ -512,8 +512,9 @@ struct NoFirstNew {};
 // splits' partials, weighted by a butterfly over the lanes that hold the
 // splits' (m, l), and the appended token when there is one (folded in by an
 // online-softmax rescale).  Partial rows and the ticket are those of
-// finish_unit's workgroup-wide path.
-template <int D, int GQA, int GPL, bool kFirst, typename QF, typename FN>
+// finish_unit's workgroup-wide path.  The loops over splits are unrolled over
+// NS >= S slots.
+template <int D, int GQA, int GPL, int NS, bool kFirst, typename QF, typename FN>
 __device__ __forceinline__ void merge_in_wave(const DecodeArgs& a, int unit, int split, int S, int nn, int slot0,
                                               float (*red)[GQA][red_pitch(D)], float (*wml)[2][GQA],
                                               float (*sm)[GQA], float (*sl)[GQA], float (*lg)[GQA], QF qf,
@@ -563,9 +564,9 @@ __device__ __forceinline__ void merge_in_wave(const DecodeArgs& a, int unit, int
     t = __builtin_amdgcn_readfirstlane(t);
     if (t != (uint32_t)(S - 1)) return;
     // the last arriver: every other split's partials and every (m, l)
-    float4 v[GPL][kWaveMergeSplits];
+    float4 v[GPL][NS];
 #pragma unroll
-    for (int sk = 0; sk < kWaveMergeSplits; ++sk) {
+    for (int sk = 0; sk < NS; ++sk) {
       if (sk < S && sk != split) {
 #pragma unroll
         for (int k = 0; k < GPL; ++k) v[k][sk] = load_agent4(rp, (sk * sstride + hk[k] * RS + ck[k]) * 4);
@@ -589,7 +590,7 @@ __device__ __forceinline__ void merge_in_wave(const DecodeArgs& a, int unit, int
       float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
       float ll = 0.0f;
 #pragma unroll
-      for (int sk = 0; sk < kWaveMergeSplits; ++sk) {
+      for (int sk = 0; sk < NS; ++sk) {
         if (sk < S) {
           acc = f4_fma(sk == split ? num[k] : v[k][sk], sm[sk][hk[k]], acc);
           ll += sl[sk][hk[k]];
@@ -701,7 +702,11 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs& a, int unit, int s
   __syncthreads();
   if constexpr (GPL <= 4) {
     if (wave_merge) {
-      if (wave == 0) merge_in_wave<D, GQA, GPL, kFirst>(a, unit, split, S, nn, slot0, red, wml, sm, sl, lg, qf, fn);
+      // unrolled over NS split slots: the smallest instance that holds S
+      if (wave == 0) {
+        if (S <= 4) merge_in_wave<D, GQA, GPL, 4, kFirst>(a, unit, split, S, nn, slot0, red, wml, sm, sl, lg, qf, fn);
+        else merge_in_wave<D, GQA, GPL, kWaveMergeSplits, kFirst>(a, unit, split, S, nn, slot0, red, wml, sm, sl, lg, qf, fn);
+      }
       return;
     }
   }
@@ -750,11 +755,12 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs& a, int unit, int s
   // ---- the last workgroup of the unit: merge ----
   // Every load of the merge goes out together: the first batch of partials,
   // the split maxima and sums, and the appended tokens' keys and values.
-  // Only the splits that exist are read; with at most two partials per
+  // Only the splits that exist are read; with at most four partials per
   // thread a short path does it (the unrolled batch's skipped slots and its
   // longer code cost about half a microsecond on this serial tail).
+  constexpr int kFew = 4;
   float4 v[kMergeBatch];
-  const bool few = S <= 2 * NSG;
+  const bool few = S <= kFew * NSG;
   const bool in_wave = S * GQA <= kWave;                    // every split's (m, l) in one wave
   auto load_batch = [&](int j0) {
 #pragma unroll
@@ -766,7 +772,7 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs& a, int unit, int s
   if (S > 1) {
     if (few) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < kFew; ++j) {
         const int sk = sgi + NSG * j;
         if (sk < S) v[j] = load_agent4(rp, (sk * sstride + h * RS + c0) * 4);
       }
@@ -874,7 +880,7 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs& a, int unit, int s
   float4 num = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   if (few) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < kFew; ++j) {
       const int sk = sgi + NSG * j;
       if (sk < S) num = f4_fma(v[j], sm[sk][h], num);
     }
