@@ -47,13 +47,13 @@ HBM_PEAK_GBS = 8000.0
 # write (FETCH_SIZE x 2, WRITE_SIZE x 1).  Each describes the kernels named
 # in profiles/ and is None while those kernels have changed since the
 # counters were taken.
-DECODE_CALL_TRAFFIC = 39_721_160     # decode_i8_kernel, 4096-token Llama-3-8B shape (algorithmic 37.78 MB)
-LONG_CALL_TRAFFIC = 140_313_696      # one 131072-token layer (algorithmic 138.8 MB)
+DECODE_CALL_TRAFFIC = 39_638_179     # decode_i8_kernel, 4096-token Llama-3-8B shape (algorithmic 37.78 MB)
+LONG_CALL_TRAFFIC = 140_358_073      # one 131072-token layer (algorithmic 138.8 MB)
 # 128 appends (16 flushes + 128 window copies) and one block-attention call
 # (block_kernel + block_merge_kernel).
 APPEND_RUN_TRAFFIC = {4: 444_055_424, 8: 479_014_967}
 BLOCK_CALL_TRAFFIC = 2_067_551_539    # the cache is streamed once per query-row tile
-PAGED_CALL_TRAFFIC = 43_810_154      # paged decode, ragged lengths (algorithmic 41.42 MB)
+PAGED_CALL_TRAFFIC = 43_744_240      # paged decode, ragged lengths (algorithmic 41.42 MB)
 PAGED_BLOCK_CALL_TRAFFIC = 2_180_594_893  # the video block over a paged cache
 
 
