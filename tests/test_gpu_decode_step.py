@@ -13,7 +13,7 @@ import torch
 
 import kvq_synth as ks
 import quantized_kv_cache_kvq_amd as kvq
-from harness import Pair, max_abs, note
+from harness import Pair, f32, max_abs, note
 
 pytestmark = pytest.mark.gpu
 needs_gpu = pytest.mark.skipif(not torch.cuda.is_available(), reason="no GPU")
@@ -122,3 +122,61 @@ def test_decode_step_errors_leave_state_unchanged():
     torch.cuda.synchronize()
     assert (c.state.quantized, c.state.tail, c.state.total) == before
     p.check_buffers()
+
+
+@needs_gpu
+def test_decode_steps_captured_in_one_graph():
+    """Twelve decode steps, one of them through a 128-token flush, captured in
+    one HIP graph and replayed once: every output and the final cache bytes
+    equal those of the same steps run eagerly (bit for bit), and the cache
+    matches the oracle's."""
+    w = ks.small(ks.LLAMA3_DECODE, batch=2, kv_heads=2, q_heads=8)
+    steps = 12
+    pairs = []
+    for _ in range(2):
+        p = Pair(w, 512)
+        s = ks.Stream(w, seed=77)
+        k, v = ks.kv_pair(s, 380)          # window of 252 tokens: the fourth step flushes
+        p.append(k, v)
+        pairs.append(p)
+    s = ks.Stream(w, seed=78)
+    inputs = []
+    for _ in range(steps):
+        k, v = ks.kv_pair(s, 1)
+        inputs.append((k, v, ks.decode_query(s)))
+    dev = [(k.cuda(), v.cuda(), q.cuda()) for k, v, q in inputs]
+    shape = (w.batch, w.q_heads, w.head_dim)
+    # eager
+    pe = pairs[0]
+    ws_e = pe.cache.workspace(w.q_heads, 1)
+    outs_e = [torch.full(shape, float("nan"), device="cuda") for _ in range(steps)]
+    for (k, v, q), out in zip(dev, outs_e):
+        pe.cache.decode_step(k, v, q, out, ws_e)
+    # captured, then replayed once
+    pg = pairs[1]
+    ws_g = pg.cache.workspace(w.q_heads, 1)
+    outs_g = [torch.full(shape, float("nan"), device="cuda") for _ in range(steps)]
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    note("decode steps graph capture")
+    flushed = 0
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(graph, stream=cap):
+            for (k, v, q), out in zip(dev, outs_g):
+                pg.cache.decode_step(k, v, q, out, ws_g, stream=cap)
+                flushed += pg.cache.state.flushed_last
+    torch.cuda.current_stream().wait_stream(cap)
+    assert flushed == 128
+    graph.replay()
+    torch.cuda.synchronize()
+    for i in range(steps):
+        assert torch.equal(outs_g[i], outs_e[i]), i
+    for name in ("k_codes", "v_codes", "k_scale", "v_scale", "k_tail", "v_tail"):
+        assert torch.equal(getattr(pg.cache, name), getattr(pe.cache, name)), name
+    for k, v, _ in inputs:
+        pg.ost = pg.oracle.append_and_partition(pg.ost, f32(k), f32(v), w.residual)
+    pg.check_state()
+    pg.check_buffers()
+    assert max_abs(outs_g[-1].cpu().numpy(), pg.decode_ref(inputs[-1][2])) <= TOL
