@@ -1166,8 +1166,8 @@ def run_hbm_read(args, log):
 
 def run_mfma_peak(args, log):
     """Matrix-core throughput of the probe loop (eight independent chains per
-    wave, register operands), per instruction kind, at two and four waves per
-    SIMD."""
+    wave, register operands), per instruction kind, at one, two and four waves
+    per SIMD."""
     import torch
 
     from quantized_kv_cache_kvq_amd import probes
@@ -1178,7 +1178,7 @@ def run_mfma_peak(args, log):
     iters = 4000
     res = {}
     for kind, (name, ops) in probes.MFMA_KINDS.items():
-        for wgs in (512, 1024):
+        for wgs in (256, 512, 1024):
             for _ in range(2):
                 probes.mfma(kind, wgs, iters, sink)
             torch.cuda.synchronize()

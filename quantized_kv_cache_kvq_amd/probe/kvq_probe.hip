@@ -54,6 +54,7 @@ typedef __bf16 bf8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
 typedef float f4_t __attribute__((ext_vector_type(4)));
 typedef int i4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 // Eight independent accumulator chains per wave, operands in registers
 // (derived from the lane id so that nothing is constant-folded).
@@ -77,6 +78,31 @@ __global__ __launch_bounds__(kThreads) void mfma_kernel(int iters, uint32_t* sin
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) fold ^= (uint32_t)(acc[j][0] ^ acc[j][1] ^ acc[j][2] ^ acc[j][3]);
+  } else if constexpr (KIND == 3 || KIND == 4) {
+    // 32x32x16: sixteen accumulator registers per chain
+    f32x16_t acc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      acc[j] = f32x16_t{};
+      acc[j][0] = (float)j;
+    }
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if constexpr (KIND == 3)
+          acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf8_t, u),
+                                                           __builtin_bit_cast(bf8_t, make_uint4(w[3], w[2], w[1], w[0])),
+                                                           acc[j], 0, 0, 0);
+        else
+          acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(h8_t, u),
+                                                          __builtin_bit_cast(h8_t, make_uint4(w[3], w[2], w[1], w[0])),
+                                                          acc[j], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) fold ^= __float_as_uint(acc[j][e]);
   } else {
     f4_t acc[8];
 #pragma unroll
@@ -148,6 +174,8 @@ extern "C" int kvq_probe_mfma(int32_t kind, int32_t workgroups, int32_t iters, u
     case 0: hipLaunchKernelGGL(mfma_kernel<0>, grid, block, 0, s, iters, sink); break;
     case 1: hipLaunchKernelGGL(mfma_kernel<1>, grid, block, 0, s, iters, sink); break;
     case 2: hipLaunchKernelGGL(mfma_kernel<2>, grid, block, 0, s, iters, sink); break;
+    case 3: hipLaunchKernelGGL(mfma_kernel<3>, grid, block, 0, s, iters, sink); break;
+    case 4: hipLaunchKernelGGL(mfma_kernel<4>, grid, block, 0, s, iters, sink); break;
     default: return 1;
   }
   return launch_status();

@@ -13,7 +13,8 @@ EXPORTED = ("kvq_probe_stream_read", "kvq_probe_mfma", "kvq_probe_empty")
 
 # flops (or integer ops) of one matrix instruction of each kind
 MFMA_KINDS = {0: ("v_mfma_f32_16x16x32_bf16", 16384), 1: ("v_mfma_f32_16x16x32_f16", 16384),
-              2: ("v_mfma_i32_16x16x64_i8", 32768)}
+              2: ("v_mfma_i32_16x16x64_i8", 32768), 3: ("v_mfma_f32_32x32x16_bf16", 32768),
+              4: ("v_mfma_f32_32x32x16_f16", 32768)}
 
 _lib: Optional[ctypes.CDLL] = None
 
