@@ -15,7 +15,9 @@
 // wave keeps one online-softmax state per query head (m, l, acc) in the log2
 // domain.  The workgroup folds its waves into one partial; the last
 // workgroup of each (batch, KV head) to finish merges the partials (see
-// finish_unit), or, above 64 splits, a second, small kernel does.  With a
+// finish_unit; with up to eight splits and at most one appended token its
+// wave 0 does the fold, the publication and the merge alone, see
+// merge_in_wave), or, above 64 splits, a second, small kernel does.  With a
 // single split the workgroup writes the output itself.  No device-scope
 // fence is used: on gfx950 one costs a whole-L2 writeback and invalidate
 // per workgroup.
