@@ -63,7 +63,7 @@ def test_decode_step_llama_shape_across_a_flush():
 
 
 @needs_gpu
-@pytest.mark.parametrize("n_new,num_splits", [(3, 0), (1, 1), (16, 2), (5, 7)])
+@pytest.mark.parametrize("n_new,num_splits", [(3, 0), (1, 1), (16, 2), (5, 7), (1, 6)])
 def test_decode_step_token_counts_and_splits(n_new, num_splits):
     w = ks.small(ks.LLAMA3_DECODE, batch=1, kv_heads=2, q_heads=8)
     note(f"decode step n_new={n_new} splits={num_splits}")
@@ -75,7 +75,7 @@ def test_decode_step_token_counts_and_splits(n_new, num_splits):
 
 
 @needs_gpu
-@pytest.mark.parametrize("D,bits,qmax,gqa", [(64, 8, 127, 2), (128, 2, 1, 1), (64, 4, 7, 8)])
+@pytest.mark.parametrize("D,bits,qmax,gqa", [(64, 8, 127, 2), (128, 2, 1, 1), (64, 4, 7, 8), (128, 4, 7, 8)])
 def test_decode_step_other_shapes(D, bits, qmax, gqa):
     w = ks.small(ks.LLAMA3_DECODE, batch=2, kv_heads=2, q_heads=2 * gqa, head_dim=D, code_bits=bits,
                  qmax=qmax)
